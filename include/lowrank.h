@@ -1,0 +1,174 @@
+/*
+ * lowrank.h -- C ABI of the low-rank decomposed hot path on AMD MI355X (gfx950).
+ *
+ * Citation key: "DeInfer/en" is the English technical summary page of
+ * "DeInfer: Efficient Parallel Inferencing for Decomposed Large Language
+ * Models" (gist.science); "DeInfer/es" is the Spanish page ("Resumen
+ * Técnico"), "DeInfer/zh" the Chinese page.
+ *
+ * A dense weight W[d_in, d_out] is replaced by two smaller matrices (W ~ A B,
+ * DeInfer/en §1).  The layer applies the downward projection into rank space
+ * and then the upward projection (DeInfer/en §2.A):
+ *
+ *     t = x . U_r        (U_r: [d_in, r])      stage 1
+ *     y = t . V_r        (V_r: [r, d_out])     stage 2
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     device memory, keeps no pointer after returning, and holds no global
+ *     state except immutable device properties.
+ *   - Asynchrony: work is enqueued on `stream` and never synchronised; every
+ *     call may be captured into a HIP graph (no memset/memcpy nodes, no host
+ *     reads of device data).  Calls are reentrant; two calls in flight must
+ *     not share a workspace.
+ *   - Errors: every call returns lr_status.  LR_OK means the work was
+ *     enqueued.  Any other value is returned by host-side argument checks and
+ *     means nothing was enqueued -- except LR_ERR_HIP, reported when the HIP
+ *     runtime rejects a launch (earlier launches of that call may have been
+ *     enqueued).  The library never aborts.
+ *   - Device data cannot be checked from the host without breaking graph
+ *     capture, so kernels defend themselves: out-of-range remap entries give
+ *     zero rows and device counts are clamped to their capacity.
+ *   - Layout: row-major 2-D arrays with explicit leading dimensions (in
+ *     elements).  The factors are stored transposed, one output's weights
+ *     contiguous along the reduction axis:
+ *         Ut = U_r^T  as [r, d_in]    with ldu >= d_in
+ *         Vt = V_r^T  as [d_out, r]   with ldv >= r
+ *     so a tensor-parallel share (U_r split by input rows, V_r split by output
+ *     columns) is a plain sub-matrix: Ut + row0 with the full ldu, and
+ *     Vt + col0 * ldv.
+ *   - bf16 operands: pointers 16-byte aligned and leading dimensions a
+ *     multiple of 8 elements (LR_ERR_ALIGN otherwise).  fp32 operands: 4-byte
+ *     aligned, any leading dimension.
+ */
+#ifndef LOWRANK_H
+#define LOWRANK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  LR_OK = 0,
+  LR_ERR_ARG = 1,         /* null pointer, non-positive size, ld < width, bad flag */
+  LR_ERR_DTYPE = 2,       /* dtype not supported by this entry point */
+  LR_ERR_ALIGN = 3,       /* vectorised operand misaligned or ld not a multiple of 8 */
+  LR_ERR_WORKSPACE = 4,   /* workspace missing or smaller than lowrank_workspace_bytes */
+  LR_ERR_CAPACITY = 5,    /* packed rows exceed the fixed capacity */
+  LR_ERR_HIP = 6,         /* the HIP runtime rejected a launch */
+  LR_ERR_UNSUPPORTED = 7  /* valid request outside what this build implements */
+} lr_status;
+
+typedef enum { LR_F32 = 0, LR_BF16 = 1 } lr_dtype;
+
+/* flags of lowrank_linear_forward */
+enum {
+  LR_FULL = 0,         /* y = (x U_r) V_r; t_io written too when non-NULL          */
+  LR_STAGE1_ONLY = 1,  /* t_io = x U_r (t_io required; Vt, y unused)              */
+  LR_STAGE2_ONLY = 2   /* y = t_io V_r (t_io read; x, Ut unused)                   */
+};
+
+/*
+ * lowrank_linear_forward -- the decomposed linear, DeInfer/en §2.A (downward
+ * projection, then upward projection), DeInfer/es §2 "Comunicación de Bajo
+ * Rango Eficiente".  With LR_STAGE1_ONLY on one tensor-parallel share (x and
+ * Ut restricted to the share's input rows) it forms the partial rank-r
+ * intermediate that the shares would exchange in rank space; LR_STAGE2_ONLY on
+ * an output-column shard of V_r is the pages' "shard mode" upward projection.
+ *
+ *   dt       LR_F32: x, Ut, Vt, y are float; LR_BF16: they are bfloat16.
+ *            Accumulation is fp32 in both cases; bf16 outputs are rounded to
+ *            nearest even.
+ *   T        number of token rows (>= 1).  T <= 64 runs the decode path
+ *            (weights streamed once from HBM); larger T runs the prefill path
+ *            (fused two-stage MFMA kernel, the rank-r tile kept on chip).
+ *   x        [T, d_in], ldx        (stage 1 input)
+ *   Ut       [r, d_in], ldu        (U_r transposed)
+ *   Vt       [d_out, r], ldv       (V_r transposed)
+ *   y        [T, d_out], ldy       (output of LR_FULL / LR_STAGE2_ONLY)
+ *   t_io     float [T, r], ldt     optional for LR_FULL (written), required
+ *            for the stage-only flags (written by stage 1, read by stage 2).
+ *   workspace, workspace_bytes
+ *            device scratch of at least
+ *            lowrank_workspace_bytes(0, dt, T, d_in, r, d_out, 0) bytes,
+ *            256-byte aligned; NULL allowed when that size is 0.
+ */
+lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in, int64_t r, int64_t d_out,
+                                 const void* x, int64_t ldx, const void* Ut, int64_t ldu,
+                                 const void* Vt, int64_t ldv, void* y, int64_t ldy,
+                                 float* t_io, int64_t ldt, unsigned flags, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kv_remap_gather -- the graph-replay copy of DeInfer/en §2.C (and DeInfer/es
+ * §2, "Etapa de Reproducción del Gráfico"): rows of a paged pool are copied
+ * into a compact buffer at a fixed address, following the remapping index
+ * list built by the preparation stage.
+ *
+ *   for j < min(*n_valid, cap) (or j < cap when n_valid is NULL):
+ *       dst[j, 0:row_elems] = src[remap[j], 0:row_elems]  if 0 <= remap[j] < src_rows
+ *                           = 0                           otherwise
+ *   rows j >= *n_valid are left untouched.  Bit-exact copy.
+ *
+ *   dt        element type (LR_BF16 or LR_F32); only the width matters.
+ *   src       device [src_rows, src_ld]
+ *   remap     device int32 [cap]
+ *   n_valid   device int32 scalar or NULL; read by the kernel, so it may
+ *             change between replays of a captured graph.
+ *   dst       device [cap, dst_ld]
+ *   Vector path when both row pitches and pointers are 16-byte aligned;
+ *   otherwise a 2-byte/4-byte path (never an error).
+ */
+lr_status kv_remap_gather(lr_dtype dt, const void* src, int64_t src_rows, int64_t src_ld,
+                          const int32_t* remap, int64_t cap, const int32_t* n_valid,
+                          int64_t row_elems, void* dst, int64_t dst_ld, hipStream_t stream);
+
+/*
+ * lowrank_prepare_decode -- host-side preparation stage of DeInfer/en §2.C
+ * ("scan the paged memory for physically contiguous blocks ... remapping
+ * index list"), DeInfer/zh (remapping table), DeInfer/es §2 "Etapa de
+ * Preparación".  Runs on the CPU, touches host memory only.
+ *
+ * Sequence i has lengths[i] cached tokens and decodes one new token at
+ * position lengths[i]; its compact segment holds lengths[i] + 1 rows.
+ * Logical row p of sequence i lives at physical row
+ * tables[i * table_ld + p / block] * block + p % block.
+ *
+ * Outputs (host arrays supplied by the caller):
+ *   remap[cap]        physical source row of each packed row; -1 past n_valid
+ *   seq_off[B + 1]    prefix sums of lengths[i] + 1
+ *   pos[B]            position of each new token (= lengths[i])
+ *   slot_mapping[B]   physical row the new token's latents are written to
+ *   *n_valid          seq_off[B]
+ *   *n_runs           number of maximal runs of physically consecutive blocks
+ *   runs              optional int32 [max_runs, 3] of (src_row, dst_row, rows)
+ * Errors: LR_ERR_ARG (null/negative, a block index < 0 or a table too short
+ * for lengths[i] + 1 rows), LR_ERR_CAPACITY (seq_off[B] > cap, or more runs
+ * than max_runs when runs is non-NULL).
+ */
+lr_status lowrank_prepare_decode(int64_t B, const int32_t* lengths, const int32_t* tables,
+                                 int64_t table_ld, int64_t block, int64_t cap, int32_t* remap,
+                                 int32_t* seq_off, int32_t* pos, int32_t* slot_mapping,
+                                 int32_t* n_valid, int32_t* n_runs, int32_t* runs,
+                                 int64_t max_runs);
+
+/* Device scratch needed by an entry point.  which = 0: lowrank_linear_forward
+ * (T_or_B = T, cap unused); which = 1: lowrank_layer_decode_step. */
+size_t lowrank_workspace_bytes(int which, lr_dtype dt, int64_t T_or_B, int64_t d_in, int64_t r,
+                               int64_t d_out, int64_t cap);
+
+const char* lowrank_status_string(lr_status s);
+
+/* Library ABI version (major * 100 + minor). */
+int lowrank_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWRANK_H */

@@ -1,0 +1,156 @@
+"""rank_decomposed_amd -- the low-rank decomposed hot path on AMD MI355X.
+
+Python binding of liblowrank.so with the C ABI's names.  The functions only
+marshal arguments (shapes, leading dimensions, pointers, the current HIP
+stream) from PyTorch tensors; every step of the computation runs in the
+library's HIP kernels (or, for the preparation stage, its host C++ code).
+PyTorch provides device memory and streams.
+
+Layout reminder (include/lowrank.h): x [T, d_in], Ut = U_r^T [r, d_in],
+Vt = V_r^T [d_out, r], y [T, d_out], t [T, r] fp32; row-major with explicit
+leading dimensions, so tensor-parallel shares are plain slices
+(``Ut[:, rows]``, ``Vt[cols, :]``).
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import _lib
+from ._lib import (LR_BF16, LR_F32, LR_FULL, LR_STAGE1_ONLY, LR_STAGE2_ONLY, LowrankError,
+                   load, status_string)
+
+__all__ = [
+    "lowrank_linear_forward", "kv_remap_gather", "lowrank_prepare_decode",
+    "lowrank_workspace_bytes", "lowrank_status_string", "lowrank_version",
+    "LR_F32", "LR_BF16", "LR_FULL", "LR_STAGE1_ONLY", "LR_STAGE2_ONLY", "LowrankError", "load",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LR_BF16
+    if t.dtype == torch.float32:
+        return LR_F32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return int(t.stride(0)) if t.shape[0] > 1 else max(int(t.stride(0)), int(t.shape[1]))
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return C.c_void_p(s.cuda_stream)
+
+
+def lowrank_workspace_bytes(which: int, dtype: int, T_or_B: int, d_in: int, r: int,
+                            d_out: int = 0, cap: int = 0) -> int:
+    return int(load().lowrank_workspace_bytes(which, dtype, T_or_B, d_in, r, d_out, cap))
+
+
+def lowrank_status_string(s: int) -> str:
+    return status_string(s)
+
+
+def lowrank_version() -> int:
+    return int(load().lowrank_version())
+
+
+def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, workspace=None,
+                           stream=None):
+    """y = (x U_r) V_r (or one stage of it, see lowrank.h).  Tensors on one
+    HIP device; Ut = U_r^T [r, d_in], Vt = V_r^T [d_out, r]; t_io fp32 [T, r].
+    Returns y (allocated when not given and a stage 2 runs)."""
+    torch = _torch()
+    lib = load()
+    ref = x if x is not None else t_io
+    dev = ref.device
+    if flags == LR_STAGE2_ONLY:
+        T, r = t_io.shape
+        d_in = int(Ut.shape[1]) if Ut is not None else 1
+        dt = _dtype_code(Vt)
+    else:
+        T, d_in = x.shape
+        r = int(Ut.shape[0])
+        dt = _dtype_code(x)
+    d_out = int(Vt.shape[0]) if Vt is not None else 1
+    if y is None and flags != LR_STAGE1_ONLY:
+        y = torch.empty((T, d_out), dtype=Vt.dtype, device=dev)
+    need = lowrank_workspace_bytes(0, dt, T, d_in, r, d_out)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.lowrank_linear_forward(
+        dt, T, d_in, r, d_out,
+        _ptr(x), _ld(x) if x is not None else 0,
+        _ptr(Ut), _ld(Ut) if Ut is not None else 0,
+        _ptr(Vt), _ld(Vt) if Vt is not None else 0,
+        _ptr(y), _ld(y) if y is not None else 0,
+        _ptr(t_io), _ld(t_io) if t_io is not None else 0,
+        flags, _ptr(workspace), ws_bytes, _stream(stream, dev))
+    _lib.check(st, "lowrank_linear_forward")
+    return y
+
+
+def kv_remap_gather(src, remap, dst, n_valid=None, row_elems=None, stream=None):
+    """dst[j] = src[remap[j]] (zero row for invalid indices) for j < n_valid
+    (device int32 scalar tensor, or all rows of remap when None)."""
+    lib = load()
+    re = int(row_elems if row_elems is not None else src.shape[1])
+    st = lib.kv_remap_gather(_dtype_code(src), _ptr(src), int(src.shape[0]), _ld(src),
+                             _ptr(remap), int(remap.numel()), _ptr(n_valid), re, _ptr(dst),
+                             _ld(dst), _stream(stream, src.device))
+    _lib.check(st, "kv_remap_gather")
+    return dst
+
+
+def lowrank_prepare_decode(lengths, tables, block: int, cap: int, want_runs: bool = False):
+    """Host preparation stage: returns a dict of numpy int32 arrays remap[cap],
+    seq_off[B+1], pos[B], slot_mapping[B] and ints n_valid, n_runs (plus
+    runs[n_runs, 3] when want_runs)."""
+    lib = load()
+    lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+    B = lengths.shape[0]
+    if isinstance(tables, np.ndarray) and tables.ndim == 2:
+        tab = np.ascontiguousarray(tables, dtype=np.int32)
+    else:
+        width = max((len(t) for t in tables), default=1)
+        tab = np.full((B, max(width, 1)), -1, dtype=np.int32)
+        for i, t in enumerate(tables):
+            tab[i, :len(t)] = t
+    remap = np.empty(cap, np.int32)
+    seq_off = np.empty(B + 1, np.int32)
+    pos = np.empty(max(B, 1), np.int32)
+    slots = np.empty(max(B, 1), np.int32)
+    nv = np.zeros(1, np.int32)
+    nr = np.zeros(1, np.int32)
+    max_runs = int(tab.size) if want_runs else 0
+    runs = np.empty((max(max_runs, 1), 3), np.int32)
+
+    def P(a):
+        return a.ctypes.data_as(C.c_void_p)
+
+    st = lib.lowrank_prepare_decode(B, P(lengths), P(tab), tab.shape[1], block, cap, P(remap),
+                                    P(seq_off), P(pos), P(slots), P(nv), P(nr),
+                                    P(runs) if want_runs else None, max_runs)
+    _lib.check(st, "lowrank_prepare_decode")
+    out = {"remap": remap, "seq_off": seq_off, "pos": pos[:B], "slot_mapping": slots[:B],
+           "n_valid": int(nv[0]), "n_runs": int(nr[0])}
+    if want_runs:
+        out["runs"] = runs[:out["n_runs"]].copy()
+    return out

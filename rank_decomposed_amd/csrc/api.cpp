@@ -1,0 +1,103 @@
+// C ABI of liblowrank: host-side argument checks and path selection.  No
+// allocation, no synchronisation, no global mutable state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lowrank.h"
+#include "lr_kernels.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" int lowrank_version(void) { return 100; }
+
+extern "C" const char* lowrank_status_string(lr_status s) {
+  switch (s) {
+    case LR_OK: return "ok";
+    case LR_ERR_ARG: return "invalid argument";
+    case LR_ERR_DTYPE: return "unsupported dtype";
+    case LR_ERR_ALIGN: return "misaligned operand or leading dimension";
+    case LR_ERR_WORKSPACE: return "workspace missing or too small";
+    case LR_ERR_CAPACITY: return "capacity exceeded";
+    case LR_ERR_HIP: return "HIP runtime error";
+    case LR_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+static size_t linear_ws(lr_dtype dt, int64_t T, int64_t d_in, int64_t r) {
+  if (dt == LR_F32) return lr::f32_workspace_bytes(T, r);
+  if (T <= 64) return lr::decode_workspace_bytes(T, d_in, r);
+  return lr::prefill_workspace_bytes(T, r);
+}
+
+extern "C" size_t lowrank_workspace_bytes(int which, lr_dtype dt, int64_t T_or_B, int64_t d_in,
+                                          int64_t r, int64_t d_out, int64_t cap) {
+  (void)d_out;
+  (void)cap;
+  if (T_or_B <= 0 || d_in <= 0 || r <= 0) return 0;
+  if (which == 0) {
+    if (dt != LR_F32 && dt != LR_BF16) return 0;
+    return linear_ws(dt, T_or_B, d_in, r);
+  }
+  return 0;
+}
+
+extern "C" lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in, int64_t r,
+                                            int64_t d_out, const void* x, int64_t ldx,
+                                            const void* Ut, int64_t ldu, const void* Vt,
+                                            int64_t ldv, void* y, int64_t ldy, float* t_io,
+                                            int64_t ldt, unsigned flags, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  if (dt != LR_F32 && dt != LR_BF16) return LR_ERR_DTYPE;
+  if (flags > 2) return LR_ERR_ARG;
+  if (T <= 0 || d_in <= 0 || r <= 0 || d_out <= 0) return LR_ERR_ARG;
+  if (T > INT32_MAX || d_in > INT32_MAX || r > INT32_MAX || d_out > INT32_MAX) return LR_ERR_ARG;
+  const bool s1 = flags != LR_STAGE2_ONLY, s2 = flags != LR_STAGE1_ONLY;
+  if (s1 && (!x || !Ut || ldx < d_in || ldu < d_in)) return LR_ERR_ARG;
+  if (s2 && (!Vt || !y || ldv < r || ldy < d_out)) return LR_ERR_ARG;
+  if (flags != LR_FULL && !t_io) return LR_ERR_ARG;
+  if (t_io && ldt < r) return LR_ERR_ARG;
+  if (t_io && !aligned(t_io, 4)) return LR_ERR_ALIGN;
+  if (dt == LR_BF16) {
+    if (s1 && (!aligned(x, 16) || !aligned(Ut, 16) || ldx % 8 || ldu % 8)) return LR_ERR_ALIGN;
+    if (s2 && (!aligned(Vt, 16) || ldv % 8 || !aligned(y, 2))) return LR_ERR_ALIGN;
+  } else {
+    if (s1 && (!aligned(x, 4) || !aligned(Ut, 4))) return LR_ERR_ALIGN;
+    if (s2 && (!aligned(Vt, 4) || !aligned(y, 4))) return LR_ERR_ALIGN;
+  }
+  const size_t need = linear_ws(dt, T, d_in, r);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return LR_ERR_WORKSPACE;
+
+  lr::DecodeLinear d{T, d_in, r, d_out, x, ldx, Ut, ldu, Vt, ldv, y, ldy, t_io, ldt, flags,
+                     workspace};
+  hipError_t e;
+  if (dt == LR_F32)
+    e = lr::linear_f32(d, stream);
+  else if (T <= 64)
+    e = lr::decode_linear_bf16(d, stream);
+  else
+    e = lr::prefill_linear_bf16(d, stream);
+  return e == hipSuccess ? LR_OK : LR_ERR_HIP;
+}
+
+extern "C" lr_status kv_remap_gather(lr_dtype dt, const void* src, int64_t src_rows,
+                                     int64_t src_ld, const int32_t* remap, int64_t cap,
+                                     const int32_t* n_valid, int64_t row_elems, void* dst,
+                                     int64_t dst_ld, hipStream_t stream) {
+  if (dt != LR_F32 && dt != LR_BF16) return LR_ERR_DTYPE;
+  const int eb = dt == LR_F32 ? 4 : 2;
+  if (!src || !remap || !dst) return LR_ERR_ARG;
+  if (src_rows <= 0 || cap <= 0 || row_elems <= 0) return LR_ERR_ARG;
+  if (src_ld < row_elems || dst_ld < row_elems) return LR_ERR_ARG;
+  if (cap > INT32_MAX) return LR_ERR_ARG;
+  if (!aligned(src, eb) || !aligned(dst, eb) || !aligned(remap, 4)) return LR_ERR_ALIGN;
+  if (n_valid && !aligned(n_valid, 4)) return LR_ERR_ALIGN;
+  hipError_t e = lr::remap_gather(eb, src, src_rows, src_ld, remap, cap, n_valid, row_elems, dst,
+                                  dst_ld, stream);
+  return e == hipSuccess ? LR_OK : LR_ERR_HIP;
+}

@@ -1,0 +1,448 @@
+// Prefill path of the decomposed linear (many token rows, MFMA-bound).
+//
+// DeInfer/en §2.A: t = x U_r (downward projection), y = t V_r (upward
+// projection).  For T > 64 both contractions are dense bf16 GEMMs.
+//
+// Fused kernel: a workgroup owns BM = 64 token rows.  Stage 1 computes the
+// whole rank-r tile t[64, r] chunk by chunk on MFMA 16x16x32 and parks it in
+// LDS as bf16 (round to nearest even); stage 2 reads it straight from LDS as
+// the A operand of y = t V_r.  t never touches HBM.  Every workgroup streams
+// all of U_r and V_r, so the kernel's intensity against L2 is BM flop per
+// weight byte; the weights stay L2/MALL-resident while the 256 CUs walk them
+// in the same order.
+//
+// Wave layout: the 4 waves share the 64 rows (4 row blocks of 16) and split
+// each 512-wide column chunk into 4 x 128 (8 column blocks of 16 per wave).
+// Per 32-wide k-step a wave issues 32 MFMAs on 4 A fragments (LDS) and 8 B
+// fragments (weights, global -> VGPR, prefetched one step ahead).
+//
+// Plain kernel: C = A . B^T on a 128x128 tile with LDS double buffering, for
+// the stage-only calls (tensor-parallel share) and for ranks too large for the
+// on-chip tile.
+#include "lr_common.h"
+#include "lr_kernels.h"
+
+namespace lr {
+
+namespace {
+
+constexpr int kBM = 64;         // fused: token rows per workgroup
+constexpr int kNB = 8;          // fused: 16-wide column blocks per wave
+constexpr int kChunk = 4 * kNB * 16;  // 512 columns per chunk
+constexpr int kXPitch = 40;     // fused: x staging row pitch (elements)
+constexpr int kLdsMax = 163840; // gfx950 LDS per workgroup
+
+__device__ __forceinline__ u32x4 lds16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+struct FusedArgs {
+  const uint16_t* x;
+  int64_t ldx;
+  const uint16_t* ut;
+  int64_t ldu;
+  const uint16_t* vt;
+  int64_t ldv;
+  uint16_t* y;
+  int64_t ldy;
+  int M, d_in, r, d_out;
+  int r_pad;  // multiple of 32
+};
+
+// One 32-wide k-step of a 64 x 128 wave tile: acc[mb][nb] += A[mb] . B[nb]^T
+__device__ __forceinline__ void wave_step(f32x4 (&acc)[4][kNB], const u32x4 (&a)[4],
+                                          const u32x4 (&b)[kNB]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = mfma16x16x32(a[mb], b[nb], acc[mb][nb]);
+}
+
+// B fragments of one k-step: rows row0 + nb*16 + (lane & 15), k .. k+7.
+__device__ __forceinline__ void load_b(u32x4 (&b)[kNB], const uint16_t* base, int64_t ld,
+                                       int row0, int nrows, int k, int kmax, int lane) {
+  const int rr = lane & 15;
+  const int kk = k + (lane >> 4) * 8;
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int row = row0 + nb * 16 + rr;
+    if (row < nrows && kk < kmax) {
+      u32x4 v = ldg16(base + (int64_t)row * ld + kk);
+      b[nb] = (kk + 8 > kmax) ? mask_tail(v, kk, kmax) : v;
+    } else {
+      b[nb] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+template <bool XLDS>
+__global__ __launch_bounds__(256, 1) void fused_kernel(FusedArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int tpitch = p.r_pad + 8;
+  uint16_t* ts = smem;                          // [64][tpitch]
+  uint16_t* xs = smem + kBM * tpitch;           // [2][64][kXPitch] when XLDS
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * kBM;
+  const int rr = lane & 15;
+  const int kq = (lane >> 4) * 8;
+
+  // ---------------- stage 1: ts = bf16(x[m0:m0+64] . U_r) ----------------
+  // x rows of this lane's A fragments (global path)
+  const int ksteps1 = (p.d_in + 31) / 32;
+  for (int c0 = 0; c0 < p.r_pad; c0 += kChunk) {
+    f32x4 acc[4][kNB];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int row0 = c0 + wave * (kNB * 16);
+    const bool active = row0 < p.r_pad;
+
+    u32x4 bcur[kNB], bnxt[kNB];
+    if (active) load_b(bcur, p.ut, p.ldu, row0, p.r, 0, p.d_in, lane);
+
+    // x staging: thread t moves row t/4, k-chunk (t%4)*8 of each 32-wide step
+    const int xrow = threadIdx.x >> 2, xk = (threadIdx.x & 3) * 8;
+    const bool xrow_ok = (m0 + xrow) < p.M;
+    const uint16_t* xsrc = p.x + (int64_t)(xrow_ok ? m0 + xrow : 0) * p.ldx;
+    u32x4 xreg = u32x4{0, 0, 0, 0};
+    if (XLDS) {
+      if (xrow_ok && xk < p.d_in) {
+        xreg = ldg16(xsrc + xk);
+        if (xk + 8 > p.d_in) xreg = mask_tail(xreg, xk, p.d_in);
+      }
+      *reinterpret_cast<u32x4*>(xs + xrow * kXPitch + xk) = xreg;
+      __syncthreads();
+    }
+    for (int s = 0; s < ksteps1; ++s) {
+      const int k = s * 32;
+      const int buf = s & 1;
+      if (XLDS && s + 1 < ksteps1) {
+        const int kn = k + 32 + xk;
+        xreg = u32x4{0, 0, 0, 0};
+        if (xrow_ok && kn < p.d_in) {
+          xreg = ldg16(xsrc + kn);
+          if (kn + 8 > p.d_in) xreg = mask_tail(xreg, kn, p.d_in);
+        }
+      }
+      if (active && s + 1 < ksteps1) load_b(bnxt, p.ut, p.ldu, row0, p.r, k + 32, p.d_in, lane);
+      u32x4 a[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        if (XLDS) {
+          a[mb] = lds16(xs + buf * (kBM * kXPitch) + (mb * 16 + rr) * kXPitch + kq);
+        } else {
+          const int row = m0 + mb * 16 + rr;
+          const int kk = k + kq;
+          a[mb] = u32x4{0, 0, 0, 0};
+          if (row < p.M && kk < p.d_in) {
+            u32x4 v = ldg16(p.x + (int64_t)row * p.ldx + kk);
+            a[mb] = (kk + 8 > p.d_in) ? mask_tail(v, kk, p.d_in) : v;
+          }
+        }
+      }
+      if (active) wave_step(acc, a, bcur);
+      if (XLDS) {
+        if (s + 1 < ksteps1)
+          *reinterpret_cast<u32x4*>(xs + (buf ^ 1) * (kBM * kXPitch) + xrow * kXPitch + xk) = xreg;
+        __syncthreads();
+      }
+      if (active && s + 1 < ksteps1) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) bcur[nb] = bnxt[nb];
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const int col = row0 + nb * 16 + rr;
+          if (col < p.r_pad) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int tok = mb * 16 + (lane >> 4) * 4 + v;
+              ts[tok * tpitch + col] = (uint16_t)f2bf(acc[mb][nb][v]);
+            }
+          }
+        }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- stage 2: y[m0:m0+64] = ts . V_r ----------------
+  const int ksteps2 = p.r_pad / 32;
+  for (int c0 = 0; c0 < p.d_out; c0 += kChunk) {
+    const int row0 = c0 + wave * (kNB * 16);
+    if (row0 >= p.d_out) continue;
+    f32x4 acc[4][kNB];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 bcur[kNB], bnxt[kNB];
+    load_b(bcur, p.vt, p.ldv, row0, p.d_out, 0, p.r, lane);
+    for (int s = 0; s < ksteps2; ++s) {
+      const int k = s * 32;
+      if (s + 1 < ksteps2) load_b(bnxt, p.vt, p.ldv, row0, p.d_out, k + 32, p.r, lane);
+      u32x4 a[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) a[mb] = lds16(ts + (mb * 16 + rr) * tpitch + k + kq);
+      wave_step(acc, a, bcur);
+      if (s + 1 < ksteps2) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) bcur[nb] = bnxt[nb];
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int col = row0 + nb * 16 + rr;
+        if (col >= p.d_out) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tok = m0 + mb * 16 + (lane >> 4) * 4 + v;
+          if (tok < p.M) p.y[(int64_t)tok * p.ldy + col] = (uint16_t)f2bf(acc[mb][nb][v]);
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------ plain GEMM
+// C[M, N] = A[M, K] . B[N, K]^T ; A bf16 or fp32 (rounded to bf16 on load),
+// B bf16, C fp32 or bf16.
+constexpr int gBM = 128, gBN = 128, gBK = 32, gPitch = 40;
+
+struct GemmArgs {
+  const void* a;
+  int64_t lda;
+  const uint16_t* b;
+  int64_t ldb;
+  void* c;
+  int64_t ldc;
+  int M, N, K;
+};
+
+template <bool A_F32, bool C_F32>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][gBM * gPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][gBN * gPitch];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int m0 = blockIdx.y * gBM, n0 = blockIdx.x * gBN;
+  const int rr = lane & 15, kq = (lane >> 4) * 8;
+
+  // staging map: 512 chunks of 8 elements per tile; thread t takes t and t+256
+  auto load_a = [&](int k, u32x4 (&reg)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = threadIdx.x + i * 256;
+      const int row = ch >> 2, kk = k + (ch & 3) * 8;
+      const int grow = m0 + row;
+      reg[i] = u32x4{0, 0, 0, 0};
+      if (grow < p.M && kk < p.K) {
+        if (A_F32) {
+          const float* src = static_cast<const float*>(p.a) + (int64_t)grow * p.lda + kk;
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = (kk + e < p.K) ? src[e] : 0.f;
+          reg[i] = u32x4{pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]), pack_bf2(f[4], f[5]),
+                         pack_bf2(f[6], f[7])};
+        } else {
+          u32x4 v = ldg16(static_cast<const uint16_t*>(p.a) + (int64_t)grow * p.lda + kk);
+          reg[i] = (kk + 8 > p.K) ? mask_tail(v, kk, p.K) : v;
+        }
+      }
+    }
+  };
+  auto load_b = [&](int k, u32x4 (&reg)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = threadIdx.x + i * 256;
+      const int row = ch >> 2, kk = k + (ch & 3) * 8;
+      const int grow = n0 + row;
+      reg[i] = u32x4{0, 0, 0, 0};
+      if (grow < p.N && kk < p.K) {
+        u32x4 v = ldg16(p.b + (int64_t)grow * p.ldb + kk);
+        reg[i] = (kk + 8 > p.K) ? mask_tail(v, kk, p.K) : v;
+      }
+    }
+  };
+  auto store = [&](uint16_t* dst, const u32x4 (&reg)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = threadIdx.x + i * 256;
+      *reinterpret_cast<u32x4*>(dst + (ch >> 2) * gPitch + (ch & 3) * 8) = reg[i];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ksteps = (p.K + gBK - 1) / gBK;
+  u32x4 ra[2], rb[2];
+  load_a(0, ra);
+  load_b(0, rb);
+  store(As[0], ra);
+  store(Bs[0], rb);
+  __syncthreads();
+  for (int s = 0; s < ksteps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < ksteps) {
+      load_a((s + 1) * gBK, ra);
+      load_b((s + 1) * gBK, rb);
+    }
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = lds16(As[buf] + (wm + i * 16 + rr) * gPitch + kq);
+      b[i] = lds16(Bs[buf] + (wn + i * 16 + rr) * gPitch + kq);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+    if (s + 1 < ksteps) {
+      store(As[buf ^ 1], ra);
+      store(Bs[buf ^ 1], rb);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn + j * 16 + rr;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm + i * 16 + (lane >> 4) * 4 + v;
+        if (row >= p.M) continue;
+        if (C_F32)
+          static_cast<float*>(p.c)[(int64_t)row * p.ldc + col] = acc[i][j][v];
+        else
+          static_cast<uint16_t*>(p.c)[(int64_t)row * p.ldc + col] = (uint16_t)f2bf(acc[i][j][v]);
+      }
+    }
+}
+
+template <bool A_F32, bool C_F32>
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
+  dim3 grid((g.N + gBN - 1) / gBN, (g.M + gBM - 1) / gBM);
+  hipLaunchKernelGGL((gemm_nt_kernel<A_F32, C_F32>), grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+int64_t rup(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+size_t fused_lds_bytes(int64_t r, bool xlds) {
+  const int64_t r_pad = rup(r, 32);
+  return (size_t)kBM * (r_pad + 8) * 2 + (xlds ? (size_t)2 * kBM * kXPitch * 2 : 0);
+}
+
+}  // namespace
+
+static bool fused_fits(int64_t r, bool* xlds) {
+  if (fused_lds_bytes(r, true) <= (size_t)kLdsMax) {
+    *xlds = true;
+    return true;
+  }
+  if (fused_lds_bytes(r, false) <= (size_t)kLdsMax) {
+    *xlds = false;
+    return true;
+  }
+  return false;
+}
+
+// Only a full call whose rank tile does not fit on chip (and that was given
+// no t_io) parks t in the workspace, as bf16 [T, round_up(r, 8)].
+size_t prefill_workspace_bytes(int64_t T, int64_t r) {
+  bool xl;
+  if (fused_fits(r, &xl)) return 0;
+  return (size_t)rup(T * rup(r, 8) * 2, 256);
+}
+
+hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st) {
+  bool xlds = false;
+  if (d.flags == 0 && d.t_io == nullptr && fused_fits(d.r, &xlds)) {
+    FusedArgs f{};
+    f.x = static_cast<const uint16_t*>(d.x);
+    f.ldx = d.ldx;
+    f.ut = static_cast<const uint16_t*>(d.Ut);
+    f.ldu = d.ldu;
+    f.vt = static_cast<const uint16_t*>(d.Vt);
+    f.ldv = d.ldv;
+    f.y = static_cast<uint16_t*>(d.y);
+    f.ldy = d.ldy;
+    f.M = (int)d.T;
+    f.d_in = (int)d.d_in;
+    f.r = (int)d.r;
+    f.d_out = (int)d.d_out;
+    f.r_pad = (int)rup(d.r, 32);
+    const size_t lds = fused_lds_bytes(d.r, xlds);
+    const dim3 grid((unsigned)((d.T + kBM - 1) / kBM));
+    hipError_t e;
+    if (xlds) {
+      e = hipFuncSetAttribute((const void*)fused_kernel<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(fused_kernel<true>, grid, dim3(256), lds, st, f);
+    } else {
+      e = hipFuncSetAttribute((const void*)fused_kernel<false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(fused_kernel<false>, grid, dim3(256), lds, st, f);
+    }
+    return hipGetLastError();
+  }
+
+  // Unfused: stage 1 into fp32 t_io (stage-1-only / t requested) or bf16
+  // workspace, then stage 2 from it.
+  hipError_t e = hipSuccess;
+  const int64_t ldtb = rup(d.r, 8);
+  uint16_t* tws = static_cast<uint16_t*>(d.workspace);
+  if (d.flags != 2) {
+    GemmArgs g{};
+    g.a = d.x;
+    g.lda = d.ldx;
+    g.b = static_cast<const uint16_t*>(d.Ut);
+    g.ldb = d.ldu;
+    g.M = (int)d.T;
+    g.N = (int)d.r;
+    g.K = (int)d.d_in;
+    if (d.t_io) {
+      g.c = d.t_io;
+      g.ldc = d.ldt;
+      e = launch_gemm<false, true>(g, st);
+    } else {
+      g.c = tws;
+      g.ldc = ldtb;
+      e = launch_gemm<false, false>(g, st);
+    }
+    if (e != hipSuccess || d.flags == 1) return e;
+  }
+  GemmArgs g{};
+  if (d.t_io) {
+    g.a = d.t_io;
+    g.lda = d.ldt;
+  } else {
+    g.a = tws;
+    g.lda = ldtb;
+  }
+  g.b = static_cast<const uint16_t*>(d.Vt);
+  g.ldb = d.ldv;
+  g.c = d.y;
+  g.ldc = d.ldy;
+  g.M = (int)d.T;
+  g.N = (int)d.d_out;
+  g.K = (int)d.r;
+  return d.t_io ? launch_gemm<true, false>(g, st) : launch_gemm<false, false>(g, st);
+}
+
+}  // namespace lr

@@ -1,0 +1,66 @@
+// Device helpers shared by the HIP kernels of the low-rank hot path (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// 16 bytes of bf16 viewed as the 8-element MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// D = A(16x32) * B(32x16) + C on bf16 inputs, fp32 accumulate.
+// Operand lanes: lane l supplies row (l % 16) of A / column (l % 16) of B and
+// the k-group (l / 16) of 8 consecutive k.  Result: lane l holds
+// C[4 * (l / 16) + v][l % 16], v = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Non-temporal 16-byte load for weights streamed exactly once.
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Zero the bf16 elements of a 16-byte chunk whose index (k0 + e) >= kmax.
+__device__ __forceinline__ u32x4 mask_tail(u32x4 v, int k0, int kmax) {
+  int valid = kmax - k0;
+  if (valid >= 8) return v;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = 2 * i;
+    uint32_t m = (e < valid ? 0x0000ffffu : 0u) | (e + 1 < valid ? 0xffff0000u : 0u);
+    w[i] &= m;
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+}  // namespace lr

@@ -1,0 +1,44 @@
+// Host-side entry points of the kernel files (internal to liblowrank).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lr {
+
+// One decomposed-linear request after argument checks (see lowrank.h).
+struct DecodeLinear {
+  int64_t T, d_in, r, d_out;
+  const void* x;
+  int64_t ldx;
+  const void* Ut;
+  int64_t ldu;
+  const void* Vt;
+  int64_t ldv;
+  void* y;
+  int64_t ldy;
+  float* t_io;
+  int64_t ldt;
+  unsigned flags;
+  void* workspace;
+};
+
+// bf16, T <= 64: streamed skinny MFMA path.
+size_t decode_workspace_bytes(int64_t T, int64_t d_in, int64_t r);
+hipError_t decode_linear_bf16(const DecodeLinear& d, hipStream_t st);
+
+// bf16, T > 64: fused two-stage MFMA path (or two GEMMs).
+size_t prefill_workspace_bytes(int64_t T, int64_t r);
+hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st);
+
+// fp32, any T: tiled SIMT path.
+size_t f32_workspace_bytes(int64_t T, int64_t r);
+hipError_t linear_f32(const DecodeLinear& d, hipStream_t st);
+
+// Remap gather (bit copy of rows).
+hipError_t remap_gather(int elem_bytes, const void* src, int64_t src_rows, int64_t src_ld,
+                        const int32_t* remap, int64_t cap, const int32_t* n_valid,
+                        int64_t row_elems, void* dst, int64_t dst_ld, hipStream_t st);
+
+}  // namespace lr

@@ -132,6 +132,8 @@ def fast_factors(seed: int, d_in: int, d_out: int, r: int):
     H1, H2 Haar column sets and s the r largest singular values of an
     N(0, 1/d_in) matrix.  O(d r^2) instead of the O(d^3) SVD; used for the
     7B/13B-shaped workloads."""
+    if not 0 < r <= min(d_in, d_out):
+        raise ValueError("rank %d outside 1..min(d_in, d_out)" % r)
     g = rng(seed)
     s = _gaussian_singular_values(g, d_in, d_out)[:r] / np.sqrt(d_in)
     rs = np.sqrt(s)

@@ -1,0 +1,104 @@
+"""The C ABI library loads, exports every symbol include/lowrank.h declares,
+and rejects bad arguments on the host before launching anything (CPU only:
+no call here reaches a kernel launch)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import rank_decomposed_amd as lr
+from rank_decomposed_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "lowrank.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:lr_status|size_t|const char\*|int)\s+(\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for n in ("lowrank_linear_forward", "kv_remap_gather", "lowrank_prepare_decode",
+              "lowrank_workspace_bytes", "lowrank_status_string", "lowrank_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lr.load()
+    for n in header_functions():
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_status_strings_and_version():
+    assert lr.lowrank_status_string(0) == "ok"
+    for s in range(1, 8):
+        assert lr.lowrank_status_string(s) not in ("ok", "unknown status")
+    assert lr.lowrank_status_string(99) == "unknown status"
+    assert lr.lowrank_version() >= 100
+
+
+A16 = 1 << 20      # fake 16-byte-aligned "device" addresses: never dereferenced,
+A2 = A16 + 2       # every call below fails validation before any launch
+
+
+def _fwd(**kw):
+    args = dict(dt=_lib.LR_BF16, T=4, d_in=64, r=16, d_out=32, x=A16, ldx=64, Ut=A16, ldu=64,
+                Vt=A16, ldv=16, y=A16, ldy=32, t=None, ldt=0, flags=0, ws=None, wsb=0, st=None)
+    args.update(kw)
+    return lr.load().lowrank_linear_forward(
+        args["dt"], args["T"], args["d_in"], args["r"], args["d_out"], args["x"], args["ldx"],
+        args["Ut"], args["ldu"], args["Vt"], args["ldv"], args["y"], args["ldy"], args["t"],
+        args["ldt"], args["flags"], args["ws"], args["wsb"], args["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), _lib.LR_ERR_DTYPE),
+    (dict(T=0), _lib.LR_ERR_ARG),
+    (dict(d_in=-1), _lib.LR_ERR_ARG),
+    (dict(r=0), _lib.LR_ERR_ARG),
+    (dict(x=None), _lib.LR_ERR_ARG),
+    (dict(Vt=None), _lib.LR_ERR_ARG),
+    (dict(ldx=63), _lib.LR_ERR_ARG),
+    (dict(ldv=8), _lib.LR_ERR_ARG),
+    (dict(flags=3), _lib.LR_ERR_ARG),
+    (dict(flags=1), _lib.LR_ERR_ARG),           # stage-only needs t_io
+    (dict(flags=2), _lib.LR_ERR_ARG),
+    (dict(x=A2), _lib.LR_ERR_ALIGN),
+    (dict(ldx=68, ldu=68), _lib.LR_ERR_ALIGN),  # bf16 ld must be a multiple of 8
+    (dict(ldv=20), _lib.LR_ERR_ALIGN),
+    (dict(t=A16 + 1, ldt=16), _lib.LR_ERR_ALIGN),
+    (dict(ws=None, wsb=0), _lib.LR_ERR_WORKSPACE),   # decode path needs scratch
+    (dict(ws=A16, wsb=16), _lib.LR_ERR_WORKSPACE),
+    (dict(ws=A16 + 16, wsb=1 << 30), _lib.LR_ERR_WORKSPACE),  # not 256-aligned
+])
+def test_linear_rejects_bad_arguments(kw, status):
+    assert _fwd(**kw) == status
+
+
+def test_workspace_sizes():
+    # decode path: split-K partials plus the bf16 hi/lo copy of t
+    assert lr.lowrank_workspace_bytes(0, lr.LR_BF16, 64, 4096, 1228, 4096) > 0
+    # fused prefill keeps t on chip: no workspace
+    assert lr.lowrank_workspace_bytes(0, lr.LR_BF16, 16384, 4096, 819, 4096) == 0
+    # rank tile too large for LDS: t parked in the workspace as bf16
+    assert lr.lowrank_workspace_bytes(0, lr.LR_BF16, 4096, 640, 1494, 640) >= 4096 * 1496 * 2
+    assert lr.lowrank_workspace_bytes(0, lr.LR_F32, 4, 512, 128, 512) >= 4 * 128 * 4
+    assert lr.lowrank_workspace_bytes(0, lr.LR_BF16, 0, 4096, 1228, 4096) == 0
+
+
+def test_gather_rejects_bad_arguments():
+    g = lr.load().kv_remap_gather
+    assert g(5, A16, 10, 8, A16, 4, None, 8, A16, 8, None) == _lib.LR_ERR_DTYPE
+    assert g(_lib.LR_BF16, None, 10, 8, A16, 4, None, 8, A16, 8, None) == _lib.LR_ERR_ARG
+    assert g(_lib.LR_BF16, A16, 0, 8, A16, 4, None, 8, A16, 8, None) == _lib.LR_ERR_ARG
+    assert g(_lib.LR_BF16, A16, 10, 4, A16, 4, None, 8, A16, 8, None) == _lib.LR_ERR_ARG
+    assert g(_lib.LR_BF16, A16, 10, 8, A16, 4, None, 8, A16, 4, None) == _lib.LR_ERR_ARG
+    assert g(_lib.LR_BF16, A16 + 1, 10, 8, A16, 4, None, 8, A16, 8, None) == _lib.LR_ERR_ALIGN
+    assert g(_lib.LR_BF16, A16, 10, 8, A16 + 2, 4, None, 8, A16, 8, None) == _lib.LR_ERR_ALIGN
+    assert g(_lib.LR_F32, A16 + 2, 10, 8, A16, 4, None, 8, A16, 8, None) == _lib.LR_ERR_ALIGN

@@ -1,0 +1,117 @@
+"""lowrank_linear_forward on the GPU against the fp64 oracle.
+
+Bar: max|gpu - ref| / max|ref| <= 1e-5 (fp32) and <= 2e-2 (bf16); bit-exact on
+integer-valued cases.  Leading-dimension padding is NaN-filled, so any
+unmasked read of it fails the test."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_decomposed_amd as lr
+import synth
+from gpu_util import bits, dev, make_linear, maxrel, padded, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+BF16_TOL, F32_TOL = 2e-2, 1e-5
+
+
+def _run(case, T, dtype, flags=lr.LR_FULL, with_t=False):
+    d = dev()
+    r = case["dUt"].shape[0]
+    t_io = torch.full((T, r), float("nan"), dtype=torch.float32, device=d) if with_t else None
+    y = lr.lowrank_linear_forward(case["dx"], case["dUt"], case["dVt"], t_io=t_io, flags=flags)
+    torch.cuda.synchronize()
+    return y, t_io
+
+
+def test_config1_fp32_512_r128_T4():
+    # 512 x 512, r = 128, 4 tokens, SVD factors with sqrt(sigma) on both sides
+    c = make_linear(synth.seed_of(1), 4, 512, 128, 512, "f32", fast=False,
+                    svd_weight_seed=synth.seed_of(1, 0, 0, synth.KIND_W))
+    y, t = _run(c, 4, "f32", with_t=True)
+    tr, yr = oracle.linear(c["x"], c["U"], c["V"])
+    assert maxrel(to_f64(t), tr) <= F32_TOL
+    assert maxrel(to_f64(y), yr) <= F32_TOL
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 16, 17, 33, 64])
+def test_fp32_ragged_tokens(T):
+    c = make_linear(11 + T, T, 200, 37, 130, "f32", fast=True, ld_extra=3)
+    y, _ = _run(c, T, "f32")
+    assert maxrel(to_f64(y), oracle.linear(c["x"], c["U"], c["V"])[1]) <= F32_TOL
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 16, 17, 32, 33, 48, 64])
+@pytest.mark.parametrize("shape", [(1024, 300, 768), (520, 45, 1100), (96, 7, 40)])
+def test_bf16_decode_path(T, shape):
+    d_in, r, d_out = shape
+    c = make_linear(1000 + T + d_in, T, d_in, r, d_out, "bf16", fast=True, ld_extra=8)
+    y, t = _run(c, T, "bf16", with_t=True)
+    tr, yr = oracle.linear(c["x"], c["U"], c["V"])
+    assert maxrel(to_f64(t), tr) <= 1e-5          # t stays fp32 on the decode path
+    assert maxrel(to_f64(y), yr) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [65, 130, 1000])
+@pytest.mark.parametrize("shape", [(512, 300, 700), (1300, 1250, 1280), (40, 33, 72)])
+def test_bf16_prefill_path(T, shape):
+    d_in, r, d_out = shape
+    c = make_linear(2000 + T + r, T, d_in, r, d_out, "bf16", fast=True, ld_extra=8)
+    y, _ = _run(c, T, "bf16")
+    assert maxrel(to_f64(y), oracle.linear(c["x"], c["U"], c["V"])[1]) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [5, 64, 200])
+def test_bf16_stage_flags(T):
+    c = make_linear(3000 + T, T, 640, 96, 320, "bf16", fast=True)
+    d = dev()
+    t = torch.empty((T, 96), dtype=torch.float32, device=d)
+    lr.lowrank_linear_forward(c["dx"], c["dUt"], None, t_io=t, flags=lr.LR_STAGE1_ONLY)
+    y = lr.lowrank_linear_forward(None, None, c["dVt"], t_io=t, flags=lr.LR_STAGE2_ONLY)
+    torch.cuda.synchronize()
+    tr, yr = oracle.linear(c["x"], c["U"], c["V"])
+    assert maxrel(to_f64(t), tr) <= 1e-5
+    assert maxrel(to_f64(y), yr) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [1, 9, 64, 100, 300])
+def test_integer_cases_bit_exact(T):
+    # entries in {-1, 0, 1}, d_in <= 16, r <= 8: every partial sum is an integer
+    # of magnitude <= 128, exactly representable in bf16, so the result is exact
+    g = synth.seed_of(9, 0, 0, 0) + T
+    x = synth.ternary(g, (T, 16))
+    U = synth.ternary(g + 1, (16, 8))
+    V = synth.ternary(g + 2, (8, 40))
+    dx = padded(synth.bf16_bits(x), 24, "bf16")
+    du = padded(synth.bf16_bits(np.ascontiguousarray(U.T)), 24, "bf16")
+    dv = padded(synth.bf16_bits(np.ascontiguousarray(V.T)), 16, "bf16")
+    t = torch.empty((T, 8), dtype=torch.float32, device=dev())
+    y = lr.lowrank_linear_forward(dx, du, dv, t_io=t if T <= 64 else None)
+    torch.cuda.synchronize()
+    tr, yr = oracle.linear(x, U, V)
+    assert np.array_equal(bits(y), synth.bf16_bits(yr))
+    if T <= 64:
+        assert np.array_equal(to_f64(t), tr)
+
+
+@pytest.mark.parametrize("T", [1, 64, 128])
+def test_signed_permutation_7b_shape_bit_exact(T):
+    # q-shaped 4096 -> 1228 -> 4096: U_r has one +-1 per column, V_r at most
+    # 128 +-1 entries per column; with integer x in [-2, 2] every sum is an
+    # integer < 256, exact in bf16
+    g = np.random.default_rng(synth.seed_of(9, 1, 0, 0) + T)
+    d, r = 4096, 1228
+    U = np.zeros((d, r))
+    U[g.permutation(d)[:r], np.arange(r)] = g.choice([-1.0, 1.0], r)
+    V = np.zeros((r, d))
+    for n in range(d):
+        rows = g.choice(r, 3, replace=False)
+        V[rows, n] = g.choice([-1.0, 1.0], 3)
+    x = g.integers(-2, 3, size=(T, d)).astype(np.float64)
+    dx = to_dev(synth.bf16_bits(x), "bf16")
+    du = to_dev(synth.bf16_bits(np.ascontiguousarray(U.T)), "bf16")
+    dv = padded(synth.bf16_bits(np.ascontiguousarray(V.T)), 1232, "bf16")
+    y = lr.lowrank_linear_forward(dx, du, dv)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y), synth.bf16_bits(oracle.linear(x, U, V)[1]))
