@@ -1,0 +1,316 @@
+"""Throughput of the low-rank decomposed linear on one MI355X.
+
+Workload: the seven projections of a LLaMA-7B-shaped decoder layer
+(q, k, v, o: 4096x4096; gate, up: 4096x11008; down: 11008x4096), each
+decomposed at parameter ratio 0.6 (r = floor(0.6 d_in d_out / (d_in + d_out))
+= 1228 / 1791), bf16, decode with T = 1, 8, 32 and 64 tokens.  One step runs
+every T over 32 distinct layer sets (7.8 GB of factors, far beyond the 256 MB
+MALL), so weights stream from HBM as in a real 32-layer decode.
+
+Prints one JSON line: whole-job tokens/s (tokens x layer sets / s), the
+roofline of the dominant launch, and the fp64 CPU oracle timed on a bounded
+sample of the same workload.  Also reports the prefill configuration (16384
+rows, ratio 0.4 and 0.2) under "prefill" as context.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+BF16_PEAK = 2.5e15         # flop/s, MI355X dense bf16 MFMA
+SHAPES = {"q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4096),
+          "gate": (4096, 11008), "up": (4096, 11008), "down": (11008, 4096)}
+ROLES = ("q", "k", "v", "o", "gate", "up", "down")
+TOKENS = (1, 8, 32, 64)
+
+
+def rank(rho, a, b):
+    from fractions import Fraction
+    return int((Fraction(str(rho)) * a * b) // (a + b))
+
+
+def decode_bytes(T, d_in, r, d_out):
+    """Algorithmic HBM bytes of one decode projection: both factors once, x in,
+    y out (bf16); the rank-r intermediate stays on chip."""
+    return 2 * r * (d_in + d_out) + 2 * T * (d_in + d_out)
+
+
+def ld8(n):
+    return (n + 7) // 8 * 8
+
+
+def make_layer_sets(torch, dev, rho, n_sets, seed):
+    """Layer set 0: seeded factors with the law of a truncated SVD of an
+    N(0, 1/d_in) weight (synth.fast_factors).  Sets 1.. reuse them under a
+    seeded signed permutation of the rank components (U_r P D, D P^T V_r): the
+    same product, distinct bytes in memory."""
+    import synth
+    base = {}
+    for i, role in enumerate(ROLES):
+        d_in, d_out = SHAPES[role]
+        r = rank(rho, d_in, d_out)
+        U, V = synth.fast_factors(synth.seed_of(2, 0, i, synth.KIND_W), d_in, d_out, r)
+        ut = torch.zeros((r, ld8(d_in)), dtype=torch.bfloat16, device=dev)
+        vt = torch.zeros((d_out, ld8(r)), dtype=torch.bfloat16, device=dev)
+        ut[:, :d_in] = torch.from_numpy(synth.bf16_bits(U.T).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        vt[:, :r] = torch.from_numpy(synth.bf16_bits(V.T).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        base[role] = (ut, vt, r, U, V)
+    sets = []
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    for s in range(n_sets):
+        layer = {}
+        for role in ROLES:
+            ut, vt, r, _, _ = base[role]
+            if s == 0:
+                layer[role] = (ut, vt, r)
+                continue
+            perm = torch.randperm(r, generator=g).to(dev)
+            sign = (torch.randint(0, 2, (r,), generator=g) * 2 - 1).to(dev).to(torch.bfloat16)
+            u2 = torch.zeros_like(ut)
+            v2 = torch.zeros_like(vt)
+            u2[:, :] = ut[perm] * sign[:, None]
+            v2[:, :r] = vt[:, :r][:, perm] * sign[None, :]
+            layer[role] = (u2, v2, r)
+        sets.append(layer)
+    return base, sets
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layer-sets", type=int, default=32)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the low-rank path here has no "
+              "cross-GPU exchange; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rank_decomposed_amd as lr
+
+    dev = torch.device("cuda:0")
+    lr.load()
+    stream = torch.cuda.current_stream(dev)
+    base, sets = make_layer_sets(torch, dev, 0.6, args.layer_sets, 1234)
+    gen = torch.Generator(device=dev).manual_seed(2_000_001)
+    xs = {T: {d: torch.randn((T, d), generator=gen, device=dev).to(torch.bfloat16)
+              for d in (4096, 11008)} for T in TOKENS}
+    ys = {T: {d: torch.empty((T, d), dtype=torch.bfloat16, device=dev) for d in (4096, 11008)}
+          for T in TOKENS}
+    ws_bytes = max(lr.lowrank_workspace_bytes(0, lr.LR_BF16, T, SHAPES[r][0],
+                                              rank(0.6, *SHAPES[r]), SHAPES[r][1])
+                   for T in TOKENS for r in ROLES)
+    ws = torch.zeros(ws_bytes + 256, dtype=torch.uint8, device=dev)
+
+    def call(T, layer, role):
+        ut, vt, r = layer[role]
+        d_in, d_out = SHAPES[role]
+        lr.lowrank_linear_forward(xs[T][d_in], ut[:, :d_in], vt[:, :r], y=ys[T][d_out],
+                                  workspace=ws)
+
+    def step():
+        for T in TOKENS:
+            for layer in sets:
+                for role in ROLES:
+                    call(T, layer, role)
+
+    def capture(fn):
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    # the whole step (896 launches) is one HIP graph, as in the pages' decode
+    step_graph = capture(step)
+    for _ in range(args.warmup):
+        step_graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = time_graph(step_graph, args.steps)
+    wall = time.perf_counter() - t0
+    tokens_per_step = sum(TOKENS) * len(sets)
+    value = tokens_per_step / (ms_step / 1e3)
+
+    # per-launch durations: for each projection class and T, a graph of one
+    # launch per layer set (distinct weights), timed with events on the stream
+    per = {}
+    count = {"q": 4, "gate": 2, "down": 1}      # launches of each class per layer set
+    for T in TOKENS:
+        for role in ("q", "gate", "down"):
+            g = capture(lambda: [call(T, layer, role) for layer in sets])
+            us = 1e3 * time_graph(g, max(3, args.steps)) / len(sets)
+            del g
+            d_in, d_out = SHAPES[role]
+            nbytes = decode_bytes(T, d_in, rank(0.6, d_in, d_out), d_out)
+            per["%s_T%d" % (role, T)] = {"us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
+                                         "frac": round(nbytes / (us * 1e-6) / HBM_PEAK, 4),
+                                         "bytes": nbytes, "share": us * count[role]}
+    total_share = sum(v["share"] for v in per.values())
+    for v in per.values():
+        v["share"] = round(v["share"] / total_share, 4)
+    per_T = {}
+    for T in TOKENS:
+        bt = sum(decode_bytes(T, SHAPES[r][0], rank(0.6, *SHAPES[r]), SHAPES[r][1]) for r in ROLES)
+        per_T[str(T)] = bt
+    dom = max(per, key=lambda k: per[k]["share"])
+    dom_role, dom_T = dom.split("_T")
+    d_in, d_out = SHAPES[dom_role]
+    dom_bytes = per[dom]["bytes"]
+    dom_us = per[dom]["us"]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+
+    result = {
+        "metric": "low-rank linear tokens/s at 7B shapes (decode+prefill); % of HBM/MFMA roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s (x 7-projection layer set)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "LLaMA-7B decomposed projections (q,k,v,o 4096x4096; gate,up "
+                               "4096x11008; down 11008x4096), ratio 0.6, decode T=1,8,32,64, "
+                               "32 rotating layer sets",
+                   "tokens_per_step": tokens_per_step, "layer_sets": len(sets)},
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_kernel (lowrank_linear_forward decode), %s %dx%dx%d T=%s"
+                               % (dom_role, d_in, rank(0.6, d_in, d_out), d_out, dom_T),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
+                     "bytes_per_launch": dom_bytes, "us_per_launch": dom_us},
+        "launches": per,
+        "wall_s": round(wall, 3),
+    }
+
+    # whole-step roofline fraction (all T, all projections)
+    step_bytes = len(sets) * sum(per_T.values())
+    result["step_hbm_frac"] = round(step_bytes / (ms_step * 1e-3) / HBM_PEAK, 4)
+
+    if not args.no_prefill:
+        result["prefill"] = prefill(torch, lr, dev, stream)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def prefill(torch, lr, dev, stream, M=16384, reps=3):
+    """16384 rows (8 x 2048) through the seven projections at ratio 0.4 and
+    0.2 on the fused kernel; MFMA-bound, so one layer set suffices."""
+    import synth
+    out = {}
+    gen = torch.Generator(device=dev).manual_seed(3_000_001)
+    x = {d: torch.randn((M, d), generator=gen, device=dev).to(torch.bfloat16) for d in (4096, 11008)}
+    y = {d: torch.empty((M, d), dtype=torch.bfloat16, device=dev) for d in (4096, 11008)}
+    for rho in (0.4, 0.2):
+        fac = {}
+        flops = 0
+        for i, role in enumerate(ROLES):
+            d_in, d_out = SHAPES[role]
+            r = rank(rho, d_in, d_out)
+            ut = (torch.randn((r, d_in), generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+            vt = torch.zeros((d_out, ld8(r)), dtype=torch.bfloat16, device=dev)
+            vt[:, :r] = (torch.randn((d_out, r), generator=gen, device=dev) * 0.05)
+            fac[role] = (ut, vt[:, :r], r)
+            flops += 2 * M * r * (d_in + d_out)
+        ws = torch.zeros(max(lr.lowrank_workspace_bytes(0, lr.LR_BF16, M, SHAPES[r_][0],
+                                                        fac[r_][2], SHAPES[r_][1])
+                             for r_ in ROLES) + 256, dtype=torch.uint8, device=dev)
+
+        def run():
+            for role in ROLES:
+                ut, vt, r = fac[role]
+                d_in, d_out = SHAPES[role]
+                lr.lowrank_linear_forward(x[d_in], ut, vt, y=y[d_out], workspace=ws)
+        run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        # single-launch time of the largest projection (gate)
+        ut, vt, r = fac["gate"]
+        a.record(stream)
+        for _ in range(reps):
+            lr.lowrank_linear_forward(x[4096], ut, vt, y=y[11008], workspace=ws)
+        b.record(stream)
+        torch.cuda.synchronize()
+        gate_us = 1e3 * a.elapsed_time(b) / reps
+        gate_fl = 2 * M * r * (4096 + 11008)
+        out["rho%.1f" % rho] = {
+            "tokens_per_s": round(M / (ms * 1e-3), 1), "ms_per_layer_set": round(ms, 4),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
+            "gate_us": round(gate_us, 2),
+            "gate_frac": round(gate_fl / (gate_us * 1e-6) / BF16_PEAK, 4)}
+    return out
+
+
+def cpu_baseline(base, seconds):
+    """fp64 oracle on the host: the seven projections of layer set 0 at each
+    decode T, repeated until about `seconds` of CPU time; tokens x layer sets
+    per second, as the GPU value."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+    xs = {T: {d: synth.tokens(synth.seed_of(2, 0, 0, synth.KIND_X) + T, T, d)
+              for d in (4096, 11008)} for T in TOKENS}
+    tokens, passes = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for T in TOKENS:
+            for role in ROLES:
+                _, _, r, U, V = base[role]
+                oracle.linear(xs[T][SHAPES[role][0]], U, V)
+            tokens += T
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(tokens / el, 2), "unit": "tokens/s (x 7-projection layer set)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": "%d passes of layer set 0 (7 projections) at T=1,8,32,64, fp64 numpy, "
+                      "%.1f s" % (passes, el)}
+
+
+if __name__ == "__main__":
+    main()

@@ -96,7 +96,12 @@ enum {
  *   workspace, workspace_bytes
  *            device scratch of at least
  *            lowrank_workspace_bytes(0, dt, T, d_in, r, d_out, 0) bytes,
- *            256-byte aligned; NULL allowed when that size is 0.
+ *            256-byte aligned; NULL allowed when that size is 0.  It must be
+ *            zero-filled before its first use: the decode path keeps its
+ *            work counters there and returns them to zero when a call
+ *            completes, so later calls (and graph replays) need no clearing.
+ *            A workspace may serve calls of any shape in turn, never two calls
+ *            in flight at once.
  */
 lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in, int64_t r, int64_t d_out,
                                  const void* x, int64_t ldx, const void* Ut, int64_t ldu,

@@ -93,7 +93,9 @@ def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, w
         y = torch.empty((T, d_out), dtype=Vt.dtype, device=dev)
     need = lowrank_workspace_bytes(0, dt, T, d_in, r, d_out)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        # zero-filled: the decode kernel's counters must start at zero (it
+        # leaves them at zero when it finishes)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.lowrank_linear_forward(
         dt, T, d_in, r, d_out,

@@ -28,20 +28,19 @@ extern "C" const char* lowrank_status_string(lr_status s) {
   return "unknown status";
 }
 
-static size_t linear_ws(lr_dtype dt, int64_t T, int64_t d_in, int64_t r) {
+static size_t linear_ws(lr_dtype dt, int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
   if (dt == LR_F32) return lr::f32_workspace_bytes(T, r);
-  if (T <= 64) return lr::decode_workspace_bytes(T, d_in, r);
+  if (T <= 64) return lr::decode_workspace_bytes(T, d_in, r, d_out);
   return lr::prefill_workspace_bytes(T, r);
 }
 
 extern "C" size_t lowrank_workspace_bytes(int which, lr_dtype dt, int64_t T_or_B, int64_t d_in,
                                           int64_t r, int64_t d_out, int64_t cap) {
-  (void)d_out;
   (void)cap;
-  if (T_or_B <= 0 || d_in <= 0 || r <= 0) return 0;
+  if (T_or_B <= 0 || d_in <= 0 || r <= 0 || d_out <= 0) return 0;
   if (which == 0) {
     if (dt != LR_F32 && dt != LR_BF16) return 0;
-    return linear_ws(dt, T_or_B, d_in, r);
+    return linear_ws(dt, T_or_B, d_in, r, d_out);
   }
   return 0;
 }
@@ -69,7 +68,7 @@ extern "C" lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in
     if (s1 && (!aligned(x, 4) || !aligned(Ut, 4))) return LR_ERR_ALIGN;
     if (s2 && (!aligned(Vt, 4) || !aligned(y, 4))) return LR_ERR_ALIGN;
   }
-  const size_t need = linear_ws(dt, T, d_in, r);
+  const size_t need = linear_ws(dt, T, d_in, r, d_out);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return LR_ERR_WORKSPACE;
 

@@ -25,7 +25,7 @@ struct DecodeLinear {
 };
 
 // bf16, T <= 64: streamed skinny MFMA path.
-size_t decode_workspace_bytes(int64_t T, int64_t d_in, int64_t r);
+size_t decode_workspace_bytes(int64_t T, int64_t d_in, int64_t r, int64_t d_out);
 hipError_t decode_linear_bf16(const DecodeLinear& d, hipStream_t st);
 
 // bf16, T > 64: fused two-stage MFMA path (or two GEMMs).

@@ -115,3 +115,49 @@ def test_signed_permutation_7b_shape_bit_exact(T):
     y = lr.lowrank_linear_forward(dx, du, dv)
     torch.cuda.synchronize()
     assert np.array_equal(bits(y), synth.bf16_bits(oracle.linear(x, U, V)[1]))
+
+
+@pytest.mark.parametrize("T", [1, 24, 64])
+def test_decode_workspace_returns_to_zero_and_is_deterministic(T):
+    c = make_linear(4000 + T, T, 2048, 700, 1536, "bf16", fast=True)
+    need = lr.lowrank_workspace_bytes(0, lr.LR_BF16, T, 2048, 700, 1536)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    outs = [bits(lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"], workspace=ws))
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    ctl = ws[:512].view(torch.int32).cpu().numpy()
+    assert ctl[0] == 0 and ctl[32] == 0 and ctl[64] == 0 and ctl[96] == 0, ctl  # done, ready, go, err
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    _, yr = oracle.linear(c["x"], c["U"], c["V"])
+    assert maxrel(synth.bf16_value(outs[0]), yr) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [8, 64, 256])
+def test_graph_replay_matches_eager(T):
+    # captured once, replayed with new inputs copied into the captured buffers
+    c = make_linear(5000 + T, T, 1024, 300, 2048, "bf16", fast=True)
+    d = dev()
+    need = lr.lowrank_workspace_bytes(0, lr.LR_BF16, T, 1024, 300, 2048)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=d)
+    y = torch.empty((T, 2048), dtype=torch.bfloat16, device=d)
+    x = c["dx"].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lr.lowrank_linear_forward(x, c["dUt"], c["dVt"], y=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lr.lowrank_linear_forward(x, c["dUt"], c["dVt"], y=y, workspace=ws)
+    for rep in range(3):
+        xn = make_linear(5100 + 10 * rep + T, T, 1024, 300, 2048, "bf16", fast=True)
+        x.copy_(xn["dx"])
+        g.replay()
+        torch.cuda.synchronize()
+        got = bits(y)
+        eager = bits(lr.lowrank_linear_forward(x, c["dUt"], c["dVt"], workspace=ws))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager), rep
+        _, yr = oracle.linear(xn["x"], c["U"], c["V"])
+        assert maxrel(synth.bf16_value(got), yr) <= BF16_TOL
