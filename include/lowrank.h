@@ -162,12 +162,92 @@ lr_status lowrank_prepare_decode(int64_t B, const int32_t* lengths, const int32_
                                  int32_t* n_valid, int32_t* n_runs, int32_t* runs,
                                  int64_t max_runs);
 
-/* Device scratch needed by an entry point.  which = 0: lowrank_linear_forward
- * (T_or_B = T, cap unused); which = 1: lowrank_layer_decode_step. */
+/*
+ * lowrank_rope_table -- rotary-embedding table for the decode step:
+ * table[p][i] = (cos(p w_i), sin(p w_i)), w_i = theta^(-2i/head_dim),
+ * p < max_pos, i < head_dim/2, computed on the device in double precision and
+ * stored as float.  A constant of the model; build it once.  The rotation
+ * (rotate-half pairing (i, i + head_dim/2)) is the LLaMA convention the
+ * decode step assumes; the pages do not specify it.
+ */
+lr_status lowrank_rope_table(int64_t head_dim, int64_t max_pos, float theta, float* table,
+                             hipStream_t stream);
+
+/*
+ * Weights of one decoder layer whose seven linears (q, k, v, o, gate, up,
+ * down, in this order) are decomposed (DeInfer/en §2.D: attention and GLU MLP
+ * variants, per-layer ratios -- r[] may differ per linear and per layer).
+ * Ut[k] is U_r^T [r[k], d_in] and Vt[k] is V_r^T [d_out, r[k]], bf16, 16-byte
+ * aligned, ld a multiple of 8.  Norm weights are bf16 [d_model].
+ */
+typedef struct {
+  int64_t d_model, n_heads, n_kv_heads, head_dim, d_ffn;  /* head_dim 64 or 128 */
+  float eps;                                              /* RMSNorm epsilon */
+  const void* Ut[7];
+  int64_t ldu[7];
+  const void* Vt[7];
+  int64_t ldv[7];
+  int64_t r[7];
+  const void* attn_norm;
+  const void* ffn_norm;
+  const float* rope;        /* lowrank_rope_table output */
+  int64_t rope_max_pos;     /* positions the table covers */
+} lr_layer_weights;
+
+/*
+ * Paged cache of rank-r latents and the preparation-stage outputs of one
+ * decode step (DeInfer/en §2.C; see lowrank_prepare_decode).  The pools hold
+ * this layer's cached latents x U_k and x U_v (before rotary), one bf16 row
+ * per token slot.  Every array is device memory at a fixed address; its
+ * contents may change between replays of a captured graph.
+ */
+typedef struct {
+  void* k_pool;
+  void* v_pool;                  /* [pool_rows, pool_ld] bf16, pool_ld >= r_k, r_v */
+  int64_t pool_rows, pool_ld;
+  const int32_t* slot_mapping;   /* [B] slot of each new token's latents */
+  const int32_t* remap;          /* [cap] source slot of each packed row */
+  const int32_t* seq_off;        /* [B + 1] packed-row offsets */
+  const int32_t* pos;            /* [B] position of each new token */
+  const int32_t* n_valid;        /* scalar: packed rows in use (= seq_off[B]) */
+  int64_t B, cap, max_seq_rows;  /* capacities fixing every grid; max_seq_rows >= L_i + 1 */
+} lr_decode_state;
+
+/* Device scratch of lowrank_layer_decode_step for these shapes (compact and
+ * reconstructed K/V buffers, activations, attention partials, linear
+ * scratch).  Zero-fill it before its first use. */
+size_t lowrank_decode_step_workspace_bytes(const lr_layer_weights* w, const lr_decode_state* s);
+
+/*
+ * lowrank_layer_decode_step -- one decoder layer for B sequences, one new
+ * token each, in place on the fp32 residual stream h [B, d_model]:
+ *   x = RMSNorm(h) ; q = RoPE(lowrank_q(x), pos) ; latents x U_k, x U_v
+ *   appended at slot_mapping (bf16) ; compact copy of every sequence's
+ *   latents through remap (DeInfer/en §2.C replay copy) ; K = RoPE(buf_k V_k),
+ *   V = buf_v V_v by a fixed-size GEMM over cap rows (the "large, fixed-size
+ *   GEMM", rows past *n_valid skipped) ; softmax attention of each query over
+ *   its sequence's rows ; h += lowrank_o(o) ; x = RMSNorm(h) ;
+ *   h += lowrank_down(silu(lowrank_gate(x)) * lowrank_up(x)).
+ * Launches only; fixed grids, no host reads of device data, no allocation:
+ * capture 32 calls (one per layer) in one graph and replay it each step
+ * after refreshing the preparation arrays.
+ * Errors: LR_ERR_ARG / LR_ERR_ALIGN / LR_ERR_UNSUPPORTED (head_dim not 64 or
+ * 128) / LR_ERR_WORKSPACE from host checks, LR_ERR_HIP from the runtime.
+ */
+lr_status lowrank_layer_decode_step(const lr_layer_weights* w, const lr_decode_state* s,
+                                    float* h, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Device scratch of lowrank_linear_forward (which = 0; cap unused).  Other
+ * values of which return 0: the decode step has its own sizing call. */
 size_t lowrank_workspace_bytes(int which, lr_dtype dt, int64_t T_or_B, int64_t d_in, int64_t r,
                                int64_t d_out, int64_t cap);
 
 const char* lowrank_status_string(lr_status s);
+
+/* sizeof(lr_layer_weights) for which = 0, sizeof(lr_decode_state) for
+ * which = 1 (lets bindings verify their struct layout); 0 otherwise. */
+size_t lowrank_abi_sizeof(int which);
 
 /* Library ABI version (major * 100 + minor). */
 int lowrank_version(void);

@@ -156,3 +156,64 @@ def lowrank_prepare_decode(lengths, tables, block: int, cap: int, want_runs: boo
     if want_runs:
         out["runs"] = runs[:out["n_runs"]].copy()
     return out
+
+
+# ------------------------------------------------------------------ decode step
+from ._lib import DecodeState, LayerWeights  # noqa: E402
+
+LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
+__all__ += ["LayerWeights", "DecodeState", "layer_weights", "decode_state",
+            "lowrank_rope_table", "lowrank_decode_step_workspace_bytes",
+            "lowrank_layer_decode_step", "LINEARS"]
+
+
+def lowrank_rope_table(head_dim: int, max_pos: int, theta: float, table, stream=None):
+    """Fill table (device float [max_pos, head_dim/2, 2]) with cos/sin."""
+    _lib.check(load().lowrank_rope_table(head_dim, max_pos, theta, _ptr(table),
+                                         _stream(stream, table.device)), "lowrank_rope_table")
+    return table
+
+
+def layer_weights(cfg: dict, Ut: dict, Vt: dict, attn_norm, ffn_norm, rope, rope_max_pos: int):
+    """Build lr_layer_weights from tensors: Ut[name] = U_r^T [r, d_in] and
+    Vt[name] = V_r^T [d_out, r] bf16 views (name in LINEARS).  The returned
+    struct keeps references to the tensors it points to."""
+    w = LayerWeights()
+    w.d_model, w.n_heads, w.n_kv_heads = cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"]
+    w.head_dim, w.d_ffn = cfg["head_dim"], cfg["d_ffn"]
+    w.eps = cfg.get("eps", 1e-5)
+    for k, name in enumerate(LINEARS):
+        u, v = Ut[name], Vt[name]
+        w.Ut[k], w.ldu[k] = u.data_ptr(), _ld(u)
+        w.Vt[k], w.ldv[k] = v.data_ptr(), _ld(v)
+        w.r[k] = u.shape[0]
+    w.attn_norm, w.ffn_norm = attn_norm.data_ptr(), ffn_norm.data_ptr()
+    w.rope, w.rope_max_pos = rope.data_ptr(), rope_max_pos
+    w._keep = (Ut, Vt, attn_norm, ffn_norm, rope)
+    return w
+
+
+def decode_state(k_pool, v_pool, slot_mapping, remap, seq_off, pos, n_valid, max_seq_rows: int):
+    """Build lr_decode_state from device tensors (pools [pool_rows, pool_ld]
+    bf16; int32 prep arrays; n_valid a 1-element int32 tensor)."""
+    s = DecodeState()
+    s.k_pool, s.v_pool = k_pool.data_ptr(), v_pool.data_ptr()
+    s.pool_rows, s.pool_ld = k_pool.shape[0], _ld(k_pool)
+    s.slot_mapping, s.remap, s.seq_off = slot_mapping.data_ptr(), remap.data_ptr(), seq_off.data_ptr()
+    s.pos, s.n_valid = pos.data_ptr(), n_valid.data_ptr()
+    s.B, s.cap, s.max_seq_rows = slot_mapping.numel(), remap.numel(), max_seq_rows
+    s._keep = (k_pool, v_pool, slot_mapping, remap, seq_off, pos, n_valid)
+    return s
+
+
+def lowrank_decode_step_workspace_bytes(w: LayerWeights, s: DecodeState) -> int:
+    return int(load().lowrank_decode_step_workspace_bytes(C.byref(w), C.byref(s)))
+
+
+def lowrank_layer_decode_step(w: LayerWeights, s: DecodeState, h, workspace, stream=None):
+    """One decoder layer in place on h (fp32 [B, d_model])."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _lib.check(load().lowrank_layer_decode_step(C.byref(w), C.byref(s), _ptr(h), _ptr(workspace),
+                                                nbytes, _stream(stream, h.device)),
+               "lowrank_layer_decode_step")
+    return h

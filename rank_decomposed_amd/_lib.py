@@ -28,7 +28,28 @@ SIGNATURES = {
     "lowrank_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int, _i64, _i64, _i64, _i64, _i64]),
     "lowrank_status_string": (C.c_char_p, [C.c_int]),
     "lowrank_version": (C.c_int, []),
+    "lowrank_abi_sizeof": (C.c_size_t, [C.c_int]),
+    "lowrank_rope_table": (C.c_int, [_i64, _i64, C.c_float, _p, _p]),
+    "lowrank_decode_step_workspace_bytes": (C.c_size_t, [_p, _p]),
+    "lowrank_layer_decode_step": (C.c_int, [_p, _p, _p, _p, _sz, _p]),
 }
+
+
+class LayerWeights(C.Structure):
+    """lr_layer_weights (include/lowrank.h)."""
+    _fields_ = [("d_model", C.c_int64), ("n_heads", C.c_int64), ("n_kv_heads", C.c_int64),
+                ("head_dim", C.c_int64), ("d_ffn", C.c_int64), ("eps", C.c_float),
+                ("Ut", C.c_void_p * 7), ("ldu", C.c_int64 * 7), ("Vt", C.c_void_p * 7),
+                ("ldv", C.c_int64 * 7), ("r", C.c_int64 * 7), ("attn_norm", C.c_void_p),
+                ("ffn_norm", C.c_void_p), ("rope", C.c_void_p), ("rope_max_pos", C.c_int64)]
+
+
+class DecodeState(C.Structure):
+    """lr_decode_state (include/lowrank.h)."""
+    _fields_ = [("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("pool_rows", C.c_int64),
+                ("pool_ld", C.c_int64), ("slot_mapping", C.c_void_p), ("remap", C.c_void_p),
+                ("seq_off", C.c_void_p), ("pos", C.c_void_p), ("n_valid", C.c_void_p),
+                ("B", C.c_int64), ("cap", C.c_int64), ("max_seq_rows", C.c_int64)]
 
 _lib = None
 

@@ -14,6 +14,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 extern "C" int lowrank_version(void) { return 100; }
 
+extern "C" size_t lowrank_abi_sizeof(int which) {
+  return which == 0 ? sizeof(lr_layer_weights) : (which == 1 ? sizeof(lr_decode_state) : 0);
+}
+
 extern "C" const char* lowrank_status_string(lr_status s) {
   switch (s) {
     case LR_OK: return "ok";

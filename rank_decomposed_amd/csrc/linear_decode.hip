@@ -59,6 +59,8 @@ struct DecArgs {
   int64_t ldv;
   uint16_t* y;
   int64_t ldy;
+  float* yacc;  // optional: yacc[T, ldacc] += y (fp32) instead of writing y
+  int64_t ldacc;
   float* t32;  // optional fp32 t [T, ldt32] (stage-1 output)
   int64_t ldt32;
   uint16_t* thi;  // bf16 t [T, ldtb]
@@ -307,6 +309,8 @@ __device__ void finish_tile(const DecArgs& p, float* red, int rt, int s, int S, 
       const uint32_t hi = f2bf(v);
       store_coherent(p.thi + (int64_t)tok * p.ldtb + n, (uint16_t)hi);
       if (SPLIT) store_coherent(p.tlo + (int64_t)tok * p.ldtb + n, (uint16_t)f2bf(v - bf2f(hi)));
+    } else if (p.yacc) {
+      p.yacc[(int64_t)tok * p.ldacc + n] += v;   // each element owned by one tile
     } else {
       p.y[(int64_t)tok * p.ldy + n] = (uint16_t)f2bf(v);
     }
@@ -443,6 +447,8 @@ hipError_t decode_linear_bf16(const DecodeLinear& d, hipStream_t st) {
   a.ldv = d.ldv;
   a.y = static_cast<uint16_t*>(d.y);
   a.ldy = d.ldy;
+  a.yacc = d.y_acc;
+  a.ldacc = d.ld_acc;
   a.t32 = d.t_io;
   a.ldt32 = d.ldt;
   a.thi = reinterpret_cast<uint16_t*>(ws + pl.off_thi);

@@ -341,6 +341,25 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
 
 int64_t rup(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
+}  // namespace
+
+hipError_t gemm_nt_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                        int64_t ldc, int M, int N, int K, hipStream_t st) {
+  GemmArgs g{};
+  g.a = A;
+  g.lda = lda;
+  g.b = static_cast<const uint16_t*>(B);
+  g.ldb = ldb;
+  g.c = C;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return launch_gemm<false, false>(g, st);
+}
+
+namespace {
+
 size_t fused_lds_bytes(int64_t r, bool xlds) {
   const int64_t r_pad = rup(r, 32);
   return (size_t)kBM * (r_pad + 8) * 2 + (xlds ? (size_t)2 * kBM * kXPitch * 2 : 0);

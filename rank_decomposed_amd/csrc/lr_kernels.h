@@ -22,6 +22,10 @@ struct DecodeLinear {
   int64_t ldt;
   unsigned flags;
   void* workspace;
+  // optional (decode path only): y_acc[T, ld_acc] += y in fp32 instead of
+  // writing y; used for residual updates
+  float* y_acc = nullptr;
+  int64_t ld_acc = 0;
 };
 
 // bf16, T <= 64: streamed skinny MFMA path.
@@ -35,6 +39,10 @@ hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st);
 // fp32, any T: tiled SIMT path.
 size_t f32_workspace_bytes(int64_t T, int64_t r);
 hipError_t linear_f32(const DecodeLinear& d, hipStream_t st);
+
+// Plain bf16 GEMM C[M, N] = A[M, K] . B[N, K]^T into bf16 C (prefill helper).
+hipError_t gemm_nt_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                        int64_t ldc, int M, int N, int K, hipStream_t st);
 
 // Remap gather (bit copy of rows).
 hipError_t remap_gather(int elem_bytes, const void* src, int64_t src_rows, int64_t src_ld,

@@ -102,3 +102,25 @@ def test_gather_rejects_bad_arguments():
     assert g(_lib.LR_BF16, A16 + 1, 10, 8, A16, 4, None, 8, A16, 8, None) == _lib.LR_ERR_ALIGN
     assert g(_lib.LR_BF16, A16, 10, 8, A16 + 2, 4, None, 8, A16, 8, None) == _lib.LR_ERR_ALIGN
     assert g(_lib.LR_F32, A16 + 2, 10, 8, A16, 4, None, 8, A16, 8, None) == _lib.LR_ERR_ALIGN
+
+
+def test_struct_layouts_match_the_library():
+    import ctypes
+    lib = lr.load()
+    assert lib.lowrank_abi_sizeof(0) == ctypes.sizeof(lr.LayerWeights)
+    assert lib.lowrank_abi_sizeof(1) == ctypes.sizeof(lr.DecodeState)
+    assert lib.lowrank_abi_sizeof(2) == 0
+
+
+def test_decode_step_rejects_bad_arguments():
+    import ctypes
+    lib = lr.load()
+    w, s = lr.LayerWeights(), lr.DecodeState()
+    h = ctypes.c_void_p(A16)
+    # all-zero structs: rejected by the host checks before any launch
+    assert lib.lowrank_layer_decode_step(None, ctypes.byref(s), h, None, 0, None) == _lib.LR_ERR_ARG
+    assert lib.lowrank_layer_decode_step(ctypes.byref(w), ctypes.byref(s), h, None, 0,
+                                         None) == _lib.LR_ERR_ARG
+    assert lib.lowrank_decode_step_workspace_bytes(ctypes.byref(w), ctypes.byref(s)) == 0
+    assert lib.lowrank_rope_table(7, 10, 10000.0, A16, None) == _lib.LR_ERR_ARG
+    assert lib.lowrank_rope_table(64, 0, 10000.0, A16, None) == _lib.LR_ERR_ARG
