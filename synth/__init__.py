@@ -174,3 +174,96 @@ def block_tables(seed: int, lengths: np.ndarray, block: int = 16,
         tables.append(flat[pos:pos + n].copy())
         pos += n
     return tables, total
+
+
+# ------------------------------------- counter-based generator (numpy/torch)
+# value(seed, i) for a flat element index i: two rounds of the MurmurHash3
+# 32-bit finaliser give four 16-bit uniforms u_k; their centred, scaled sum
+# (Irwin-Hall with n = 4) approximates N(0, 1).  Integer steps are identical
+# in numpy (uint64) and torch (int64, low 32 bits kept after each product),
+# the final scaling is one IEEE double division, so both twins agree bit for
+# bit and a GPU can materialise gigabytes of inputs whose rows the CPU side
+# regenerates one by one.
+_M32 = 0xFFFFFFFF
+_IH_MEAN = 4 * 65535 / 2.0
+_IH_SD = float(np.sqrt(4 * (65536.0 ** 2 - 1) / 12.0))
+
+
+def _fmix32_np(h):
+    h = h & _M32
+    h ^= h >> 16
+    h = (h * 0x85EBCA6B) & _M32
+    h ^= h >> 13
+    h = (h * 0xC2B2AE35) & _M32
+    h ^= h >> 16
+    return h
+
+
+def hash_normal(seed: int, index) -> np.ndarray:
+    """Approximately N(0,1) values at flat indices (numpy, fp64)."""
+    i = np.asarray(index, dtype=np.uint64)
+    s = np.uint64(seed & _M32)
+    a = _fmix32_np((i * np.uint64(2) * np.uint64(0x9E3779B1) + s) & np.uint64(_M32))
+    b = _fmix32_np(((i * np.uint64(2) + np.uint64(1)) * np.uint64(0x9E3779B1) + s)
+                   & np.uint64(_M32))
+    tot = (a & 0xFFFF) + (a >> 16) + (b & 0xFFFF) + (b >> 16)
+    return (tot.astype(np.float64) - _IH_MEAN) / _IH_SD
+
+
+def hash_normal_torch(seed: int, index):
+    """The same values as hash_normal for an int64 torch tensor of indices
+    (any device); returns float64."""
+    import torch
+
+    m = 0xFFFFFFFF
+
+    def fmix(h):
+        h = h & m
+        h = h ^ (h >> 16)
+        h = (h * 0x85EBCA6B) & m
+        h = h ^ (h >> 13)
+        h = (h * 0xC2B2AE35) & m
+        return h ^ (h >> 16)
+
+    i = index.to(torch.int64)
+    s = seed & m
+    a = fmix((i * 2 * 0x9E3779B1 + s) & m)
+    b = fmix(((i * 2 + 1) * 0x9E3779B1 + s) & m)
+    tot = (a & 0xFFFF) + (a >> 16) + (b & 0xFFFF) + (b >> 16)
+    return (tot.to(torch.float64) - _IH_MEAN) / _IH_SD
+
+
+def hash_bf16_rows_torch(seed: int, rows: int, ld: int, device):
+    """Device [rows, ld] bf16 tensor of hash_normal(seed, row * ld + col),
+    rounded fp64 -> fp32 -> bf16 as bf16_bits does; built in row chunks."""
+    import torch
+
+    out = torch.empty((rows, ld), dtype=torch.bfloat16, device=device)
+    step = max(1, (1 << 24) // ld)
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        idx = torch.arange(r0 * ld, r1 * ld, dtype=torch.int64, device=device)
+        out[r0:r1] = hash_normal_torch(seed, idx).to(torch.float32).to(torch.bfloat16).view(
+            r1 - r0, ld)
+    return out
+
+
+def hash_rows(seed: int, rows, ld: int) -> np.ndarray:
+    """fp64 values of the bf16-rounded hash_normal rows (numpy twin of
+    hash_bf16_rows_torch) for the given physical row indices."""
+    rows = np.asarray(rows, dtype=np.int64)
+    idx = rows[:, None] * ld + np.arange(ld)[None, :]
+    return bf16_value(bf16_bits(hash_normal(seed, idx)))
+
+
+def rank_permutation(seed: int, r: int):
+    """Seeded permutation and signs of the rank components: (U_r P D, D P^T V_r)
+    has the same product and the same law as (U_r, V_r)."""
+    g = rng(seed)
+    return g.permutation(r), g.choice(np.array([-1.0, 1.0]), r)
+
+
+# -------------------------------------------- 32-layer decode-step workload
+DECODE_STEP_7B = {"d_model": 4096, "n_heads": 32, "n_kv_heads": 32, "head_dim": 128,
+                  "d_ffn": 11008, "eps": 1e-5, "rho": 0.2, "B": 64, "n_layers": 32,
+                  "block": 16, "len_lo": 128, "len_hi": 4096}

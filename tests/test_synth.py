@@ -63,3 +63,25 @@ def test_block_tables_partition_pool():
     assert used.min() >= 0 and used.max() < nb
     for L, t in zip(lengths, tables):
         assert len(t) == (L + 1 + 15) // 16
+
+
+def test_hash_generator_numpy_torch_twins_agree_bitwise():
+    idx = np.concatenate([np.arange(5000), np.array([2**31 - 1, 2**32 + 7, 10**12])])
+    a = synth.hash_normal(12345, idx)
+    b = synth.hash_normal_torch(12345, torch.from_numpy(idx)).numpy()
+    assert np.array_equal(a, b)
+    rows = synth.hash_rows(77, [0, 3, 9], 24)
+    full = synth.hash_bf16_rows_torch(77, 10, 24, "cpu")
+    got = full.float().double().numpy()[[0, 3, 9]]
+    assert np.array_equal(rows, got)
+    # roughly standard normal
+    v = synth.hash_normal(1, np.arange(200000))
+    assert abs(v.mean()) < 0.01 and abs(v.std() - 1.0) < 0.01
+    assert abs(np.mean(v ** 4) - 3.0) < 0.5   # Irwin-Hall(4) kurtosis 2.7
+
+
+def test_rank_permutation_keeps_the_product():
+    U, V = synth.fast_factors(3, 40, 50, 12)
+    perm, sign = synth.rank_permutation(9, 12)
+    U2, V2 = U[:, perm] * sign[None, :], V[perm, :] * sign[:, None]
+    assert np.allclose(U2 @ V2, U @ V, atol=1e-13)
