@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--layer-sets", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-step", action="store_true", help="skip the 32-layer decode step")
+    ap.add_argument("--step-layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -219,6 +221,11 @@ def main():
 
     if not args.no_prefill:
         result["prefill"] = prefill(torch, lr, dev, stream)
+    if not args.no_step:
+        del sets
+        torch.cuda.empty_cache()
+        result["decode_step"] = decode_step(torch, lr, dev, stream, args.step_layers,
+                                            max(3, args.steps // 2))
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
@@ -278,6 +285,83 @@ def prefill(torch, lr, dev, stream, M=16384, reps=3):
             "gate_us": round(gate_us, 2),
             "gate_frac": round(gate_fl / (gate_us * 1e-6) / BF16_PEAK, 4)}
     return out
+
+
+def decode_step(torch, lr, dev, stream, n_layers, reps):
+    """The 32-layer decode step of a LLaMA-7B-shaped decoder decomposed at
+    ratio 0.2 (64 sequences, cached lengths uniform in [128, 4096]) captured
+    once in a HIP graph and replayed; preparation stage timed separately."""
+    from synth.decode_step import DecodeStepInputs
+    si = DecodeStepInputs(n_layers=n_layers, device=dev)
+    c = si.cfg
+    t0 = time.perf_counter()
+    prep = lr.lowrank_prepare_decode(si.lengths, si.tables, si.block, si.cap)
+    prep_ms = 1e3 * (time.perf_counter() - t0)
+    rope = torch.empty((si.max_seq_rows, c["head_dim"] // 2, 2), dtype=torch.float32, device=dev)
+    lr.lowrank_rope_table(c["head_dim"], si.max_seq_rows, 10000.0, rope)
+    dp = {k: torch.from_numpy(np.ascontiguousarray(prep[k])).to(dev)
+          for k in ("remap", "seq_off", "pos", "slot_mapping")}
+    nv = torch.tensor([prep["n_valid"]], dtype=torch.int32, device=dev)
+    layers = []
+    for li in range(n_layers):
+        Ut, Vt, g1, g2 = si.device_layer(li)
+        w = lr.layer_weights(c, Ut, Vt, g1, g2, rope, si.max_seq_rows)
+        st = lr.decode_state(si.device_pool(li, 0), si.device_pool(li, 1), dp["slot_mapping"],
+                             dp["remap"], dp["seq_off"], dp["pos"], nv, si.max_seq_rows)
+        layers.append((w, st))
+    ws = torch.zeros(lr.lowrank_decode_step_workspace_bytes(*layers[0]), dtype=torch.uint8,
+                     device=dev)
+    h0 = torch.from_numpy(si.h0.astype(np.float32)).to(dev)
+    h = h0.clone()
+
+    def step():
+        h.copy_(h0)
+        for w, st in layers:
+            lr.lowrank_layer_decode_step(w, st, h, ws)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    # per-kernel roofline budget of one layer (algorithmic bytes / flops)
+    nvr, B = prep["n_valid"], c["B"]
+    dkv = c["n_kv_heads"] * c["head_dim"]
+    rk, rv = si.ranks["k"], si.ranks["v"]
+    from synth.decode_step import dims
+    lin_bytes = sum(2 * si.ranks[n] * (a_ + b_) + 2 * B * (a_ + b_)
+                    for n, (a_, b_) in dims(c).items())
+    gather_bytes = 2 * nvr * (rk + rv) * 2
+    recon_flops = 2.0 * nvr * (rk + rv) * dkv
+    recon_bytes = nvr * (rk + rv) * 2 + 2 * nvr * dkv * 2
+    attn_bytes = 2 * nvr * dkv * 2
+    roof_s = (lin_bytes / HBM_PEAK + gather_bytes / HBM_PEAK
+              + max(recon_flops / BF16_PEAK, recon_bytes / HBM_PEAK) + attn_bytes / HBM_PEAK)
+    roof_ms = 1e3 * roof_s * n_layers
+    del layers, ws, g
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": round(B / (ms * 1e-3), 1), "ms_per_step": round(ms, 3),
+            "layers": n_layers, "sequences": B, "n_valid_rows": int(nvr),
+            "roof_ms": round(roof_ms, 3), "frac": round(roof_ms / ms, 4),
+            "prep_ms_host": round(prep_ms, 3),
+            "per_layer_roof_us": {"linears": round(1e6 * lin_bytes / HBM_PEAK, 2),
+                                  "gather": round(1e6 * gather_bytes / HBM_PEAK, 2),
+                                  "recon": round(1e6 * max(recon_flops / BF16_PEAK,
+                                                           recon_bytes / HBM_PEAK), 2),
+                                  "attention": round(1e6 * attn_bytes / HBM_PEAK, 2)}}
 
 
 def cpu_baseline(base, seconds):
