@@ -13,12 +13,17 @@
 //
 // Wave layout: the 4 waves share the 64 rows (4 row blocks of 16) and split
 // each 512-wide column chunk into 4 x 128 (8 column blocks of 16 per wave).
-// Per 32-wide k-step a wave issues 32 MFMAs on 4 A fragments (LDS) and 8 B
-// fragments (weights, global -> VGPR, prefetched one step ahead).
+// Operands come straight from memory into registers with raw buffer loads
+// (rows past a matrix edge read zero, so no branches), two 32-wide k-steps
+// ahead in a register ring.  The k-loop body has no conditionals, so the
+// compiler keeps the ring's loads in flight across steps; the one partial
+// k-step (K not a multiple of 32) is masked after the loop.
 //
 // Plain kernel: C = A . B^T on a 128x128 tile with LDS double buffering, for
 // the stage-only calls (tensor-parallel share) and for ranks too large for the
 // on-chip tile.
+#include <mutex>
+
 #include "lr_common.h"
 #include "lr_kernels.h"
 
@@ -26,15 +31,12 @@ namespace lr {
 
 namespace {
 
-constexpr int kBM = 64;         // fused: token rows per workgroup
-constexpr int kNB = 8;          // fused: 16-wide column blocks per wave
-constexpr int kChunk = 4 * kNB * 16;  // 512 columns per chunk
-constexpr int kXPitch = 40;     // fused: x staging row pitch (elements)
-constexpr int kLdsMax = 163840; // gfx950 LDS per workgroup
-
-__device__ __forceinline__ u32x4 lds16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
+constexpr int kBM = 64;                 // fused: token rows per workgroup
+constexpr int kMB = kBM / 16;           // fused: 16-row blocks per wave
+constexpr int kNB = 8;                  // fused: 16-wide column blocks per wave
+constexpr int kChunk = 4 * kNB * 16;    // 512 columns per chunk
+constexpr int kRing = 2;                // k-steps of operands in flight per wave
+constexpr int kLdsMax = 163840;         // gfx950 LDS per workgroup
 
 struct FusedArgs {
   const uint16_t* x;
@@ -49,122 +51,66 @@ struct FusedArgs {
   int r_pad;  // multiple of 32
 };
 
-// One 32-wide k-step of a 64 x 128 wave tile: acc[mb][nb] += A[mb] . B[nb]^T
-__device__ __forceinline__ void wave_step(f32x4 (&acc)[4][kNB], const u32x4 (&a)[4],
-                                          const u32x4 (&b)[kNB]) {
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = mfma16x16x32(a[mb], b[nb], acc[mb][nb]);
-}
-
-// B fragments of one k-step: rows row0 + nb*16 + (lane & 15), k .. k+7.
-__device__ __forceinline__ void load_b(u32x4 (&b)[kNB], const uint16_t* base, int64_t ld,
-                                       int row0, int nrows, int k, int kmax, int lane) {
-  const int rr = lane & 15;
-  const int kk = k + (lane >> 4) * 8;
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const int row = row0 + nb * 16 + rr;
-    if (row < nrows && kk < kmax) {
-      u32x4 v = ldg16(base + (int64_t)row * ld + kk);
-      b[nb] = (kk + 8 > kmax) ? mask_tail(v, kk, kmax) : v;
-    } else {
-      b[nb] = u32x4{0, 0, 0, 0};
-    }
-  }
-}
-
-template <bool XLDS>
 __global__ __launch_bounds__(256, 1) void fused_kernel(FusedArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int tpitch = p.r_pad + 8;
-  uint16_t* ts = smem;                          // [64][tpitch]
-  uint16_t* xs = smem + kBM * tpitch;           // [2][64][kXPitch] when XLDS
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  uint16_t* ts = smem;  // [64][tpitch] bf16 rank tile
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m0 = blockIdx.x * kBM;
-  const int rr = lane & 15;
-  const int kq = (lane >> 4) * 8;
+  const int rr = lane & 15, kq = (lane >> 4) * 8;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint64_t)p.M * p.ldx * 2);
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.ut, (uint64_t)p.r * p.ldu * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vt, (uint64_t)p.d_out * p.ldv * 2);
 
   // ---------------- stage 1: ts = bf16(x[m0:m0+64] . U_r) ----------------
-  // x rows of this lane's A fragments (global path)
-  const int ksteps1 = (p.d_in + 31) / 32;
-  for (int c0 = 0; c0 < p.r_pad; c0 += kChunk) {
-    f32x4 acc[4][kNB];
+  {
+    const int ks = (p.d_in + 31) / 32;
+    const bool tail = (p.d_in % 32) != 0;
+    const int kf = tail ? ks - 1 : ks;  // k-steps needing no mask
+    for (int c0 = 0; c0 < p.r_pad; c0 += kChunk) {
+      const int row0 = c0 + wave * kNB * 16;
+      if (row0 >= p.r_pad) continue;  // wave-uniform
+      f32x4 acc[kMB][kNB];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int i = 0; i < kMB; ++i)
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int row0 = c0 + wave * (kNB * 16);
-    const bool active = row0 < p.r_pad;
-
-    u32x4 bcur[kNB], bnxt[kNB];
-    if (active) load_b(bcur, p.ut, p.ldu, row0, p.r, 0, p.d_in, lane);
-
-    // x staging: thread t moves row t/4, k-chunk (t%4)*8 of each 32-wide step
-    const int xrow = threadIdx.x >> 2, xk = (threadIdx.x & 3) * 8;
-    const bool xrow_ok = (m0 + xrow) < p.M;
-    const uint16_t* xsrc = p.x + (int64_t)(xrow_ok ? m0 + xrow : 0) * p.ldx;
-    u32x4 xreg = u32x4{0, 0, 0, 0};
-    if (XLDS) {
-      if (xrow_ok && xk < p.d_in) {
-        xreg = ldg16(xsrc + xk);
-        if (xk + 8 > p.d_in) xreg = mask_tail(xreg, xk, p.d_in);
+        for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      u32x4 bq[kRing][kNB], aq[kRing][kMB];
+#pragma unroll
+      for (int q = 0; q < kRing; ++q) {
+        frag_load<kNB>(bq[q], ru, p.ldu, row0, q * 32, lane);
+        frag_load<kMB>(aq[q], rx, p.ldx, m0, q * 32, lane);
       }
-      *reinterpret_cast<u32x4*>(xs + xrow * kXPitch + xk) = xreg;
-      __syncthreads();
-    }
-    for (int s = 0; s < ksteps1; ++s) {
-      const int k = s * 32;
-      const int buf = s & 1;
-      if (XLDS && s + 1 < ksteps1) {
-        const int kn = k + 32 + xk;
-        xreg = u32x4{0, 0, 0, 0};
-        if (xrow_ok && kn < p.d_in) {
-          xreg = ldg16(xsrc + kn);
-          if (kn + 8 > p.d_in) xreg = mask_tail(xreg, kn, p.d_in);
+      int s = 0;
+      for (; s + kRing <= kf; s += kRing) {
+#pragma unroll
+        for (int q = 0; q < kRing; ++q) {
+          frag_mma<kMB, kNB>(acc, aq[q], bq[q]);
+          // steps past the end load in-range junk or zeros and are never used
+          frag_load<kNB>(bq[q], ru, p.ldu, row0, (s + q + kRing) * 32, lane);
+          frag_load<kMB>(aq[q], rx, p.ldx, m0, (s + q + kRing) * 32, lane);
         }
       }
-      if (active && s + 1 < ksteps1) load_b(bnxt, p.ut, p.ldu, row0, p.r, k + 32, p.d_in, lane);
-      u32x4 a[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        if (XLDS) {
-          a[mb] = lds16(xs + buf * (kBM * kXPitch) + (mb * 16 + rr) * kXPitch + kq);
-        } else {
-          const int row = m0 + mb * 16 + rr;
-          const int kk = k + kq;
-          a[mb] = u32x4{0, 0, 0, 0};
-          if (row < p.M && kk < p.d_in) {
-            u32x4 v = ldg16(p.x + (int64_t)row * p.ldx + kk);
-            a[mb] = (kk + 8 > p.d_in) ? mask_tail(v, kk, p.d_in) : v;
-          }
+      for (int q = 0; q < kRing; ++q) {
+        if (s + q < kf) {
+          frag_mma<kMB, kNB>(acc, aq[q], bq[q]);
+        } else if (tail && s + q == kf) {
+          frag_mask<kNB>(bq[q], kf * 32, p.d_in, lane);
+          frag_mask<kMB>(aq[q], kf * 32, p.d_in, lane);
+          frag_mma<kMB, kNB>(acc, aq[q], bq[q]);
         }
       }
-      if (active) wave_step(acc, a, bcur);
-      if (XLDS) {
-        if (s + 1 < ksteps1)
-          *reinterpret_cast<u32x4*>(xs + (buf ^ 1) * (kBM * kXPitch) + xrow * kXPitch + xk) = xreg;
-        __syncthreads();
-      }
-      if (active && s + 1 < ksteps1) {
+      // rows of U_r^T past r read as zero, so columns [r, r_pad) of ts are 0
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) bcur[nb] = bnxt[nb];
-      }
-    }
-    if (active) {
+      for (int i = 0; i < kMB; ++i)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const int col = row0 + nb * 16 + rr;
+        for (int j = 0; j < kNB; ++j) {
+          const int col = row0 + j * 16 + rr;
           if (col < p.r_pad) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int tok = mb * 16 + (lane >> 4) * 4 + v;
-              ts[tok * tpitch + col] = (uint16_t)f2bf(acc[mb][nb][v]);
-            }
+            for (int v = 0; v < 4; ++v)
+              ts[(i * 16 + (lane >> 4) * 4 + v) * tpitch + col] = (uint16_t)f2bf(acc[i][j][v]);
           }
         }
     }
@@ -172,41 +118,55 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(FusedArgs p) {
   __syncthreads();
 
   // ---------------- stage 2: y[m0:m0+64] = ts . V_r ----------------
-  const int ksteps2 = p.r_pad / 32;
-  for (int c0 = 0; c0 < p.d_out; c0 += kChunk) {
-    const int row0 = c0 + wave * (kNB * 16);
-    if (row0 >= p.d_out) continue;
-    f32x4 acc[4][kNB];
+  {
+    const int ks = p.r_pad / 32;
+    const bool tail = (p.r % 32) != 0;
+    const int kf = tail ? ks - 1 : ks;
+    for (int c0 = 0; c0 < p.d_out; c0 += kChunk) {
+      const int row0 = c0 + wave * kNB * 16;
+      if (row0 >= p.d_out) continue;
+      f32x4 acc[kMB][kNB];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int i = 0; i < kMB; ++i)
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 bcur[kNB], bnxt[kNB];
-    load_b(bcur, p.vt, p.ldv, row0, p.d_out, 0, p.r, lane);
-    for (int s = 0; s < ksteps2; ++s) {
-      const int k = s * 32;
-      if (s + 1 < ksteps2) load_b(bnxt, p.vt, p.ldv, row0, p.d_out, k + 32, p.r, lane);
-      u32x4 a[4];
+        for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      u32x4 bq[kRing][kNB];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) a[mb] = lds16(ts + (mb * 16 + rr) * tpitch + k + kq);
-      wave_step(acc, a, bcur);
-      if (s + 1 < ksteps2) {
+      for (int q = 0; q < kRing; ++q) frag_load<kNB>(bq[q], rv, p.ldv, row0, q * 32, lane);
+      int s = 0;
+      for (; s + kRing <= kf; s += kRing) {
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) bcur[nb] = bnxt[nb];
-      }
-    }
+        for (int q = 0; q < kRing; ++q) {
+          u32x4 a[kMB];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const int col = row0 + nb * 16 + rr;
-        if (col >= p.d_out) continue;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tok = m0 + mb * 16 + (lane >> 4) * 4 + v;
-          if (tok < p.M) p.y[(int64_t)tok * p.ldy + col] = (uint16_t)f2bf(acc[mb][nb][v]);
+          for (int i = 0; i < kMB; ++i) a[i] = lds16(ts + (i * 16 + rr) * tpitch + (s + q) * 32 + kq);
+          frag_mma<kMB, kNB>(acc, a, bq[q]);
+          frag_load<kNB>(bq[q], rv, p.ldv, row0, (s + q + kRing) * 32, lane);
         }
       }
+#pragma unroll
+      for (int q = 0; q < kRing; ++q) {
+        if (s + q < kf || (tail && s + q == kf)) {
+          if (s + q == kf) frag_mask<kNB>(bq[q], kf * 32, p.r, lane);
+          u32x4 a[kMB];
+#pragma unroll
+          for (int i = 0; i < kMB; ++i) a[i] = lds16(ts + (i * 16 + rr) * tpitch + (s + q) * 32 + kq);
+          frag_mma<kMB, kNB>(acc, a, bq[q]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+          const int col = row0 + j * 16 + rr;
+          if (col >= p.d_out) continue;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int tok = m0 + i * 16 + (lane >> 4) * 4 + v;
+            if (tok < p.M) p.y[(int64_t)tok * p.ldy + col] = (uint16_t)f2bf(acc[i][j][v]);
+          }
+        }
+    }
   }
 }
 
@@ -360,36 +320,25 @@ hipError_t gemm_nt_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, 
 
 namespace {
 
-size_t fused_lds_bytes(int64_t r, bool xlds) {
-  const int64_t r_pad = rup(r, 32);
-  return (size_t)kBM * (r_pad + 8) * 2 + (xlds ? (size_t)2 * kBM * kXPitch * 2 : 0);
-}
+size_t fused_lds_bytes(int64_t r) { return (size_t)kBM * (rup(r, 32) + 8) * 2; }
 
 }  // namespace
 
-static bool fused_fits(int64_t r, bool* xlds) {
-  if (fused_lds_bytes(r, true) <= (size_t)kLdsMax) {
-    *xlds = true;
-    return true;
-  }
-  if (fused_lds_bytes(r, false) <= (size_t)kLdsMax) {
-    *xlds = false;
-    return true;
-  }
-  return false;
-}
+static bool fused_fits(int64_t r) { return fused_lds_bytes(r) <= (size_t)kLdsMax; }
 
 // Only a full call whose rank tile does not fit on chip (and that was given
 // no t_io) parks t in the workspace, as bf16 [T, round_up(r, 8)].
 size_t prefill_workspace_bytes(int64_t T, int64_t r) {
-  bool xl;
-  if (fused_fits(r, &xl)) return 0;
+  if (fused_fits(r)) return 0;
   return (size_t)rup(T * rup(r, 8) * 2, 256);
 }
 
 hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st) {
-  bool xlds = false;
-  if (d.flags == 0 && d.t_io == nullptr && fused_fits(d.r, &xlds)) {
+  // buffer-load offsets are 32-bit: the fused kernel needs every operand
+  // (plus one tile of rows past its end) under 2 GiB
+  const bool small = (d.T + kBM) * d.ldx * 2 < (1ll << 31) && (d.r + 128) * d.ldu * 2 < (1ll << 31) &&
+                     (d.d_out + 512) * d.ldv * 2 < (1ll << 31);
+  if (d.flags == 0 && d.t_io == nullptr && fused_fits(d.r) && small) {
     FusedArgs f{};
     f.x = static_cast<const uint16_t*>(d.x);
     f.ldx = d.ldx;
@@ -404,20 +353,13 @@ hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st) {
     f.r = (int)d.r;
     f.d_out = (int)d.d_out;
     f.r_pad = (int)rup(d.r, 32);
-    const size_t lds = fused_lds_bytes(d.r, xlds);
-    const dim3 grid((unsigned)((d.T + kBM - 1) / kBM));
-    hipError_t e;
-    if (xlds) {
-      e = hipFuncSetAttribute((const void*)fused_kernel<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(fused_kernel<true>, grid, dim3(256), lds, st, f);
-    } else {
-      e = hipFuncSetAttribute((const void*)fused_kernel<false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(fused_kernel<false>, grid, dim3(256), lds, st, f);
-    }
+    const size_t lds = fused_lds_bytes(d.r);
+    static std::once_flag lds_once;  // raise the dynamic-LDS limit once per process
+    std::call_once(lds_once, [] {
+      (void)hipFuncSetAttribute((const void*)fused_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    });
+    hipLaunchKernelGGL(fused_kernel, dim3((unsigned)((d.T + kBM - 1) / kBM)), dim3(256), lds, st, f);
     return hipGetLastError();
   }
 

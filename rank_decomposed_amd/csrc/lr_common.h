@@ -63,4 +63,49 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int k0, int kmax) {
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zero, so tiles past a matrix edge need no branches.  Word 3 is the
+// gfx9-family raw-buffer configuration.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// NB 16-row MFMA fragments of one 32-wide k-step of a row-major bf16 matrix:
+// lane l gets row row0 + nb*16 + (l & 15), elements k + 8*(l >> 4) .. +8.
+template <int NB>
+__device__ __forceinline__ void frag_load(u32x4 (&f)[NB], __amdgpu_buffer_rsrc_t rs, int64_t ld,
+                                          int row0, int k, int lane) {
+  const int row = lane & 15, kk = k + (lane >> 4) * 8;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    f[nb] = bload(rs, (uint32_t)(((int64_t)(row0 + nb * 16 + row) * ld + kk) * 2));
+}
+
+// Zero the elements >= kmax of fragments loaded at k-step base k.
+template <int NB>
+__device__ __forceinline__ void frag_mask(u32x4 (&f)[NB], int k, int kmax, int lane) {
+  const int kk = k + (lane >> 4) * 8;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) f[nb] = mask_tail(f[nb], kk, kmax);
+}
+
+template <int MB, int NB>
+__device__ __forceinline__ void frag_mma(f32x4 (&acc)[MB][NB], const u32x4 (&a)[MB],
+                                         const u32x4 (&b)[NB]) {
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+}
+
+__device__ __forceinline__ u32x4 lds16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
 }  // namespace lr
