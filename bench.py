@@ -33,6 +33,11 @@ ROLES = ("q", "k", "v", "o", "gate", "up", "down")
 TOKENS = (1, 8, 32, 64)
 
 
+def log(msg):
+    """Progress of the legs on stderr (stdout carries only the JSON line)."""
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
 def rank(rho, a, b):
     from fractions import Fraction
     return int((Fraction(str(rho)) * a * b) // (a + b))
@@ -86,6 +91,15 @@ def make_layer_sets(torch, dev, rho, n_sets, seed):
     return base, sets
 
 
+def pack_sets(lr, sets):
+    """Replace each set's row-major factors by fragment-packed copies."""
+    for layer in sets:
+        for role in list(layer):
+            ut, vt, r = layer[role]
+            d_in = SHAPES[role][0]
+            layer[role] = (lr.pack_factor(ut[:, :d_in]), lr.pack_factor(vt[:, :r]), r)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +111,8 @@ def main():
     ap.add_argument("--no-step", action="store_true", help="skip the 32-layer decode step")
     ap.add_argument("--step-layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--layout", choices=("packed", "rowmajor"), default="packed",
+                    help="device layout of the decode factors")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the low-rank path here has no "
@@ -110,6 +126,9 @@ def main():
     lr.load()
     stream = torch.cuda.current_stream(dev)
     base, sets = make_layer_sets(torch, dev, 0.6, args.layer_sets, 1234)
+    if args.layout == "packed":
+        pack_sets(lr, sets)
+        torch.cuda.synchronize()
     gen = torch.Generator(device=dev).manual_seed(2_000_001)
     xs = {T: {d: torch.randn((T, d), generator=gen, device=dev).to(torch.bfloat16)
               for d in (4096, 11008)} for T in TOKENS}
@@ -123,8 +142,9 @@ def main():
     def call(T, layer, role):
         ut, vt, r = layer[role]
         d_in, d_out = SHAPES[role]
-        lr.lowrank_linear_forward(xs[T][d_in], ut[:, :d_in], vt[:, :r], y=ys[T][d_out],
-                                  workspace=ws)
+        if args.layout == "rowmajor":
+            ut, vt = ut[:, :d_in], vt[:, :r]
+        lr.lowrank_linear_forward(xs[T][d_in], ut, vt, y=ys[T][d_out], workspace=ws)
 
     def step():
         for T in TOKENS:
@@ -154,8 +174,10 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
+    log("factors ready (%s layout)" % args.layout)
     # the whole step (896 launches) is one HIP graph, as in the pages' decode
     step_graph = capture(step)
+    log("decode step graph captured")
     for _ in range(args.warmup):
         step_graph.replay()
     torch.cuda.synchronize()
@@ -164,6 +186,7 @@ def main():
     wall = time.perf_counter() - t0
     tokens_per_step = sum(TOKENS) * len(sets)
     value = tokens_per_step / (ms_step / 1e3)
+    log("decode step timed: %.3f ms" % ms_step)
 
     # per-launch durations: for each projection class and T, a graph of one
     # launch per layer set (distinct weights), timed with events on the stream
@@ -179,6 +202,7 @@ def main():
             per["%s_T%d" % (role, T)] = {"us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
                                          "frac": round(nbytes / (us * 1e-6) / HBM_PEAK, 4),
                                          "bytes": nbytes, "share": us * count[role]}
+        log("per-launch timing T=%d done" % T)
     total_share = sum(v["share"] for v in per.values())
     for v in per.values():
         v["share"] = round(v["share"] / total_share, 4)
@@ -204,7 +228,8 @@ def main():
         "config": {"workload": "LLaMA-7B decomposed projections (q,k,v,o 4096x4096; gate,up "
                                "4096x11008; down 11008x4096), ratio 0.6, decode T=1,8,32,64, "
                                "32 rotating layer sets",
-                   "tokens_per_step": tokens_per_step, "layer_sets": len(sets)},
+                   "tokens_per_step": tokens_per_step, "layer_sets": len(sets),
+                   "factor_layout": args.layout},
         "roofline": {"bound": "hbm",
                      "kernel": "decode_kernel (lowrank_linear_forward decode), %s %dx%dx%d T=%s"
                                % (dom_role, d_in, rank(0.6, d_in, d_out), d_out, dom_T),
@@ -221,14 +246,17 @@ def main():
 
     if not args.no_prefill:
         result["prefill"] = prefill(torch, lr, dev, stream)
+        log("prefill leg done")
     if not args.no_step:
         del sets
         torch.cuda.empty_cache()
         result["decode_step"] = decode_step(torch, lr, dev, stream, args.step_layers,
                                             max(3, args.steps // 2))
+        log("decode-step leg done")
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
+        log("cpu baseline done")
     print(json.dumps(result), flush=True)
 
 

@@ -66,12 +66,41 @@ typedef enum {
 
 typedef enum { LR_F32 = 0, LR_BF16 = 1 } lr_dtype;
 
-/* flags of lowrank_linear_forward */
+/* flags of lowrank_linear_forward: one mode, optionally | LR_PACKED_WEIGHTS */
 enum {
   LR_FULL = 0,         /* y = (x U_r) V_r; t_io written too when non-NULL          */
   LR_STAGE1_ONLY = 1,  /* t_io = x U_r (t_io required; Vt, y unused)              */
-  LR_STAGE2_ONLY = 2   /* y = t_io V_r (t_io read; x, Ut unused)                   */
+  LR_STAGE2_ONLY = 2,  /* y = t_io V_r (t_io read; x, Ut unused)                   */
+  LR_PACKED_WEIGHTS = 4 /* bf16, T <= 64: Ut and Vt are fragment-packed (below);
+                           ldu / ldv are their block pitches in steps           */
 };
+
+/*
+ * Fragment-packed factors (bf16 decode path).  A row-major factor W[N, K]
+ * (Ut: N = r, K = d_in; Vt: N = d_out, K = r) is stored as 16-row blocks,
+ * each a run of 32-column steps; one step of one block is the 1 KiB a wave
+ * feeds to a 16x16x32 matrix-core instruction as its weight operand, so the
+ * decode kernels stream contiguous memory (row-major steps touch 16 rows x
+ * 64 bytes per load, which wastes HBM bandwidth on long rows):
+ *     element (n, k) -> ((b * pitch + s) * 64 + lane) * 8 + e      (elements)
+ *     b = n / 16, s = k / 32, lane = n % 16 + 16 * ((k % 32) / 8), e = k % 8
+ * pitch (steps per block) >= ceil(K / 32).  Entries past N or K are zero.
+ * Tensor-parallel shares stay views: input rows [k0, k1) of U_r (k0 a
+ * multiple of 32) are Ut_packed + (k0 / 32) * 512 with the same pitch, output
+ * columns [n0, n1) of V_r (n0 a multiple of 16) are Vt_packed + (n0 / 16) *
+ * pitch * 512.
+ *
+ * lowrank_packed_bytes: ceil(N / 16) * ceil(K / 32) * 1024 (pitch =
+ * ceil(K / 32)); 0 for non-positive sizes.
+ * lowrank_pack_factor: packed = pack(W), W bf16 [N, K] row-major with pitch
+ * ld (elements), packed of at least ceil(N / 16) * pitch * 1024 bytes; both
+ * device pointers 16-byte aligned, ld a multiple of 8.  Bit-exact copy.
+ * Errors: LR_ERR_ARG (null, non-positive size, ld < K, pitch < ceil(K / 32)),
+ * LR_ERR_ALIGN, LR_ERR_HIP.
+ */
+size_t lowrank_packed_bytes(int64_t N, int64_t K);
+lr_status lowrank_pack_factor(const void* W, int64_t N, int64_t K, int64_t ld, void* packed,
+                              int64_t pitch, hipStream_t stream);
 
 /*
  * lowrank_linear_forward -- the decomposed linear, DeInfer/en §2.A (downward
@@ -102,6 +131,13 @@ enum {
  *            completes, so later calls (and graph replays) need no clearing.
  *            A workspace may serve calls of any shape in turn, never two calls
  *            in flight at once.
+ *   Errors: LR_ERR_DTYPE, LR_ERR_ARG (sizes, missing operands), LR_ERR_ALIGN,
+ *   LR_ERR_WORKSPACE; LR_ERR_UNSUPPORTED on the bf16 decode path (T <= 64)
+ *   when r or a leading dimension reaches 2^24 elements (or a packed pitch
+ *   2^16 steps: the kernel addresses its tiles with 32-bit offsets), and for
+ *   LR_PACKED_WEIGHTS with fp32 or T > 64; LR_ERR_HIP if a launch fails.
+ *   Loads never reach past an operand's last element (the padding after the
+ *   last row of a strided view need not be allocated).
  */
 lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in, int64_t r, int64_t d_out,
                                  const void* x, int64_t ldx, const void* Ut, int64_t ldu,

@@ -18,13 +18,14 @@ import ctypes as C
 import numpy as np
 
 from . import _lib
-from ._lib import (LR_BF16, LR_F32, LR_FULL, LR_STAGE1_ONLY, LR_STAGE2_ONLY, LowrankError,
-                   load, status_string)
+from ._lib import (LR_BF16, LR_F32, LR_FULL, LR_PACKED_WEIGHTS, LR_STAGE1_ONLY, LR_STAGE2_ONLY,
+                   LowrankError, load, status_string)
 
 __all__ = [
     "lowrank_linear_forward", "kv_remap_gather", "lowrank_prepare_decode",
     "lowrank_workspace_bytes", "lowrank_status_string", "lowrank_version",
-    "LR_F32", "LR_BF16", "LR_FULL", "LR_STAGE1_ONLY", "LR_STAGE2_ONLY", "LowrankError", "load",
+    "LR_F32", "LR_BF16", "LR_FULL", "LR_STAGE1_ONLY", "LR_STAGE2_ONLY", "LR_PACKED_WEIGHTS",
+    "LowrankError", "load", "PackedFactor", "pack_factor", "lowrank_packed_bytes",
 ]
 
 
@@ -71,16 +72,67 @@ def lowrank_version() -> int:
     return int(load().lowrank_version())
 
 
+class PackedFactor:
+    """A bf16 factor W[N, K] in the fragment-packed layout of lowrank.h: a
+    view (base element offset, N, K, block pitch in steps) of a flat bf16
+    device tensor.  ``cols(k0, k1)`` and ``rows(n0, n1)`` give the
+    tensor-parallel share views (k0 a multiple of 32, n0 of 16)."""
+
+    def __init__(self, storage, N: int, K: int, pitch: int, offset: int = 0):
+        self.storage, self.N, self.K, self.pitch, self.offset = storage, N, K, pitch, offset
+        self.shape = (N, K)
+        self.dtype = storage.dtype
+        self.device = storage.device
+
+    def data_ptr(self) -> int:
+        return self.storage.data_ptr() + 2 * self.offset
+
+    def cols(self, k0: int, k1: int) -> "PackedFactor":
+        if k0 % 32 or not 0 <= k0 < k1 <= self.K:
+            raise ValueError("column share must start at a multiple of 32")
+        return PackedFactor(self.storage, self.N, k1 - k0, self.pitch, self.offset + k0 // 32 * 512)
+
+    def rows(self, n0: int, n1: int) -> "PackedFactor":
+        if n0 % 16 or not 0 <= n0 < n1 <= self.N:
+            raise ValueError("row share must start at a multiple of 16")
+        return PackedFactor(self.storage, n1 - n0, self.K, self.pitch,
+                            self.offset + n0 // 16 * self.pitch * 512)
+
+
+def lowrank_packed_bytes(N: int, K: int) -> int:
+    return int(load().lowrank_packed_bytes(N, K))
+
+
+def pack_factor(W, stream=None) -> PackedFactor:
+    """Fragment-packed copy of a row-major bf16 device matrix W[N, K]."""
+    torch = _torch()
+    N, K = (int(v) for v in W.shape)
+    pitch = (K + 31) // 32
+    out = torch.empty(lowrank_packed_bytes(N, K) // 2, dtype=torch.bfloat16, device=W.device)
+    st = load().lowrank_pack_factor(_ptr(W), N, K, _ld(W), _ptr(out), pitch,
+                                    _stream(stream, W.device))
+    _lib.check(st, "lowrank_pack_factor")
+    return PackedFactor(out, N, K, pitch)
+
+
+def _wld(w) -> int:
+    return w.pitch if isinstance(w, PackedFactor) else _ld(w)
+
+
 def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, workspace=None,
                            stream=None):
     """y = (x U_r) V_r (or one stage of it, see lowrank.h).  Tensors on one
     HIP device; Ut = U_r^T [r, d_in], Vt = V_r^T [d_out, r]; t_io fp32 [T, r].
-    Returns y (allocated when not given and a stage 2 runs)."""
+    Ut / Vt may be PackedFactor views (bf16, T <= 64), which sets
+    LR_PACKED_WEIGHTS.  Returns y (allocated when not given and a stage 2 runs)."""
     torch = _torch()
     lib = load()
     ref = x if x is not None else t_io
     dev = ref.device
-    if flags == LR_STAGE2_ONLY:
+    if isinstance(Ut, PackedFactor) or isinstance(Vt, PackedFactor):
+        flags |= LR_PACKED_WEIGHTS
+    mode = flags & ~LR_PACKED_WEIGHTS
+    if mode == LR_STAGE2_ONLY:
         T, r = t_io.shape
         d_in = int(Ut.shape[1]) if Ut is not None else 1
         dt = _dtype_code(Vt)
@@ -89,7 +141,7 @@ def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, w
         r = int(Ut.shape[0])
         dt = _dtype_code(x)
     d_out = int(Vt.shape[0]) if Vt is not None else 1
-    if y is None and flags != LR_STAGE1_ONLY:
+    if y is None and mode != LR_STAGE1_ONLY:
         y = torch.empty((T, d_out), dtype=Vt.dtype, device=dev)
     need = lowrank_workspace_bytes(0, dt, T, d_in, r, d_out)
     if workspace is None and need > 0:
@@ -100,8 +152,8 @@ def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, w
     st = lib.lowrank_linear_forward(
         dt, T, d_in, r, d_out,
         _ptr(x), _ld(x) if x is not None else 0,
-        _ptr(Ut), _ld(Ut) if Ut is not None else 0,
-        _ptr(Vt), _ld(Vt) if Vt is not None else 0,
+        _ptr(Ut), _wld(Ut) if Ut is not None else 0,
+        _ptr(Vt), _wld(Vt) if Vt is not None else 0,
         _ptr(y), _ld(y) if y is not None else 0,
         _ptr(t_io), _ld(t_io) if t_io is not None else 0,
         flags, _ptr(workspace), ws_bytes, _stream(stream, dev))

@@ -15,6 +15,7 @@ LR_OK, LR_ERR_ARG, LR_ERR_DTYPE, LR_ERR_ALIGN, LR_ERR_WORKSPACE, LR_ERR_CAPACITY
     LR_ERR_HIP, LR_ERR_UNSUPPORTED = range(8)
 LR_F32, LR_BF16 = 0, 1
 LR_FULL, LR_STAGE1_ONLY, LR_STAGE2_ONLY = 0, 1, 2
+LR_PACKED_WEIGHTS = 4
 
 # every symbol include/lowrank.h declares, with (restype, argtypes)
 _i64, _u, _sz, _p, _pi32 = C.c_int64, C.c_uint, C.c_size_t, C.c_void_p, C.c_void_p
@@ -32,6 +33,8 @@ SIGNATURES = {
     "lowrank_rope_table": (C.c_int, [_i64, _i64, C.c_float, _p, _p]),
     "lowrank_decode_step_workspace_bytes": (C.c_size_t, [_p, _p]),
     "lowrank_layer_decode_step": (C.c_int, [_p, _p, _p, _p, _sz, _p]),
+    "lowrank_packed_bytes": (C.c_size_t, [_i64, _i64]),
+    "lowrank_pack_factor": (C.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p]),
 }
 
 

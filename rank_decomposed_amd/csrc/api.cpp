@@ -56,18 +56,24 @@ extern "C" lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in
                                             int64_t ldt, unsigned flags, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream) {
   if (dt != LR_F32 && dt != LR_BF16) return LR_ERR_DTYPE;
-  if (flags > 2) return LR_ERR_ARG;
+  const bool packed = (flags & LR_PACKED_WEIGHTS) != 0;
+  const unsigned mode = flags & ~(unsigned)LR_PACKED_WEIGHTS;
+  if (mode > 2) return LR_ERR_ARG;
   if (T <= 0 || d_in <= 0 || r <= 0 || d_out <= 0) return LR_ERR_ARG;
   if (T > INT32_MAX || d_in > INT32_MAX || r > INT32_MAX || d_out > INT32_MAX) return LR_ERR_ARG;
-  const bool s1 = flags != LR_STAGE2_ONLY, s2 = flags != LR_STAGE1_ONLY;
-  if (s1 && (!x || !Ut || ldx < d_in || ldu < d_in)) return LR_ERR_ARG;
-  if (s2 && (!Vt || !y || ldv < r || ldy < d_out)) return LR_ERR_ARG;
-  if (flags != LR_FULL && !t_io) return LR_ERR_ARG;
+  const bool s1 = mode != LR_STAGE2_ONLY, s2 = mode != LR_STAGE1_ONLY;
+  // row-major factors: ld in elements; packed: block pitch in 32-column steps
+  const int64_t ku = packed ? (d_in + 31) / 32 : d_in, kv = packed ? (r + 31) / 32 : r;
+  if (s1 && (!x || !Ut || ldx < d_in || ldu < ku)) return LR_ERR_ARG;
+  if (s2 && (!Vt || !y || ldv < kv || ldy < d_out)) return LR_ERR_ARG;
+  if (mode != LR_FULL && !t_io) return LR_ERR_ARG;
   if (t_io && ldt < r) return LR_ERR_ARG;
   if (t_io && !aligned(t_io, 4)) return LR_ERR_ALIGN;
+  if (packed && (dt != LR_BF16 || T > 64)) return LR_ERR_UNSUPPORTED;
   if (dt == LR_BF16) {
-    if (s1 && (!aligned(x, 16) || !aligned(Ut, 16) || ldx % 8 || ldu % 8)) return LR_ERR_ALIGN;
-    if (s2 && (!aligned(Vt, 16) || ldv % 8 || !aligned(y, 2))) return LR_ERR_ALIGN;
+    if (s1 && (!aligned(x, 16) || !aligned(Ut, 16) || ldx % 8 || (!packed && ldu % 8)))
+      return LR_ERR_ALIGN;
+    if (s2 && (!aligned(Vt, 16) || (!packed && ldv % 8) || !aligned(y, 2))) return LR_ERR_ALIGN;
   } else {
     if (s1 && (!aligned(x, 4) || !aligned(Ut, 4))) return LR_ERR_ALIGN;
     if (s2 && (!aligned(Vt, 4) || !aligned(y, 4))) return LR_ERR_ALIGN;
@@ -76,8 +82,10 @@ extern "C" lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return LR_ERR_WORKSPACE;
 
-  lr::DecodeLinear d{T, d_in, r, d_out, x, ldx, Ut, ldu, Vt, ldv, y, ldy, t_io, ldt, flags,
+  lr::DecodeLinear d{T, d_in, r, d_out, x, ldx, Ut, ldu, Vt, ldv, y, ldy, t_io, ldt, mode,
                      workspace};
+  d.packed = packed;
+  if (dt == LR_BF16 && T <= 64 && !lr::decode_supported(d)) return LR_ERR_UNSUPPORTED;
   hipError_t e;
   if (dt == LR_F32)
     e = lr::linear_f32(d, stream);
@@ -85,6 +93,19 @@ extern "C" lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in
     e = lr::decode_linear_bf16(d, stream);
   else
     e = lr::prefill_linear_bf16(d, stream);
+  return e == hipSuccess ? LR_OK : LR_ERR_HIP;
+}
+
+extern "C" size_t lowrank_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return (size_t)((N + 15) / 16) * (size_t)((K + 31) / 32) * 1024;
+}
+
+extern "C" lr_status lowrank_pack_factor(const void* W, int64_t N, int64_t K, int64_t ld,
+                                         void* packed, int64_t pitch, hipStream_t stream) {
+  if (!W || !packed || N <= 0 || K <= 0 || ld < K || pitch < (K + 31) / 32) return LR_ERR_ARG;
+  if (!aligned(W, 16) || !aligned(packed, 16) || ld % 8) return LR_ERR_ALIGN;
+  hipError_t e = lr::pack_factor_bf16(W, N, K, ld, packed, pitch, stream);
   return e == hipSuccess ? LR_OK : LR_ERR_HIP;
 }
 

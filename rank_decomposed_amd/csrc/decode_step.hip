@@ -147,7 +147,7 @@ __global__ __launch_bounds__(512, 1) void recon_kernel(ReconArgs p) {
   const int rr = lane & 15, kq = (lane >> 4) * 8;
 
   // stage the latent tile, zero past K
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (uint64_t)p.cap * p.lda * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, view_bytes(p.cap, p.K, p.lda));
   const int kch = p.k_pad / 8;
   for (int e = threadIdx.x; e < rBM * kch; e += 512) {
     const int row = e / kch, k = (e % kch) * 8;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(512, 1) void recon_kernel(ReconArgs p) {
   }
   __syncthreads();
 
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b, (uint64_t)p.N * p.ldb * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b, view_bytes(p.N, p.K, p.ldb));
   const int ks = p.k_pad / 32;
   const bool tail = (p.K % 32) != 0;
   const int kf = tail ? ks - 1 : ks;
@@ -439,6 +439,8 @@ lr_status check_step(const lr_layer_weights* w, const lr_decode_state* s, const 
     if (!w->Ut[k] || !w->Vt[k] || w->r[k] <= 0) return LR_ERR_ARG;
     if (w->ldu[k] < din[k] || w->ldv[k] < w->r[k]) return LR_ERR_ARG;
     if (!al16(w->Ut[k]) || !al16(w->Vt[k]) || w->ldu[k] % 8 || w->ldv[k] % 8) return LR_ERR_ALIGN;
+    if (w->ldu[k] >= (1 << 24) || w->ldv[k] >= (1 << 24) || din[k] >= (1 << 24))
+      return LR_ERR_UNSUPPORTED;
   }
   if (s->pool_ld < w->r[1] || s->pool_ld < w->r[2]) return LR_ERR_ARG;
   // the reconstruction keeps a 128-row latent tile in LDS

@@ -8,32 +8,44 @@
 // is nearly free next to the HBM stream and it avoids the VALU ceiling of a
 // dot-product GEMV once T grows past ~16.
 //
+// Weights come row-major or fragment-packed (each 16-row x 32-column step
+// stored as the 1 KiB the matrix cores consume, so a wave streams contiguous
+// memory; row-major steps touch 16 rows x 64 B per load, which costs a third
+// of the HBM rate on long rows).
+//
 // One kernel per projection; the grid holds every stage-1 tile and then every
-// stage-2 tile, tile = blockIdx.x.  Workgroups are dispatched to each XCD in
-// index order and stage-1 tiles never wait, so a waiting stage-2 tile can
-// never hold resources that a stage-1 tile it waits for still needs.
-//   stage-1 tile: RT weight rows of U_r^T x one K range.  The 4 waves split
-//     the K range, are reduced through LDS, and with several K ranges per row
-//     tile the partials meet in the workspace; the last to arrive sums them in
-//     K-range order (deterministic) and publishes t (fp32 for t_io, bf16 for
-//     stage 2; for T <= 16 also the bf16 residual t - bf16(t), so stage 2 sees
-//     ~16 mantissa bits at the cost of a second MFMA).
-//   stage-2 tile: RT rows of V_r^T x one K range.  It issues the loads of its
-//     first round of V_r fragments *before* waiting for t, so the V_r stream
-//     overlaps stage 1; then it waits for the "t ready" flag, reads t and
-//     finishes like a stage-1 tile, writing y in bf16.
+// stage-2 tile, tile = blockIdx.x.  Workgroups are dispatched in index order
+// and stage-1 tiles never wait, so a waiting stage-2 tile can never hold
+// resources that a stage-1 tile it waits for still needs.
+//   Every tile is one workgroup of 16 waves on a block of weight rows over a
+//   K range: the waves split the range into contiguous runs and their
+//   partial products meet in a fixed-order tree through LDS.
+//   stage-1 tile: 16*RB1 rows of U_r^T over one of S1 K ranges (S1 > 1 only
+//     where a row block alone would give a workgroup more bytes than it
+//     streams quickly).  With S1 > 1 the partials meet in the workspace and
+//     the last tile of the row block to arrive sums them in K-range order.
+//     The finishing tile publishes its rows of t (fp32 for t_io, bf16 for
+//     stage 2; for T <= 16 also the bf16 residual t - bf16(t), so stage 2
+//     sees ~16 mantissa bits at the cost of a second MFMA) and bumps the
+//     "t ready" counter; the last one raises the GO flag.
+//   stage-2 tile: 16*RB2 rows of V_r^T over all of r.  Each wave issues the
+//     loads of its first PF steps of V_r *before* waiting for GO, so the V_r
+//     stream overlaps stage 1; then it reads t and finishes, writing y in
+//     bf16 (or adding into an fp32 accumulator).
 // Synchronisation avoids cache-wide operations and hot addresses:
-//   * data that crosses workgroups (stage-1 partials, the published t) is
-//     written with device-coherent stores and the writer waits for their
-//     completion before it bumps a counter, so no L2 write-back is needed;
-//     partials are read back with device-coherent loads, and a stage-2 tile
-//     issues one device-scope acquire (L1/L2 invalidate) before reading t;
+//   * data that crosses workgroups (partials, t) is written with
+//     device-coherent stores and the writer waits for their completion before
+//     it bumps a counter; readers use device-coherent loads, so neither side
+//     writes back or invalidates a cache;
 //   * device-scope atomics on one address serialise (~10 ns each on this
-//     part), so producers count on one cache line, the last producer raises a
-//     flag on another line, and waiting tiles poll only the flag.
-// Counters live in the workspace and are returned to zero by the last
-// workgroup, so consecutive calls (and graph replays) need no memset.  Every
-// wait is bounded: past ~1 s it records an error flag and proceeds.
+//     part), so a tile issues at most two, and waiting tiles poll the GO flag,
+//     which only the last producer writes.
+// Counters live in the workspace and return to zero within the call: the
+// last arrival of each row block clears its counter, the last stage-1 tile
+// clears the ready counter, and the last stage-2 tile past the wait clears
+// GO and the stage-2 counter, so consecutive calls (and graph replays) need
+// no memset.  Every wait is bounded: past ~1 s it records an error flag and
+// proceeds.
 #include <algorithm>
 
 #include "lr_common.h"
@@ -43,18 +55,25 @@ namespace lr {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 16;
+constexpr int kThreads = 64 * kWaves;
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kOutside = 0x80000000u;  // past every buffer (tiles stay < 2 GiB)
+constexpr int kCoherentLoad = 16;           // buffer-load cache policy: device scope
 
 // control block (uint32 words) at the start of the workspace; each hot word
-// on a cache line of its own
-enum { CTL_DONE = 0, CTL_TREADY = 32, CTL_GO = 64, CTL_ERR = 96, CTL_CNT = 128 };
+// on a cache line of its own, then one arrival counter per stage-1 row block.
+// Its size is the same for every call, so that data of one call never lands
+// on words another call (of another shape, same workspace) takes as zeroed
+// counters.
+enum { CTL_TREADY = 0, CTL_GO = 32, CTL_DONE2 = 64, CTL_ERR = 96, CTL_CNT = 128,
+       CTL_WORDS = 4096 };
 
 struct DecArgs {
   const uint16_t* x;
   int64_t ldx;
   const uint16_t* ut;
-  int64_t ldu;
+  int64_t ldu;  // row pitch in elements, or block pitch in steps when packed
   const uint16_t* vt;
   int64_t ldv;
   uint16_t* y;
@@ -66,13 +85,13 @@ struct DecArgs {
   uint16_t* thi;  // bf16 t [T, ldtb]
   uint16_t* tlo;  // bf16 residual (T <= 16)
   int64_t ldtb;
-  float* part;     // partial tiles of both stages
-  uint32_t* ctl;   // control block + per-row-tile arrival counters
+  float* part;    // stage-1 split-K partials
+  uint32_t* ctl;  // control block
   int T, d_in, r, d_out;
-  int nrt1, S1, kc1;  // stage 1: row tiles, K ranges, K range width
-  int nrt2, S2, kc2;  // stage 2
-  int64_t part2_off;  // float offset of stage-2 partials in part
-  int t_ready_target; // stage-1 row tiles that publish t before stage 2 may start
+  int nb1, S1, kc1;  // stage-1 row blocks, K ranges per block, K range width
+  int n2;            // stage-2 tiles
+  int wait;          // stage-2 tiles wait for the stage-1 tiles of this launch
+  int packed;        // weights fragment-packed
 };
 
 // Relaxed device-scope atomics: on gfx950 these are plain loads/stores with
@@ -84,280 +103,328 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t load_relaxed(uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void store_coherent(float* p, float v) {
+__device__ __forceinline__ void store_relaxed(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void store_coherent(uint16_t* p, uint16_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// wait until every memory operation this thread issued has completed
+// wait until every memory operation this wave issued has completed
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
-__device__ __forceinline__ void store_relaxed(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// NB fragments of one k-step at byte offset step_off from the per-lane bases
+// off[]; a dead step goes to an offset outside the buffer (reads zero, no
+// memory access).  COH selects device-coherent loads.
+template <int NB, bool COH>
+__device__ __forceinline__ void frag_load_at(u32x4 (&f)[NB], __amdgpu_buffer_rsrc_t rs,
+                                             const uint32_t (&off)[NB], uint32_t step_off,
+                                             bool live) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int o = (int)(live ? off[nb] + step_off : kOutside);
+    f[nb] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, COH ? kCoherentLoad : 0));
+  }
 }
 
-// One tile: rows [row0, row0 + 16*RB) of B, K range [kbeg, kend); each wave
-// takes a contiguous run of 32-wide k-steps and walks it KSW steps at a time.
-// Result (reduced over the 4 waves) left in LDS as red[NREG][64] with
-// element (reg, lane) -> token tb*16 + 4*(lane>>4) + v, row row0 + rb*16 + (lane&15),
-// reg = (tb*RB + rb)*4 + v.
-template <int TB, int RB, int KSW, bool SPLIT, bool WAIT>
-__device__ void tile_product(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Alo,
-                             int64_t lda, const uint16_t* __restrict__ B, int64_t ldb, int T,
-                             int N, int row0, int kbeg, int kend, float* red, uint32_t* ctl,
-                             int ready_target) {
-  // RB 16-row blocks per wave; all 4 waves share the rows and split K
+// Weight operand of one tile: rows [row0, row0 + 16*RB) over K range
+// [kbeg, kend) (kbeg a multiple of 32), as a buffer based at the tile's first
+// element plus per-lane fragment offsets and the byte stride of one k-step.
+template <int RB>
+struct WeightTile {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off[RB];
+  uint32_t step;
+  __device__ WeightTile(const uint16_t* B, int64_t ld, bool packed, int N, int row0, int kbeg,
+                        int kend, int lane) {
+    const int ksteps = (kend - kbeg + 31) / 32;
+    if (packed) {
+      // fragment (block b, step s) at ((b*ld + s)*64 + lane)*16 bytes
+      const int b0 = row0 / 16, nb = min(RB, (N + 15) / 16 - b0);
+      rs = make_rsrc(B + ((int64_t)b0 * ld + kbeg / 32) * 512,
+                     ((uint64_t)(nb - 1) * ld + ksteps) * 1024);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) off[r] = (uint32_t)((r * ld * 64 + lane) * 16);
+      step = 1024;
+    } else {
+      rs = make_rsrc(B + (int64_t)row0 * ld + kbeg,
+                     view_bytes(min(N - row0, 16 * RB), kend - kbeg, ld));
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        off[r] = (uint32_t)(((r * 16 + (lane & 15)) * ld + (lane >> 4) * 8) * 2);
+      step = 64;
+    }
+  }
+};
+
+// This wave's share of one tile: weight rows [row0, row0 + 16*RB) against
+// A[0:T, kbeg:kend), over the wave's contiguous run of 32-wide k-steps.  Per
+// round the wave issues the weight loads, then the activation loads, then
+// the MFMAs.  Rows past T or N and steps past the wave's run fall outside
+// the buffers and read zero, so the step loop has no branches; only a ragged
+// last step (K range not a multiple of 32) is masked, after the loop.
+// A stage-2 tile (WAIT) first issues the weight loads of its first PF steps,
+// then waits for GO, then reads t with device-coherent loads.
+// acc[tb][rb] lane l holds C[token tb*16 + 4*(l>>4) + v][row row0 + rb*16 + (l&15)].
+template <int TB, int RB, int KSW, int PF, bool SPLIT, bool WAIT>
+__device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ A,
+                             const uint16_t* __restrict__ Alo, int64_t lda,
+                             const uint16_t* __restrict__ B, int64_t ldb, bool packed, int T,
+                             int N, int row0, int kbeg, int kend, uint32_t* ctl, bool wait) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int rr = lane & 15;
   const int kq = (lane >> 4) * 8;
+  const int K = kend - kbeg;
+  const WeightTile<RB> w(B, ldb, packed, N, row0, kbeg, kend, lane);
+  const uint64_t abytes = view_bytes(min(T, 16 * TB), K, lda);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + kbeg, abytes);
+  const __amdgpu_buffer_rsrc_t ral = make_rsrc((SPLIT ? Alo : A) + kbeg, abytes);
+  uint32_t aoff[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) aoff[tb] = (uint32_t)(((tb * 16 + (lane & 15)) * lda + kq) * 2);
 
-  const int nsteps = (kend - kbeg + 31) / 32;
+  const int nsteps = (K + 31) / 32;
+  const int nfull = K / 32;
   const int per = (nsteps + kWaves - 1) / kWaves;  // contiguous k-steps per wave
-  const int s_lo = wave * per;
+  const int s_lo = min(nsteps, wave * per);
   const int s_hi = min(nsteps, s_lo + per);
+  const int s_full = min(s_hi, nfull);
 
-  const uint16_t* brow[RB];
-  bool bok[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = row0 + rb * 16 + rr;
-    bok[rb] = row < N;
-    brow[rb] = B + (int64_t)(bok[rb] ? row : 0) * ldb;
-  }
-  const uint16_t* arow[TB];
-  const uint16_t* alrow[TB];
-  bool aok[TB];
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb) {
-    const int tok = tb * 16 + rr;
-    aok[tb] = tok < T;
-    arow[tb] = A + (int64_t)(aok[tb] ? tok : 0) * lda;
-    alrow[tb] = SPLIT ? Alo + (int64_t)(aok[tb] ? tok : 0) * lda : nullptr;
-  }
-
-  f32x4 acc[TB][RB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[tb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < RB; ++r) acc[tb][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bool waited = !WAIT;
-  for (int s0 = s_lo; s0 < s_hi || !waited; s0 += KSW) {
-    u32x4 bv[KSW][RB];
+  // KSW steps whose weights are in bv: load the activations, multiply
+  auto round = [&](const u32x4 (*bv)[RB], int sb) {
+    u32x4 av[KSW][TB], alv[KSW][TB];
 #pragma unroll
     for (int i = 0; i < KSW; ++i) {
-      const int s = s0 + i;
-      const int k = kbeg + s * 32 + kq;
-      const bool kin = s < s_hi && k < kend;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        u32x4 v = u32x4{0, 0, 0, 0};
-        if (kin && bok[rb]) {
-          v = ldg16_stream(brow[rb] + k);
-          if (k + 8 > kend) v = mask_tail(v, k, kend);
-        }
-        bv[i][rb] = v;
-      }
-    }
-    if (!waited) {
-      // the first round of weights is in flight; now wait for t
-      if (threadIdx.x == 0 && ready_target > 0) {
-        uint32_t spins = 0;
-        while (load_relaxed(ctl + CTL_GO) == 0u) {
-          __builtin_amdgcn_s_sleep(8);
-          if (++spins > kSpinLimit) {
-            store_relaxed(ctl + CTL_ERR, 1u);
-            break;
-          }
-        }
-        fence_acquire();
-      }
-      __syncthreads();
-      waited = true;
+      frag_load_at<TB, WAIT>(av[i], ra, aoff, (sb + i) * 64, sb + i < s_full);
+      if (SPLIT) frag_load_at<TB, WAIT>(alv[i], ral, aoff, (sb + i) * 64, sb + i < s_full);
     }
 #pragma unroll
-    for (int i = 0; i < KSW; ++i) {
-      const int s = s0 + i;
-      // wave-uniform skip only: MFMA reads every lane's operands, so lanes
-      // past kend take part with zero-filled fragments
-      if (s >= s_hi) continue;
-      const int k = kbeg + s * 32 + kq;
-      const bool kin = k < kend;
-      u32x4 av[TB], alv[TB];
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        av[tb] = (kin && aok[tb]) ? ldg16(arow[tb] + k) : u32x4{0, 0, 0, 0};
-        if (SPLIT) alv[tb] = (kin && aok[tb]) ? ldg16(alrow[tb] + k) : u32x4{0, 0, 0, 0};
-        if (kin && k + 8 > kend) {
-          av[tb] = mask_tail(av[tb], k, kend);
-          if (SPLIT) alv[tb] = mask_tail(alv[tb], k, kend);
-        }
-      }
+    for (int i = 0; i < KSW; ++i)
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          acc[tb][rb] = mfma16x16x32(av[tb], bv[i][rb], acc[tb][rb]);
-          if (SPLIT) acc[tb][rb] = mfma16x16x32(alv[tb], bv[i][rb], acc[tb][rb]);
+        for (int r = 0; r < RB; ++r) {
+          acc[tb][r] = mfma16x16x32(av[i][tb], bv[i][r], acc[tb][r]);
+          if (SPLIT) acc[tb][r] = mfma16x16x32(alv[i][tb], bv[i][r], acc[tb][r]);
         }
-    }
-    if (s0 >= s_hi) break;  // wait-only round of an idle wave
-  }
+  };
 
-  // reduce the 4 waves: ((w0 + w2) + (w1 + w3)), fixed order
-  constexpr int NREG = TB * RB * 4;
-  float* buf0 = red;               // [NREG][64]
-  float* buf1 = red + NREG * 64;   // [NREG][64]
-  if (wave >= 2) {
-    float* b = wave == 2 ? buf0 : buf1;
+  int s0 = s_lo;
+  if (WAIT) {
+    u32x4 bp[PF][RB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
+    for (int i = 0; i < PF; ++i)
+      frag_load_at<RB, false>(bp[i], w.rs, w.off, (s_lo + i) * w.step, s_lo + i < s_full);
+    if (wait && threadIdx.x == 0) {
+      uint32_t spins = 0;
+      while (load_relaxed(ctl + CTL_GO) == 0u) {
+        __builtin_amdgcn_s_sleep(8);
+        if (++spins > kSpinLimit) {
+          store_relaxed(ctl + CTL_ERR, 1u);
+          break;
+        }
+      }
+    }
+    __syncthreads();
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) b[((tb * RB + rb) * 4 + v) * 64 + lane] = acc[tb][rb][v];
+    for (int i0 = 0; i0 < PF; i0 += KSW) round(bp + i0, s_lo + i0);
+    s0 = s_lo + PF;
   }
-  __syncthreads();
-  if (wave < 2) {
-    float* b = wave == 0 ? buf0 : buf1;
+  for (; s0 < s_full; s0 += KSW) {
+    u32x4 bv[KSW][RB];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[tb][rb][v] += b[((tb * RB + rb) * 4 + v) * 64 + lane];
+    for (int i = 0; i < KSW; ++i)
+      frag_load_at<RB, false>(bv[i], w.rs, w.off, (s0 + i) * w.step, s0 + i < s_full);
+    round(bv, s0);
   }
-  __syncthreads();
-  if (wave == 1) {
+  if (nfull < nsteps && nfull >= s_lo && nfull < s_hi) {
+    // ragged last step of the K range, owned by this wave
+    const int kk = nfull * 32 + kq;
+    u32x4 bv[RB], av[TB], alv[TB];
+    frag_load_at<RB, false>(bv, w.rs, w.off, nfull * w.step, true);
+    frag_load_at<TB, WAIT>(av, ra, aoff, nfull * 64, true);
+    if (SPLIT) frag_load_at<TB, WAIT>(alv, ral, aoff, nfull * 64, true);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) bv[r] = mask_tail_nb(bv[r], kk, K);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      av[tb] = mask_tail_nb(av[tb], kk, K);
+      if (SPLIT) alv[tb] = mask_tail_nb(alv[tb], kk, K);
+    }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) buf1[((tb * RB + rb) * 4 + v) * 64 + lane] = acc[tb][rb][v];
+      for (int r = 0; r < RB; ++r) {
+        acc[tb][r] = mfma16x16x32(av[tb], bv[r], acc[tb][r]);
+        if (SPLIT) acc[tb][r] = mfma16x16x32(alv[tb], bv[r], acc[tb][r]);
+      }
   }
-  __syncthreads();
-  if (wave == 0) {
+}
+
+// Sum the 16 waves' partial products into wave 0, in a fixed order:
+// pass h adds wave w + h into wave w (h = 8, 4, 2, 1).
+template <int TB, int RB>
+__device__ void tree_reduce(f32x4 (&acc)[TB][RB], float* red) {
+  constexpr int NR = TB * RB * 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int h = kWaves / 2; h >= 1; h >>= 1) {
+    if (wave >= h && wave < 2 * h) {
+      float* b = red + (wave - h) * NR * 64;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) b[((tb * RB + r) * 4 + v) * 64 + lane] = acc[tb][r][v];
+    }
+    __syncthreads();
+    if (wave < h) {
+      const float* b = red + wave * NR * 64;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[tb][r][v] += b[((tb * RB + r) * 4 + v) * 64 + lane];
+    }
+    __syncthreads();
+  }
+}
+
+// Wave 0 of a stage-1 tile with S1 > 1: park the tile's partial, count the
+// arrival; the last arrival of the row block sums all S1 partials in K-range
+// order into acc and returns true.
+template <int TB, int RB>
+__device__ bool meet_partials(f32x4 (&acc)[TB][RB], const DecArgs& p, int blk, int s) {
+  constexpr int NR = TB * RB * 4;
+  const int lane = threadIdx.x & 63;
+  float* base = p.part + (int64_t)blk * p.S1 * (NR * 64) + lane;
+  float* mine = base + (int64_t)s * (NR * 64);
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) store_coherent(mine + ((tb * RB + r) * 4 + v) * 64, acc[tb][r][v]);
+  wait_memory();
+  uint32_t old = 0;
+  if (lane == 0) old = atomic_add_agent(p.ctl + CTL_CNT + blk, 1u);
+  old = __builtin_amdgcn_readfirstlane(old);
+  if (old != (uint32_t)(p.S1 - 1)) return false;
+  if (lane == 0) store_relaxed(p.ctl + CTL_CNT + blk, 0u);  // every sibling has arrived
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[tb][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // loads go out JB partials at a time (~64 registers) so that their round
+  // trips overlap
+  constexpr int JB = NR >= 64 ? 1 : (64 / NR > 8 ? 8 : 64 / NR);
+  for (int j0 = 0; j0 < p.S1; j0 += JB) {
+    float l[JB][NR];
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const float* pj = base + (int64_t)min(j0 + jj, p.S1 - 1) * (NR * 64);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) l[jj][i] = load_coherent(pj + i * 64);
+    }
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float add = l[jj][(tb * RB + r) * 4 + v];
+            acc[tb][r][v] = j0 + jj < p.S1 ? acc[tb][r][v] + add : acc[tb][r][v];
+          }
+  }
+  return true;
+}
+
+template <int TB, int RB1, int RB2, int KSW1, int KSW2, int PF, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs p) {
+  constexpr int NREG = TB * (RB1 > RB2 ? RB1 : RB2) * 4;
+  __shared__ float red[(kWaves / 2) * NREG * 64];
+  const int tile = (int)blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n1 = p.nb1 * p.S1;
+
+  if (tile < n1) {
+    const int blk = tile / p.S1, s = tile % p.S1;
+    const int row0 = blk * 16 * RB1;
+    const int kbeg = s * p.kc1, kend = min(p.d_in, kbeg + p.kc1);
+    f32x4 acc[TB][RB1];
+    tile_product<TB, RB1, KSW1, KSW1, false, false>(acc, p.x, nullptr, p.ldx, p.ut, p.ldu,
+                                                    p.packed != 0, p.T, p.r, row0, kbeg, kend,
+                                                    p.ctl, false);
+    tree_reduce<TB, RB1>(acc, red);
+    if (wave != 0) return;
+    if (p.S1 > 1 && !meet_partials<TB, RB1>(acc, p, blk, s)) return;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB1; ++rb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int e = ((tb * RB + rb) * 4 + v) * 64 + lane;
-          buf0[e] = acc[tb][rb][v] + buf1[e];
+          const int tok = tb * 16 + 4 * (lane >> 4) + v, n = row0 + rb * 16 + (lane & 15);
+          if (tok >= p.T || n >= p.r) continue;
+          const float val = acc[tb][rb][v];
+          if (p.t32) p.t32[(int64_t)tok * p.ldt32 + n] = val;
+          const uint32_t hi = f2bf(val);
+          store_coherent(p.thi + (int64_t)tok * p.ldtb + n, (uint16_t)hi);
+          if (SPLIT) store_coherent(p.tlo + (int64_t)tok * p.ldtb + n, (uint16_t)f2bf(val - bf2f(hi)));
         }
-  }
-  __syncthreads();
-}
-
-// Map a flat result element e = reg*64 + lane to (token, row offset).
-template <int RB>
-__device__ __forceinline__ void elem_coords(int e, int* tok, int* row) {
-  const int reg = e >> 6, lane = e & 63;
-  const int v = reg & 3, rb = (reg >> 2) % RB, tb = (reg >> 2) / RB;
-  *tok = tb * 16 + 4 * (lane >> 4) + v;
-  *row = rb * 16 + (lane & 15);
-}
-
-// Stage epilogue: sum split-K partials if needed, then write t (stage 1) or
-// y (stage 2).  Called by every thread of the workgroup.
-template <int TB, int RB, bool SPLIT, bool STAGE1>
-__device__ void finish_tile(const DecArgs& p, float* red, int rt, int s, int S, int row0,
-                            uint32_t* sh_flag) {
-  constexpr int NREG = TB * RB * 4;
-  float* part = STAGE1 ? p.part : p.part + p.part2_off;
-  uint32_t* cnt = p.ctl + CTL_CNT + (STAGE1 ? 0 : p.nrt1);
-  bool final_tile = true;
-  if (S > 1) {
-    float* mine = part + ((int64_t)rt * S + s) * (NREG * 64);
-    for (int e = threadIdx.x; e < NREG * 64; e += 256) store_coherent(mine + e, red[e]);
-    wait_memory();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t old = atomic_add_agent(cnt + rt, 1u);
-      *sh_flag = (old == (uint32_t)(S - 1)) ? 1u : 0u;
-      if (*sh_flag) store_relaxed(cnt + rt, 0u);  // every sibling has arrived
-    }
-    __syncthreads();
-    final_tile = *sh_flag != 0;
-    if (final_tile) {
-      const float* base = part + (int64_t)rt * S * (NREG * 64);
-      for (int e = threadIdx.x; e < NREG * 64; e += 256) {
-        float v = 0.f;
-        for (int j = 0; j < S; ++j) v += load_coherent(base + (int64_t)j * (NREG * 64) + e);
-        red[e] = v;
-      }
-      __syncthreads();
-    }
-  }
-  if (!final_tile) return;
-  const int N = STAGE1 ? p.r : p.d_out;
-  for (int e = threadIdx.x; e < NREG * 64; e += 256) {
-    int tok, ro;
-    elem_coords<RB>(e, &tok, &ro);
-    const int n = row0 + ro;
-    if (tok >= p.T || n >= N) continue;
-    const float v = red[e];
-    if (STAGE1) {
-      if (p.t32) p.t32[(int64_t)tok * p.ldt32 + n] = v;
-      const uint32_t hi = f2bf(v);
-      store_coherent(p.thi + (int64_t)tok * p.ldtb + n, (uint16_t)hi);
-      if (SPLIT) store_coherent(p.tlo + (int64_t)tok * p.ldtb + n, (uint16_t)f2bf(v - bf2f(hi)));
-    } else if (p.yacc) {
-      p.yacc[(int64_t)tok * p.ldacc + n] += v;   // each element owned by one tile
-    } else {
-      p.y[(int64_t)tok * p.ldy + n] = (uint16_t)f2bf(v);
-    }
-  }
-  if (STAGE1) {
-    wait_memory();
-    __syncthreads();
-    if (threadIdx.x == 0) {
+    wait_memory();  // this block's t is visible device-wide before it is counted
+    if (lane == 0) {
       const uint32_t old = atomic_add_agent(p.ctl + CTL_TREADY, 1u);
-      if (old == (uint32_t)(p.t_ready_target - 1)) store_relaxed(p.ctl + CTL_GO, 1u);
+      if (old == (uint32_t)(p.nb1 - 1)) {  // every row block has published
+        store_relaxed(p.ctl + CTL_TREADY, 0u);
+        if (p.wait) store_relaxed(p.ctl + CTL_GO, 1u);
+      }
     }
-  }
-}
-
-template <int TB, int RB1, int RB2, int KSW, bool SPLIT>
-__global__ __launch_bounds__(256) void decode_kernel(DecArgs p) {
-  constexpr int NREG = TB * (RB1 > RB2 ? RB1 : RB2) * 4;
-  __shared__ float red[2 * NREG * 64];
-  __shared__ uint32_t sh_flag;
-
-  const int n1 = p.nrt1 * p.S1, n2 = p.nrt2 * p.S2;
-  const int tile = (int)blockIdx.x;
-  if (tile < n1) {
-    const int rt = tile / p.S1, s = tile % p.S1;
-    const int kbeg = s * p.kc1, kend = min(p.d_in, kbeg + p.kc1);
-    tile_product<TB, RB1, KSW, false, false>(p.x, nullptr, p.ldx, p.ut, p.ldu, p.T, p.r,
-                                             rt * 16 * RB1, kbeg, kend, red, p.ctl, 0);
-    finish_tile<TB, RB1, SPLIT, true>(p, red, rt, s, p.S1, rt * 16 * RB1, &sh_flag);
-  } else {
-    const int t2 = tile - n1;
-    const int rt = t2 / p.S2, s = t2 % p.S2;
-    const int kbeg = s * p.kc2, kend = min(p.r, kbeg + p.kc2);
-    tile_product<TB, RB2, KSW, SPLIT, true>(p.thi, p.tlo, p.ldtb, p.vt, p.ldv, p.T, p.d_out,
-                                            rt * 16 * RB2, kbeg, kend, red, p.ctl,
-                                            p.t_ready_target);
-    finish_tile<TB, RB2, SPLIT, false>(p, red, rt, s, p.S2, rt * 16 * RB2, &sh_flag);
+    return;
   }
 
-  // the last workgroup to finish returns the counters to zero
-  if (threadIdx.x == 0) {
-    const uint32_t total = (uint32_t)(n1 + n2);
-    const uint32_t old = atomic_add_agent(p.ctl + CTL_DONE, 1u);
-    if (old == total - 1) {
-      store_relaxed(p.ctl + CTL_TREADY, 0u);
-      store_relaxed(p.ctl + CTL_GO, 0u);
-      store_relaxed(p.ctl + CTL_DONE, 0u);
-    }
+  const int row0 = (tile - n1) * 16 * RB2;
+  f32x4 acc[TB][RB2];
+  tile_product<TB, RB2, KSW2, PF, SPLIT, true>(acc, p.thi, p.tlo, p.ldtb, p.vt, p.ldv,
+                                               p.packed != 0, p.T, p.d_out, row0, 0, p.r, p.ctl,
+                                               p.wait != 0);
+  // count this tile past the wait; the last one clears GO for the next call
+  uint32_t old = 0;
+  if (p.wait && threadIdx.x == 0) old = atomic_add_agent(p.ctl + CTL_DONE2, 1u);
+  tree_reduce<TB, RB2>(acc, red);
+  if (wave != 0) return;
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int rb = 0; rb < RB2; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = tb * 16 + 4 * (lane >> 4) + v, n = row0 + rb * 16 + (lane & 15);
+        if (tok >= p.T || n >= p.d_out) continue;
+        const float val = acc[tb][rb][v];
+        if (p.yacc)
+          p.yacc[(int64_t)tok * p.ldacc + n] += val;  // each element owned by one tile
+        else
+          p.y[(int64_t)tok * p.ldy + n] = (uint16_t)f2bf(val);
+      }
+  if (p.wait && threadIdx.x == 0 && old == (uint32_t)(p.n2 - 1)) {
+    store_relaxed(p.ctl + CTL_GO, 0u);
+    store_relaxed(p.ctl + CTL_DONE2, 0u);
   }
 }
 
@@ -380,52 +447,49 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // Tiling of one call; identical on the sizing and launch sides.
 struct Plan {
-  int TB, RB1, RB2;
-  int nrt1, S1, kc1, nrt2, S2, kc2;
+  int TB, RB1, RB2, nb1, S1, kc1, n2;
   int64_t ldtb;
-  size_t off_part, part2_off_floats, off_thi, off_tlo, bytes;
+  size_t off_part, off_thi, off_tlo, bytes;
 };
 
 Plan make_plan(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
   Plan pl{};
   pl.TB = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
-  pl.RB1 = pl.TB;                   // activation re-reads ~ T / (16 RB1) of the weight bytes
-  pl.RB2 = pl.TB == 4 ? 2 : pl.TB;
-  // stage 1: split K until ~512 tiles are in flight, but keep each K range
-  // >= kc_min so the fp32 partials stay a small fraction of the weight bytes
-  const int RT1 = 16 * pl.RB1;
-  pl.nrt1 = (int)((r + RT1 - 1) / RT1);
-  const int kc_min = pl.TB == 1 ? 128 : 512;
-  int S1 = (int)((512 + pl.nrt1 - 1) / pl.nrt1);
-  int kc1 = (int)round_up((d_in + S1 - 1) / S1, 128);
-  if (kc1 < kc_min) kc1 = kc_min;
-  S1 = (int)((d_in + kc1 - 1) / kc1);
-  pl.S1 = S1;
-  pl.kc1 = kc1;
-  // stage 2: one tile per row block, whole K (several register rounds)
-  const int RT2 = 16 * pl.RB2;
-  pl.nrt2 = (int)((d_out + RT2 - 1) / RT2);
-  pl.S2 = 1;
-  pl.kc2 = (int)round_up(r, 32);
+  pl.RB1 = pl.TB == 1 ? 1 : 2;
+  pl.RB2 = 2;
+  pl.nb1 = (int)((r + 16 * pl.RB1 - 1) / (16 * pl.RB1));
+  pl.n2 = (int)((d_out + 16 * pl.RB2 - 1) / (16 * pl.RB2));
+  // split K when a row block would hand one workgroup more than ~256 KiB of
+  // weight and activation bytes (one workgroup streams ~40 GB/s)
+  const int64_t rows = 16 * pl.RB1 + std::min<int64_t>(T, 16 * pl.TB);
+  const int64_t kc_max = std::max<int64_t>(32, (262144 / (2 * rows)) / 32 * 32);
+  const int64_t steps = (d_in + 31) / 32;
+  pl.S1 = (int)((d_in + kc_max - 1) / kc_max);
+  if (CTL_CNT + pl.nb1 > CTL_WORDS) pl.S1 = 1;  // no counters for that many row blocks
+  pl.kc1 = (int)((steps + pl.S1 - 1) / pl.S1 * 32);
+  pl.S1 = (int)((d_in + pl.kc1 - 1) / pl.kc1);
   pl.ldtb = round_up(r, 8);
-  const size_t tile1 = (size_t)pl.TB * pl.RB1 * 4 * 64, tile2 = (size_t)pl.TB * pl.RB2 * 4 * 64;
-  const size_t p1 = pl.S1 > 1 ? (size_t)pl.nrt1 * pl.S1 * tile1 : 0;
-  const size_t p2 = pl.S2 > 1 ? (size_t)pl.nrt2 * pl.S2 * tile2 : 0;
-  const size_t ctl_bytes = round_up(4 * (CTL_CNT + pl.nrt1 + pl.nrt2), 256);
-  pl.off_part = ctl_bytes;
-  pl.part2_off_floats = p1;
-  pl.off_thi = round_up(pl.off_part + (p1 + p2) * 4, 256);
+  const size_t nr1 = (size_t)pl.TB * pl.RB1 * 4 * 64;  // floats per stage-1 tile
+  const size_t part = pl.S1 > 1 ? (size_t)pl.nb1 * pl.S1 * nr1 * 4 : 0;
+  pl.off_part = 4 * CTL_WORDS;
+  pl.off_thi = round_up(pl.off_part + part, 256);
   const size_t tb_bytes = round_up(T * pl.ldtb * 2, 256);
   pl.off_tlo = pl.off_thi + tb_bytes;
   pl.bytes = pl.off_tlo + tb_bytes;
   return pl;
 }
 
-template <int TB, int RB1, int RB2>
+// Per token block: weight rows per tile (16*RB1, 16*RB2), k-steps per round
+// (KSW1, KSW2) and stage-2 prefetch depth PF, sized so a wave holds at most
+// ~64 registers of loads in flight.
+template <int TB>
 hipError_t launch_decode(const DecArgs& a, int grid, hipStream_t st) {
-  constexpr int KSW = 8 / TB;
-  hipLaunchKernelGGL((decode_kernel<TB, RB1, RB2, KSW, TB == 1>), dim3(grid), dim3(256), 0, st,
-                     a);
+  if (TB == 1)
+    hipLaunchKernelGGL((decode_kernel<1, 1, 2, 8, 4, 4, true>), dim3(grid), dim3(kThreads), 0, st, a);
+  else if (TB == 2)
+    hipLaunchKernelGGL((decode_kernel<2, 2, 2, 4, 2, 4, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<4, 2, 2, 2, 2, 4, false>), dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -460,17 +524,16 @@ hipError_t decode_linear_bf16(const DecodeLinear& d, hipStream_t st) {
   a.d_in = (int)d.d_in;
   a.r = (int)d.r;
   a.d_out = (int)d.d_out;
-  a.nrt1 = pl.nrt1;
+  a.nb1 = pl.nb1;
   a.S1 = pl.S1;
   a.kc1 = pl.kc1;
-  a.nrt2 = pl.nrt2;
-  a.S2 = pl.S2;
-  a.kc2 = pl.kc2;
-  a.part2_off = (int64_t)pl.part2_off_floats;
-  a.t_ready_target = pl.nrt1;
+  a.n2 = pl.n2;
+  a.wait = 1;
+  a.packed = d.packed ? 1 : 0;
 
   if (d.flags == 1) {  // stage 1 only
-    a.nrt2 = 0;
+    a.n2 = 0;
+    a.wait = 0;
   } else if (d.flags == 2) {  // stage 2 only: t from t_io
     const int64_t total = d.T * pl.ldtb;
     int blocks = (int)((total + 255) / 256);
@@ -479,14 +542,14 @@ hipError_t decode_linear_bf16(const DecodeLinear& d, hipStream_t st) {
                        (int)d.r, a.thi, pl.TB == 1 ? a.tlo : (uint16_t*)nullptr, pl.ldtb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    a.nrt1 = 0;
-    a.t_ready_target = 0;
+    a.nb1 = 0;
+    a.wait = 0;
   }
-  const int grid = a.nrt1 * a.S1 + a.nrt2 * a.S2;
+  const int grid = a.nb1 * a.S1 + a.n2;
   switch (pl.TB) {
-    case 1: return launch_decode<1, 1, 1>(a, grid, st);
-    case 2: return launch_decode<2, 2, 2>(a, grid, st);
-    default: return launch_decode<4, 4, 2>(a, grid, st);
+    case 1: return launch_decode<1>(a, grid, st);
+    case 2: return launch_decode<2>(a, grid, st);
+    default: return launch_decode<4>(a, grid, st);
   }
 }
 

@@ -58,9 +58,9 @@ __global__ __launch_bounds__(256, 1) void fused_kernel(FusedArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m0 = blockIdx.x * kBM;
   const int rr = lane & 15, kq = (lane >> 4) * 8;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint64_t)p.M * p.ldx * 2);
-  const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.ut, (uint64_t)p.r * p.ldu * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vt, (uint64_t)p.d_out * p.ldv * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, view_bytes(p.M, p.d_in, p.ldx));
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.ut, view_bytes(p.r, p.d_in, p.ldu));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vt, view_bytes(p.d_out, p.r, p.ldv));
 
   // ---------------- stage 1: ts = bf16(x[m0:m0+64] . U_r) ----------------
   {

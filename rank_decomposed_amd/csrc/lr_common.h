@@ -49,6 +49,17 @@ __device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Branch-free variant of mask_tail for hot loops (selects, no early exit).
+__device__ __forceinline__ u32x4 mask_tail_nb(u32x4 v, int k0, int kmax) {
+  const int valid = kmax - k0;
+  u32x4 m;
+  m.x = (0 < valid ? 0x0000ffffu : 0u) | (1 < valid ? 0xffff0000u : 0u);
+  m.y = (2 < valid ? 0x0000ffffu : 0u) | (3 < valid ? 0xffff0000u : 0u);
+  m.z = (4 < valid ? 0x0000ffffu : 0u) | (5 < valid ? 0xffff0000u : 0u);
+  m.w = (6 < valid ? 0x0000ffffu : 0u) | (7 < valid ? 0xffff0000u : 0u);
+  return v & m;
+}
+
 // Zero the bf16 elements of a 16-byte chunk whose index (k0 + e) >= kmax.
 __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int k0, int kmax) {
   int valid = kmax - k0;
@@ -70,6 +81,14 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int k0, int kmax) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+// Bytes of a row-major bf16 view [rows, cols] with pitch ld (elements), from
+// its first element to the end of the 16-byte granule holding its last one.
+// As a buffer extent it keeps every load inside the view's own rows: the
+// padding after the last row is never read, wherever the allocation ends.
+__device__ __forceinline__ uint64_t view_bytes(int64_t rows, int64_t cols, int64_t ld) {
+  return rows <= 0 || cols <= 0 ? 0 : ((((uint64_t)(rows - 1) * ld + cols) * 2 + 15) & ~15ull);
 }
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {

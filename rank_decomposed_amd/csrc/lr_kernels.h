@@ -26,9 +26,21 @@ struct DecodeLinear {
   // writing y; used for residual updates
   float* y_acc = nullptr;
   int64_t ld_acc = 0;
+  // bf16 paths: Ut/Vt fragment-packed, ldu/ldv = block pitch in 32-column steps
+  bool packed = false;
 };
 
 // bf16, T <= 64: streamed skinny MFMA path.
+// The decode kernel addresses each 64-row tile with 32-bit offsets: every
+// leading dimension (and r) must stay below 2^24 elements.
+inline bool decode_supported(const DecodeLinear& d) {
+  const int64_t lim = int64_t(1) << 24;
+  if (d.packed) return d.ldx < lim && d.ldu < (1 << 16) && d.ldv < (1 << 16) && d.r < lim;
+  return d.ldx < lim && d.ldu < lim && d.ldv < lim && d.r < lim;
+}
+// Fragment-packed copy of a row-major bf16 W[N, K] (layout in lowrank.h).
+hipError_t pack_factor_bf16(const void* W, int64_t N, int64_t K, int64_t ld, void* packed,
+                            int64_t pitch, hipStream_t st);
 size_t decode_workspace_bytes(int64_t T, int64_t d_in, int64_t r, int64_t d_out);
 hipError_t decode_linear_bf16(const DecodeLinear& d, hipStream_t st);
 

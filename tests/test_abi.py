@@ -76,6 +76,9 @@ def _fwd(**kw):
     (dict(ws=None, wsb=0), _lib.LR_ERR_WORKSPACE),   # decode path needs scratch
     (dict(ws=A16, wsb=16), _lib.LR_ERR_WORKSPACE),
     (dict(ws=A16 + 16, wsb=1 << 30), _lib.LR_ERR_WORKSPACE),  # not 256-aligned
+    # decode path: 32-bit tile offsets need every ld below 2^24 elements
+    (dict(ldx=1 << 24, ws=A16, wsb=1 << 30), _lib.LR_ERR_UNSUPPORTED),
+    (dict(ldv=1 << 24, ws=A16, wsb=1 << 30), _lib.LR_ERR_UNSUPPORTED),
 ])
 def test_linear_rejects_bad_arguments(kw, status):
     assert _fwd(**kw) == status

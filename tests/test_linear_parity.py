@@ -161,3 +161,23 @@ def test_graph_replay_matches_eager(T):
         assert np.array_equal(got, eager), rep
         _, yr = oracle.linear(xn["x"], c["U"], c["V"])
         assert maxrel(synth.bf16_value(got), yr) <= BF16_TOL
+
+
+def test_decode_workspace_shared_across_shapes():
+    # one workspace serves calls of different shapes in turn: the data one call
+    # leaves in it must never sit where a later call keeps its counters (a
+    # call with few row blocks followed by one with many, split-K on both)
+    d = dev()
+    shapes = [(64, 4096, 300, 512), (1, 8192, 1100, 1200), (33, 2048, 600, 640),
+              (1, 8192, 1100, 1200), (8, 11008, 90, 200)]
+    need = max(lr.lowrank_workspace_bytes(0, lr.LR_BF16, *s) for s in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=d)
+    for i, (T, d_in, r, d_out) in enumerate(shapes):
+        c = make_linear(7000 + i, T, d_in, r, d_out, "bf16", fast=True)
+        y_shared = lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"], workspace=ws)
+        y_fresh = lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"])
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y_shared), bits(y_fresh)), (T, d_in, r, d_out)
+        assert maxrel(to_f64(y_shared), oracle.linear(c["x"], c["U"], c["V"])[1]) <= BF16_TOL
+    ctl = ws[:16384].view(torch.int32).cpu().numpy()
+    assert not ctl.any(), np.nonzero(ctl)      # every counter and flag back at zero
