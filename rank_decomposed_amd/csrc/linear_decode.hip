@@ -47,6 +47,7 @@
 // no memset.  Every wait is bounded: past ~1 s it records an error flag and
 // proceeds.
 #include <algorithm>
+#include <mutex>
 
 #include "lr_common.h"
 #include "lr_kernels.h"
@@ -117,6 +118,14 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 }
 // wait until every memory operation this wave issued has completed
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+// workgroup barrier for LDS exchange only: waits for this wave's LDS
+// operations (lgkmcnt 0; vmcnt and expcnt left at their maxima) but not for
+// its global memory operations, unlike __syncthreads
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // NB fragments of one k-step at byte offset step_off from the per-lane bases
 // off[]; a dead step goes to an offset outside the buffer (reads zero, no
@@ -272,97 +281,54 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
   }
 }
 
-// Sum the 16 waves' partial products into wave 0, in a fixed order:
-// pass h adds wave w + h into wave w (h = 8, 4, 2, 1).
+// Park each wave's partial product in LDS as red[wave][reg][lane].
 template <int TB, int RB>
-__device__ void tree_reduce(f32x4 (&acc)[TB][RB], float* red) {
+__device__ __forceinline__ void park(const f32x4 (&acc)[TB][RB], float* red) {
   constexpr int NR = TB * RB * 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int h = kWaves / 2; h >= 1; h >>= 1) {
-    if (wave >= h && wave < 2 * h) {
-      float* b = red + (wave - h) * NR * 64;
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) b[((tb * RB + r) * 4 + v) * 64 + lane] = acc[tb][r][v];
-    }
-    __syncthreads();
-    if (wave < h) {
-      const float* b = red + wave * NR * 64;
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[tb][r][v] += b[((tb * RB + r) * 4 + v) * 64 + lane];
-    }
-    __syncthreads();
-  }
-}
-
-// Wave 0 of a stage-1 tile with S1 > 1: park the tile's partial, count the
-// arrival; the last arrival of the row block sums all S1 partials in K-range
-// order into acc and returns true.
-template <int TB, int RB>
-__device__ bool meet_partials(f32x4 (&acc)[TB][RB], const DecArgs& p, int blk, int s) {
-  constexpr int NR = TB * RB * 4;
-  const int lane = threadIdx.x & 63;
-  float* base = p.part + (int64_t)blk * p.S1 * (NR * 64) + lane;
-  float* mine = base + (int64_t)s * (NR * 64);
+  float* b = red + (threadIdx.x >> 6) * NR * 64 + (threadIdx.x & 63);
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) store_coherent(mine + ((tb * RB + r) * 4 + v) * 64, acc[tb][r][v]);
-  wait_memory();
-  uint32_t old = 0;
-  if (lane == 0) old = atomic_add_agent(p.ctl + CTL_CNT + blk, 1u);
-  old = __builtin_amdgcn_readfirstlane(old);
-  if (old != (uint32_t)(p.S1 - 1)) return false;
-  if (lane == 0) store_relaxed(p.ctl + CTL_CNT + blk, 0u);  // every sibling has arrived
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-    for (int r = 0; r < RB; ++r) acc[tb][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // loads go out JB partials at a time (~64 registers) so that their round
-  // trips overlap
-  constexpr int JB = NR >= 64 ? 1 : (64 / NR > 8 ? 8 : 64 / NR);
-  for (int j0 = 0; j0 < p.S1; j0 += JB) {
-    float l[JB][NR];
-#pragma unroll
-    for (int jj = 0; jj < JB; ++jj) {
-      const float* pj = base + (int64_t)min(j0 + jj, p.S1 - 1) * (NR * 64);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) l[jj][i] = load_coherent(pj + i * 64);
-    }
-#pragma unroll
-    for (int jj = 0; jj < JB; ++jj)
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float add = l[jj][(tb * RB + r) * 4 + v];
-            acc[tb][r][v] = j0 + jj < p.S1 ? acc[tb][r][v] + add : acc[tb][r][v];
-          }
-  }
-  return true;
+      for (int v = 0; v < 4; ++v) b[((tb * RB + r) * 4 + v) * 64] = acc[tb][r][v];
 }
 
-template <int TB, int RB1, int RB2, int KSW1, int KSW2, int PF, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs p) {
-  constexpr int NREG = TB * (RB1 > RB2 ? RB1 : RB2) * 4;
-  __shared__ float red[(kWaves / 2) * NREG * 64];
+// Element e of a parked tile summed over the 16 waves, pairwise in a fixed
+// order (w + 8, then + 4, + 2, + 1).
+template <int NR>
+__device__ __forceinline__ float sum_waves(const float* red, int e) {
+  float v[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) v[w] = red[w * NR * 64 + e];
+#pragma unroll
+  for (int h = kWaves / 2; h >= 1; h >>= 1)
+#pragma unroll
+    for (int w = 0; w < h; ++w) v[w] += v[w + h];
+  return v[0];
+}
+
+// Element e = reg*64 + lane of a tile -> token and row offset (MFMA 16x16
+// accumulator layout, reg = (tb*RB + rb)*4 + v).
+template <int RB>
+__device__ __forceinline__ void elem_coords(int e, int* tok, int* row) {
+  const int reg = e >> 6, lane = e & 63;
+  const int v = reg & 3, rb = (reg >> 2) % RB, tb = (reg >> 2) / RB;
+  *tok = tb * 16 + 4 * (lane >> 4) + v;
+  *row = rb * 16 + (lane & 15);
+}
+
+template <int TB, int RB1, int RB2, int KSW1, int KSW2, int PF, bool SPLIT, int WG_PER_CU>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4 * WG_PER_CU)))
+void decode_kernel(DecArgs p) {
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [16][NR][64], + padding
+  __shared__ uint32_t sh_last;
   const int tile = (int)blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n1 = p.nb1 * p.S1;
 
   if (tile < n1) {
+    constexpr int NR = TB * RB1 * 4, NE = NR * 64;
+    constexpr int EPT = (NE + kThreads - 1) / kThreads;  // elements per thread
     const int blk = tile / p.S1, s = tile % p.S1;
     const int row0 = blk * 16 * RB1;
     const int kbeg = s * p.kc1, kend = min(p.d_in, kbeg + p.kc1);
@@ -370,25 +336,64 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs p) {
     tile_product<TB, RB1, KSW1, KSW1, false, false>(acc, p.x, nullptr, p.ldx, p.ut, p.ldu,
                                                     p.packed != 0, p.T, p.r, row0, kbeg, kend,
                                                     p.ctl, false);
-    tree_reduce<TB, RB1>(acc, red);
-    if (wave != 0) return;
-    if (p.S1 > 1 && !meet_partials<TB, RB1>(acc, p, blk, s)) return;
+    park<TB, RB1>(acc, red);
+    lds_barrier();
+    float val[EPT];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
+    for (int i = 0; i < EPT; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      val[i] = e < NE ? sum_waves<NR>(red, e) : 0.f;
+    }
+    if (p.S1 > 1) {
+      // the K ranges of the row block meet in the workspace; the last to
+      // arrive sums them in K-range order (loads a few partials at a time so
+      // that their round trips overlap)
+      float* base = p.part + (int64_t)blk * p.S1 * NE + threadIdx.x;
 #pragma unroll
-      for (int rb = 0; rb < RB1; ++rb)
+      for (int i = 0; i < EPT; ++i)
+        if (threadIdx.x + i * kThreads < NE) store_coherent(base + (int64_t)s * NE + i * kThreads, val[i]);
+      wait_memory();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint32_t old = atomic_add_agent(p.ctl + CTL_CNT + blk, 1u);
+        sh_last = old == (uint32_t)(p.S1 - 1);
+        if (sh_last) store_relaxed(p.ctl + CTL_CNT + blk, 0u);  // every sibling has arrived
+      }
+      __syncthreads();
+      if (!sh_last) return;
+      constexpr int JB = 8;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tok = tb * 16 + 4 * (lane >> 4) + v, n = row0 + rb * 16 + (lane & 15);
-          if (tok >= p.T || n >= p.r) continue;
-          const float val = acc[tb][rb][v];
-          if (p.t32) p.t32[(int64_t)tok * p.ldt32 + n] = val;
-          const uint32_t hi = f2bf(val);
-          store_coherent(p.thi + (int64_t)tok * p.ldtb + n, (uint16_t)hi);
-          if (SPLIT) store_coherent(p.tlo + (int64_t)tok * p.ldtb + n, (uint16_t)f2bf(val - bf2f(hi)));
-        }
+      for (int i = 0; i < EPT; ++i) val[i] = 0.f;
+      for (int j0 = 0; j0 < p.S1; j0 += JB) {
+        float l[JB][EPT];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+          for (int i = 0; i < EPT; ++i)
+            l[jj][i] = threadIdx.x + i * kThreads < NE
+                           ? load_coherent(base + (int64_t)min(j0 + jj, p.S1 - 1) * NE + i * kThreads)
+                           : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+          for (int i = 0; i < EPT; ++i) val[i] = j0 + jj < p.S1 ? val[i] + l[jj][i] : val[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      int tok, ro;
+      elem_coords<RB1>(e, &tok, &ro);
+      const int n = row0 + ro;
+      if (e >= NE || tok >= p.T || n >= p.r) continue;
+      if (p.t32) p.t32[(int64_t)tok * p.ldt32 + n] = val[i];
+      const uint32_t hi = f2bf(val[i]);
+      store_coherent(p.thi + (int64_t)tok * p.ldtb + n, (uint16_t)hi);
+      if (SPLIT) store_coherent(p.tlo + (int64_t)tok * p.ldtb + n, (uint16_t)f2bf(val[i] - bf2f(hi)));
+    }
     wait_memory();  // this block's t is visible device-wide before it is counted
-    if (lane == 0) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
       const uint32_t old = atomic_add_agent(p.ctl + CTL_TREADY, 1u);
       if (old == (uint32_t)(p.nb1 - 1)) {  // every row block has published
         store_relaxed(p.ctl + CTL_TREADY, 0u);
@@ -398,30 +403,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs p) {
     return;
   }
 
+  constexpr int NR = TB * RB2 * 4, NE = NR * 64;
+  constexpr int EPT = (NE + kThreads - 1) / kThreads;
   const int row0 = (tile - n1) * 16 * RB2;
   f32x4 acc[TB][RB2];
   tile_product<TB, RB2, KSW2, PF, SPLIT, true>(acc, p.thi, p.tlo, p.ldtb, p.vt, p.ldv,
-                                               p.packed != 0, p.T, p.d_out, row0, 0, p.r, p.ctl,
-                                               p.wait != 0);
-  // count this tile past the wait; the last one clears GO for the next call
+                                               p.packed != 0, p.T, p.d_out, row0, 0, p.r,
+                                               p.ctl, p.wait != 0);
+  // count this tile past the wait; the last one clears GO for the next call.
+  // The LDS barrier does not wait for global memory, so this contended
+  // atomic's round trip overlaps the reduction.
   uint32_t old = 0;
   if (p.wait && threadIdx.x == 0) old = atomic_add_agent(p.ctl + CTL_DONE2, 1u);
-  tree_reduce<TB, RB2>(acc, red);
-  if (wave != 0) return;
+  park<TB, RB2>(acc, red);
+  lds_barrier();
 #pragma unroll
-  for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-    for (int rb = 0; rb < RB2; ++rb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = tb * 16 + 4 * (lane >> 4) + v, n = row0 + rb * 16 + (lane & 15);
-        if (tok >= p.T || n >= p.d_out) continue;
-        const float val = acc[tb][rb][v];
-        if (p.yacc)
-          p.yacc[(int64_t)tok * p.ldacc + n] += val;  // each element owned by one tile
-        else
-          p.y[(int64_t)tok * p.ldy + n] = (uint16_t)f2bf(val);
-      }
+  for (int i = 0; i < EPT; ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    int tok, ro;
+    elem_coords<RB2>(e, &tok, &ro);
+    const int n = row0 + ro;
+    if (e >= NE || tok >= p.T || n >= p.d_out) continue;
+    const float val = sum_waves<NR>(red, e);
+    if (p.yacc)
+      p.yacc[(int64_t)tok * p.ldacc + n] += val;  // each element owned by one tile
+    else
+      p.y[(int64_t)tok * p.ldy + n] = (uint16_t)f2bf(val);
+  }
   if (p.wait && threadIdx.x == 0 && old == (uint32_t)(p.n2 - 1)) {
     store_relaxed(p.ctl + CTL_GO, 0u);
     store_relaxed(p.ctl + CTL_DONE2, 0u);
@@ -481,16 +489,36 @@ Plan make_plan(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
 
 // Per token block: weight rows per tile (16*RB1, 16*RB2), k-steps per round
 // (KSW1, KSW2) and stage-2 prefetch depth PF, sized so a wave holds at most
-// ~64 registers of loads in flight.
+// ~64 registers of loads in flight (two 16-wave workgroups fit a CU).
+// The dynamic LDS holds the parked partial products; `spread` pads it past
+// half the CU's LDS so that each workgroup gets a CU of its own -- better for
+// grids that fit the GPU at once (the dispatcher would otherwise stack two on
+// one CU and halve the CUs streaming), worse for larger grids, which then
+// could not keep their stage-2 tiles resident.
+constexpr int kLdsMax = 163840;
+
+template <int TB, int RB1, int RB2, int KSW1, int KSW2, int PF, bool SPLIT, int WPC>
+hipError_t launch_one(const DecArgs& a, int grid, bool spread, hipStream_t st) {
+  constexpr int NR = TB * (RB1 > RB2 ? RB1 : RB2) * 4;
+  constexpr size_t red_bytes = (size_t)kWaves * NR * 64 * 4;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_kernel<TB, RB1, RB2, KSW1, KSW2, PF, SPLIT, WPC>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 1024);
+  });
+  const size_t lds = spread ? std::max<size_t>(red_bytes, kLdsMax / 2 + 1024) : red_bytes;
+  hipLaunchKernelGGL((decode_kernel<TB, RB1, RB2, KSW1, KSW2, PF, SPLIT, WPC>), dim3(grid),
+                     dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
 template <int TB>
 hipError_t launch_decode(const DecArgs& a, int grid, hipStream_t st) {
-  if (TB == 1)
-    hipLaunchKernelGGL((decode_kernel<1, 1, 2, 8, 4, 4, true>), dim3(grid), dim3(kThreads), 0, st, a);
-  else if (TB == 2)
-    hipLaunchKernelGGL((decode_kernel<2, 2, 2, 4, 2, 4, false>), dim3(grid), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<4, 2, 2, 2, 2, 4, false>), dim3(grid), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  const bool spread = grid <= 400;
+  if (TB == 1) return launch_one<1, 1, 2, 8, 4, 4, true, 2>(a, grid, spread, st);
+  if (TB == 2) return launch_one<2, 2, 2, 2, 2, 4, false, 2>(a, grid, spread, st);
+  return launch_one<4, 2, 2, 2, 2, 4, false, 1>(a, grid, spread, st);
 }
 
 }  // namespace
