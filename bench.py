@@ -31,6 +31,9 @@ SHAPES = {"q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4
           "gate": (4096, 11008), "up": (4096, 11008), "down": (11008, 4096)}
 ROLES = ("q", "k", "v", "o", "gate", "up", "down")
 TOKENS = (1, 8, 32, 64)
+# launches of a layer set: projections that read the same input go out as one
+# grouped launch (lowrank_linear_forward_group); o and down read other data
+GROUPS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",)))
 
 
 def log(msg):
@@ -132,25 +135,32 @@ def main():
     gen = torch.Generator(device=dev).manual_seed(2_000_001)
     xs = {T: {d: torch.randn((T, d), generator=gen, device=dev).to(torch.bfloat16)
               for d in (4096, 11008)} for T in TOKENS}
-    ys = {T: {d: torch.empty((T, d), dtype=torch.bfloat16, device=dev) for d in (4096, 11008)}
-          for T in TOKENS}
-    ws_bytes = max(lr.lowrank_workspace_bytes(0, lr.LR_BF16, T, SHAPES[r][0],
-                                              rank(0.6, *SHAPES[r]), SHAPES[r][1])
-                   for T in TOKENS for r in ROLES)
-    ws = torch.zeros(ws_bytes + 256, dtype=torch.uint8, device=dev)
+    ys = {T: {role: torch.empty((T, SHAPES[role][1]), dtype=torch.bfloat16, device=dev)
+              for role in ROLES} for T in TOKENS}
 
-    def call(T, layer, role):
+    def member(T, layer, role):
         ut, vt, r = layer[role]
         d_in, d_out = SHAPES[role]
         if args.layout == "rowmajor":
             ut, vt = ut[:, :d_in], vt[:, :r]
-        lr.lowrank_linear_forward(xs[T][d_in], ut, vt, y=ys[T][d_out], workspace=ws)
+        return dict(x=xs[T][d_in], Ut=ut, Vt=vt, y=ys[T][role])
+
+    ws_bytes = max(lr.lowrank_group_workspace_bytes(T, [member(T, sets[0], r) for r in roles])
+                   for T in TOKENS for _, roles in GROUPS)
+    ws = torch.zeros(ws_bytes + 256, dtype=torch.uint8, device=dev)
+
+    def call(T, layer, roles):
+        if len(roles) == 1:
+            m = member(T, layer, roles[0])
+            lr.lowrank_linear_forward(m["x"], m["Ut"], m["Vt"], y=m["y"], workspace=ws)
+        else:
+            lr.lowrank_linear_forward_group([member(T, layer, r) for r in roles], workspace=ws)
 
     def step():
         for T in TOKENS:
             for layer in sets:
-                for role in ROLES:
-                    call(T, layer, role)
+                for _, roles in GROUPS:
+                    call(T, layer, roles)
 
     def capture(fn):
         side = torch.cuda.Stream(dev)
@@ -175,7 +185,7 @@ def main():
         return a.elapsed_time(b) / reps
 
     log("factors ready (%s layout)" % args.layout)
-    # the whole step (896 launches) is one HIP graph, as in the pages' decode
+    # the whole step (512 launches) is one HIP graph, as in the pages' decode
     step_graph = capture(step)
     log("decode step graph captured")
     for _ in range(args.warmup):
@@ -188,20 +198,19 @@ def main():
     value = tokens_per_step / (ms_step / 1e3)
     log("decode step timed: %.3f ms" % ms_step)
 
-    # per-launch durations: for each projection class and T, a graph of one
-    # launch per layer set (distinct weights), timed with events on the stream
+    # per-launch durations: for each launch class and T, a graph of one launch
+    # per layer set (distinct weights), timed with events on the stream
     per = {}
-    count = {"q": 4, "gate": 2, "down": 1}      # launches of each class per layer set
     for T in TOKENS:
-        for role in ("q", "gate", "down"):
-            g = capture(lambda: [call(T, layer, role) for layer in sets])
+        for name, roles in GROUPS:
+            g = capture(lambda: [call(T, layer, roles) for layer in sets])
             us = 1e3 * time_graph(g, max(3, args.steps)) / len(sets)
             del g
-            d_in, d_out = SHAPES[role]
-            nbytes = decode_bytes(T, d_in, rank(0.6, d_in, d_out), d_out)
-            per["%s_T%d" % (role, T)] = {"us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
+            nbytes = sum(decode_bytes(T, SHAPES[r][0], rank(0.6, *SHAPES[r]), SHAPES[r][1])
+                         for r in roles)
+            per["%s_T%d" % (name, T)] = {"us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
                                          "frac": round(nbytes / (us * 1e-6) / HBM_PEAK, 4),
-                                         "bytes": nbytes, "share": us * count[role]}
+                                         "bytes": nbytes, "share": us}
         log("per-launch timing T=%d done" % T)
     total_share = sum(v["share"] for v in per.values())
     for v in per.values():
@@ -211,8 +220,8 @@ def main():
         bt = sum(decode_bytes(T, SHAPES[r][0], rank(0.6, *SHAPES[r]), SHAPES[r][1]) for r in ROLES)
         per_T[str(T)] = bt
     dom = max(per, key=lambda k: per[k]["share"])
-    dom_role, dom_T = dom.split("_T")
-    d_in, d_out = SHAPES[dom_role]
+    dom_name, dom_T = dom.split("_T")
+    dom_roles = dict(GROUPS)[dom_name]
     dom_bytes = per[dom]["bytes"]
     dom_us = per[dom]["us"]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -227,12 +236,15 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "LLaMA-7B decomposed projections (q,k,v,o 4096x4096; gate,up "
                                "4096x11008; down 11008x4096), ratio 0.6, decode T=1,8,32,64, "
-                               "32 rotating layer sets",
+                               "32 rotating layer sets; q,k,v and gate,up as grouped launches",
                    "tokens_per_step": tokens_per_step, "layer_sets": len(sets),
                    "factor_layout": args.layout},
         "roofline": {"bound": "hbm",
-                     "kernel": "decode_kernel (lowrank_linear_forward decode), %s %dx%dx%d T=%s"
-                               % (dom_role, d_in, rank(0.6, d_in, d_out), d_out, dom_T),
+                     "kernel": "decode_kernel (%s), %s T=%s" % (
+                         "lowrank_linear_forward_group" if len(dom_roles) > 1
+                         else "lowrank_linear_forward",
+                         " + ".join("%s %dx%dx%d" % (r, SHAPES[r][0], rank(0.6, *SHAPES[r]),
+                                                     SHAPES[r][1]) for r in dom_roles), dom_T),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
                      "bytes_per_launch": dom_bytes, "us_per_launch": dom_us},

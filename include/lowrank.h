@@ -146,6 +146,45 @@ lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in, int64_t r
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * lowrank_linear_forward_group -- n independent decomposed linears
+ * (DeInfer/en §2.A, as lowrank_linear_forward) over the same T token rows in
+ * one launch: bf16 decode path only (1 <= T <= 64, 1 <= n <= 8).  Meant for
+ * the projections of a decoder layer that read the same input (q, k, v;
+ * gate, up): one launch instead of n, and one linear's hand-over from stage
+ * 1 to stage 2 overlaps the others' weight streams.  Results are bit for bit
+ * those of n separate lowrank_linear_forward calls.
+ *
+ *   lin[i]   one linear, operands as in lowrank_linear_forward (bf16 x, Ut,
+ *            Vt, y; fp32 t_io):
+ *              Vt == NULL   stage 1 only: t_io = x U_r (t_io required)
+ *              y_acc != NULL  y_acc[T, ld_acc] += y in fp32 (y unused)
+ *              otherwise    y = bf16((x U_r) V_r), t_io written when given
+ *   flags    0 or LR_PACKED_WEIGHTS (then every Ut / Vt is fragment-packed,
+ *            ldu / ldv block pitches in steps).
+ *   workspace  at least lowrank_group_workspace_bytes(T, n, lin) bytes,
+ *            256-byte aligned, zero-filled before first use (as for
+ *            lowrank_linear_forward, whose workspaces it may share: both keep
+ *            their counters in the same fixed area at its start).
+ * Errors: LR_ERR_ARG (n or T out of range, a missing operand, ld < width),
+ * LR_ERR_ALIGN, LR_ERR_WORKSPACE, LR_ERR_UNSUPPORTED (a leading dimension,
+ * pitch or r past the decode path's limits), LR_ERR_HIP.
+ */
+typedef struct {
+  int64_t d_in, r, d_out;
+  const void* x;  int64_t ldx;
+  const void* Ut; int64_t ldu;
+  const void* Vt; int64_t ldv;
+  void* y;        int64_t ldy;
+  float* y_acc;   int64_t ld_acc;
+  float* t_io;    int64_t ldt;
+} lr_linear;
+
+size_t lowrank_group_workspace_bytes(int64_t T, int n, const lr_linear* lin);
+lr_status lowrank_linear_forward_group(int64_t T, int n, const lr_linear* lin, unsigned flags,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
  * kv_remap_gather -- the graph-replay copy of DeInfer/en §2.C (and DeInfer/es
  * §2, "Etapa de Reproducción del Gráfico"): rows of a paged pool are copied
  * into a compact buffer at a fixed address, following the remapping index
@@ -171,9 +210,10 @@ lr_status kv_remap_gather(lr_dtype dt, const void* src, int64_t src_rows, int64_
 
 /*
  * lowrank_prepare_decode -- host-side preparation stage of DeInfer/en §2.C
- * ("scan the paged memory for physically contiguous blocks ... remapping
- * index list"), DeInfer/zh (remapping table), DeInfer/es §2 "Etapa de
- * Preparación".  Runs on the CPU, touches host memory only.
+ * (the paged cache is walked for runs of physically adjacent blocks, and a
+ * remapping index list is emitted), DeInfer/zh (remapping table),
+ * DeInfer/es §2 "Etapa de Preparación".  Runs on the CPU, touches host
+ * memory only.
  *
  * Sequence i has lengths[i] cached tokens and decodes one new token at
  * position lengths[i]; its compact segment holds lengths[i] + 1 rows.
@@ -282,7 +322,8 @@ size_t lowrank_workspace_bytes(int which, lr_dtype dt, int64_t T_or_B, int64_t d
 const char* lowrank_status_string(lr_status s);
 
 /* sizeof(lr_layer_weights) for which = 0, sizeof(lr_decode_state) for
- * which = 1 (lets bindings verify their struct layout); 0 otherwise. */
+ * which = 1, sizeof(lr_linear) for which = 2 (lets bindings verify their
+ * struct layout); 0 otherwise. */
 size_t lowrank_abi_sizeof(int which);
 
 /* Library ABI version (major * 100 + minor). */

@@ -26,6 +26,7 @@ __all__ = [
     "lowrank_workspace_bytes", "lowrank_status_string", "lowrank_version",
     "LR_F32", "LR_BF16", "LR_FULL", "LR_STAGE1_ONLY", "LR_STAGE2_ONLY", "LR_PACKED_WEIGHTS",
     "LowrankError", "load", "PackedFactor", "pack_factor", "lowrank_packed_bytes",
+    "lowrank_linear_forward_group", "lowrank_group_workspace_bytes",
 ]
 
 
@@ -159,6 +160,58 @@ def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, w
         flags, _ptr(workspace), ws_bytes, _stream(stream, dev))
     _lib.check(st, "lowrank_linear_forward")
     return y
+
+
+def _group_structs(linears):
+    arr = (_lib.Linear * len(linears))()
+    for i, L in enumerate(linears):
+        x, Ut, Vt = L["x"], L["Ut"], L.get("Vt")
+        y, y_acc, t_io = L.get("y"), L.get("y_acc"), L.get("t_io")
+        a = arr[i]
+        a.d_in, a.r = int(x.shape[1]), int(Ut.shape[0])
+        a.d_out = int(Vt.shape[0]) if Vt is not None else 1
+        a.x, a.ldx = x.data_ptr(), _ld(x)
+        a.Ut, a.ldu = Ut.data_ptr(), _wld(Ut)
+        if Vt is not None:
+            a.Vt, a.ldv = Vt.data_ptr(), _wld(Vt)
+        if y is not None:
+            a.y, a.ldy = y.data_ptr(), _ld(y)
+        if y_acc is not None:
+            a.y_acc, a.ld_acc = y_acc.data_ptr(), _ld(y_acc)
+        if t_io is not None:
+            a.t_io, a.ldt = t_io.data_ptr(), _ld(t_io)
+    return arr
+
+
+def lowrank_group_workspace_bytes(T: int, linears) -> int:
+    arr = _group_structs(linears)
+    return int(load().lowrank_group_workspace_bytes(T, len(linears), C.cast(arr, C.c_void_p)))
+
+
+def lowrank_linear_forward_group(linears, workspace=None, stream=None):
+    """n independent bf16 decode linears over the same T <= 64 rows in one
+    launch.  Each entry: dict with x [T, d_in], Ut, Vt (None: stage 1 only),
+    y (allocated when missing and neither y_acc nor stage-1-only), y_acc
+    (fp32, added to), t_io (fp32).  Ut / Vt may be PackedFactor views (then
+    all of them must be).  Returns the list of y (None where not written)."""
+    torch = _torch()
+    lib = load()
+    T = int(linears[0]["x"].shape[0])
+    dev = linears[0]["x"].device
+    packed = any(isinstance(L["Ut"], PackedFactor) for L in linears)
+    for L in linears:
+        if L.get("Vt") is not None and L.get("y") is None and L.get("y_acc") is None:
+            L["y"] = torch.empty((T, int(L["Vt"].shape[0])), dtype=torch.bfloat16, device=dev)
+    arr = _group_structs(linears)
+    need = int(lib.lowrank_group_workspace_bytes(T, len(linears), C.cast(arr, C.c_void_p)))
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.lowrank_linear_forward_group(T, len(linears), C.cast(arr, C.c_void_p),
+                                          LR_PACKED_WEIGHTS if packed else 0, _ptr(workspace),
+                                          ws_bytes, _stream(stream, dev))
+    _lib.check(st, "lowrank_linear_forward_group")
+    return [L.get("y") for L in linears]
 
 
 def kv_remap_gather(src, remap, dst, n_valid=None, row_elems=None, stream=None):

@@ -34,6 +34,8 @@ SIGNATURES = {
     "lowrank_decode_step_workspace_bytes": (C.c_size_t, [_p, _p]),
     "lowrank_layer_decode_step": (C.c_int, [_p, _p, _p, _p, _sz, _p]),
     "lowrank_packed_bytes": (C.c_size_t, [_i64, _i64]),
+    "lowrank_group_workspace_bytes": (C.c_size_t, [_i64, C.c_int, _p]),
+    "lowrank_linear_forward_group": (C.c_int, [_i64, C.c_int, _p, _u, _p, _sz, _p]),
     "lowrank_pack_factor": (C.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p]),
 }
 
@@ -45,6 +47,15 @@ class LayerWeights(C.Structure):
                 ("Ut", C.c_void_p * 7), ("ldu", C.c_int64 * 7), ("Vt", C.c_void_p * 7),
                 ("ldv", C.c_int64 * 7), ("r", C.c_int64 * 7), ("attn_norm", C.c_void_p),
                 ("ffn_norm", C.c_void_p), ("rope", C.c_void_p), ("rope_max_pos", C.c_int64)]
+
+
+class Linear(C.Structure):
+    """lr_linear (include/lowrank.h)."""
+    _fields_ = [("d_in", C.c_int64), ("r", C.c_int64), ("d_out", C.c_int64),
+                ("x", C.c_void_p), ("ldx", C.c_int64), ("Ut", C.c_void_p), ("ldu", C.c_int64),
+                ("Vt", C.c_void_p), ("ldv", C.c_int64), ("y", C.c_void_p), ("ldy", C.c_int64),
+                ("y_acc", C.c_void_p), ("ld_acc", C.c_int64), ("t_io", C.c_void_p),
+                ("ldt", C.c_int64)]
 
 
 class DecodeState(C.Structure):

@@ -15,7 +15,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 extern "C" int lowrank_version(void) { return 100; }
 
 extern "C" size_t lowrank_abi_sizeof(int which) {
-  return which == 0 ? sizeof(lr_layer_weights) : (which == 1 ? sizeof(lr_decode_state) : 0);
+  switch (which) {
+    case 0: return sizeof(lr_layer_weights);
+    case 1: return sizeof(lr_decode_state);
+    case 2: return sizeof(lr_linear);
+    default: return 0;
+  }
 }
 
 extern "C" const char* lowrank_status_string(lr_status s) {
@@ -93,6 +98,64 @@ extern "C" lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in
     e = lr::decode_linear_bf16(d, stream);
   else
     e = lr::prefill_linear_bf16(d, stream);
+  return e == hipSuccess ? LR_OK : LR_ERR_HIP;
+}
+
+namespace {
+
+// Host checks of one member of a group; fills the kernel-side description.
+lr_status group_member(int64_t T, const lr_linear& L, bool packed, lr::DecodeLinear* d) {
+  if (L.d_in <= 0 || L.r <= 0 || L.d_out <= 0) return LR_ERR_ARG;
+  if (L.d_in > INT32_MAX || L.r > INT32_MAX || L.d_out > INT32_MAX) return LR_ERR_ARG;
+  const bool s2 = L.Vt != nullptr;
+  const int64_t ku = packed ? (L.d_in + 31) / 32 : L.d_in, kv = packed ? (L.r + 31) / 32 : L.r;
+  if (!L.x || !L.Ut || L.ldx < L.d_in || L.ldu < ku) return LR_ERR_ARG;
+  if (!s2 && !L.t_io) return LR_ERR_ARG;
+  if (s2 && (L.ldv < kv || (!L.y_acc && (!L.y || L.ldy < L.d_out)) ||
+             (L.y_acc && L.ld_acc < L.d_out)))
+    return LR_ERR_ARG;
+  if (L.t_io && L.ldt < L.r) return LR_ERR_ARG;
+  if (!aligned(L.x, 16) || !aligned(L.Ut, 16) || L.ldx % 8 || (!packed && L.ldu % 8))
+    return LR_ERR_ALIGN;
+  if (s2 && (!aligned(L.Vt, 16) || (!packed && L.ldv % 8))) return LR_ERR_ALIGN;
+  if (s2 && !L.y_acc && !aligned(L.y, 2)) return LR_ERR_ALIGN;
+  if ((L.y_acc && !aligned(L.y_acc, 4)) || (L.t_io && !aligned(L.t_io, 4))) return LR_ERR_ALIGN;
+  *d = lr::DecodeLinear{T, L.d_in, L.r, L.d_out, L.x, L.ldx, L.Ut, L.ldu, L.Vt, L.ldv, L.y,
+                        L.ldy, L.t_io, L.ldt, s2 ? 0u : 1u, nullptr};
+  d->y_acc = L.y_acc;
+  d->ld_acc = L.ld_acc;
+  d->packed = packed;
+  if (!lr::decode_supported(*d)) return LR_ERR_UNSUPPORTED;
+  return LR_OK;
+}
+
+}  // namespace
+
+extern "C" size_t lowrank_group_workspace_bytes(int64_t T, int n, const lr_linear* lin) {
+  if (T <= 0 || T > 64 || n < 1 || n > 8 || !lin) return 0;
+  lr::DecodeLinear d[8];
+  for (int i = 0; i < n; ++i) {
+    if (lin[i].d_in <= 0 || lin[i].r <= 0 || lin[i].d_out <= 0) return 0;
+    d[i] = lr::DecodeLinear{T, lin[i].d_in, lin[i].r, lin[i].d_out};
+  }
+  return lr::decode_group_workspace_bytes(d, n);
+}
+
+extern "C" lr_status lowrank_linear_forward_group(int64_t T, int n, const lr_linear* lin,
+                                                  unsigned flags, void* workspace,
+                                                  size_t workspace_bytes, hipStream_t stream) {
+  if (!lin || n < 1 || n > 8 || T <= 0 || T > 64) return LR_ERR_ARG;
+  if (flags & ~(unsigned)LR_PACKED_WEIGHTS) return LR_ERR_ARG;
+  const bool packed = flags != 0;
+  lr::DecodeLinear d[8];
+  for (int i = 0; i < n; ++i) {
+    const lr_status st = group_member(T, lin[i], packed, &d[i]);
+    if (st != LR_OK) return st;
+  }
+  const size_t need = lowrank_group_workspace_bytes(T, n, lin);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return LR_ERR_WORKSPACE;
+  d[0].workspace = workspace;
+  const hipError_t e = lr::decode_group_bf16(d, n, stream);
   return e == hipSuccess ? LR_OK : LR_ERR_HIP;
 }
 

@@ -61,16 +61,19 @@ constexpr int kThreads = 64 * kWaves;
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr uint32_t kOutside = 0x80000000u;  // past every buffer (tiles stay < 2 GiB)
 constexpr int kCoherentLoad = 16;           // buffer-load cache policy: device scope
+constexpr int kMaxGroup = 8;                // linears per launch
 
-// control block (uint32 words) at the start of the workspace; each hot word
-// on a cache line of its own, then one arrival counter per stage-1 row block.
-// Its size is the same for every call, so that data of one call never lands
-// on words another call (of another shape, same workspace) takes as zeroed
+// One control block (uint32 words) per linear of a launch, all of them at
+// the start of the workspace: each hot word on a cache line of its own, then
+// one arrival counter per stage-1 row block.  Their place and size are the
+// same for every call, so that data of one call never lands on words another
+// call (of another shape or group size, same workspace) takes as zeroed
 // counters.
 enum { CTL_TREADY = 0, CTL_GO = 32, CTL_DONE2 = 64, CTL_ERR = 96, CTL_CNT = 128,
        CTL_WORDS = 4096 };
 
-struct DecArgs {
+// One linear of a launch.
+struct LinArgs {
   const uint16_t* x;
   int64_t ldx;
   const uint16_t* ut;
@@ -88,11 +91,19 @@ struct DecArgs {
   int64_t ldtb;
   float* part;    // stage-1 split-K partials
   uint32_t* ctl;  // control block
-  int T, d_in, r, d_out;
+  int d_in, r, d_out;
   int nb1, S1, kc1;  // stage-1 row blocks, K ranges per block, K range width
   int n2;            // stage-2 tiles
+  int first1, first2;  // index of the linear's first stage-1 / stage-2 tile
   int wait;          // stage-2 tiles wait for the stage-1 tiles of this launch
   int packed;        // weights fragment-packed
+};
+
+// A launch: up to kMaxGroup independent linears over the same T token rows;
+// every stage-1 tile of every linear comes before every stage-2 tile.
+struct DecArgs {
+  LinArgs lin[kMaxGroup];
+  int n, T, n1;  // linears, tokens, stage-1 tiles in all
 };
 
 // Relaxed device-scope atomics: on gfx950 these are plain loads/stores with
@@ -319,22 +330,26 @@ __device__ __forceinline__ void elem_coords(int e, int* tok, int* row) {
 }
 
 template <int TB, int RB1, int RB2, int KSW1, int KSW2, int PF, bool SPLIT, int WG_PER_CU>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4 * WG_PER_CU)))
-void decode_kernel(DecArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4 * WG_PER_CU, 4 * WG_PER_CU)))
+void decode_kernel(DecArgs args) {
   extern __shared__ __attribute__((aligned(16))) float red[];  // [16][NR][64], + padding
   __shared__ uint32_t sh_last;
   const int tile = (int)blockIdx.x;
-  const int n1 = p.nb1 * p.S1;
+  const int T = args.T;
 
-  if (tile < n1) {
+  if (tile < args.n1) {
+    int li = 0;  // the linear owning this stage-1 tile (workgroup-uniform)
+    while (li + 1 < args.n && tile >= args.lin[li + 1].first1) ++li;
+    const LinArgs& p = args.lin[li];
     constexpr int NR = TB * RB1 * 4, NE = NR * 64;
     constexpr int EPT = (NE + kThreads - 1) / kThreads;  // elements per thread
-    const int blk = tile / p.S1, s = tile % p.S1;
+    const int t1 = tile - p.first1;
+    const int blk = t1 / p.S1, s = t1 % p.S1;
     const int row0 = blk * 16 * RB1;
     const int kbeg = s * p.kc1, kend = min(p.d_in, kbeg + p.kc1);
     f32x4 acc[TB][RB1];
     tile_product<TB, RB1, KSW1, KSW1, false, false>(acc, p.x, nullptr, p.ldx, p.ut, p.ldu,
-                                                    p.packed != 0, p.T, p.r, row0, kbeg, kend,
+                                                    p.packed != 0, T, p.r, row0, kbeg, kend,
                                                     p.ctl, false);
     park<TB, RB1>(acc, red);
     lds_barrier();
@@ -385,7 +400,7 @@ void decode_kernel(DecArgs p) {
       int tok, ro;
       elem_coords<RB1>(e, &tok, &ro);
       const int n = row0 + ro;
-      if (e >= NE || tok >= p.T || n >= p.r) continue;
+      if (e >= NE || tok >= T || n >= p.r) continue;
       if (p.t32) p.t32[(int64_t)tok * p.ldt32 + n] = val[i];
       const uint32_t hi = f2bf(val[i]);
       store_coherent(p.thi + (int64_t)tok * p.ldtb + n, (uint16_t)hi);
@@ -403,12 +418,15 @@ void decode_kernel(DecArgs p) {
     return;
   }
 
+  int li = 0;  // the linear owning this stage-2 tile (workgroup-uniform)
+  while (li + 1 < args.n && tile >= args.lin[li + 1].first2) ++li;
+  const LinArgs& p = args.lin[li];
   constexpr int NR = TB * RB2 * 4, NE = NR * 64;
   constexpr int EPT = (NE + kThreads - 1) / kThreads;
-  const int row0 = (tile - n1) * 16 * RB2;
+  const int row0 = (tile - p.first2) * 16 * RB2;
   f32x4 acc[TB][RB2];
   tile_product<TB, RB2, KSW2, PF, SPLIT, true>(acc, p.thi, p.tlo, p.ldtb, p.vt, p.ldv,
-                                               p.packed != 0, p.T, p.d_out, row0, 0, p.r,
+                                               p.packed != 0, T, p.d_out, row0, 0, p.r,
                                                p.ctl, p.wait != 0);
   // count this tile past the wait; the last one clears GO for the next call.
   // The LDS barrier does not wait for global memory, so this contended
@@ -423,7 +441,7 @@ void decode_kernel(DecArgs p) {
     int tok, ro;
     elem_coords<RB2>(e, &tok, &ro);
     const int n = row0 + ro;
-    if (e >= NE || tok >= p.T || n >= p.d_out) continue;
+    if (e >= NE || tok >= T || n >= p.d_out) continue;
     const float val = sum_waves<NR>(red, e);
     if (p.yacc)
       p.yacc[(int64_t)tok * p.ldacc + n] += val;  // each element owned by one tile
@@ -453,12 +471,15 @@ __global__ __launch_bounds__(256) void split_t_kernel(const float* __restrict__ 
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// Tiling of one call; identical on the sizing and launch sides.
+// Tiling of one linear; identical on the sizing and launch sides.  Offsets
+// are relative to the linear's data region (after the control blocks).
 struct Plan {
   int TB, RB1, RB2, nb1, S1, kc1, n2;
   int64_t ldtb;
   size_t off_part, off_thi, off_tlo, bytes;
 };
+
+constexpr size_t kCtlBytes = (size_t)kMaxGroup * CTL_WORDS * 4;
 
 Plan make_plan(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
   Plan pl{};
@@ -467,38 +488,42 @@ Plan make_plan(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
   pl.RB2 = 2;
   pl.nb1 = (int)((r + 16 * pl.RB1 - 1) / (16 * pl.RB1));
   pl.n2 = (int)((d_out + 16 * pl.RB2 - 1) / (16 * pl.RB2));
-  // split K when a row block would hand one workgroup more than ~256 KiB of
-  // weight and activation bytes (one workgroup streams ~40 GB/s)
+  // split K when a row block would hand one workgroup more than ~256 KiB
+  // (128 KiB for 17..32 tokens) of weight and activation bytes: one
+  // workgroup streams only ~40 GB/s.  Measured on the 7B shapes; more K
+  // ranges than 6 cost more in meeting partials than they gain (32 tokens).
   const int64_t rows = 16 * pl.RB1 + std::min<int64_t>(T, 16 * pl.TB);
-  const int64_t kc_max = std::max<int64_t>(32, (262144 / (2 * rows)) / 32 * 32);
+  const int64_t budget = pl.TB == 2 ? 131072 : 262144;
+  const int64_t kc_max = std::max<int64_t>(32, (budget / (2 * rows)) / 32 * 32);
   const int64_t steps = (d_in + 31) / 32;
   pl.S1 = (int)((d_in + kc_max - 1) / kc_max);
+  if (pl.TB == 2 && pl.S1 > 6) pl.S1 = 6;
   if (CTL_CNT + pl.nb1 > CTL_WORDS) pl.S1 = 1;  // no counters for that many row blocks
   pl.kc1 = (int)((steps + pl.S1 - 1) / pl.S1 * 32);
   pl.S1 = (int)((d_in + pl.kc1 - 1) / pl.kc1);
   pl.ldtb = round_up(r, 8);
   const size_t nr1 = (size_t)pl.TB * pl.RB1 * 4 * 64;  // floats per stage-1 tile
   const size_t part = pl.S1 > 1 ? (size_t)pl.nb1 * pl.S1 * nr1 * 4 : 0;
-  pl.off_part = 4 * CTL_WORDS;
-  pl.off_thi = round_up(pl.off_part + part, 256);
+  pl.off_part = 0;
+  pl.off_thi = round_up(part, 256);
   const size_t tb_bytes = round_up(T * pl.ldtb * 2, 256);
   pl.off_tlo = pl.off_thi + tb_bytes;
   pl.bytes = pl.off_tlo + tb_bytes;
   return pl;
 }
 
-// Per token block: weight rows per tile (16*RB1, 16*RB2), k-steps per round
-// (KSW1, KSW2) and stage-2 prefetch depth PF, sized so a wave holds at most
-// ~64 registers of loads in flight (two 16-wave workgroups fit a CU).
-// The dynamic LDS holds the parked partial products; `spread` pads it past
-// half the CU's LDS so that each workgroup gets a CU of its own -- better for
-// grids that fit the GPU at once (the dispatcher would otherwise stack two on
-// one CU and halve the CUs streaming), worse for larger grids, which then
-// could not keep their stage-2 tiles resident.
+// Two builds per token block.  "spread": one workgroup per CU (the dynamic
+// LDS is padded past half the CU's), up to 128 registers per lane, so a wave
+// keeps a whole round of loads in flight -- for grids that fit the GPU at
+// once (the dispatcher would otherwise stack two workgroups on one CU and
+// halve the CUs streaming).  "dense": two workgroups per CU (64 registers,
+// half-size rounds) for larger grids, which then keep all their stage-2 tiles
+// resident.  Template arguments: weight rows per tile (16*RB1, 16*RB2),
+// k-steps per round (KSW1, KSW2), stage-2 prefetch depth PF.
 constexpr int kLdsMax = 163840;
 
 template <int TB, int RB1, int RB2, int KSW1, int KSW2, int PF, bool SPLIT, int WPC>
-hipError_t launch_one(const DecArgs& a, int grid, bool spread, hipStream_t st) {
+hipError_t launch_one(const DecArgs& a, int grid, hipStream_t st) {
   constexpr int NR = TB * (RB1 > RB2 ? RB1 : RB2) * 4;
   constexpr size_t red_bytes = (size_t)kWaves * NR * 64 * 4;
   static std::once_flag once;
@@ -507,7 +532,7 @@ hipError_t launch_one(const DecArgs& a, int grid, bool spread, hipStream_t st) {
         reinterpret_cast<const void*>(&decode_kernel<TB, RB1, RB2, KSW1, KSW2, PF, SPLIT, WPC>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 1024);
   });
-  const size_t lds = spread ? std::max<size_t>(red_bytes, kLdsMax / 2 + 1024) : red_bytes;
+  const size_t lds = WPC == 1 ? std::max<size_t>(red_bytes, kLdsMax / 2 + 1024) : red_bytes;
   hipLaunchKernelGGL((decode_kernel<TB, RB1, RB2, KSW1, KSW2, PF, SPLIT, WPC>), dim3(grid),
                      dim3(kThreads), lds, st, a);
   return hipGetLastError();
@@ -516,69 +541,103 @@ hipError_t launch_one(const DecArgs& a, int grid, bool spread, hipStream_t st) {
 template <int TB>
 hipError_t launch_decode(const DecArgs& a, int grid, hipStream_t st) {
   const bool spread = grid <= 400;
-  if (TB == 1) return launch_one<1, 1, 2, 8, 4, 4, true, 2>(a, grid, spread, st);
-  if (TB == 2) return launch_one<2, 2, 2, 2, 2, 4, false, 2>(a, grid, spread, st);
-  return launch_one<4, 2, 2, 2, 2, 4, false, 1>(a, grid, spread, st);
+  if (TB == 1)
+    return spread ? launch_one<1, 1, 2, 8, 4, 4, true, 1>(a, grid, st)
+                  : launch_one<1, 1, 2, 4, 2, 2, true, 2>(a, grid, st);
+  if (TB == 2)
+    return spread ? launch_one<2, 2, 2, 4, 2, 4, false, 1>(a, grid, st)
+                  : launch_one<2, 2, 2, 2, 1, 2, false, 2>(a, grid, st);
+  return launch_one<4, 2, 2, 2, 2, 4, false, 1>(a, grid, st);
 }
 
 }  // namespace
 
-size_t decode_workspace_bytes(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
-  return make_plan(T, d_in, r, d_out).bytes;
+size_t decode_group_workspace_bytes(const DecodeLinear* d, int n) {
+  size_t bytes = kCtlBytes;
+  for (int i = 0; i < n; ++i)
+    bytes += round_up(make_plan(d[i].T, d[i].d_in, d[i].r, d[i].d_out).bytes, 256);
+  return bytes;
 }
 
-hipError_t decode_linear_bf16(const DecodeLinear& d, hipStream_t st) {
-  const Plan pl = make_plan(d.T, d.d_in, d.r, d.d_out);
-  char* ws = static_cast<char*>(d.workspace);
-  DecArgs a{};
-  a.x = static_cast<const uint16_t*>(d.x);
-  a.ldx = d.ldx;
-  a.ut = static_cast<const uint16_t*>(d.Ut);
-  a.ldu = d.ldu;
-  a.vt = static_cast<const uint16_t*>(d.Vt);
-  a.ldv = d.ldv;
-  a.y = static_cast<uint16_t*>(d.y);
-  a.ldy = d.ldy;
-  a.yacc = d.y_acc;
-  a.ldacc = d.ld_acc;
-  a.t32 = d.t_io;
-  a.ldt32 = d.ldt;
-  a.thi = reinterpret_cast<uint16_t*>(ws + pl.off_thi);
-  a.tlo = reinterpret_cast<uint16_t*>(ws + pl.off_tlo);
-  a.ldtb = pl.ldtb;
-  a.part = reinterpret_cast<float*>(ws + pl.off_part);
-  a.ctl = reinterpret_cast<uint32_t*>(ws);
-  a.T = (int)d.T;
-  a.d_in = (int)d.d_in;
-  a.r = (int)d.r;
-  a.d_out = (int)d.d_out;
-  a.nb1 = pl.nb1;
-  a.S1 = pl.S1;
-  a.kc1 = pl.kc1;
-  a.n2 = pl.n2;
-  a.wait = 1;
-  a.packed = d.packed ? 1 : 0;
+size_t decode_workspace_bytes(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
+  return kCtlBytes + round_up(make_plan(T, d_in, r, d_out).bytes, 256);
+}
 
-  if (d.flags == 1) {  // stage 1 only
-    a.n2 = 0;
-    a.wait = 0;
-  } else if (d.flags == 2) {  // stage 2 only: t from t_io
-    const int64_t total = d.T * pl.ldtb;
-    int blocks = (int)((total + 255) / 256);
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(split_t_kernel, dim3(blocks), dim3(256), 0, st, d.t_io, d.ldt, (int)d.T,
-                       (int)d.r, a.thi, pl.TB == 1 ? a.tlo : (uint16_t*)nullptr, pl.ldtb);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    a.nb1 = 0;
-    a.wait = 0;
+hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
+  if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+  const int64_t T = ds[0].T;
+  char* ws = static_cast<char*>(ds[0].workspace);
+  DecArgs a{};
+  a.n = n;
+  a.T = (int)T;
+  size_t off = kCtlBytes;
+  int n1 = 0, TB = 1;
+  for (int i = 0; i < n; ++i) {
+    const DecodeLinear& d = ds[i];
+    const Plan pl = make_plan(T, d.d_in, d.r, d.d_out);
+    TB = pl.TB;
+    char* data = ws + off;
+    off += round_up(pl.bytes, 256);
+    LinArgs& L = a.lin[i];
+    L.x = static_cast<const uint16_t*>(d.x);
+    L.ldx = d.ldx;
+    L.ut = static_cast<const uint16_t*>(d.Ut);
+    L.ldu = d.ldu;
+    L.vt = static_cast<const uint16_t*>(d.Vt);
+    L.ldv = d.ldv;
+    L.y = static_cast<uint16_t*>(d.y);
+    L.ldy = d.ldy;
+    L.yacc = d.y_acc;
+    L.ldacc = d.ld_acc;
+    L.t32 = d.t_io;
+    L.ldt32 = d.ldt;
+    L.thi = reinterpret_cast<uint16_t*>(data + pl.off_thi);
+    L.tlo = reinterpret_cast<uint16_t*>(data + pl.off_tlo);
+    L.ldtb = pl.ldtb;
+    L.part = reinterpret_cast<float*>(data + pl.off_part);
+    L.ctl = reinterpret_cast<uint32_t*>(ws + (size_t)i * CTL_WORDS * 4);
+    L.d_in = (int)d.d_in;
+    L.r = (int)d.r;
+    L.d_out = (int)d.d_out;
+    L.nb1 = pl.nb1;
+    L.S1 = pl.S1;
+    L.kc1 = pl.kc1;
+    L.n2 = pl.n2;
+    L.wait = 1;
+    L.packed = d.packed ? 1 : 0;
+    if (d.flags == 1) {  // stage 1 only
+      L.n2 = 0;
+      L.wait = 0;
+    } else if (d.flags == 2) {  // stage 2 only: t from t_io
+      const int64_t total = T * pl.ldtb;
+      int blocks = (int)((total + 255) / 256);
+      if (blocks > 1024) blocks = 1024;
+      hipLaunchKernelGGL(split_t_kernel, dim3(blocks), dim3(256), 0, st, d.t_io, d.ldt, (int)T,
+                         (int)d.r, L.thi, pl.TB == 1 ? L.tlo : (uint16_t*)nullptr, pl.ldtb);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      L.nb1 = 0;
+      L.wait = 0;
+    }
+    L.first1 = n1;
+    n1 += L.nb1 * L.S1;
   }
-  const int grid = a.nb1 * a.S1 + a.n2;
-  switch (pl.TB) {
+  a.n1 = n1;
+  int grid = n1;
+  for (int i = 0; i < n; ++i) {
+    a.lin[i].first2 = grid;
+    grid += a.lin[i].n2;
+  }
+  if (grid == 0) return hipSuccess;
+  switch (TB) {
     case 1: return launch_decode<1>(a, grid, st);
     case 2: return launch_decode<2>(a, grid, st);
     default: return launch_decode<4>(a, grid, st);
   }
+}
+
+hipError_t decode_linear_bf16(const DecodeLinear& d, hipStream_t st) {
+  return decode_group_bf16(&d, 1, st);
 }
 
 }  // namespace lr

@@ -43,6 +43,10 @@ hipError_t pack_factor_bf16(const void* W, int64_t N, int64_t K, int64_t ld, voi
                             int64_t pitch, hipStream_t st);
 size_t decode_workspace_bytes(int64_t T, int64_t d_in, int64_t r, int64_t d_out);
 hipError_t decode_linear_bf16(const DecodeLinear& d, hipStream_t st);
+// Up to 8 independent linears over the same T (<= 64) token rows in one
+// launch; they share the workspace of ds[0] (decode_group_workspace_bytes).
+size_t decode_group_workspace_bytes(const DecodeLinear* ds, int n);
+hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st);
 
 // bf16, T > 64: fused two-stage MFMA path (or two GEMMs).
 size_t prefill_workspace_bytes(int64_t T, int64_t r);

@@ -1,6 +1,7 @@
 """The C ABI library loads, exports every symbol include/lowrank.h declares,
 and rejects bad arguments on the host before launching anything (CPU only:
 no call here reaches a kernel launch)."""
+import ctypes
 import ctypes as C
 import os
 import re
@@ -112,7 +113,8 @@ def test_struct_layouts_match_the_library():
     lib = lr.load()
     assert lib.lowrank_abi_sizeof(0) == ctypes.sizeof(lr.LayerWeights)
     assert lib.lowrank_abi_sizeof(1) == ctypes.sizeof(lr.DecodeState)
-    assert lib.lowrank_abi_sizeof(2) == 0
+    assert lib.lowrank_abi_sizeof(2) == ctypes.sizeof(_lib.Linear)
+    assert lib.lowrank_abi_sizeof(3) == 0
 
 
 def test_decode_step_rejects_bad_arguments():
@@ -127,3 +129,48 @@ def test_decode_step_rejects_bad_arguments():
     assert lib.lowrank_decode_step_workspace_bytes(ctypes.byref(w), ctypes.byref(s)) == 0
     assert lib.lowrank_rope_table(7, 10, 10000.0, A16, None) == _lib.LR_ERR_ARG
     assert lib.lowrank_rope_table(64, 0, 10000.0, A16, None) == _lib.LR_ERR_ARG
+
+
+def _group(n=2, T=4, flags=0, ws=A16, wsb=1 << 30, **kw):
+    arr = (_lib.Linear * max(n, 1))()
+    for a in arr:
+        a.d_in, a.r, a.d_out = 64, 16, 32
+        a.x, a.ldx, a.Ut, a.ldu, a.Vt, a.ldv, a.y, a.ldy = A16, 64, A16, 64, A16, 16, A16, 32
+    for k, v in kw.items():
+        setattr(arr[0], k, v)
+    return lr.load().lowrank_linear_forward_group(T, n, ctypes.cast(arr, ctypes.c_void_p), flags,
+                                                  ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), _lib.LR_ERR_ARG),
+    (dict(n=9), _lib.LR_ERR_ARG),
+    (dict(T=65), _lib.LR_ERR_ARG),
+    (dict(T=0), _lib.LR_ERR_ARG),
+    (dict(flags=1), _lib.LR_ERR_ARG),                 # only LR_PACKED_WEIGHTS is a group flag
+    (dict(x=None), _lib.LR_ERR_ARG),
+    (dict(Vt=None), _lib.LR_ERR_ARG),                 # stage 1 only needs t_io
+    (dict(y=None), _lib.LR_ERR_ARG),
+    (dict(ldu=60), _lib.LR_ERR_ARG),
+    (dict(x=A2), _lib.LR_ERR_ALIGN),
+    (dict(ldv=20), _lib.LR_ERR_ALIGN),
+    (dict(ws=None), _lib.LR_ERR_WORKSPACE),
+    (dict(wsb=1024), _lib.LR_ERR_WORKSPACE),
+    (dict(ldx=1 << 24), _lib.LR_ERR_UNSUPPORTED),
+])
+def test_group_rejects_bad_arguments(kw, status):
+    assert _group(**kw) == status
+
+
+def test_group_workspace_covers_single_calls():
+    # a group's workspace holds every member's own scratch plus the fixed
+    # control area that single calls use too
+    arr = (_lib.Linear * 3)()
+    shapes = [(4096, 1228, 4096), (4096, 1228, 4096), (4096, 1791, 11008)]
+    for a, (d_in, r, d_out) in zip(arr, shapes):
+        a.d_in, a.r, a.d_out = d_in, r, d_out
+    g = lr.load().lowrank_group_workspace_bytes(8, 3, ctypes.cast(arr, ctypes.c_void_p))
+    singles = [lr.lowrank_workspace_bytes(0, lr.LR_BF16, 8, *sh) for sh in shapes]
+    assert g >= max(singles)
+    assert g <= sum(singles)
+    assert lr.load().lowrank_group_workspace_bytes(65, 3, ctypes.cast(arr, ctypes.c_void_p)) == 0

@@ -1,0 +1,124 @@
+"""lowrank_linear_forward_group on the GPU: several independent decode
+linears in one launch give bit for bit what separate calls give, and match
+the fp64 oracle (stage-1-only and accumulate members included)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_decomposed_amd as lr
+from gpu_util import bits, dev, make_linear, maxrel, to_f64
+
+pytestmark = pytest.mark.gpu
+BF16_TOL = 2e-2
+SHAPES = [(1024, 300, 1024), (1024, 96, 256), (1024, 120, 256)]     # q-, k-, v-like
+
+
+def _cases(T, seed, shapes=SHAPES):
+    return [make_linear(seed + i, T, d_in, r, d_out, "bf16", fast=True, ld_extra=8)
+            for i, (d_in, r, d_out) in enumerate(shapes)]
+
+
+@pytest.mark.parametrize("T", [1, 8, 16, 17, 33, 64])
+def test_group_matches_separate_calls_and_oracle(T):
+    cs = _cases(T, 8000 + T)
+    x = cs[0]["dx"]                      # one input for all members, as q, k, v share it
+    for c in cs[1:]:
+        c["x"] = cs[0]["x"]
+    ts = [torch.empty((T, c["dUt"].shape[0]), dtype=torch.float32, device=dev()) for c in cs]
+    ys = lr.lowrank_linear_forward_group(
+        [dict(x=x, Ut=c["dUt"], Vt=c["dVt"], t_io=t) for c, t in zip(cs, ts)])
+    sep_t = [torch.empty_like(t) for t in ts]
+    sep = [lr.lowrank_linear_forward(x, c["dUt"], c["dVt"], t_io=t) for c, t in zip(cs, sep_t)]
+    torch.cuda.synchronize()
+    for c, y, t, ys_, ts_ in zip(cs, ys, ts, sep, sep_t):
+        assert np.array_equal(bits(y), bits(ys_))
+        assert np.array_equal(to_f64(t), to_f64(ts_))
+        tr, yr = oracle.linear(cs[0]["x"], c["U"], c["V"])
+        assert maxrel(to_f64(t), tr) <= 1e-5
+        assert maxrel(to_f64(y), yr) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [4, 40])
+def test_group_mixed_members(T):
+    # member 0: full; member 1: stage 1 only (the latent of a k projection);
+    # member 2: accumulates into an fp32 residual
+    cs = _cases(T, 8100 + T, [(640, 200, 640), (640, 64, 128), (640, 150, 512)])
+    x = cs[0]["dx"]
+    d = dev()
+    t1 = torch.full((T, 64), float("nan"), dtype=torch.float32, device=d)
+    g = torch.Generator(device="cpu").manual_seed(T)
+    acc0 = torch.randn((T, 512), generator=g, dtype=torch.float32)
+    acc = acc0.clone().to(d)
+    ys = lr.lowrank_linear_forward_group([dict(x=x, Ut=cs[0]["dUt"], Vt=cs[0]["dVt"]),
+                                          dict(x=x, Ut=cs[1]["dUt"], t_io=t1),
+                                          dict(x=x, Ut=cs[2]["dUt"], Vt=cs[2]["dVt"], y_acc=acc)])
+    torch.cuda.synchronize()
+    xv = cs[0]["x"]
+    assert maxrel(to_f64(ys[0]), oracle.linear(xv, cs[0]["U"], cs[0]["V"])[1]) <= BF16_TOL
+    assert ys[1] is None and ys[2] is None
+    assert maxrel(to_f64(t1), oracle.linear(xv, cs[1]["U"], cs[1]["V"])[0]) <= 1e-5
+    added = to_f64(acc) - acc0.double().numpy()
+    assert maxrel(added, oracle.linear(xv, cs[2]["U"], cs[2]["V"])[1]) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_group_packed_matches_row_major(T):
+    cs = _cases(T, 8200 + T)
+    x = cs[0]["dx"]
+    rm = lr.lowrank_linear_forward_group([dict(x=x, Ut=c["dUt"], Vt=c["dVt"]) for c in cs])
+    pk = lr.lowrank_linear_forward_group([dict(x=x, Ut=lr.pack_factor(c["dUt"]),
+                                               Vt=lr.pack_factor(c["dVt"])) for c in cs])
+    torch.cuda.synchronize()
+    for a, b in zip(rm, pk):
+        assert np.array_equal(bits(a), bits(b))
+
+
+def test_group_and_single_calls_share_a_workspace():
+    d = dev()
+    cs = _cases(8, 8300)
+    x = cs[0]["dx"]
+    ws = torch.zeros(4 << 20, dtype=torch.uint8, device=d)
+    lin = [dict(x=x, Ut=c["dUt"], Vt=c["dVt"]) for c in cs]
+    assert lr.lowrank_group_workspace_bytes(8, lin) <= ws.numel()
+    for rep in range(3):
+        y0 = lr.lowrank_linear_forward(x, cs[0]["dUt"], cs[0]["dVt"], workspace=ws)
+        ys = lr.lowrank_linear_forward_group(lin, workspace=ws)
+        y2 = lr.lowrank_linear_forward(x, cs[2]["dUt"], cs[2]["dVt"], workspace=ws)
+        torch.cuda.synchronize()
+        ref = [lr.lowrank_linear_forward(x, c["dUt"], c["dVt"]) for c in cs]
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y0), bits(ref[0]))
+        assert np.array_equal(bits(y2), bits(ref[2]))
+        for a, b in zip(ys, ref):
+            assert np.array_equal(bits(a), bits(b))
+        for L in lin:
+            L.pop("y", None)
+    ctl = ws[:8 * 16384].view(torch.int32).cpu().numpy()
+    assert not ctl.any()
+
+
+def test_group_graph_replay():
+    d = dev()
+    cs = _cases(16, 8400)
+    x = cs[0]["dx"].clone()
+    ws = torch.zeros(4 << 20, dtype=torch.uint8, device=d)
+    ys = [torch.empty((16, c["dVt"].shape[0]), dtype=torch.bfloat16, device=d) for c in cs]
+    lin = [dict(x=x, Ut=c["dUt"], Vt=c["dVt"], y=y) for c, y in zip(cs, ys)]
+    lr.lowrank_linear_forward_group(lin, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(d)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lr.lowrank_linear_forward_group(lin, workspace=ws, stream=s)
+    gen = torch.Generator(device=d).manual_seed(5)
+    for rep in range(3):
+        x.copy_(torch.randn(x.shape, generator=gen, device=d).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [bits(y) for y in ys]
+        ref = [bits(lr.lowrank_linear_forward(x, c["dUt"], c["dVt"])) for c in cs]
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b)
