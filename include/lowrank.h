@@ -300,15 +300,19 @@ size_t lowrank_decode_step_workspace_bytes(const lr_layer_weights* w, const lr_d
  *   x = RMSNorm(h) ; q = RoPE(lowrank_q(x), pos) ; latents x U_k, x U_v
  *   appended at slot_mapping (bf16) ; compact copy of every sequence's
  *   latents through remap (DeInfer/en §2.C replay copy) ; K = RoPE(buf_k V_k),
- *   V = buf_v V_v by a fixed-size GEMM over cap rows (the "large, fixed-size
- *   GEMM", rows past *n_valid skipped) ; softmax attention of each query over
+ *   V = buf_v V_v by one GEMM of fixed size over cap rows (its shape and
+ *   addresses never change between steps; rows past *n_valid are skipped) ;
+ *   softmax attention of each query over
  *   its sequence's rows ; h += lowrank_o(o) ; x = RMSNorm(h) ;
  *   h += lowrank_down(silu(lowrank_gate(x)) * lowrank_up(x)).
  * Launches only; fixed grids, no host reads of device data, no allocation:
  * capture 32 calls (one per layer) in one graph and replay it each step
  * after refreshing the preparation arrays.
+ * The projections run on the decode path (q, k, v as one grouped launch,
+ * gate and up as another), so B <= 64.
  * Errors: LR_ERR_ARG / LR_ERR_ALIGN / LR_ERR_UNSUPPORTED (head_dim not 64 or
- * 128) / LR_ERR_WORKSPACE from host checks, LR_ERR_HIP from the runtime.
+ * 128, B > 64) / LR_ERR_WORKSPACE from host checks, LR_ERR_HIP from the
+ * runtime.
  */
 lr_status lowrank_layer_decode_step(const lr_layer_weights* w, const lr_decode_state* s,
                                     float* h, void* workspace, size_t workspace_bytes,

@@ -13,6 +13,7 @@
 // are read from device buffers, so one captured graph serves every step.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "lowrank.h"
@@ -390,11 +391,13 @@ StepLayout step_layout(const lr_layer_weights* w, const lr_decode_state* s) {
   L.nch = (s->max_seq_rows + kAttnChunk - 1) / kAttnChunk;
   const int64_t din[7] = {d, d, d, dq, d, d, w->d_ffn};
   const int64_t dout[7] = {dq, L.dkv, L.dkv, d, w->d_ffn, w->d_ffn, d};
-  size_t lin = 0;
-  for (int k = 0; k < 7; ++k) {
-    const size_t b = decode_workspace_bytes(B, din[k], w->r[k], dout[k]);
-    lin = b > lin ? b : lin;
-  }
+  // the projections' scratch: q,k,v and gate,up go out as groups
+  DecodeLinear g[7];
+  for (int k = 0; k < 7; ++k) g[k] = DecodeLinear{B, din[k], w->r[k], dout[k]};
+  size_t lin = decode_group_workspace_bytes(g, 3);
+  lin = std::max(lin, decode_group_workspace_bytes(g + 4, 2));
+  lin = std::max(lin, decode_workspace_bytes(B, din[3], w->r[3], dout[3]));
+  lin = std::max(lin, decode_workspace_bytes(B, din[6], w->r[6], dout[6]));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -427,7 +430,8 @@ lr_status check_step(const lr_layer_weights* w, const lr_decode_state* s, const 
   if (w->head_dim != 64 && w->head_dim != 128) return LR_ERR_UNSUPPORTED;
   if (w->n_heads % w->n_kv_heads) return LR_ERR_ARG;
   if (s->B <= 0 || s->cap <= 0 || s->max_seq_rows <= 0 || s->pool_rows <= 0) return LR_ERR_ARG;
-  if (s->B > 65535 || s->cap > INT32_MAX) return LR_ERR_ARG;
+  if (s->cap > INT32_MAX) return LR_ERR_ARG;
+  if (s->B > 64) return LR_ERR_UNSUPPORTED;  // projections run on the decode path
   if (!w->rope || w->rope_max_pos <= 0 || !w->attn_norm || !w->ffn_norm) return LR_ERR_ARG;
   if (!s->k_pool || !s->v_pool || !s->slot_mapping || !s->remap || !s->seq_off || !s->pos ||
       !s->n_valid)
@@ -509,7 +513,7 @@ extern "C" lr_status lowrank_layer_decode_step(const lr_layer_weights* w,
   } while (0)
 
   auto linear = [&](int k, const void* in, int64_t din, int64_t ldin, int64_t dout, void* y,
-                    float* yacc, float* t_out) -> hipError_t {
+                    float* yacc, float* t_out) -> DecodeLinear {
     DecodeLinear dl{};
     dl.T = B;
     dl.d_in = din;
@@ -529,16 +533,20 @@ extern "C" lr_status lowrank_layer_decode_step(const lr_layer_weights* w,
     dl.workspace = lin;
     dl.y_acc = yacc;
     dl.ld_acc = d;
-    return decode_linear_bf16(dl, st);
+    return dl;
   };
 
   // attention block
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(B), dim3(256), 0, st, h, d,
                      static_cast<const uint16_t*>(w->attn_norm), x, d, (int)d, w->eps);
   LR_CHECK(hipGetLastError());
-  LR_CHECK(linear(0, x, d, d, dq, q, nullptr, nullptr));
-  LR_CHECK(linear(1, x, d, d, L.dkv, nullptr, nullptr, latk));
-  LR_CHECK(linear(2, x, d, d, L.dkv, nullptr, nullptr, latv));
+  {
+    // q (full) and the k, v latents (stage 1 only) read the same x: one launch
+    const DecodeLinear qkv[3] = {linear(0, x, d, d, dq, q, nullptr, nullptr),
+                                 linear(1, x, d, d, L.dkv, nullptr, nullptr, latk),
+                                 linear(2, x, d, d, L.dkv, nullptr, nullptr, latv)};
+    LR_CHECK(decode_group_bf16(qkv, 3, st));
+  }
   hipLaunchKernelGGL(append_kernel, dim3(B), dim3(256), 0, st, latk, w->r[1], (int)w->r[1],
                      s->slot_mapping, s->pool_rows, static_cast<uint16_t*>(s->k_pool), s->pool_ld);
   LR_CHECK(hipGetLastError());
@@ -604,17 +612,20 @@ extern "C" lr_status lowrank_layer_decode_step(const lr_layer_weights* w,
                        dim3(64), 0, st, part, (int)w->n_heads, (int)L.nch, s->seq_off, (int)s->cap, o, dq);
   }
   LR_CHECK(hipGetLastError());
-  LR_CHECK(linear(3, o, dq, dq, d, nullptr, h, nullptr));
+  LR_CHECK(decode_linear_bf16(linear(3, o, dq, dq, d, nullptr, h, nullptr), st));
   // MLP block
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(B), dim3(256), 0, st, h, d,
                      static_cast<const uint16_t*>(w->ffn_norm), x, d, (int)d, w->eps);
   LR_CHECK(hipGetLastError());
-  LR_CHECK(linear(4, x, d, d, ffn, gate, nullptr, nullptr));
-  LR_CHECK(linear(5, x, d, d, ffn, up, nullptr, nullptr));
+  {
+    const DecodeLinear gu[2] = {linear(4, x, d, d, ffn, gate, nullptr, nullptr),
+                                linear(5, x, d, d, ffn, up, nullptr, nullptr)};
+    LR_CHECK(decode_group_bf16(gu, 2, st));
+  }
   hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((B * ffn + 255) / 256 < 4096 ? (B * ffn + 255) / 256 : 4096)),
                      dim3(256), 0, st, gate, up, m, (int64_t)B * ffn);
   LR_CHECK(hipGetLastError());
-  LR_CHECK(linear(6, m, ffn, ffn, d, nullptr, h, nullptr));
+  LR_CHECK(decode_linear_bf16(linear(6, m, ffn, ffn, d, nullptr, h, nullptr), st));
 #undef LR_CHECK
   return LR_OK;
 }

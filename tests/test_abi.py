@@ -174,3 +174,39 @@ def test_group_workspace_covers_single_calls():
     assert g >= max(singles)
     assert g <= sum(singles)
     assert lr.load().lowrank_group_workspace_bytes(65, 3, ctypes.cast(arr, ctypes.c_void_p)) == 0
+
+
+def _valid_step_structs():
+    # LLaMA-7B-shaped layer at ratio 0.2 with fake aligned addresses: passes
+    # every host check, so the calls below stop at the check named by each case
+    w, s = lr.LayerWeights(), lr.DecodeState()
+    w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.d_ffn, w.eps = 4096, 32, 32, 128, 11008, 1e-5
+    dims = [(4096, 4096)] * 4 + [(4096, 11008)] * 2 + [(11008, 4096)]
+    for k, (a, b) in enumerate(dims):
+        r = int(0.2 * a * b) // (a + b)
+        w.Ut[k], w.Vt[k], w.r[k] = A16, A16, r
+        w.ldu[k], w.ldv[k] = (a + 7) // 8 * 8, (r + 7) // 8 * 8
+    w.attn_norm = w.ffn_norm = w.rope = A16
+    w.rope_max_pos = 4112
+    s.k_pool = s.v_pool = s.slot_mapping = s.remap = s.seq_off = s.pos = s.n_valid = A16
+    s.pool_rows, s.pool_ld = 300000, 416
+    s.B, s.cap, s.max_seq_rows = 64, 64 * 4112, 4112
+    return w, s
+
+
+@pytest.mark.parametrize("field,value,status", [
+    (None, None, _lib.LR_ERR_WORKSPACE),          # valid; no workspace given
+    ("B", 65, _lib.LR_ERR_UNSUPPORTED),           # projections run on the decode path
+    ("head_dim", 96, _lib.LR_ERR_UNSUPPORTED),
+    ("pool_ld", 409, _lib.LR_ERR_ALIGN),
+    ("n_heads", 33, _lib.LR_ERR_ARG),             # not a multiple of n_kv_heads
+])
+def test_decode_step_host_checks(field, value, status):
+    w, s = _valid_step_structs()
+    if field is not None:
+        setattr(w if hasattr(w, field) and field not in ("B", "pool_ld") else s, field, value)
+    lib = lr.load()
+    assert lib.lowrank_layer_decode_step(C.byref(w), C.byref(s), C.c_void_p(A16), None, 0,
+                                         None) == status
+    if field is None:
+        assert lib.lowrank_decode_step_workspace_bytes(C.byref(w), C.byref(s)) > 0
