@@ -41,6 +41,25 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def recorded_traffic(dom):
+    """HBM bytes per launch of the dominant class from the committed counter
+    summary (profiles/decode_linear_traffic.json), or None when the class
+    differs or the decode kernel's sources changed since it was taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        rec = json.load(open(os.path.join(here, "profiles", "decode_linear_traffic.json")))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in ("linear_decode.hip", "lr_common.h", "lr_kernels.h"):
+        with open(os.path.join(here, "rank_decomposed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("class") != dom or rec.get("sources_sha256") != h.hexdigest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def rank(rho, a, b):
     from fractions import Fraction
     return int((Fraction(str(rho)) * a * b) // (a + b))
@@ -116,6 +135,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--layout", choices=("packed", "rowmajor"), default="packed",
                     help="device layout of the decode factors")
+    ap.add_argument("--probe-class", default=None,
+                    help="for hardware-counter runs: negate 256 Mi bf16 (a reference kernel "
+                         "of known traffic: 512 MiB in, 512 MiB out), run one launch class "
+                         "(e.g. gateup_T64) eagerly over every layer set twice, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the low-rank path here has no "
@@ -185,6 +208,22 @@ def main():
         return a.elapsed_time(b) / reps
 
     log("factors ready (%s layout)" % args.layout)
+    if args.probe_class:
+        name, T = args.probe_class.split("_T")
+        roles = dict(GROUPS)[name]
+        src = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)     # one elementwise kernel: reads 512 MiB, writes 512 MiB
+        torch.cuda.synchronize()
+        for _ in range(2):
+            for layer in sets:
+                call(int(T), layer, roles)
+        torch.cuda.synchronize()
+        log("probe done: reference kernel, then %d launches of %s" % (2 * len(sets),
+                                                                     args.probe_class))
+        return
     # the whole step (512 launches) is one HIP graph, as in the pages' decode
     step_graph = capture(step)
     log("decode step graph captured")
@@ -246,7 +285,8 @@ def main():
                          " + ".join("%s %dx%dx%d" % (r, SHAPES[r][0], rank(0.6, *SHAPES[r]),
                                                      SHAPES[r][1]) for r in dom_roles), dom_T),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(achieved * 1e9 / HBM_PEAK, 4),
+                     "traffic": recorded_traffic(dom),
                      "bytes_per_launch": dom_bytes, "us_per_launch": dom_us},
         "launches": per,
         "wall_s": round(wall, 3),
