@@ -62,6 +62,8 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr uint32_t kOutside = 0x80000000u;  // past every buffer (tiles stay < 2 GiB)
 constexpr int kCoherentLoad = 16;           // buffer-load cache policy: device scope
 constexpr int kMaxGroup = 8;                // linears per launch
+constexpr int kRedBudget1 = 159 * 1024;     // LDS for parked partials: one workgroup per CU
+constexpr int kRedBudget2 = 79 * 1024;      //   two workgroups per CU
 
 // One control block (uint32 words) per linear of a launch, all of them at
 // the start of the workspace: each hot word on a cache line of its own, then
@@ -94,6 +96,7 @@ struct LinArgs {
   int d_in, r, d_out;
   int nb1, S1, kc1;  // stage-1 row blocks, K ranges per block, K range width
   int n2;            // stage-2 tiles
+  int rb2;           // stage-2 tile height in 16-row blocks
   int first1, first2;  // index of the linear's first stage-1 / stage-2 tile
   int wait;          // stage-2 tiles wait for the stage-1 tiles of this launch
   int packed;        // weights fragment-packed
@@ -197,6 +200,7 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
                              const uint16_t* __restrict__ Alo, int64_t lda,
                              const uint16_t* __restrict__ B, int64_t ldb, bool packed, int T,
                              int N, int row0, int kbeg, int kend, uint32_t* ctl, bool wait) {
+  static_assert(!WAIT || PF % KSW == 0, "the prefetched steps are consumed KSW at a time");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kq = (lane >> 4) * 8;
@@ -292,11 +296,16 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
   }
 }
 
-// Park each wave's partial product in LDS as red[wave][reg][lane].
+// LDS slots for parking a tile of NR accumulator registers per lane: one
+// per wave when 16 x NR x 256 bytes fit the budget, else 8 (waves w and
+// w + 8 added in registers first).
+constexpr int park_slots(int NR, int lds_budget) { return 16 * NR * 256 <= lds_budget ? 16 : 8; }
+
+// Copy this wave's accumulators into LDS slot `slot` as red[slot][reg][lane].
 template <int TB, int RB>
-__device__ __forceinline__ void park(const f32x4 (&acc)[TB][RB], float* red) {
+__device__ __forceinline__ void park_slot(const f32x4 (&acc)[TB][RB], float* red, int slot) {
   constexpr int NR = TB * RB * 4;
-  float* b = red + (threadIdx.x >> 6) * NR * 64 + (threadIdx.x & 63);
+  float* b = red + slot * NR * 64 + (threadIdx.x & 63);
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -305,15 +314,42 @@ __device__ __forceinline__ void park(const f32x4 (&acc)[TB][RB], float* red) {
       for (int v = 0; v < 4; ++v) b[((tb * RB + r) * 4 + v) * 64] = acc[tb][r][v];
 }
 
-// Element e of a parked tile summed over the 16 waves, pairwise in a fixed
-// order (w + 8, then + 4, + 2, + 1).
-template <int NR>
+// Park the 16 waves' partial products in NSLOT slots whose sum is the tile.
+template <int TB, int RB, int NSLOT>
+__device__ __forceinline__ void park(f32x4 (&acc)[TB][RB], float* red) {
+  const int wave = threadIdx.x >> 6;
+  if (NSLOT == kWaves) {
+    park_slot<TB, RB>(acc, red, wave);
+    lds_barrier();
+    return;
+  }
+  constexpr int NR = TB * RB * 4;
+  if (wave >= 8) park_slot<TB, RB>(acc, red, wave - 8);
+  lds_barrier();
+  if (wave < 8) {
+    const float* b = red + wave * NR * 64 + (threadIdx.x & 63);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[tb][r][v] += b[((tb * RB + r) * 4 + v) * 64];
+  }
+  lds_barrier();
+  if (wave < 8) park_slot<TB, RB>(acc, red, wave);
+  lds_barrier();
+}
+
+// Element e of a parked tile summed over the slots, pairwise in a fixed order
+// (slot w + 8 -- already added in registers when there are 8 slots -- then
+// + 4, + 2, + 1: the same order either way).
+template <int NR, int NSLOT>
 __device__ __forceinline__ float sum_waves(const float* red, int e) {
-  float v[kWaves];
+  float v[NSLOT];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) v[w] = red[w * NR * 64 + e];
+  for (int w = 0; w < NSLOT; ++w) v[w] = red[w * NR * 64 + e];
 #pragma unroll
-  for (int h = kWaves / 2; h >= 1; h >>= 1)
+  for (int h = NSLOT / 2; h >= 1; h >>= 1)
 #pragma unroll
     for (int w = 0; w < h; ++w) v[w] += v[w + h];
   return v[0];
@@ -329,10 +365,48 @@ __device__ __forceinline__ void elem_coords(int e, int* tok, int* row) {
   *row = rb * 16 + (lane & 15);
 }
 
-template <int TB, int RB1, int RB2, int KSW1, int KSW2, int PF, bool SPLIT, int WG_PER_CU>
+// One stage-2 tile: 16*RB2 rows of V_r^T over all of r, then y.
+template <int TB, int RB2, int KSW2, int PF, bool SPLIT, int BUDGET>
+__device__ __forceinline__ void stage2_tile(const LinArgs& p, int T, int tile, float* red) {
+  constexpr int NR = TB * RB2 * 4, NE = NR * 64;
+  constexpr int EPT = (NE + kThreads - 1) / kThreads;
+  const int row0 = (tile - p.first2) * 16 * RB2;
+  f32x4 acc[TB][RB2];
+  tile_product<TB, RB2, KSW2, PF, SPLIT, true>(acc, p.thi, p.tlo, p.ldtb, p.vt, p.ldv,
+                                               p.packed != 0, T, p.d_out, row0, 0, p.r,
+                                               p.ctl, p.wait != 0);
+  // count this tile past the wait; the last one clears GO for the next call.
+  // The LDS barrier does not wait for global memory, so this contended
+  // atomic's round trip overlaps the reduction.
+  uint32_t old = 0;
+  if (p.wait && threadIdx.x == 0) old = atomic_add_agent(p.ctl + CTL_DONE2, 1u);
+  constexpr int NS = park_slots(NR, BUDGET);
+  park<TB, RB2, NS>(acc, red);
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    int tok, ro;
+    elem_coords<RB2>(e, &tok, &ro);
+    const int n = row0 + ro;
+    if (e >= NE || tok >= T || n >= p.d_out) continue;
+    const float val = sum_waves<NR, NS>(red, e);
+    if (p.yacc)
+      p.yacc[(int64_t)tok * p.ldacc + n] += val;  // each element owned by one tile
+    else
+      p.y[(int64_t)tok * p.ldy + n] = (uint16_t)f2bf(val);
+  }
+  if (p.wait && threadIdx.x == 0 && old == (uint32_t)(p.n2 - 1)) {
+    store_relaxed(p.ctl + CTL_GO, 0u);
+    store_relaxed(p.ctl + CTL_DONE2, 0u);
+  }
+}
+
+template <int TB, int RB1, int RB2, int RB2L, int KSW1, int KSW2, int KSW2L, int PF, int PFL,
+          bool SPLIT, int WG_PER_CU>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4 * WG_PER_CU, 4 * WG_PER_CU)))
 void decode_kernel(DecArgs args) {
-  extern __shared__ __attribute__((aligned(16))) float red[];  // [16][NR][64], + padding
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [slots][NR][64], + padding
+  constexpr int kBudget = WG_PER_CU == 1 ? kRedBudget1 : kRedBudget2;
   __shared__ uint32_t sh_last;
   const int tile = (int)blockIdx.x;
   const int T = args.T;
@@ -351,13 +425,13 @@ void decode_kernel(DecArgs args) {
     tile_product<TB, RB1, KSW1, KSW1, false, false>(acc, p.x, nullptr, p.ldx, p.ut, p.ldu,
                                                     p.packed != 0, T, p.r, row0, kbeg, kend,
                                                     p.ctl, false);
-    park<TB, RB1>(acc, red);
-    lds_barrier();
+    constexpr int NS = park_slots(NR, kBudget);
+    park<TB, RB1, NS>(acc, red);
     float val[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const int e = threadIdx.x + i * kThreads;
-      val[i] = e < NE ? sum_waves<NR>(red, e) : 0.f;
+      val[i] = e < NE ? sum_waves<NR, NS>(red, e) : 0.f;
     }
     if (p.S1 > 1) {
       // the K ranges of the row block meet in the workspace; the last to
@@ -421,37 +495,10 @@ void decode_kernel(DecArgs args) {
   int li = 0;  // the linear owning this stage-2 tile (workgroup-uniform)
   while (li + 1 < args.n && tile >= args.lin[li + 1].first2) ++li;
   const LinArgs& p = args.lin[li];
-  constexpr int NR = TB * RB2 * 4, NE = NR * 64;
-  constexpr int EPT = (NE + kThreads - 1) / kThreads;
-  const int row0 = (tile - p.first2) * 16 * RB2;
-  f32x4 acc[TB][RB2];
-  tile_product<TB, RB2, KSW2, PF, SPLIT, true>(acc, p.thi, p.tlo, p.ldtb, p.vt, p.ldv,
-                                               p.packed != 0, T, p.d_out, row0, 0, p.r,
-                                               p.ctl, p.wait != 0);
-  // count this tile past the wait; the last one clears GO for the next call.
-  // The LDS barrier does not wait for global memory, so this contended
-  // atomic's round trip overlaps the reduction.
-  uint32_t old = 0;
-  if (p.wait && threadIdx.x == 0) old = atomic_add_agent(p.ctl + CTL_DONE2, 1u);
-  park<TB, RB2>(acc, red);
-  lds_barrier();
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int e = threadIdx.x + i * kThreads;
-    int tok, ro;
-    elem_coords<RB2>(e, &tok, &ro);
-    const int n = row0 + ro;
-    if (e >= NE || tok >= T || n >= p.d_out) continue;
-    const float val = sum_waves<NR>(red, e);
-    if (p.yacc)
-      p.yacc[(int64_t)tok * p.ldacc + n] += val;  // each element owned by one tile
-    else
-      p.y[(int64_t)tok * p.ldy + n] = (uint16_t)f2bf(val);
-  }
-  if (p.wait && threadIdx.x == 0 && old == (uint32_t)(p.n2 - 1)) {
-    store_relaxed(p.ctl + CTL_GO, 0u);
-    store_relaxed(p.ctl + CTL_DONE2, 0u);
-  }
+  if (RB2L != RB2 && p.rb2 == RB2L)
+    stage2_tile<TB, RB2L, KSW2L, PFL, SPLIT, kBudget>(p, T, tile, red);
+  else
+    stage2_tile<TB, RB2, KSW2, PF, SPLIT, kBudget>(p, T, tile, red);
 }
 
 // t (fp32, caller's layout) -> bf16 (and bf16 residual) for a stage-2-only call.
@@ -485,7 +532,9 @@ Plan make_plan(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
   Plan pl{};
   pl.TB = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
   pl.RB1 = pl.TB == 1 ? 1 : 2;
-  pl.RB2 = 2;
+  // 64-row stage-2 tiles at T > 32 halve the re-reads of t (each tile reads
+  // all of it) where there are tiles enough to fill the GPU anyway
+  pl.RB2 = pl.TB == 4 && d_out >= 8192 ? 4 : 2;
   pl.nb1 = (int)((r + 16 * pl.RB1 - 1) / (16 * pl.RB1));
   pl.n2 = (int)((d_out + 16 * pl.RB2 - 1) / (16 * pl.RB2));
   // split K when a row block would hand one workgroup more than ~256 KiB
@@ -518,22 +567,31 @@ Plan make_plan(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
 // once (the dispatcher would otherwise stack two workgroups on one CU and
 // halve the CUs streaming).  "dense": two workgroups per CU (64 registers,
 // half-size rounds) for larger grids, which then keep all their stage-2 tiles
-// resident.  Template arguments: weight rows per tile (16*RB1, 16*RB2),
-// k-steps per round (KSW1, KSW2), stage-2 prefetch depth PF.
+// resident.  Template arguments: weight rows per tile (16*RB1; 16*RB2, or
+// 16*RB2L for linears the plan gives tall stage-2 tiles), k-steps per round
+// (KSW1; KSW2, KSW2L), stage-2 prefetch depth (PF, PFL; multiples of the
+// round).
 constexpr int kLdsMax = 163840;
 
-template <int TB, int RB1, int RB2, int KSW1, int KSW2, int PF, bool SPLIT, int WPC>
+template <int TB, int RB1, int RB2, int RB2L, int KSW1, int KSW2, int KSW2L, int PF, int PFL,
+          bool SPLIT, int WPC>
 hipError_t launch_one(const DecArgs& a, int grid, hipStream_t st) {
-  constexpr int NR = TB * (RB1 > RB2 ? RB1 : RB2) * 4;
-  constexpr size_t red_bytes = (size_t)kWaves * NR * 64 * 4;
+  constexpr int budget = WPC == 1 ? kRedBudget1 : kRedBudget2;
+  constexpr int NR1 = TB * RB1 * 4, NR2 = TB * (RB2L > RB2 ? RB2L : RB2) * 4;
+  constexpr size_t red1 = (size_t)park_slots(NR1, budget) * NR1 * 256;
+  constexpr size_t red2 = (size_t)park_slots(NR2, budget) * NR2 * 256;
+  constexpr size_t red_bytes = red1 > red2 ? red1 : red2;
+  static_assert(red_bytes <= (size_t)budget, "parked partials exceed the LDS budget");
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_kernel<TB, RB1, RB2, KSW1, KSW2, PF, SPLIT, WPC>),
+        reinterpret_cast<const void*>(
+            &decode_kernel<TB, RB1, RB2, RB2L, KSW1, KSW2, KSW2L, PF, PFL, SPLIT, WPC>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax - 1024);
   });
   const size_t lds = WPC == 1 ? std::max<size_t>(red_bytes, kLdsMax / 2 + 1024) : red_bytes;
-  hipLaunchKernelGGL((decode_kernel<TB, RB1, RB2, KSW1, KSW2, PF, SPLIT, WPC>), dim3(grid),
+  hipLaunchKernelGGL((decode_kernel<TB, RB1, RB2, RB2L, KSW1, KSW2, KSW2L, PF, PFL, SPLIT, WPC>),
+                     dim3(grid),
                      dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
@@ -542,12 +600,12 @@ template <int TB>
 hipError_t launch_decode(const DecArgs& a, int grid, hipStream_t st) {
   const bool spread = grid <= 400;
   if (TB == 1)
-    return spread ? launch_one<1, 1, 2, 8, 4, 4, true, 1>(a, grid, st)
-                  : launch_one<1, 1, 2, 4, 2, 2, true, 2>(a, grid, st);
+    return spread ? launch_one<1, 1, 2, 2, 8, 4, 4, 4, 4, true, 1>(a, grid, st)
+                  : launch_one<1, 1, 2, 2, 4, 2, 2, 2, 2, true, 2>(a, grid, st);
   if (TB == 2)
-    return spread ? launch_one<2, 2, 2, 4, 2, 4, false, 1>(a, grid, st)
-                  : launch_one<2, 2, 2, 2, 1, 2, false, 2>(a, grid, st);
-  return launch_one<4, 2, 2, 2, 2, 4, false, 1>(a, grid, st);
+    return spread ? launch_one<2, 2, 2, 2, 4, 2, 2, 4, 4, false, 1>(a, grid, st)
+                  : launch_one<2, 2, 2, 2, 2, 1, 1, 2, 2, false, 2>(a, grid, st);
+  return launch_one<4, 2, 2, 4, 2, 2, 1, 4, 1, false, 1>(a, grid, st);
 }
 
 }  // namespace
@@ -603,6 +661,7 @@ hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
     L.S1 = pl.S1;
     L.kc1 = pl.kc1;
     L.n2 = pl.n2;
+    L.rb2 = pl.RB2;
     L.wait = 1;
     L.packed = d.packed ? 1 : 0;
     if (d.flags == 1) {  // stage 1 only

@@ -125,7 +125,8 @@ def test_pack_factor_bit_exact(N, K, extra):
 
 @gpu
 @pytest.mark.parametrize("T", [1, 3, 8, 16, 17, 32, 33, 48, 64])
-@pytest.mark.parametrize("shape", [(1024, 300, 768), (520, 45, 1100), (96, 7, 40), (11008, 90, 200)])
+@pytest.mark.parametrize("shape", [(1024, 300, 768), (520, 45, 1100), (96, 7, 40), (11008, 90, 200),
+                                   (256, 70, 8200)])     # wide output: 64-row stage-2 tiles at T > 32
 def test_packed_decode_matches_row_major_and_oracle(T, shape):
     import torch
     import oracle
