@@ -114,8 +114,12 @@ lr_status lowrank_pack_factor(const void* W, int64_t N, int64_t K, int64_t ld, v
  *            Accumulation is fp32 in both cases; bf16 outputs are rounded to
  *            nearest even.
  *   T        number of token rows (>= 1).  T <= 64 runs the decode path
- *            (weights streamed once from HBM); larger T runs the prefill path
- *            (fused two-stage MFMA kernel, the rank-r tile kept on chip).
+ *            (weights streamed once from HBM); 64 < T < 1024 runs the fused
+ *            two-stage MFMA kernel (the rank-r tile kept on chip); from 1024
+ *            rows on, the two stages run as two large-tile MFMA GEMMs with t
+ *            parked in the workspace as bf16 (the value an fp32 t_io holds,
+ *            rounded to nearest even: the same operand stage 2 multiplies on
+ *            every path).
  *   x        [T, d_in], ldx        (stage 1 input)
  *   Ut       [r, d_in], ldu        (U_r transposed)
  *   Vt       [d_out, r], ldv       (V_r transposed)

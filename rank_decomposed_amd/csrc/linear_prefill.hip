@@ -22,6 +22,7 @@
 // Plain kernel: C = A . B^T on a 128x128 tile with LDS double buffering, for
 // the stage-only calls (tensor-parallel share) and for ranks too large for the
 // on-chip tile.
+#include <algorithm>
 #include <mutex>
 
 #include "lr_common.h"
@@ -326,14 +327,62 @@ size_t fused_lds_bytes(int64_t r) { return (size_t)kBM * (rup(r, 32) + 8) * 2; }
 
 static bool fused_fits(int64_t r) { return fused_lds_bytes(r) <= (size_t)kLdsMax; }
 
-// Only a full call whose rank tile does not fit on chip (and that was given
-// no t_io) parks t in the workspace, as bf16 [T, round_up(r, 8)].
+// From this many rows on, both stages run as large-tile GEMMs through a bf16
+// t in the workspace: the round trip of t through HBM costs well under 1 % of
+// the time of either contraction, and the 256-row tiles run the MFMA units
+// far closer to their peak than the fused kernel's 64-row tiles.
+constexpr int64_t kBigT = 1024;
+
+// Calls from kBigT rows on, and calls whose rank tile does not fit on chip,
+// park t in the workspace as bf16 [T, round_up(r, 8)]; the fused kernel
+// needs none.
 size_t prefill_workspace_bytes(int64_t T, int64_t r) {
-  if (fused_fits(r)) return 0;
+  if (T < kBigT && fused_fits(r)) return 0;
   return (size_t)rup(T * rup(r, 8) * 2, 256);
 }
 
+namespace {
+
+// bf16 copy (round to nearest even) of an fp32 [rows, cols] matrix.
+__global__ void to_bf16_kernel(const float* src, int64_t lds, uint16_t* dst, int64_t ldd,
+                               int64_t rows, int64_t cols) {
+  const int64_t n = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = i / cols, col = i % cols;
+    dst[row * ldd + col] = (uint16_t)f2bf(src[row * lds + col]);
+  }
+}
+
+// Both stages on the large-tile GEMM: t (bf16, [T, ldtb]) in the workspace;
+// an fp32 t_io is written by stage 1 beside it, or read by a stage-2-only
+// call and rounded into it first.
+hipError_t prefill_big(const DecodeLinear& d, hipStream_t st) {
+  const int64_t ldtb = rup(d.r, 8);
+  uint16_t* tws = static_cast<uint16_t*>(d.workspace);
+  hipError_t e = hipSuccess;
+  if (d.flags != 2) {
+    if (d.t_io)
+      e = gemm_nt_big(d.x, d.ldx, d.Ut, d.ldu, d.t_io, d.ldt, true, d.flags == 1 ? nullptr : tws,
+                      ldtb, d.T, d.r, d.d_in, st);
+    else
+      e = gemm_nt_big(d.x, d.ldx, d.Ut, d.ldu, tws, ldtb, false, nullptr, 0, d.T, d.r, d.d_in, st);
+    if (e != hipSuccess || d.flags == 1) return e;
+  } else {
+    const int64_t n = d.T * d.r;
+    const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(to_bf16_kernel, dim3(blocks), dim3(256), 0, st, d.t_io, d.ldt, tws, ldtb,
+                       d.T, d.r);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return gemm_nt_big(tws, ldtb, d.Vt, d.ldv, d.y, d.ldy, false, nullptr, 0, d.T, d.d_out, d.r, st);
+}
+
+}  // namespace
+
 hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st) {
+  if (d.T >= kBigT && gemm_big_supported(d.ldx, d.ldu) && gemm_big_supported(rup(d.r, 8), d.ldv))
+    return prefill_big(d, st);
   // buffer-load offsets are 32-bit: the fused kernel needs every operand
   // (plus one tile of rows past its end) under 2 GiB
   const bool small = (d.T + kBM) * d.ldx * 2 < (1ll << 31) && (d.r + 128) * d.ldu * 2 < (1ll << 31) &&

@@ -49,6 +49,13 @@ size_t decode_group_workspace_bytes(const DecodeLinear* ds, int n);
 hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st);
 
 // bf16, T > 64: fused two-stage MFMA path (or two GEMMs).
+// C[M, N] = A[M, K] . B[N, K]^T, bf16 operands (K contiguous), fp32
+// accumulation; C bf16, or fp32 with an optional bf16 copy C2.  256-row
+// tiles on MFMA 32x32x16 (many-token shapes).
+bool gemm_big_supported(int64_t lda, int64_t ldb);
+hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                       int64_t ldc, bool c_f32, uint16_t* C2, int64_t ldc2, int64_t M,
+                       int64_t N, int64_t K, hipStream_t st);
 size_t prefill_workspace_bytes(int64_t T, int64_t r);
 hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st);
 

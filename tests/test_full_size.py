@@ -61,7 +61,7 @@ def test_decode_7b_ratio06_all_tokens(role):
 @pytest.mark.parametrize("rho", [0.4, 0.2])
 @pytest.mark.parametrize("role", ["q", "gate", "down"])
 def test_prefill_7b_16384_rows_sampled(role, rho):
-    # 8 x 2048 = 16384 rows on the fused kernel; 384 seeded rows checked
+    # 8 x 2048 = 16384 rows on the two large-tile GEMMs; 384 seeded rows checked
     d_in, d_out = SHAPES_7B[role]
     ub, vb, U, V = factors(3, role, d_in, d_out, rho)
     M = 16384

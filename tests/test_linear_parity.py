@@ -62,7 +62,25 @@ def test_bf16_prefill_path(T, shape):
     assert maxrel(to_f64(y), oracle.linear(c["x"], c["U"], c["V"])[1]) <= BF16_TOL
 
 
-@pytest.mark.parametrize("T", [5, 64, 200])
+@pytest.mark.parametrize("T", [1024, 1300])
+@pytest.mark.parametrize("shape", [(512, 300, 700), (1300, 1250, 1280), (40, 33, 72),
+                                   (2000, 257, 300)])
+def test_bf16_prefill_large_tile_path(T, shape):
+    # from 1024 rows on both stages run on the 256-row GEMM: ragged rows
+    # (1300), ragged rank and output columns against 128/256-wide tiles, a
+    # ragged last k-tile (d_in 1300, 2000; r 33, 257, 300) and K < 64 (d_in 40)
+    d_in, r, d_out = shape
+    c = make_linear(2500 + T + r, T, d_in, r, d_out, "bf16", fast=True, ld_extra=8)
+    y, _ = _run(c, T, "bf16")
+    y_t, t = _run(c, T, "bf16", with_t=True)
+    tr, yr = oracle.linear(c["x"], c["U"], c["V"])
+    assert maxrel(to_f64(y), yr) <= BF16_TOL
+    assert maxrel(to_f64(t), tr) <= 1e-5
+    # stage 2 multiplies the same bf16 t whether or not t_io is requested
+    assert np.array_equal(bits(y_t), bits(y))
+
+
+@pytest.mark.parametrize("T", [5, 64, 200, 1100])
 def test_bf16_stage_flags(T):
     c = make_linear(3000 + T, T, 640, 96, 320, "bf16", fast=True)
     d = dev()
