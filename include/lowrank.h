@@ -314,9 +314,10 @@ size_t lowrank_decode_step_workspace_bytes(const lr_layer_weights* w, const lr_d
  * after refreshing the preparation arrays.
  * The projections run on the decode path (q, k, v as one grouped launch,
  * gate and up as another), so B <= 64.
- * Errors: LR_ERR_ARG / LR_ERR_ALIGN / LR_ERR_UNSUPPORTED (head_dim not 64 or
- * 128, B > 64) / LR_ERR_WORKSPACE from host checks, LR_ERR_HIP from the
- * runtime.
+ * Errors: LR_ERR_ARG / LR_ERR_ALIGN (also: rope not 16-byte aligned) /
+ * LR_ERR_UNSUPPORTED (head_dim not 64 or 128, B > 64, a factor pitch of
+ * 2^22 elements or more) / LR_ERR_WORKSPACE from host checks, LR_ERR_HIP
+ * from the runtime.
  */
 lr_status lowrank_layer_decode_step(const lr_layer_weights* w, const lr_decode_state* s,
                                     float* h, void* workspace, size_t workspace_bytes,

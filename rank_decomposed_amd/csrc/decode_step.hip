@@ -89,168 +89,6 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
   }
 }
 
-// ---------------------------------------------------------------- reconstruction
-// rec[j, :] = buf[j, 0:r] . Vt^T for rows j < *n_valid: the fixed-size GEMM of
-// the replay stage (DeInfer/en §2.C).  The grid covers the buffer capacity;
-// tiles past n_valid exit.  With a rotary table, each head's pairs
-// (c, c + hd/2) of row j are rotated by the row's position j - seq_off[i].
-//
-// A workgroup stages 128 rows of buf (all r columns, zero past r) in LDS once
-// and sweeps every output column with 8 waves; wave (mh, nq) computes rows
-// mh*64 .. +64 and 128 columns per 512-column chunk on MFMA 16x16x32, weight
-// fragments streamed two k-steps ahead in registers.  The MFMA operands are
-// swapped (weights as A) so each lane ends with 4 consecutive output columns
-// of one row: rotary partners sit in the same lane and stores are 8 bytes.
-constexpr int rBM = 128;          // latent rows per workgroup
-constexpr int rNBW = 8;           // 16-column blocks per wave (128 columns)
-constexpr int rMBW = 4;           // 16-row blocks per wave (64 rows)
-constexpr int rChunk = 4 * rNBW * 16;  // 512 columns per sweep step
-constexpr int rRing = 1;
-
-struct ReconArgs {
-  const uint16_t* a;  // [cap, lda] compact latents
-  int64_t lda;
-  const uint16_t* b;  // Vt [N, ldb]
-  int64_t ldb;
-  uint16_t* c;        // [cap, ldc]
-  int64_t ldc;
-  int cap, N, K, k_pad;
-  const int32_t* n_valid;
-  const float* rope;  // [max_pos, hd/2, 2] or null
-  int64_t max_pos;
-  int hd;
-  const int32_t* seq_off;
-  int B;
-};
-
-// LDS: latent tile [128][k_pad + 8] bf16, then (rotary only) the tile rows'
-// cos/sin pairs as fp16x2 [128][hd/2] (|cos|, |sin| <= 1: fp16's 11-bit
-// precision is below the bf16 rounding of the output)
-size_t recon_lds_bytes(int64_t r, int64_t hd) {
-  return (size_t)rBM * (rup(r, 32) + 8) * 2 + (size_t)rBM * (hd / 2) * 4;
-}
-
-// HD: head dimension when rotary is applied (64 or 128), 0 for none; a
-// compile-time constant so the rotary pairing indexes registers statically.
-template <int HD>
-__global__ __launch_bounds__(512, 1) void recon_kernel(ReconArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int apitch = p.k_pad + 8;
-  constexpr int half = HD / 2;
-  uint16_t* as = smem;                                                  // [128][apitch]
-  uint32_t* rcs = reinterpret_cast<uint32_t*>(smem + rBM * apitch);    // [128][half] fp16 cos|sin
-  int nv = *p.n_valid;
-  nv = nv < 0 ? 0 : (nv > p.cap ? p.cap : nv);
-  const int m0 = blockIdx.x * rBM;
-  if (m0 >= nv) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int mh = wave >> 2, nq = wave & 3;
-  const int rr = lane & 15, kq = (lane >> 4) * 8;
-
-  // stage the latent tile, zero past K
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, view_bytes(p.cap, p.K, p.lda));
-  const int kch = p.k_pad / 8;
-  for (int e = threadIdx.x; e < rBM * kch; e += 512) {
-    const int row = e / kch, k = (e % kch) * 8;
-    u32x4 v = bload(ra, (uint32_t)(((int64_t)(m0 + row) * p.lda + k) * 2));
-    if (k + 8 > p.K) v = mask_tail(v, k, p.K);
-    *reinterpret_cast<u32x4*>(as + row * apitch + k) = v;
-  }
-  if (HD > 0) {
-    for (int e = threadIdx.x; e < rBM * half; e += 512) {
-      const int row = e / half, fi = e % half;
-      const int j = m0 + row;
-      int lo = 0, hi = p.B;  // i with seq_off[i] <= j < seq_off[i + 1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.seq_off[mid] <= j) lo = mid; else hi = mid;
-      }
-      int pos = j - p.seq_off[lo];
-      pos = pos < 0 ? 0 : (pos >= p.max_pos ? (int)p.max_pos - 1 : pos);
-      const float cs = p.rope[((int64_t)pos * half + fi) * 2];
-      const float sn = p.rope[((int64_t)pos * half + fi) * 2 + 1];
-      const _Float16 hc = (_Float16)cs, hs = (_Float16)sn;
-      rcs[row * half + fi] = (uint32_t)__builtin_bit_cast(uint16_t, hc) |
-                             ((uint32_t)__builtin_bit_cast(uint16_t, hs) << 16);
-    }
-  }
-  __syncthreads();
-
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b, view_bytes(p.N, p.K, p.ldb));
-  const int ks = p.k_pad / 32;
-  const bool tail = (p.K % 32) != 0;
-  const int kf = tail ? ks - 1 : ks;
-  for (int c0 = 0; c0 < p.N; c0 += rChunk) {
-    const int n0 = c0 + nq * rNBW * 16;
-    if (n0 >= p.N) continue;
-    f32x4 acc[rNBW][rMBW];  // [column block][row block], C^T fragments
-#pragma unroll
-    for (int j = 0; j < rNBW; ++j)
-#pragma unroll
-      for (int i = 0; i < rMBW; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 bq[rRing][rNBW];
-#pragma unroll
-    for (int q = 0; q < rRing; ++q) frag_load<rNBW>(bq[q], rb, p.ldb, n0, q * 32, lane);
-    int s = 0;
-    for (; s + rRing <= kf; s += rRing) {
-#pragma unroll
-      for (int q = 0; q < rRing; ++q) {
-        u32x4 a[rMBW];
-#pragma unroll
-        for (int i = 0; i < rMBW; ++i)
-          a[i] = lds16(as + (mh * 64 + i * 16 + rr) * apitch + (s + q) * 32 + kq);
-        frag_mma<rNBW, rMBW>(acc, bq[q], a);
-        frag_load<rNBW>(bq[q], rb, p.ldb, n0, (s + q + rRing) * 32, lane);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < rRing; ++q) {
-      if (s + q < kf || (tail && s + q == kf)) {
-        if (s + q == kf) frag_mask<rNBW>(bq[q], kf * 32, p.K, lane);
-        u32x4 a[rMBW];
-#pragma unroll
-        for (int i = 0; i < rMBW; ++i)
-          a[i] = lds16(as + (mh * 64 + i * 16 + rr) * apitch + (s + q) * 32 + kq);
-        frag_mma<rNBW, rMBW>(acc, bq[q], a);
-      }
-    }
-    // lane holds rows (i*16 + rr) and columns n0 + j*16 + 4*(lane>>4) + v
-#pragma unroll
-    for (int i = 0; i < rMBW; ++i) {
-      const int lrow = mh * 64 + i * 16 + rr;
-      const int grow = m0 + lrow;
-      if (HD > 0) {
-        const uint32_t* tr = rcs + lrow * half;
-        constexpr int hb = half / 16;  // column blocks per half head
-#pragma unroll
-        for (int j = 0; j < rNBW; ++j) {
-          const int hc = (j * 16) % (HD > 0 ? HD : 1);  // block start inside its head
-          if (hc >= half || j + hb >= rNBW) continue;  // rotated with its partner
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const uint32_t w = tr[hc + 4 * (lane >> 4) + v];   // frequency index
-            const float cs = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-            const float sn = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-            const float a0 = acc[j][i][v], b0 = acc[j + hb][i][v];
-            acc[j][i][v] = a0 * cs - b0 * sn;
-            acc[j + hb][i][v] = b0 * cs + a0 * sn;
-          }
-        }
-      }
-      if (grow < nv) {
-#pragma unroll
-        for (int j = 0; j < rNBW; ++j) {
-          const int col = n0 + j * 16 + 4 * (lane >> 4);
-          if (col < p.N) {
-            const u32x2 w{pack_bf2(acc[j][i][0], acc[j][i][1]), pack_bf2(acc[j][i][2], acc[j][i][3])};
-            *reinterpret_cast<u32x2*>(p.c + (int64_t)grow * p.ldc + col) = w;
-          }
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- attention
 // Partial softmax attention of one query (sequence i, head h) over one chunk
 // of its packed rows [seq_off[i] + c*256, ...).  Output per chunk: running max
@@ -447,9 +285,13 @@ lr_status check_step(const lr_layer_weights* w, const lr_decode_state* s, const 
       return LR_ERR_UNSUPPORTED;
   }
   if (s->pool_ld < w->r[1] || s->pool_ld < w->r[2]) return LR_ERR_ARG;
-  // the reconstruction keeps a 128-row latent tile in LDS
-  if (recon_lds_bytes(w->r[1], w->head_dim) > 163840 ||
-      recon_lds_bytes(w->r[2], w->head_dim) > 163840)
+  // the reconstruction's rotary epilogue copies (cos, sin) rows in 16-byte
+  // chunks, addressed with 32-bit offsets
+  if (!al16(w->rope)) return LR_ERR_ALIGN;
+  if (w->rope_max_pos * w->head_dim * 4 >= (int64_t(1) << 31)) return LR_ERR_UNSUPPORTED;
+  // the reconstruction GEMM addresses a 256-row tile with 32-bit offsets
+  if (!gemm_big_supported(rup(w->r[1], 8), w->ldv[1]) ||
+      !gemm_big_supported(rup(w->r[2], 8), w->ldv[2]))
     return LR_ERR_UNSUPPORTED;
   if (!al16(s->k_pool) || !al16(s->v_pool) || s->pool_ld % 8) return LR_ERR_ALIGN;
   if (w->d_model % 8 || w->d_ffn % 8) return LR_ERR_ALIGN;
@@ -557,43 +399,15 @@ extern "C" lr_status lowrank_layer_decode_step(const lr_layer_weights* w,
                         w->r[1], kbuf, L.rk_ld, st));
   LR_CHECK(remap_gather(2, s->v_pool, s->pool_rows, s->pool_ld, s->remap, s->cap, s->n_valid,
                         w->r[2], vbuf, L.rv_ld, st));
-  ReconArgs ra{};
-  ra.cap = (int)s->cap;
-  ra.N = (int)L.dkv;
-  ra.n_valid = s->n_valid;
-  ra.max_pos = w->rope_max_pos;
-  ra.hd = (int)w->head_dim;
-  ra.seq_off = s->seq_off;
-  ra.B = B;
-  const dim3 rgrid((unsigned)((s->cap + rBM - 1) / rBM));
-  for (int kv = 0; kv < 2; ++kv) {
-    const int64_t r = w->r[1 + kv];
-    ra.a = kv ? vbuf : kbuf;
-    ra.lda = kv ? L.rv_ld : L.rk_ld;
-    ra.b = static_cast<const uint16_t*>(w->Vt[1 + kv]);
-    ra.ldb = w->ldv[1 + kv];
-    ra.c = kv ? vrec : krec;
-    ra.ldc = L.dkv;
-    ra.K = (int)r;
-    ra.k_pad = (int)rup(r, 32);
-    ra.rope = kv ? nullptr : w->rope;
-    const size_t lds = recon_lds_bytes(r, kv ? 0 : w->head_dim);
-    static std::once_flag lds_once;  // raise the dynamic-LDS limit once per process
-    std::call_once(lds_once, [] {
-      (void)hipFuncSetAttribute((const void*)recon_kernel<0>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-      (void)hipFuncSetAttribute((const void*)recon_kernel<64>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-      (void)hipFuncSetAttribute((const void*)recon_kernel<128>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-    });
-    if (kv)
-      hipLaunchKernelGGL(recon_kernel<0>, rgrid, dim3(512), lds, st, ra);
-    else if (w->head_dim == 128)
-      hipLaunchKernelGGL(recon_kernel<128>, rgrid, dim3(512), lds, st, ra);
-    else
-      hipLaunchKernelGGL(recon_kernel<64>, rgrid, dim3(512), lds, st, ra);
-    LR_CHECK(hipGetLastError());
+  // rec[j, :] = buf[j, 0:r] . Vt^T for the live rows j < *n_valid: the
+  // fixed-size GEMM of the replay stage (grid from the capacity), K rows
+  // rotated by their positions in the epilogue.
+  {
+    const BigRope rope{w->rope, w->rope_max_pos, s->seq_off, (int)B, (int)w->head_dim};
+    LR_CHECK(gemm_nt_big_rows(kbuf, L.rk_ld, w->Vt[1], w->ldv[1], krec, L.dkv, s->cap, s->n_valid,
+                              L.dkv, w->r[1], &rope, st));
+    LR_CHECK(gemm_nt_big_rows(vbuf, L.rv_ld, w->Vt[2], w->ldv[2], vrec, L.dkv, s->cap, s->n_valid,
+                              L.dkv, w->r[2], nullptr, st));
   }
   const dim3 agrid((unsigned)L.nch, (unsigned)w->n_heads, (unsigned)B);
   if (w->head_dim == 128) {

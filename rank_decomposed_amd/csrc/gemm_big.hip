@@ -3,18 +3,21 @@
 // Used for the many-token (prefill) decomposed linear: both stages, x U_r and
 // t V_r, have this form with the factors stored transposed.
 //
-// Tile 256 x BN x 64 (BN = 256 or 128), one workgroup of 4 waves, each wave
+// Tile 256 x BN x BK (BN = 256 or 128), one workgroup of 4 waves, each wave
 // 128 x BN/2.  Operand tiles move global -> LDS with direct-to-LDS buffer
-// loads (no registers in between), double-buffered: the loads of k-tile t+1
-// are in flight while tile t multiplies.  LDS rows are 128 B with the 16-B
-// chunk index XOR-swizzled by (row / 2) % 8, so the fragment reads (32 rows
-// at one chunk) hit distinct banks.  The MFMA takes the B fragment as its
-// first operand, so each lane ends with 4 consecutive output columns of one
-// row: 8- or 16-byte stores.  Tiles go to the 8 XCDs in contiguous runs
-// (workgroups are dealt to XCDs round robin), so an XCD's tiles share A rows
-// in its L2.  The last, partial k-tile is masked in registers; rows past M or
-// N and k-chunks past K read zero from outside the buffers.
+// loads (no registers in between) through a ring of NS stages: the loads of
+// the next NS - 1 k-tiles are in flight while one multiplies.  LDS rows are
+// BK * 2 bytes with the 16-byte chunk index XOR-swizzled by row, so the
+// fragment reads (32 rows at one chunk) spread over the banks.  The MFMA
+// takes the B fragment as its first operand, so each lane ends with 4
+// consecutive output columns of one row; bf16 results are staged through LDS
+// and written as whole 128-byte lines.  Tiles go to the 8 XCDs in contiguous
+// runs (workgroups are dealt to XCDs round robin), so an XCD's tiles share A
+// rows in its L2.  Rows past M or N and k-chunks past K read zero from
+// outside the buffers; the padding in the last partial chunk is zeroed in
+// LDS.
 #include <mutex>
+#include <type_traits>
 
 #include "lr_common.h"
 #include "lr_kernels.h"
@@ -23,8 +26,7 @@ namespace lr {
 
 namespace {
 
-constexpr int gBM = 256, gBK = 64;
-constexpr int gTileA = gBM * gBK * 2;  // bytes of one A tile
+constexpr int gBM = 256;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -32,7 +34,13 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// 16-byte chunk slot of (row, chunk) in a staged tile with BK * 2-byte rows:
+// 16 consecutive rows at one chunk land in 16 distinct slots of a 256-byte
+// bank window.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return BK == 64 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 2) & 3);
+}
 
 template <int VM>
 __device__ __forceinline__ void wait_vm() {
@@ -46,19 +54,21 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Direct-to-LDS loads of a ROWS x 64 operand tile: instruction i moves rows
-// 8i .. 8i+7 (lane l: row 8i + l/8, LDS slot l%8, global chunk swizzled), and
-// wave w issues instructions w, w + 4, ...; chunks past the K range (kt
-// elements left) go outside the buffer and read zero.
-template <int ROWS>
+// Direct-to-LDS loads of a ROWS x BK operand tile: instruction i moves the
+// 1 KB of rows RPI*i .. RPI*i + RPI-1 (lane l: row RPI*i + l/CPR, LDS slot
+// l%CPR, global chunk swizzled), and wave w issues instructions w, w + 4, ...;
+// chunks past the K range (kt elements left) go outside the buffer and read
+// zero.
+template <int ROWS, int BK>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kt,
                                           uint8_t* lds, int wave, int lane) {
-  const int rr = lane >> 3, slot = lane & 7;
+  constexpr int CPR = BK / 8, RPI = 64 / CPR;
+  const int rr = lane / CPR, slot = lane % CPR;
 #pragma unroll
-  for (int i = 0; i < ROWS / 32; ++i) {
+  for (int i = 0; i < ROWS / RPI / 4; ++i) {
     const int inst = wave + 4 * i;
-    const int row = inst * 8 + rr;
-    const int chunk = swz(row, slot);
+    const int row = inst * RPI + rr;
+    const int chunk = swz<BK>(row, slot);
     const int off =
         chunk * 8 < kt ? (int)(((int64_t)row * ld + k0 + chunk * 8) * 2) : (int)0x80000000;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -66,46 +76,75 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld,
   }
 }
 
-template <int NBW, bool MASK>
+template <int NBW, int BK>
 __device__ __forceinline__ void load_frags(u32x4 (&af)[4], u32x4 (&bfr)[NBW], const uint8_t* ta,
-                                           const uint8_t* tb, int wm, int wn, int lane, int ks,
-                                           int kt) {
+                                           const uint8_t* tb, int wm, int wn, int lane, int ks) {
   const int chunk = 2 * ks + (lane >> 5);
   const int r32 = lane & 31;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = wm + i * 32 + r32;
-    af[i] = *reinterpret_cast<const u32x4*>(ta + row * 128 + swz(row, chunk) * 16);
+    af[i] = *reinterpret_cast<const u32x4*>(ta + row * (BK * 2) + swz<BK>(row, chunk) * 16);
   }
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
     const int row = wn + i * 32 + r32;
-    bfr[i] = *reinterpret_cast<const u32x4*>(tb + row * 128 + swz(row, chunk) * 16);
-  }
-  if (MASK) {
-    const int kk = chunk * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = mask_tail_nb(af[i], kk, kt);
-#pragma unroll
-    for (int i = 0; i < NBW; ++i) bfr[i] = mask_tail_nb(bfr[i], kk, kt);
+    bfr[i] = *reinterpret_cast<const u32x4*>(tb + row * (BK * 2) + swz<BK>(row, chunk) * 16);
   }
 }
 
-// One 64-deep k-tile from LDS: 4 steps of 16 (fragments of step ks + 1 read
-// while step ks multiplies).
-template <int NBW, bool MASK>
-__device__ __forceinline__ void tile_mma(f32x16 (&acc)[NBW][4], const uint8_t* ta,
-                                         const uint8_t* tb, int wm, int wn, int lane, int kt) {
-  u32x4 af[2][4], bfr[2][NBW];
-  load_frags<NBW, MASK>(af[0], bfr[0], ta, tb, wm, wn, lane, 0, kt);
+// Zero the elements k >= kt of the 16-byte chunk that holds k = kt in every
+// row of a staged ROWS x BK tile (kt % 8 != 0).  Chunks wholly past kt were
+// loaded as zeros; this one holds the padding after the last column, which
+// the MFMA must not see (it may hold anything, NaN included).
+template <int ROWS, int BK>
+__device__ __forceinline__ void zero_k_tail(uint8_t* lds, int kt) {
+  const int chunk = kt >> 3;
+  for (int row = threadIdx.x; row < ROWS; row += 256) {
+    u32x4* c = reinterpret_cast<u32x4*>(lds + row * (BK * 2) + swz<BK>(row, chunk) * 16);
+    *c = mask_tail_nb(*c, chunk * 8, kt);
+  }
+}
+
+// bf16 epilogue through LDS: the wave writes its 128 x BN/2 result into its
+// own LDS region (16-byte chunks XOR-swizzled by row), then reads it back
+// row-contiguous, so each global store instruction writes whole 128-byte
+// lines instead of 16 bytes of 32 different rows.  The operand tiles are
+// dead by then (the caller has passed a barrier after the last product).
+template <int BN>
+__device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][4], uint16_t* C,
+                                             int64_t ldc, int mw, int nw, int M, int N,
+                                             uint8_t* smem, int wave, int lane) {
+  constexpr int NBW = BN / 64, WN = BN / 2, RB = WN * 2, CPR = WN / 8, RPI = 64 / CPR;
+  uint8_t* ep = smem + wave * (128 * RB);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (ks + 1 < 4)
-      load_frags<NBW, MASK>(af[(ks + 1) & 1], bfr[(ks + 1) & 1], ta, tb, wm, wn, lane, ks + 1, kt);
+  for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int i = 0; i < NBW; ++i)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[ks & 1][i], af[ks & 1][j], acc[i][j]);
+      for (int q = 0; q < 4; ++q) {
+        const int rl = 32 * j + (lane & 31), cl = 32 * i + 8 * q + 4 * (lane >> 5);
+        const int ch = (cl >> 3) ^ (rl & (CPR - 1));
+        *reinterpret_cast<u32x2*>(ep + rl * RB + ch * 16 + ((cl >> 2) & 1) * 8) =
+            u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                  pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+      }
+  // the reads below take other lanes' writes: LDS runs one wave's accesses in order
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("" ::: "memory");
+  const int chl = lane % CPR, n = nw + chl * 8;
+#pragma unroll 4
+  for (int r0 = 0; r0 < 128; r0 += RPI) {
+    const int rl = r0 + lane / CPR, m = mw + rl;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ep + rl * RB + ((chl ^ (rl & (CPR - 1))) * 16));
+    if (m >= M) continue;
+    uint16_t* c = C + (int64_t)m * ldc + n;
+    if (n + 7 < N) {
+      *reinterpret_cast<u32x4*>(c) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 8 && n + e < N; ++e) c[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
   }
 }
 
@@ -119,27 +158,58 @@ struct BigArgs {
   uint16_t* c2;   // optional bf16 copy of an fp32 output [M, ldc2], 8-byte aligned rows
   int64_t ldc2;
   int M, N, K;
-  int vec;        // C rows allow 4-element vector stores (else element stores)
+  int vec;        // C rows allow 16-byte (2) / 8-byte (1) stores, else element stores
+  const int32_t* m_valid;  // optional live row count on the device (rows past it are skipped)
+  const float* rope;       // rotary table [max_pos][hd/2] of (cos, sin), or null
+  int64_t max_pos;
+  const int32_t* seq_off;  // [nseq + 1] packed-row offsets: row m sits at position m - seq_off[i]
+  int nseq;
 };
 
-template <int BN, bool OUT_F32>
+// HD > 0: rotate each head's column pairs (c, c + HD/2) of row m by the
+// angles of the row's position (a wave's 128 columns hold whole heads).
+template <int BN, int BK>
+constexpr int big_stage_bytes() { return (gBM + BN) * BK * 2; }
+
+// LDS of one launch: the operand ring, reused by the epilogue (bf16 result
+// staging 256 * BN * 2 bytes; rotary tables 256 rows * HD * 4 bytes), then
+// (rotary) 2 KB of sequence offsets and row positions.
+template <int BN, int BK, int NS, int HD>
+constexpr int big_lds_bytes() {
+  constexpr int ring = NS * big_stage_bytes<BN, BK>();
+  constexpr int ep = gBM * BN * 2 > gBM * HD * 4 ? gBM * BN * 2 : gBM * HD * 4;
+  return (ring > ep ? ring : ep) + (HD > 0 ? 2048 : 0);
+}
+
+template <int BN, int BK, int NS, bool OUT_F32, int HD>
 __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
+  static_assert(HD == 0 || (BN == 256 && !OUT_F32 && (HD == 64 || HD == 128)), "rotary tiles");
+  static_assert((BK == 32 || BK == 64) && NS >= 2, "pipeline shape");
   constexpr int NBW = BN / 64;              // 32-column blocks per wave
-  constexpr int kTileB = BN * gBK * 2;
-  constexpr int kStage = gTileA + kTileB;
+  constexpr int kTileA = gBM * BK * 2;
+  constexpr int kStage = big_stage_bytes<BN, BK>();
+  constexpr int IPW = kStage / 1024 / 4;    // load instructions per wave per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ntn = (p.N + BN - 1) / BN, ntiles = ntn * ((p.M + gBM - 1) / gBM);
+  int M = p.M;
+  if (p.m_valid) {  // the grid covers the capacity; spread the live tiles over the XCDs
+    const int nv = *p.m_valid;
+    M = nv < 0 ? 0 : (nv > p.M ? p.M : nv);
+  }
+  const int ntn = (p.N + BN - 1) / BN, ntiles = ntn * ((M + gBM - 1) / gBM);
   const int per_xcd = (ntiles + 7) / 8;
   const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (tile >= ntiles) return;
+  if ((int)blockIdx.x / 8 >= per_xcd || tile >= ntiles) return;
   const int m0 = (tile / ntn) * gBM, n0 = (tile % ntn) * BN;
   const __amdgpu_buffer_rsrc_t ra =
-      make_rsrc(p.a + (int64_t)m0 * p.lda, view_bytes(min(p.M - m0, gBM), p.K, p.lda));
+      make_rsrc(p.a + (int64_t)m0 * p.lda, view_bytes(min(M - m0, gBM), p.K, p.lda));
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(p.b + (int64_t)n0 * p.ldb, view_bytes(min(p.N - n0, BN), p.K, p.ldb));
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * (BN / 2);
-  const int nk = (p.K + gBK - 1) / gBK;
+  const int nk = (p.K + BK - 1) / BK;
+
+  int so = 0;  // rotary: this thread's entry of the sequence offsets, staged after the loop
+  if (HD > 0 && (int)threadIdx.x <= p.nseq) so = p.seq_off[threadIdx.x];
 
   f32x16 acc[NBW][4];  // [n block][m block]; lane: one m row, 4 consecutive n per 4 regs
 #pragma unroll
@@ -147,36 +217,139 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  load_tile<gBM>(ra, p.lda, 0, p.K, smem, wave, lane);
-  load_tile<BN>(rb, p.ldb, 0, p.K, smem + gTileA, wave, lane);
-  for (int t = 0; t + 1 < nk; ++t) {
-    uint8_t* cur = smem + (t & 1) * kStage;
-    uint8_t* nxt = smem + ((t + 1) & 1) * kStage;
-    load_tile<gBM>(ra, p.lda, (t + 1) * gBK, p.K - (t + 1) * gBK, nxt, wave, lane);
-    load_tile<BN>(rb, p.ldb, (t + 1) * gBK, p.K - (t + 1) * gBK, nxt + gTileA, wave, lane);
-    wait_vm<(gBM + BN) / 32>();  // this tile's loads are done; the next tile's stay in flight
+  auto load_stage = [&](int t) {
+    uint8_t* st = smem + (t % NS) * kStage;
+    load_tile<gBM, BK>(ra, p.lda, t * BK, p.K - t * BK, st, wave, lane);
+    load_tile<BN, BK>(rb, p.ldb, t * BK, p.K - t * BK, st + kTileA, wave, lane);
+  };
+  // k-tile t's loads are done once at most the stages issued after it are
+  // pending (`younger` of them; vector-memory loads complete in order)
+  auto wait_stage = [&](int younger) {
+    if (younger >= NS - 1) wait_vm<(NS - 1) * IPW>();
+    else if (NS > 3 && younger == 2) wait_vm<(NS > 3 ? 2 : 0) * IPW>();
+    else if (NS > 2 && younger == 1) wait_vm<(NS > 2 ? 1 : 0) * IPW>();
+    else wait_vm<0>();
+  };
+  // after the wait: make every wave's part of stage t visible, zeroing the
+  // padding of a partial last k-tile first
+  auto open_stage = [&](int t) {
     lds_barrier();
-    tile_mma<NBW, false>(acc, cur, cur + gTileA, wm, wn, lane, gBK);
-    lds_barrier();
-  }
-  wait_vm<0>();
+    const int kt = p.K - t * BK;
+    if (kt < BK && (kt & 7)) {
+      uint8_t* st = smem + (t % NS) * kStage;
+      zero_k_tail<gBM, BK>(st, kt);
+      zero_k_tail<BN, BK>(st + kTileA, kt);
+      lds_barrier();
+    }
+  };
+  constexpr int KS = BK / 16;
+  u32x4 af[2][4], bfr[2][NBW];
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nk) load_stage(t);
+  wait_stage(min(NS - 2, nk - 1));
+  open_stage(0);
+  load_frags<NBW, BK>(af[0], bfr[0], smem, smem + kTileA, wm, wn, lane, 0);
+  // One barrier per k-tile: it sits in the last k-step of tile t, after the
+  // wait for tile t + 1, so the first fragments of t + 1 are read while the
+  // last products of t run; it also orders every wave's reads of tile t - 1
+  // before the loads that reuse its stage at the start of iteration t.  The
+  // last tile is peeled so that no branch skips the barrier: the compiler's
+  // LDS wait counts then stay exact (after a merge it would wait for the
+  // next tile's fragments before the current products).
+  auto k_tile = [&](int t, auto has_next) {
+    if (t + NS - 1 < nk) load_stage(t + NS - 1);
+    const uint8_t* cur = smem + (t % NS) * kStage;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int nb = (ks + 1) & 1;
+      if (ks + 1 < KS) {
+        load_frags<NBW, BK>(af[nb], bfr[nb], cur, cur + kTileA, wm, wn, lane, ks + 1);
+      } else if constexpr (decltype(has_next)::value) {
+        wait_stage(min(NS - 2, nk - 2 - t));
+        open_stage(t + 1);
+        const uint8_t* nxt = smem + ((t + 1) % NS) * kStage;
+        load_frags<NBW, BK>(af[nb], bfr[nb], nxt, nxt + kTileA, wm, wn, lane, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma32(bfr[ks & 1][i], af[ks & 1][j], acc[i][j]);
+    }
+  };
+  for (int t = 0; t + 1 < nk; ++t) k_tile(t, std::true_type{});
+  k_tile(nk - 1, std::false_type{});
   lds_barrier();
-  {
-    const uint8_t* cur = smem + ((nk - 1) & 1) * kStage;
-    const int kt = p.K - (nk - 1) * gBK;
-    if (kt < gBK)
-      tile_mma<NBW, true>(acc, cur, cur + gTileA, wm, wn, lane, kt);
-    else
-      tile_mma<NBW, false>(acc, cur, cur + gTileA, wm, wn, lane, gBK);
-  }
+  // (the barrier above: operand tiles dead, the epilogue may reuse the LDS)
 
   // acc[i][j] reg r -> n = wn + 32i + 8(r/4) + 4(lane/32) + r%4, m = wm + 32j + lane%32
+  if constexpr (HD > 0) {
+    // positions of the tile's rows from the sequence offsets (in LDS past
+    // the operand buffers), then the rows' (cos, sin) tables copied straight
+    // into LDS: row r's 16-byte chunk c at slot c ^ (r % CH)
+    constexpr int CH = HD / 4, RPI = 64 / CH, hb = HD / 64;  // hb: partner block, + HD/2
+    int* aux = reinterpret_cast<int*>(smem + big_lds_bytes<BN, BK, NS, HD>() - 2048);
+    if ((int)threadIdx.x <= p.nseq) aux[threadIdx.x] = so;
+    lds_barrier();
+    {
+      const int m = min(m0 + (int)threadIdx.x, M - 1);
+      int lo = 0, hi = p.nseq;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (aux[mid] <= m) lo = mid; else hi = mid;
+      }
+      const int pos = m - aux[lo];
+      aux[256 + threadIdx.x] = pos < 0 ? 0 : (pos >= p.max_pos ? (int)p.max_pos - 1 : pos);
+    }
+    lds_barrier();
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.rope, (uint64_t)p.max_pos * HD * 4);
+    for (int inst = wave; inst < gBM / RPI; inst += 4) {
+      const int row = inst * RPI + lane / CH, c = (lane % CH) ^ (row & (CH - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rt, (__attribute__((address_space(3))) void*)(smem + inst * 1024), 16,
+          (aux[256 + row] * HD + c * 4) * 4, 0, 0, 0);
+    }
+    wait_vm<0>();
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rl = wm + 32 * j + (lane & 31);
+      const uint8_t* tr = smem + rl * (HD * 4);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        if ((32 * i) % HD >= HD / 2) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int fi = (32 * i) % HD + 8 * q + 4 * (lane >> 5);  // 4 frequencies from fi
+          const f32x4 cs01 =
+              *reinterpret_cast<const f32x4*>(tr + ((fi / 2) ^ (rl & (CH - 1))) * 16);
+          const f32x4 cs23 =
+              *reinterpret_cast<const f32x4*>(tr + ((fi / 2 + 1) ^ (rl & (CH - 1))) * 16);
+          const float c[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
+          const float sn[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a0 = acc[i][j][4 * q + e], b0 = acc[i + hb][j][4 * q + e];
+            acc[i][j][4 * q + e] = a0 * c[e] - b0 * sn[e];
+            acc[i + hb][j][4 * q + e] = b0 * c[e] + a0 * sn[e];
+          }
+        }
+      }
+    }
+    lds_barrier();  // tables dead before the epilogue reuses the LDS
+  }
+  if (!OUT_F32 && p.vec == 2) {
+    store_staged<BN>(acc, static_cast<uint16_t*>(p.c), p.ldc, m0 + wm, n0 + wn, M, p.N, smem,
+                     wave, lane);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NBW; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = m0 + wm + 32 * j + (lane & 31);
-      if (m >= p.M) continue;
+      if (m >= M) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + wn + 32 * i + 8 * q + 4 * (lane >> 5);
@@ -185,7 +358,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
         if (OUT_F32) {
           float* c = static_cast<float*>(p.c) + (int64_t)m * p.ldc + n;
           uint16_t* c2 = p.c2 ? p.c2 + (int64_t)m * p.ldc2 + n : nullptr;
-          if (p.vec && n + 3 < p.N) {
+          if (p.vec == 2 && n + 3 < p.N) {
             *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
             if (c2) *reinterpret_cast<u32x2*>(c2) = u32x2{pack_bf2(v0, v1), pack_bf2(v2, v3)};
           } else {
@@ -197,7 +370,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
           }
         } else {
           uint16_t* c = static_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + n;
-          if (p.vec && n + 3 < p.N) {
+          if (p.vec >= 1 && n + 3 < p.N) {
             *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf2(v0, v1), pack_bf2(v2, v3)};
           } else {
             const float v[4] = {v0, v1, v2, v3};
@@ -208,18 +381,30 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
     }
 }
 
-template <int BN, bool OUT_F32>
+// k-pipeline of every launch: 32-deep k-tiles in a ring of 3 stages
+constexpr int gBK = 32, gNS = 3;
+
+template <int BN, bool OUT_F32, int HD = 0>
 hipError_t launch_big(const BigArgs& a, hipStream_t st) {
-  constexpr size_t lds = 2 * (size_t)(gTileA + BN * gBK * 2);
+  constexpr int lds = big_lds_bytes<BN, gBK, gNS, HD>();
+  static_assert(lds <= 160 * 1024, "LDS");
   static std::once_flag once;
   std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<BN, OUT_F32>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + gBM - 1) / gBM);
-  hipLaunchKernelGGL((gemm_big_kernel<BN, OUT_F32>), dim3((unsigned)((tiles + 7) / 8 * 8)),
-                     dim3(256), lds, st, a);
+  hipLaunchKernelGGL((gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD>),
+                     dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), lds, st, a);
   return hipGetLastError();
+}
+
+// 2: rows of C take 16-byte stores, 1: 8-byte stores (4 elements), 0: neither.
+int store_width(const void* C, int64_t ldc, int esize) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(C);
+  if (a % 16 == 0 && (ldc * esize) % 16 == 0) return 2;
+  return a % (4 * esize) == 0 && (ldc * esize) % (4 * esize) == 0 ? 1 : 0;
 }
 
 // Fraction of the launch's CU-rounds doing useful columns, for a tile width.
@@ -232,20 +417,38 @@ double tile_efficiency(int M, int N, int BN) {
 }  // namespace
 
 bool gemm_big_supported(int64_t lda, int64_t ldb) {
-  // 32-bit offsets within a 256-row tile
-  return lda < (int64_t(1) << 22) && ldb < (int64_t(1) << 22);
+  // 32-bit offsets within a 256-row tile; rows start on 16-byte chunks
+  return lda < (int64_t(1) << 22) && ldb < (int64_t(1) << 22) && lda % 8 == 0 && ldb % 8 == 0;
 }
 
 hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                        int64_t ldc, bool c_f32, uint16_t* C2, int64_t ldc2, int64_t M,
                        int64_t N, int64_t K, hipStream_t st) {
-  const uintptr_t cal = c_f32 ? 16 : 8;
   BigArgs a{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
-            C2, ldc2, (int)M, (int)N, (int)K,
-            (reinterpret_cast<uintptr_t>(C) % cal == 0 && ldc % 4 == 0) ? 1 : 0};
+            C2, ldc2, (int)M, (int)N, (int)K, store_width(C, ldc, c_f32 ? 4 : 2),
+            nullptr, nullptr, 0, nullptr, 0};
   const bool narrow = tile_efficiency((int)M, (int)N, 128) > tile_efficiency((int)M, (int)N, 256) + 0.05;
   if (c_f32) return narrow ? launch_big<128, true>(a, st) : launch_big<256, true>(a, st);
   return narrow ? launch_big<128, false>(a, st) : launch_big<256, false>(a, st);
+}
+
+hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t ldb, uint16_t* C,
+                            int64_t ldc, int64_t M, const int32_t* m_valid, int64_t N, int64_t K,
+                            const BigRope* rope, hipStream_t st) {
+  BigArgs a{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
+            nullptr, 0, (int)M, (int)N, (int)K, store_width(C, ldc, 2), m_valid, nullptr, 0,
+            nullptr, 0};
+  if (!rope) return launch_big<256, false>(a, st);
+  if (rope->nseq < 1 || rope->nseq > 255 || rope->max_pos < 1 ||
+      rope->max_pos * rope->hd * 4 >= (int64_t(1) << 31) || N % rope->hd)
+    return hipErrorInvalidValue;
+  a.rope = rope->table;
+  a.max_pos = rope->max_pos;
+  a.seq_off = rope->seq_off;
+  a.nseq = rope->nseq;
+  if (rope->hd == 128) return launch_big<256, false, 128>(a, st);
+  if (rope->hd == 64) return launch_big<256, false, 64>(a, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace lr

@@ -56,6 +56,22 @@ bool gemm_big_supported(int64_t lda, int64_t ldb);
 hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                        int64_t ldc, bool c_f32, uint16_t* C2, int64_t ldc2, int64_t M,
                        int64_t N, int64_t K, hipStream_t st);
+// Rotary epilogue of gemm_nt_big_rows: rows are packed sequences (row m of
+// sequence i sits at position m - seq_off[i], 1 <= nseq <= 255); table
+// [max_pos][hd/2] holds (cos, sin) pairs, 16-byte aligned, under 2 GiB; N a
+// multiple of hd (64 or 128).
+struct BigRope {
+  const float* table;
+  int64_t max_pos;
+  const int32_t* seq_off;  // [nseq + 1]
+  int nseq;
+  int hd;
+};
+// C[m, :] = A[m, :] . B^T (bf16 out) for the rows m < *m_valid (read on the
+// device, clamped to M; the grid covers M), optionally rotated per head.
+hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t ldb, uint16_t* C,
+                            int64_t ldc, int64_t M, const int32_t* m_valid, int64_t N, int64_t K,
+                            const BigRope* rope, hipStream_t st);
 size_t prefill_workspace_bytes(int64_t T, int64_t r);
 hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st);
 

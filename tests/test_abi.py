@@ -202,6 +202,7 @@ def _valid_step_structs():
     ("head_dim", 96, _lib.LR_ERR_UNSUPPORTED),
     ("pool_ld", 409, _lib.LR_ERR_ALIGN),
     ("n_heads", 33, _lib.LR_ERR_ARG),             # not a multiple of n_kv_heads
+    ("rope", A16 + 8, _lib.LR_ERR_ALIGN),         # rotary epilogue reads 16-byte quads
 ])
 def test_decode_step_host_checks(field, value, status):
     w, s = _valid_step_structs()
