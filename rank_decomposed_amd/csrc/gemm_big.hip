@@ -56,17 +56,18 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Direct-to-LDS loads of a ROWS x BK operand tile: instruction i moves the
 // 1 KB of rows RPI*i .. RPI*i + RPI-1 (lane l: row RPI*i + l/CPR, LDS slot
-// l%CPR, global chunk swizzled), and wave w issues instructions w, w + 4, ...;
-// chunks past the K range (kt elements left) go outside the buffer and read
-// zero.
-template <int ROWS, int BK>
+// l%CPR, global chunk swizzled), and wave w of NW issues instructions w,
+// w + NW, ...; chunks past the K range (kt elements left) go outside the
+// buffer and read zero.
+template <int ROWS, int BK, int NW>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kt,
                                           uint8_t* lds, int wave, int lane) {
   constexpr int CPR = BK / 8, RPI = 64 / CPR;
+  static_assert(ROWS % (RPI * NW) == 0, "whole instructions per wave");
   const int rr = lane / CPR, slot = lane % CPR;
 #pragma unroll
-  for (int i = 0; i < ROWS / RPI / 4; ++i) {
-    const int inst = wave + 4 * i;
+  for (int i = 0; i < ROWS / RPI / NW; ++i) {
+    const int inst = wave + NW * i;
     const int row = inst * RPI + rr;
     const int chunk = swz<BK>(row, slot);
     const int off =
@@ -76,13 +77,13 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld,
   }
 }
 
-template <int NBW, int BK>
-__device__ __forceinline__ void load_frags(u32x4 (&af)[4], u32x4 (&bfr)[NBW], const uint8_t* ta,
+template <int NBW, int MBW, int BK>
+__device__ __forceinline__ void load_frags(u32x4 (&af)[MBW], u32x4 (&bfr)[NBW], const uint8_t* ta,
                                            const uint8_t* tb, int wm, int wn, int lane, int ks) {
   const int chunk = 2 * ks + (lane >> 5);
   const int r32 = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MBW; ++i) {
     const int row = wm + i * 32 + r32;
     af[i] = *reinterpret_cast<const u32x4*>(ta + row * (BK * 2) + swz<BK>(row, chunk) * 16);
   }
@@ -100,27 +101,28 @@ __device__ __forceinline__ void load_frags(u32x4 (&af)[4], u32x4 (&bfr)[NBW], co
 template <int ROWS, int BK>
 __device__ __forceinline__ void zero_k_tail(uint8_t* lds, int kt) {
   const int chunk = kt >> 3;
-  for (int row = threadIdx.x; row < ROWS; row += 256) {
+  for (int row = threadIdx.x; row < ROWS; row += blockDim.x) {
     u32x4* c = reinterpret_cast<u32x4*>(lds + row * (BK * 2) + swz<BK>(row, chunk) * 16);
     *c = mask_tail_nb(*c, chunk * 8, kt);
   }
 }
 
-// bf16 epilogue through LDS: the wave writes its 128 x BN/2 result into its
-// own LDS region (16-byte chunks XOR-swizzled by row), then reads it back
+// bf16 epilogue through LDS: the wave writes its 32*MBW x BN/2 result into
+// its own LDS region (16-byte chunks XOR-swizzled by row), then reads it back
 // row-contiguous, so each global store instruction writes whole 128-byte
 // lines instead of 16 bytes of 32 different rows.  The operand tiles are
 // dead by then (the caller has passed a barrier after the last product).
-template <int BN>
-__device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][4], uint16_t* C,
+template <int BN, int MBW>
+__device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], uint16_t* C,
                                              int64_t ldc, int mw, int nw, int M, int N,
                                              uint8_t* smem, int wave, int lane) {
   constexpr int NBW = BN / 64, WN = BN / 2, RB = WN * 2, CPR = WN / 8, RPI = 64 / CPR;
-  uint8_t* ep = smem + wave * (128 * RB);
+  constexpr int WR = 32 * MBW;  // wave rows
+  uint8_t* ep = smem + wave * (WR * RB);
 #pragma unroll
   for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < MBW; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rl = 32 * j + (lane & 31), cl = 32 * i + 8 * q + 4 * (lane >> 5);
@@ -134,7 +136,7 @@ __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][4], ui
   asm volatile("" ::: "memory");
   const int chl = lane % CPR, n = nw + chl * 8;
 #pragma unroll 4
-  for (int r0 = 0; r0 < 128; r0 += RPI) {
+  for (int r0 = 0; r0 < WR; r0 += RPI) {
     const int rl = r0 + lane / CPR, m = mw + rl;
     const u32x4 v = *reinterpret_cast<const u32x4*>(ep + rl * RB + ((chl ^ (rl & (CPR - 1))) * 16));
     if (m >= M) continue;
@@ -181,14 +183,20 @@ constexpr int big_lds_bytes() {
   return (ring > ep ? ring : ep) + (HD > 0 ? 2048 : 0);
 }
 
-template <int BN, int BK, int NS, bool OUT_F32, int HD>
-__global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
+// MBW: 32-row blocks per wave.  The tile's 256 rows x BN columns are split
+// over 256 / (32 * MBW) x 2 waves: MBW = 4 gives 4 waves of 128 x BN/2 (one
+// wave per SIMD, 512 registers), MBW = 2 gives 8 waves of 64 x BN/2 (two
+// per SIMD, at most 256 registers each).
+template <int BN, int BK, int NS, bool OUT_F32, int HD, int MBW>
+__global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(BigArgs p) {
   static_assert(HD == 0 || (BN == 256 && !OUT_F32 && (HD == 64 || HD == 128)), "rotary tiles");
   static_assert((BK == 32 || BK == 64) && NS >= 2, "pipeline shape");
+  static_assert(MBW == 2 || MBW == 4, "wave tile");
+  constexpr int NW = 2 * gBM / (32 * MBW);  // waves
   constexpr int NBW = BN / 64;              // 32-column blocks per wave
   constexpr int kTileA = gBM * BK * 2;
   constexpr int kStage = big_stage_bytes<BN, BK>();
-  constexpr int IPW = kStage / 1024 / 4;    // load instructions per wave per stage
+  constexpr int IPW = kStage / 1024 / NW;   // load instructions per wave per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int M = p.M;
@@ -205,22 +213,22 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
       make_rsrc(p.a + (int64_t)m0 * p.lda, view_bytes(min(M - m0, gBM), p.K, p.lda));
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(p.b + (int64_t)n0 * p.ldb, view_bytes(min(p.N - n0, BN), p.K, p.ldb));
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * (BN / 2);
+  const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
   const int nk = (p.K + BK - 1) / BK;
 
   int so = 0;  // rotary: this thread's entry of the sequence offsets, staged after the loop
   if (HD > 0 && (int)threadIdx.x <= p.nseq) so = p.seq_off[threadIdx.x];
 
-  f32x16 acc[NBW][4];  // [n block][m block]; lane: one m row, 4 consecutive n per 4 regs
+  f32x16 acc[NBW][MBW];  // [n block][m block]; lane: one m row, 4 consecutive n per 4 regs
 #pragma unroll
   for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < MBW; ++j) acc[i][j] = f32x16{};
 
   auto load_stage = [&](int t) {
     uint8_t* st = smem + (t % NS) * kStage;
-    load_tile<gBM, BK>(ra, p.lda, t * BK, p.K - t * BK, st, wave, lane);
-    load_tile<BN, BK>(rb, p.ldb, t * BK, p.K - t * BK, st + kTileA, wave, lane);
+    load_tile<gBM, BK, NW>(ra, p.lda, t * BK, p.K - t * BK, st, wave, lane);
+    load_tile<BN, BK, NW>(rb, p.ldb, t * BK, p.K - t * BK, st + kTileA, wave, lane);
   };
   // k-tile t's loads are done once at most the stages issued after it are
   // pending (`younger` of them; vector-memory loads complete in order)
@@ -243,13 +251,13 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
     }
   };
   constexpr int KS = BK / 16;
-  u32x4 af[2][4], bfr[2][NBW];
+  u32x4 af[2][MBW], bfr[2][NBW];
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t)
     if (t < nk) load_stage(t);
   wait_stage(min(NS - 2, nk - 1));
   open_stage(0);
-  load_frags<NBW, BK>(af[0], bfr[0], smem, smem + kTileA, wm, wn, lane, 0);
+  load_frags<NBW, MBW, BK>(af[0], bfr[0], smem, smem + kTileA, wm, wn, lane, 0);
   // One barrier per k-tile: it sits in the last k-step of tile t, after the
   // wait for tile t + 1, so the first fragments of t + 1 are read while the
   // last products of t run; it also orders every wave's reads of tile t - 1
@@ -264,17 +272,17 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
     for (int ks = 0; ks < KS; ++ks) {
       const int nb = (ks + 1) & 1;
       if (ks + 1 < KS) {
-        load_frags<NBW, BK>(af[nb], bfr[nb], cur, cur + kTileA, wm, wn, lane, ks + 1);
+        load_frags<NBW, MBW, BK>(af[nb], bfr[nb], cur, cur + kTileA, wm, wn, lane, ks + 1);
       } else if constexpr (decltype(has_next)::value) {
         wait_stage(min(NS - 2, nk - 2 - t));
         open_stage(t + 1);
         const uint8_t* nxt = smem + ((t + 1) % NS) * kStage;
-        load_frags<NBW, BK>(af[nb], bfr[nb], nxt, nxt + kTileA, wm, wn, lane, 0);
+        load_frags<NBW, MBW, BK>(af[nb], bfr[nb], nxt, nxt + kTileA, wm, wn, lane, 0);
       }
 #pragma unroll
       for (int i = 0; i < NBW; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < MBW; ++j)
           acc[i][j] = mfma32(bfr[ks & 1][i], af[ks & 1][j], acc[i][j]);
     }
   };
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
     int* aux = reinterpret_cast<int*>(smem + big_lds_bytes<BN, BK, NS, HD>() - 2048);
     if ((int)threadIdx.x <= p.nseq) aux[threadIdx.x] = so;
     lds_barrier();
-    {
+    if (threadIdx.x < gBM) {
       const int m = min(m0 + (int)threadIdx.x, M - 1);
       int lo = 0, hi = p.nseq;
       while (hi - lo > 1) {
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
     }
     lds_barrier();
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.rope, (uint64_t)p.max_pos * HD * 4);
-    for (int inst = wave; inst < gBM / RPI; inst += 4) {
+    for (int inst = wave; inst < gBM / RPI; inst += NW) {
       const int row = inst * RPI + lane / CH, c = (lane % CH) ^ (row & (CH - 1));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rt, (__attribute__((address_space(3))) void*)(smem + inst * 1024), 16,
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
     wait_vm<0>();
     lds_barrier();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < MBW; ++j) {
       const int rl = wm + 32 * j + (lane & 31);
       const uint8_t* tr = smem + rl * (HD * 4);
 #pragma unroll
@@ -340,14 +348,14 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
     lds_barrier();  // tables dead before the epilogue reuses the LDS
   }
   if (!OUT_F32 && p.vec == 2) {
-    store_staged<BN>(acc, static_cast<uint16_t*>(p.c), p.ldc, m0 + wm, n0 + wn, M, p.N, smem,
-                     wave, lane);
+    store_staged<BN, MBW>(acc, static_cast<uint16_t*>(p.c), p.ldc, m0 + wm, n0 + wn, M, p.N,
+                          smem, wave, lane);
     return;
   }
 #pragma unroll
   for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < MBW; ++j) {
       const int m = m0 + wm + 32 * j + (lane & 31);
       if (m >= M) continue;
 #pragma unroll
@@ -381,8 +389,9 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(BigArgs p) {
     }
 }
 
-// k-pipeline of every launch: 32-deep k-tiles in a ring of 3 stages
-constexpr int gBK = 32, gNS = 3;
+// k-pipeline of every launch: 32-deep k-tiles in a ring of 3 stages; wave
+// tile 32 * gMBW rows
+constexpr int gBK = 32, gNS = 3, gMBW = 2;
 
 template <int BN, bool OUT_F32, int HD = 0>
 hipError_t launch_big(const BigArgs& a, hipStream_t st) {
@@ -391,12 +400,13 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD>),
+        reinterpret_cast<const void*>(&gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD, gMBW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + gBM - 1) / gBM);
-  hipLaunchKernelGGL((gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD>),
-                     dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD, gMBW>),
+                     dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(2 * gBM / (32 * gMBW) * 64), lds,
+                     st, a);
   return hipGetLastError();
 }
 
