@@ -93,6 +93,12 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
 // Partial softmax attention of one query (sequence i, head h) over one chunk
 // of its packed rows [seq_off[i] + c*256, ...).  Output per chunk: running max
 // m, sum l and unnormalised o[hd] (fp32).  K rows are already rotated.
+//
+// Rows are read coalesced: HD/8 lanes share a row, each holding 8 consecutive
+// elements (16 bytes), so one wave instruction reads 64 * 16 contiguous bytes
+// per row group.  A lane's slice of q stays in registers; a row's score is
+// summed over its lanes by cross-lane shuffles, and the p-weighted V rows are
+// summed per lane and then over the row groups in LDS.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ K,
@@ -100,10 +106,12 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     const int32_t* __restrict__ pos, const float* __restrict__ rope, int64_t max_pos, int H,
     int Hkv, int nch, int cap, float* __restrict__ part) {
   constexpr int HALF = HD / 2;
+  constexpr int LPR = HD / 8;          // lanes per row
+  constexpr int RG = 256 / LPR;        // row groups in the workgroup
   __shared__ float qs[HD];
   __shared__ float sc[kAttnChunk];
   __shared__ float red[256];
-  __shared__ float opart[256 / HALF][HD];
+  __shared__ float opart[RG][HD + 4];
   const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
   const int beg = seq_off[i];
   int n = seq_off[i + 1] - beg;
@@ -126,23 +134,31 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     qs[threadIdx.x + HALF] = (b * cs + a * sn) * scale;
   }
   __syncthreads();
-  // scores: thread t <-> row r0 + t
-  float s = -INFINITY;
-  if ((int)threadIdx.x < cnt) {
-    const uint16_t* kr = K + (int64_t)(beg + r0 + threadIdx.x) * ldkv + kvh * HD;
-    float acc = 0.f;
+  const int sub = threadIdx.x % LPR, grp = threadIdx.x / LPR;  // element slice, row group
+  float qv[8];
 #pragma unroll
-    for (int d0 = 0; d0 < HD; d0 += 8) {
-      const u32x4 w = ldg16(kr + d0);
+  for (int e = 0; e < 8; ++e) qv[e] = qs[sub * 8 + e];
+  const uint16_t* kb = K + (int64_t)(beg + r0) * ldkv + kvh * HD + sub * 8;
+  const uint16_t* vb = V + (int64_t)(beg + r0) * ldkv + kvh * HD + sub * 8;
+  // scores: row group g takes rows g, g + RG, ...
+#pragma unroll 4
+  for (int r = grp; r < kAttnChunk; r += RG) {
+    float acc = 0.f;
+    if (r < cnt) {
+      const u32x4 w = ldg16(kb + (int64_t)r * ldkv);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc = fmaf(bf2f(ww[e] & 0xffffu), qs[d0 + 2 * e], acc);
-        acc = fmaf(bf2f(ww[e] >> 16), qs[d0 + 2 * e + 1], acc);
+        acc = fmaf(bf2f(ww[e] & 0xffffu), qv[2 * e], acc);
+        acc = fmaf(bf2f(ww[e] >> 16), qv[2 * e + 1], acc);
       }
     }
-    s = acc;
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, LPR);
+    if (sub == 0) sc[r] = r < cnt ? acc : -INFINITY;
   }
+  __syncthreads();
+  const float s = sc[threadIdx.x];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int k = 128; k > 0; k >>= 1) {
@@ -160,25 +176,27 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
     __syncthreads();
   }
   const float l = red[0];
-  // o = sum_r p_r V_r: thread (pair dp, group g) walks rows g, g + G, ...
-  constexpr int G = 256 / HALF;
-  const int dp = threadIdx.x % HALF, g = threadIdx.x / HALF;
-  float o0 = 0.f, o1 = 0.f;
-  const uint16_t* vb = V + (int64_t)(beg + r0) * ldkv + kvh * HD + 2 * dp;
-  for (int r = g; r < cnt; r += G) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(vb + (int64_t)r * ldkv);
+  // o = sum_r p_r V_r: each lane sums its 8 elements over its group's rows
+  float ov[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int r = grp; r < cnt; r += RG) {
+    const u32x4 w = ldg16(vb + (int64_t)r * ldkv);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
     const float pr = sc[r];
-    o0 = fmaf(pr, bf2f(w & 0xffffu), o0);
-    o1 = fmaf(pr, bf2f(w >> 16), o1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ov[2 * e] = fmaf(pr, bf2f(ww[e] & 0xffffu), ov[2 * e]);
+      ov[2 * e + 1] = fmaf(pr, bf2f(ww[e] >> 16), ov[2 * e + 1]);
+    }
   }
-  opart[g][2 * dp] = o0;
-  opart[g][2 * dp + 1] = o1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) opart[grp][sub * 8 + e] = ov[e];
   __syncthreads();
   float* out = part + (((int64_t)i * H + h) * nch + c) * (HD + 2);
   if (threadIdx.x < HD) {
     float acc = 0.f;
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) acc += opart[gg][threadIdx.x];
+#pragma unroll 8
+    for (int gg = 0; gg < RG; ++gg) acc += opart[gg][threadIdx.x];
     out[2 + threadIdx.x] = acc;
   }
   if (threadIdx.x == 0) {
