@@ -16,6 +16,7 @@
 // rows in its L2.  Rows past M or N and k-chunks past K read zero from
 // outside the buffers; the padding in the last partial chunk is zeroed in
 // LDS.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -150,6 +151,43 @@ __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], 
   }
 }
 
+// One 32-row block j of the wave's result through its own 32 x BN/2 LDS
+// region, as in store_staged: the persistent kernel stages row block by row
+// block so that the staging fits beside its operand ring.
+template <int BN, int MBW>
+__device__ __forceinline__ void store_block(const f32x16 (&acc)[BN / 64][MBW], int j, uint16_t* C,
+                                            int64_t ldc, int mj, int nw, int M, int N,
+                                            uint8_t* ep, int lane) {
+  constexpr int NBW = BN / 64, WN = BN / 2, RB = WN * 2, CPR = WN / 8, RPI = 64 / CPR;
+#pragma unroll
+  for (int i = 0; i < NBW; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rl = lane & 31, cl = 32 * i + 8 * q + 4 * (lane >> 5);
+      const int ch = (cl >> 3) ^ (rl & (CPR - 1));
+      *reinterpret_cast<u32x2*>(ep + rl * RB + ch * 16 + ((cl >> 2) & 1) * 8) =
+          u32x2{pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // other lanes' writes are read below (in-order LDS)
+  asm volatile("" ::: "memory");
+  const int chl = lane % CPR, n = nw + chl * 8;
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int rl = r0 + lane / CPR, m = mj + rl;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ep + rl * RB + ((chl ^ (rl & (CPR - 1))) * 16));
+    if (m >= M) continue;
+    uint16_t* c = C + (int64_t)m * ldc + n;
+    if (n + 7 < N) {
+      *reinterpret_cast<u32x4*>(c) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 8 && n + e < N; ++e) c[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+  asm volatile("" ::: "memory");
+}
+
 struct BigArgs {
   const uint16_t* a;
   int64_t lda;
@@ -168,8 +206,6 @@ struct BigArgs {
   int nseq;
 };
 
-// HD > 0: rotate each head's column pairs (c, c + HD/2) of row m by the
-// angles of the row's position (a wave's 128 columns hold whole heads).
 template <int BN, int BK>
 constexpr int big_stage_bytes() { return (gBM + BN) * BK * 2; }
 
@@ -183,6 +219,8 @@ constexpr int big_lds_bytes() {
   return (ring > ep ? ring : ep) + (HD > 0 ? 2048 : 0);
 }
 
+// HD > 0: rotate each head's column pairs (c, c + HD/2) of row m by the
+// angles of the row's position (a wave's 128 columns hold whole heads).
 // MBW: 32-row blocks per wave.  The tile's 256 rows x BN columns are split
 // over 256 / (32 * MBW) x 2 waves: MBW = 4 gives 4 waves of 128 x BN/2 (one
 // wave per SIMD, 512 registers), MBW = 2 gives 8 waves of 64 x BN/2 (two
@@ -389,9 +427,143 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
     }
 }
 
+// Persistent variant (bf16 output, 16-byte row stores, no rotary): one
+// workgroup per CU walks its XCD's tiles x*per_xcd + w, + G/8, ... and the
+// k-pipeline runs straight across tile boundaries: the next tile's first
+// stages are in flight, and its first fragments in registers, while a tile's
+// result leaves through LDS (one 32-row block at a time, in the LDS past the
+// ring) and its stores drain behind the next tile's products.
+template <int BN, int BK, int NS, int MBW>
+constexpr int persist_lds_bytes() {
+  return NS * big_stage_bytes<BN, BK>() + (2 * gBM / (32 * MBW)) * 32 * BN;
+}
+
+template <int BN, int BK, int NS, int MBW>
+__global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_persist_kernel(BigArgs p) {
+  static_assert((BK == 32 || BK == 64) && NS >= 2 && (MBW == 2 || MBW == 4), "shape");
+  constexpr int NW = 2 * gBM / (32 * MBW), NBW = BN / 64, KS = BK / 16;
+  constexpr int kTileA = gBM * BK * 2;
+  constexpr int kStage = big_stage_bytes<BN, BK>();
+  constexpr int IPW = kStage / 1024 / NW;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int M = p.M;
+  if (p.m_valid) {
+    const int nv = *p.m_valid;
+    M = nv < 0 ? 0 : (nv > p.M ? p.M : nv);
+  }
+  const int ntn = (p.N + BN - 1) / BN, ntiles = ntn * ((M + gBM - 1) / gBM);
+  const int per_xcd = (ntiles + 7) / 8, wpx = (int)gridDim.x / 8;
+  const int first = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+  const int end = min(((int)blockIdx.x % 8 + 1) * per_xcd, ntiles);
+  if (first >= end) return;
+  const int mine = (end - first + wpx - 1) / wpx;  // tiles first, first + wpx, ...
+  const int nk = (p.K + BK - 1) / BK, total = mine * nk;
+  const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
+  uint8_t* ep = smem + NS * kStage + wave * (32 * BN);  // this wave's 32 x BN/2 staging
+
+  auto load_stage = [&](int g) {
+    const int tl = first + (g / nk) * wpx, t = g % nk;
+    const int m0 = (tl / ntn) * gBM, n0 = (tl % ntn) * BN;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(p.a + (int64_t)m0 * p.lda, view_bytes(min(M - m0, gBM), p.K, p.lda));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(p.b + (int64_t)n0 * p.ldb, view_bytes(min(p.N - n0, BN), p.K, p.ldb));
+    uint8_t* st = smem + (g % NS) * kStage;
+    load_tile<gBM, BK, NW>(ra, p.lda, t * BK, p.K - t * BK, st, wave, lane);
+    load_tile<BN, BK, NW>(rb, p.ldb, t * BK, p.K - t * BK, st + kTileA, wave, lane);
+  };
+  auto wait_stage = [&](int younger) {
+    if (younger >= NS - 1) wait_vm<(NS - 1) * IPW>();
+    else if (NS > 3 && younger == 2) wait_vm<(NS > 3 ? 2 : 0) * IPW>();
+    else if (NS > 2 && younger == 1) wait_vm<(NS > 2 ? 1 : 0) * IPW>();
+    else wait_vm<0>();
+  };
+  auto open_stage = [&](int g) {
+    lds_barrier();
+    const int kt = p.K - (g % nk) * BK;
+    if (kt < BK && (kt & 7)) {
+      uint8_t* st = smem + (g % NS) * kStage;
+      zero_k_tail<gBM, BK>(st, kt);
+      zero_k_tail<BN, BK>(st + kTileA, kt);
+      lds_barrier();
+    }
+  };
+  f32x16 acc[NBW][MBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i)
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) acc[i][j] = f32x16{};
+  u32x4 af[2][MBW], bfr[2][NBW];
+#pragma unroll
+  for (int g = 0; g < NS - 1; ++g)
+    if (g < total) load_stage(g);
+  wait_stage(min(NS - 2, total - 1));
+  open_stage(0);
+  load_frags<NBW, MBW, BK>(af[0], bfr[0], smem, smem + kTileA, wm, wn, lane, 0);
+  // As in gemm_big_kernel: one barrier per k-tile, in its last k-step after
+  // the wait for the next k-tile (here possibly the next tile's first), with
+  // the last k-tile peeled.  Stores issued by an epilogue only make the later
+  // load waits stricter: loads complete in order among themselves.
+  auto k_tile = [&](int g, auto has_next) {
+    if (g + NS - 1 < total) load_stage(g + NS - 1);
+    const uint8_t* cur = smem + (g % NS) * kStage;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int nb = (ks + 1) & 1;
+      if (ks + 1 < KS) {
+        load_frags<NBW, MBW, BK>(af[nb], bfr[nb], cur, cur + kTileA, wm, wn, lane, ks + 1);
+      } else if constexpr (decltype(has_next)::value) {
+        wait_stage(min(NS - 2, total - 2 - g));
+        open_stage(g + 1);
+        const uint8_t* nxt = smem + ((g + 1) % NS) * kStage;
+        load_frags<NBW, MBW, BK>(af[nb], bfr[nb], nxt, nxt + kTileA, wm, wn, lane, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int j = 0; j < MBW; ++j)
+          acc[i][j] = mfma32(bfr[ks & 1][i], af[ks & 1][j], acc[i][j]);
+    }
+    if (g % nk == nk - 1) {  // tile done: store it and start the next from zero
+      const int tl = first + (g / nk) * wpx;
+      const int m0 = (tl / ntn) * gBM, n0 = (tl % ntn) * BN;
+#pragma unroll
+      for (int j = 0; j < MBW; ++j)
+        store_block<BN, MBW>(acc, j, static_cast<uint16_t*>(p.c), p.ldc, m0 + wm + 32 * j,
+                             n0 + wn, M, p.N, ep, lane);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int j = 0; j < MBW; ++j) acc[i][j] = f32x16{};
+    }
+  };
+  for (int g = 0; g + 1 < total; ++g) k_tile(g, std::true_type{});
+  k_tile(total - 1, std::false_type{});
+}
+
 // k-pipeline of every launch: 32-deep k-tiles in a ring of 3 stages; wave
 // tile 32 * gMBW rows
 constexpr int gBK = 32, gNS = 3, gMBW = 2;
+
+// Persistent launch: one workgroup per CU (the grid is a multiple of 8 and
+// at most 256), for bf16 output with 16-byte row stores and no rotary.
+template <int BN>
+hipError_t launch_persist(const BigArgs& a, hipStream_t st) {
+  constexpr int lds = persist_lds_bytes<BN, gBK, gNS, gMBW>();
+  static_assert(lds <= 160 * 1024, "LDS");
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_persist_kernel<BN, gBK, gNS, gMBW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  });
+  const int tiles = ((a.N + BN - 1) / BN) * ((a.M + gBM - 1) / gBM);
+  const int grid = std::min(256, (tiles + 7) / 8 * 8);
+  hipLaunchKernelGGL((gemm_persist_kernel<BN, gBK, gNS, gMBW>), dim3((unsigned)grid),
+                     dim3(2 * gBM / (32 * gMBW) * 64), lds, st, a);
+  return hipGetLastError();
+}
 
 template <int BN, bool OUT_F32, int HD = 0>
 hipError_t launch_big(const BigArgs& a, hipStream_t st) {
@@ -448,7 +620,9 @@ hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t l
   BigArgs a{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
             nullptr, 0, (int)M, (int)N, (int)K, store_width(C, ldc, 2), m_valid, nullptr, 0,
             nullptr, 0};
-  if (!rope) return launch_big<256, false>(a, st);
+  // without rotary: the persistent kernel (its stores drain behind the next
+  // tile's products; worth it where the output is large against K)
+  if (!rope) return a.vec == 2 ? launch_persist<256>(a, st) : launch_big<256, false>(a, st);
   if (rope->nseq < 1 || rope->nseq > 255 || rope->max_pos < 1 ||
       rope->max_pos * rope->hd * 4 >= (int64_t(1) << 31) || N % rope->hd)
     return hipErrorInvalidValue;
