@@ -9,73 +9,12 @@
 // device).  Pure data movement: one 16-byte load and store per lane, a row of
 // 409..1024 bf16 elements is one or two wave-wide transactions.  Invalid
 // source indices produce zero rows; nothing is read out of bounds.
-//
-// Rows of up to 2 KiB (the latent rows) take the unrolled path: a wave holds
-// kRows rows in flight (their remap entries, then all their loads, then all
-// their stores), so the loop does not wait out one memory round trip per
-// row.
 #include "lr_common.h"
 #include "lr_kernels.h"
 
 namespace lr {
 
 namespace {
-
-constexpr int kRows = 4;  // rows in flight per wave on the unrolled path
-
-// Rows of at most 128 16-byte chunks (row_bytes <= 2048): lane l moves chunks
-// l and l + 64 of each of kRows rows per iteration, then the 2-byte tail.
-__global__ __launch_bounds__(256) void gather16_rows_kernel(
-    const char* __restrict__ src, int64_t src_rows, int64_t src_pitch,
-    const int32_t* __restrict__ remap, int64_t cap, const int32_t* n_valid, int64_t row_bytes,
-    char* __restrict__ dst, int64_t dst_pitch) {
-  int64_t nv = cap;
-  if (n_valid) {
-    const int64_t v = *n_valid;
-    nv = v < 0 ? 0 : (v < cap ? v : cap);
-  }
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t nw = (int64_t)gridDim.x * 4;
-  const int nvec = (int)(row_bytes / 16);
-  const int64_t tail = nvec * 16 + 2 * lane;  // this lane's tail byte offset
-  for (int64_t j0 = wid; j0 < nv; j0 += nw * kRows) {
-    const char* srow[kRows];
-    bool live[kRows], ok[kRows];
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-      const int64_t j = j0 + u * nw;
-      live[u] = j < nv;
-      const int64_t s = live[u] ? remap[j] : -1;
-      ok[u] = s >= 0 && s < src_rows;
-      srow[u] = src + (ok[u] ? s : 0) * src_pitch;
-    }
-    u32x4 v[kRows][2];
-    uint16_t t[kRows];
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = lane + 64 * h;
-        v[u][h] = ok[u] && c < nvec ? *reinterpret_cast<const u32x4*>(srow[u] + c * 16)
-                                    : u32x4{0, 0, 0, 0};
-      }
-      t[u] = ok[u] && tail < row_bytes ? *reinterpret_cast<const uint16_t*>(srow[u] + tail)
-                                       : (uint16_t)0;
-    }
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-      if (!live[u]) continue;
-      char* drow = dst + (j0 + u * nw) * dst_pitch;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = lane + 64 * h;
-        if (c < nvec) *reinterpret_cast<u32x4*>(drow + c * 16) = v[u][h];
-      }
-      if (tail < row_bytes) *reinterpret_cast<uint16_t*>(drow + tail) = t[u];
-    }
-  }
-}
 
 // VEC = bytes moved per lane per access (16, 4 or 2)
 template <int VEC>
@@ -131,12 +70,7 @@ hipError_t remap_gather(int elem_bytes, const void* src, int64_t src_rows, int64
   int64_t waves = cap < 8192 ? cap : 8192;
   if (waves < 1) waves = 1;
   const dim3 grid((unsigned)((waves + 3) / 4));
-  const bool al16 = sp % 16 == 0 && dp % 16 == 0 && sa % 16 == 0 && da % 16 == 0;
-  if (al16 && row_bytes <= 2048 && row_bytes % 2 == 0) {
-    // the tail is one 2-byte access per lane: at most 128 tail bytes
-    hipLaunchKernelGGL(gather16_rows_kernel, grid, dim3(256), 0, st, (const char*)src, src_rows,
-                       sp, remap, cap, n_valid, row_bytes, (char*)dst, dp);
-  } else if (al16) {
+  if (sp % 16 == 0 && dp % 16 == 0 && sa % 16 == 0 && da % 16 == 0) {
     hipLaunchKernelGGL(gather_kernel<16>, grid, dim3(256), 0, st, (const char*)src, src_rows, sp,
                        remap, cap, n_valid, row_bytes, (char*)dst, dp);
   } else if (sp % 4 == 0 && dp % 4 == 0 && sa % 4 == 0 && da % 4 == 0) {
