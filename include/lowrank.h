@@ -253,12 +253,20 @@ lr_status lowrank_prepare_decode(int64_t B, const int32_t* lengths, const int32_
 lr_status lowrank_rope_table(int64_t head_dim, int64_t max_pos, float theta, float* table,
                              hipStream_t stream);
 
+/* MLP of a decoder layer (lr_layer_weights.mlp). */
+enum {
+  LR_MLP_SWIGLU = 0, /* down(silu(gate(x)) * up(x)): slots 4, 5, 6 */
+  LR_MLP_RELU = 1    /* fc2(relu(fc1(x))): fc1 in slot 4, fc2 in slot 6, slot 5 unused */
+};
+
 /*
- * Weights of one decoder layer whose seven linears (q, k, v, o, gate, up,
- * down, in this order) are decomposed (DeInfer/en §2.D: attention and GLU MLP
- * variants, per-layer ratios -- r[] may differ per linear and per layer).
- * Ut[k] is U_r^T [r[k], d_in] and Vt[k] is V_r^T [d_out, r[k]], bf16, 16-byte
- * aligned, ld a multiple of 8.  Norm weights are bf16 [d_model].
+ * Weights of one decoder layer whose linears (q, k, v, o, gate, up, down, in
+ * this order) are decomposed (DeInfer/en §2.D: MHA/GQA/MQA attention through
+ * n_kv_heads, GLU and non-GLU MLPs through mlp, per-layer ratios -- r[] may
+ * differ per linear and per layer).  Ut[k] is U_r^T [r[k], d_in] and Vt[k]
+ * is V_r^T [d_out, r[k]], bf16, 16-byte aligned, ld a multiple of 8 (slot 5
+ * is ignored, and may be NULL, when mlp = LR_MLP_RELU).  Norm weights are
+ * bf16 [d_model].
  */
 typedef struct {
   int64_t d_model, n_heads, n_kv_heads, head_dim, d_ffn;  /* head_dim 64 or 128 */
@@ -272,6 +280,7 @@ typedef struct {
   const void* ffn_norm;
   const float* rope;        /* lowrank_rope_table output */
   int64_t rope_max_pos;     /* positions the table covers */
+  int64_t mlp;              /* LR_MLP_SWIGLU or LR_MLP_RELU */
 } lr_layer_weights;
 
 /*
@@ -308,16 +317,17 @@ size_t lowrank_decode_step_workspace_bytes(const lr_layer_weights* w, const lr_d
  *   addresses never change between steps; rows past *n_valid are skipped) ;
  *   softmax attention of each query over
  *   its sequence's rows ; h += lowrank_o(o) ; x = RMSNorm(h) ;
- *   h += lowrank_down(silu(lowrank_gate(x)) * lowrank_up(x)).
+ *   h += lowrank_down(silu(lowrank_gate(x)) * lowrank_up(x))  (LR_MLP_SWIGLU), or
+ *   h += lowrank_fc2(relu(lowrank_fc1(x)))  (LR_MLP_RELU).
  * Launches only; fixed grids, no host reads of device data, no allocation:
  * capture 32 calls (one per layer) in one graph and replay it each step
  * after refreshing the preparation arrays.
  * The projections run on the decode path (q, k, v as one grouped launch,
  * gate and up as another), so B <= 64.
- * Errors: LR_ERR_ARG / LR_ERR_ALIGN (also: rope not 16-byte aligned) /
- * LR_ERR_UNSUPPORTED (head_dim not 64 or 128, B > 64, a factor pitch of
- * 2^22 elements or more) / LR_ERR_WORKSPACE from host checks, LR_ERR_HIP
- * from the runtime.
+ * Errors: LR_ERR_ARG (also: mlp not LR_MLP_SWIGLU / LR_MLP_RELU) /
+ * LR_ERR_ALIGN (also: rope not 16-byte aligned) / LR_ERR_UNSUPPORTED
+ * (head_dim not 64 or 128, B > 64, a factor pitch of 2^22 elements or more)
+ * / LR_ERR_WORKSPACE from host checks, LR_ERR_HIP from the runtime.
  */
 lr_status lowrank_layer_decode_step(const lr_layer_weights* w, const lr_decode_state* s,
                                     float* h, void* workspace, size_t workspace_bytes,

@@ -23,7 +23,7 @@ from .lowrank import (rank_for_ratio, truncated_factors, linear, linear_loops,
                       tp_share_stage1, tp_share_stage2)
 from .paging import (logical_to_physical, contiguous_runs, prepare_decode,
                      remap_gather, remap_gather_loops)
-from .decoder import (rmsnorm, rope, attention_one, silu, decode_layer_seq,
+from .decoder import (rmsnorm, rope, attention_one, silu, relu, decode_layer_seq,
                       decode_layer, decode_step)
 
 __all__ = [
@@ -31,6 +31,6 @@ __all__ = [
     "tp_share_stage1", "tp_share_stage2",
     "logical_to_physical", "contiguous_runs", "prepare_decode", "remap_gather",
     "remap_gather_loops",
-    "rmsnorm", "rope", "attention_one", "silu", "decode_layer_seq",
+    "rmsnorm", "rope", "attention_one", "silu", "relu", "decode_layer_seq",
     "decode_layer", "decode_step",
 ]

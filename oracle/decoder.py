@@ -6,15 +6,16 @@ The pages: decomposed models must rebuild the KV cache while decoding, by
 multiplying the cached low-rank rows by the upward projection matrices
 (DeInfer/en §1 third bottleneck and §2.C "Graph Replay Stage"; DeInfer/es §1
 "Incompatibilidad con CUDA Graph").  The layer around it is LLaMA-shaped:
-MHA/GQA attention and a GLU MLP (DeInfer/en §2.D; DeInfer/es §2
-"Generalización").
+MHA/GQA/MQA attention and a GLU or non-GLU MLP (DeInfer/en §2.D; DeInfer/es
+§2 "Generalización").
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): the cache holds the pre-rotary latents x U_k and x U_v; rotary
 is applied to the reconstructed keys (it cannot be folded into V_k); RMSNorm
 eps = 1e-5; rotate-half rotary with base 10000; softmax scale 1/sqrt(head_dim);
 the new token sits at position L (its cached length) and attends to all L + 1
-rows; SwiGLU MLP; fp64 throughout.
+rows; the GLU MLP is SwiGLU, the non-GLU one (OPT-style) is fc2(relu(fc1 x))
+with fc1 and fc2 in the "gate" and "down" slots; fp64 throughout.
 """
 from __future__ import annotations
 
@@ -70,6 +71,11 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
+def relu(z):
+    z = np.asarray(z, np.float64)
+    return np.maximum(z, 0.0)
+
+
 def _lin(x, w, role):
     return (x @ w["U"][role]) @ w["V"][role]
 
@@ -79,7 +85,8 @@ def decode_layer_seq(h, w, lat_k, lat_v, L: int, cfg):
 
     h[d] residual stream; w: {'U': {role: U_r}, 'V': {role: V_r}, 'g1', 'g2'};
     lat_k[L, r_k], lat_v[L, r_v]: the cached latents in logical order; cfg:
-    n_heads, n_kv_heads, head_dim, eps, rope_theta.
+    n_heads, n_kv_heads, head_dim, eps, rope_theta, mlp ("swiglu" by default,
+    or "relu": fc1 in the "gate" slot, fc2 in "down", no "up").
     Returns (h_out[d], new_k_latent[r_k], new_v_latent[r_v])."""
     H, Hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     eps, theta = cfg.get("eps", 1e-5), cfg.get("rope_theta", 10000.0)
@@ -97,7 +104,10 @@ def decode_layer_seq(h, w, lat_k, lat_v, L: int, cfg):
     o = attention_one(q, K, V).reshape(H * hd)
     h = h + _lin(o, w, "o")
     x2 = rmsnorm(h, w["g2"], eps)
-    m = silu(_lin(x2, w, "gate")) * _lin(x2, w, "up")
+    if cfg.get("mlp", "swiglu") == "relu":
+        m = relu(_lin(x2, w, "gate"))
+    else:
+        m = silu(_lin(x2, w, "gate")) * _lin(x2, w, "up")
     h = h + _lin(m, w, "down")
     return h, lk, lv
 

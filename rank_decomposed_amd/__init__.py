@@ -266,10 +266,11 @@ def lowrank_prepare_decode(lengths, tables, block: int, cap: int, want_runs: boo
 # ------------------------------------------------------------------ decode step
 from ._lib import DecodeState, LayerWeights  # noqa: E402
 
+LR_MLP_SWIGLU, LR_MLP_RELU = 0, 1  # lr_layer_weights.mlp
 LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
 __all__ += ["LayerWeights", "DecodeState", "layer_weights", "decode_state",
             "lowrank_rope_table", "lowrank_decode_step_workspace_bytes",
-            "lowrank_layer_decode_step", "LINEARS"]
+            "lowrank_layer_decode_step", "LINEARS", "LR_MLP_SWIGLU", "LR_MLP_RELU"]
 
 
 def lowrank_rope_table(head_dim: int, max_pos: int, theta: float, table, stream=None):
@@ -281,13 +282,18 @@ def lowrank_rope_table(head_dim: int, max_pos: int, theta: float, table, stream=
 
 def layer_weights(cfg: dict, Ut: dict, Vt: dict, attn_norm, ffn_norm, rope, rope_max_pos: int):
     """Build lr_layer_weights from tensors: Ut[name] = U_r^T [r, d_in] and
-    Vt[name] = V_r^T [d_out, r] bf16 views (name in LINEARS).  The returned
-    struct keeps references to the tensors it points to."""
+    Vt[name] = V_r^T [d_out, r] bf16 views (name in LINEARS).  cfg["mlp"] is
+    "swiglu" (default) or "relu"; a ReLU MLP takes fc1 as "gate" and fc2 as
+    "down" and needs no "up".  The returned struct keeps references to the
+    tensors it points to."""
     w = LayerWeights()
     w.d_model, w.n_heads, w.n_kv_heads = cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"]
     w.head_dim, w.d_ffn = cfg["head_dim"], cfg["d_ffn"]
     w.eps = cfg.get("eps", 1e-5)
+    w.mlp = {"swiglu": LR_MLP_SWIGLU, "relu": LR_MLP_RELU}[cfg.get("mlp", "swiglu")]
     for k, name in enumerate(LINEARS):
+        if w.mlp == LR_MLP_RELU and name == "up":
+            continue
         u, v = Ut[name], Vt[name]
         w.Ut[k], w.ldu[k] = u.data_ptr(), _ld(u)
         w.Vt[k], w.ldv[k] = v.data_ptr(), _ld(v)

@@ -46,7 +46,8 @@ class LayerWeights(C.Structure):
                 ("head_dim", C.c_int64), ("d_ffn", C.c_int64), ("eps", C.c_float),
                 ("Ut", C.c_void_p * 7), ("ldu", C.c_int64 * 7), ("Vt", C.c_void_p * 7),
                 ("ldv", C.c_int64 * 7), ("r", C.c_int64 * 7), ("attn_norm", C.c_void_p),
-                ("ffn_norm", C.c_void_p), ("rope", C.c_void_p), ("rope_max_pos", C.c_int64)]
+                ("ffn_norm", C.c_void_p), ("rope", C.c_void_p), ("rope_max_pos", C.c_int64),
+                ("mlp", C.c_int64)]
 
 
 class Linear(C.Structure):

@@ -78,6 +78,14 @@ __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ l
     pool[s * pool_ld + j] = (uint16_t)f2bf(lat[(int64_t)b * ldl + j]);
 }
 
+// ---------------------------------------------------------------- ReLU
+// m = max(z, 0) on bf16, the non-GLU MLP's activation (NaN passes through).
+__global__ __launch_bounds__(256) void relu_kernel(const uint16_t* __restrict__ z,
+                                                   uint16_t* __restrict__ m, int64_t n) {
+  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
+    m[e] = bf2f(z[e]) < 0.f ? (uint16_t)0 : z[e];
+}
+
 // ---------------------------------------------------------------- SiLU * up
 __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restrict__ gate,
                                                        const uint16_t* __restrict__ up,
@@ -251,7 +259,8 @@ StepLayout step_layout(const lr_layer_weights* w, const lr_decode_state* s) {
   DecodeLinear g[7];
   for (int k = 0; k < 7; ++k) g[k] = DecodeLinear{B, din[k], w->r[k], dout[k]};
   size_t lin = decode_group_workspace_bytes(g, 3);
-  lin = std::max(lin, decode_group_workspace_bytes(g + 4, 2));
+  lin = std::max(lin, w->mlp == LR_MLP_RELU ? decode_workspace_bytes(B, din[4], w->r[4], dout[4])
+                                            : decode_group_workspace_bytes(g + 4, 2));
   lin = std::max(lin, decode_workspace_bytes(B, din[3], w->r[3], dout[3]));
   lin = std::max(lin, decode_workspace_bytes(B, din[6], w->r[6], dout[6]));
   size_t off = 0;
@@ -272,7 +281,7 @@ StepLayout step_layout(const lr_layer_weights* w, const lr_decode_state* s) {
   L.part = take(B * w->n_heads * L.nch * (w->head_dim + 2) * 4);
   L.o = take(B * dq * 2);
   L.gate = take(B * w->d_ffn * 2);
-  L.up = take(B * w->d_ffn * 2);
+  L.up = w->mlp == LR_MLP_RELU ? L.gate : take(B * w->d_ffn * 2);
   L.m = take(B * w->d_ffn * 2);
   L.total = off;
   return L;
@@ -295,7 +304,9 @@ lr_status check_step(const lr_layer_weights* w, const lr_decode_state* s, const 
   const int64_t dq = w->n_heads * w->head_dim, dkv = w->n_kv_heads * w->head_dim;
   const int64_t din[7] = {w->d_model, w->d_model, w->d_model, dq, w->d_model, w->d_model, w->d_ffn};
   const int64_t dout[7] = {dq, dkv, dkv, w->d_model, w->d_ffn, w->d_ffn, w->d_model};
+  if (w->mlp != LR_MLP_SWIGLU && w->mlp != LR_MLP_RELU) return LR_ERR_ARG;
   for (int k = 0; k < 7; ++k) {
+    if (k == 5 && w->mlp == LR_MLP_RELU) continue;  // no up projection
     if (!w->Ut[k] || !w->Vt[k] || w->r[k] <= 0) return LR_ERR_ARG;
     if (w->ldu[k] < din[k] || w->ldv[k] < w->r[k]) return LR_ERR_ARG;
     if (!al16(w->Ut[k]) || !al16(w->Vt[k]) || w->ldu[k] % 8 || w->ldv[k] % 8) return LR_ERR_ALIGN;
@@ -449,13 +460,16 @@ extern "C" lr_status lowrank_layer_decode_step(const lr_layer_weights* w,
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(B), dim3(256), 0, st, h, d,
                      static_cast<const uint16_t*>(w->ffn_norm), x, d, (int)d, w->eps);
   LR_CHECK(hipGetLastError());
-  {
+  const dim3 egrid((unsigned)((B * ffn + 255) / 256 < 4096 ? (B * ffn + 255) / 256 : 4096));
+  if (w->mlp == LR_MLP_RELU) {
+    LR_CHECK(decode_linear_bf16(linear(4, x, d, d, ffn, gate, nullptr, nullptr), st));
+    hipLaunchKernelGGL(relu_kernel, egrid, dim3(256), 0, st, gate, m, (int64_t)B * ffn);
+  } else {
     const DecodeLinear gu[2] = {linear(4, x, d, d, ffn, gate, nullptr, nullptr),
                                 linear(5, x, d, d, ffn, up, nullptr, nullptr)};
     LR_CHECK(decode_group_bf16(gu, 2, st));
+    hipLaunchKernelGGL(silu_mul_kernel, egrid, dim3(256), 0, st, gate, up, m, (int64_t)B * ffn);
   }
-  hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((B * ffn + 255) / 256 < 4096 ? (B * ffn + 255) / 256 : 4096)),
-                     dim3(256), 0, st, gate, up, m, (int64_t)B * ffn);
   LR_CHECK(hipGetLastError());
   LR_CHECK(decode_linear_bf16(linear(6, m, ffn, ffn, d, nullptr, h, nullptr), st));
 #undef LR_CHECK

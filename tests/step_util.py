@@ -53,7 +53,8 @@ def pad_dev(bits, ld):
 
 class Step:
     """B sequences with given cached lengths, n_layers layers, paged latent
-    pools with seeded placement."""
+    pools with seeded placement.  ranks: one {name: r} for every layer, or a
+    list with one per layer (per-layer ratios)."""
 
     def __init__(self, cfg_id, cfg, ranks, lengths, n_layers, block=16, fast=False,
                  max_seq_rows=None, cap=None, slack_blocks=3):
@@ -65,8 +66,8 @@ class Step:
         self.pool_rows = nblocks * block
         self.max_seq_rows = max_seq_rows or int(self.lengths.max() + 1)
         self.cap = cap or int(B * ((self.max_seq_rows + 15) // 16 * 16))
-        rk, rv = ranks["k"], ranks["v"]
-        self.pool_ld = ld8(max(rk, rv), 8)
+        per_layer = ranks if isinstance(ranks, (list, tuple)) else [ranks] * n_layers
+        self.pool_ld = ld8(max(max(rk["k"], rk["v"]) for rk in per_layer), 8)
         d = dev()
         self.layers, self.weights, self.pools_np_k, self.pools_np_v = [], [], [], []
         self.pools_k, self.pools_v = [], []
@@ -74,7 +75,7 @@ class Step:
                                 device=d)
         lr.lowrank_rope_table(cfg["head_dim"], self.max_seq_rows, 10000.0, self.rope)
         for li in range(n_layers):
-            vals, Ut, Vt, g1, g2 = make_layer(cfg_id, li, cfg, ranks, fast)
+            vals, Ut, Vt, g1, g2 = make_layer(cfg_id, li, cfg, per_layer[li], fast)
             self.layers.append(vals)
             self.weights.append(lr.layer_weights(cfg, Ut, Vt, g1, g2, self.rope,
                                                  self.max_seq_rows))

@@ -203,6 +203,7 @@ def _valid_step_structs():
     ("pool_ld", 409, _lib.LR_ERR_ALIGN),
     ("n_heads", 33, _lib.LR_ERR_ARG),             # not a multiple of n_kv_heads
     ("rope", A16 + 8, _lib.LR_ERR_ALIGN),         # rotary epilogue reads 16-byte quads
+    ("mlp", 2, _lib.LR_ERR_ARG),                  # neither SwiGLU nor ReLU
 ])
 def test_decode_step_host_checks(field, value, status):
     w, s = _valid_step_structs()
@@ -213,3 +214,20 @@ def test_decode_step_host_checks(field, value, status):
                                          None) == status
     if field is None:
         assert lib.lowrank_decode_step_workspace_bytes(C.byref(w), C.byref(s)) > 0
+
+
+def test_decode_step_relu_mlp_needs_no_up_projection():
+    # a non-GLU layer leaves slot 5 empty and still passes every host check
+    w, s = _valid_step_structs()
+    w.mlp = lr.LR_MLP_RELU
+    w.Ut[5] = w.Vt[5] = None
+    w.r[5] = 0
+    lib = lr.load()
+    assert lib.lowrank_layer_decode_step(C.byref(w), C.byref(s), C.c_void_p(A16), None, 0,
+                                         None) == _lib.LR_ERR_WORKSPACE
+    relu_ws = lib.lowrank_decode_step_workspace_bytes(C.byref(w), C.byref(s))
+    w.mlp = lr.LR_MLP_SWIGLU
+    assert lib.lowrank_layer_decode_step(C.byref(w), C.byref(s), C.c_void_p(A16), None, 0,
+                                         None) == _lib.LR_ERR_ARG     # SwiGLU needs slot 5
+    w2, s2 = _valid_step_structs()
+    assert 0 < relu_ws < lib.lowrank_decode_step_workspace_bytes(C.byref(w2), C.byref(s2))

@@ -57,6 +57,49 @@ def test_three_layers_full_rank_against_oracle():
     assert err <= TOL
 
 
+def test_relu_mlp_layers_against_oracle():
+    # non-GLU (OPT-style) MLP: fc2(relu(fc1 x)), fc1 and fc2 in the gate and
+    # down slots, no up projection
+    cfg = dict(small_cfg(4, 2, 64, d_ffn=640), mlp="relu")
+    st = Step(81, cfg, ranks_for(cfg), [0, 9, 31, 64, 200], n_layers=2)
+    h = st.run()
+    torch.cuda.synchronize()
+    err = maxrel(to_f64(h), st.oracle())
+    print("relu mlp, two layers: max rel err %.2e" % err)
+    assert err <= TOL
+
+
+def test_per_layer_ratios_in_one_graph():
+    # three layers at different ranks (ratios ~1/2, 1/3, 1/5 of full rank)
+    # captured in one graph; replays match eager execution bit for bit and
+    # the oracle to the bar
+    cfg = small_cfg(4, 4, 64, d_ffn=448)
+    ranks = [ranks_for(cfg, frac) for frac in (2, 3, 5)]
+    st = Step(85, cfg, ranks, [4, 50, 0, 130], n_layers=3)
+    h_in = st.h.clone()
+    eager = st.run().clone()
+    torch.cuda.synchronize()
+    err = maxrel(to_f64(eager), st.oracle())
+    print("per-layer ratios: max rel err %.2e" % err)
+    assert err <= TOL
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        st.h.copy_(h_in)
+        st.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.run()
+    for _ in range(3):
+        st.h.copy_(h_in)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.h, eager)
+
+
 def test_graph_replay_with_new_lengths_matches_eager():
     cfg = small_cfg(4, 2, 64)
     lengths = np.array([5, 33, 0, 100])

@@ -259,6 +259,14 @@ def _tiny_layer_weights(seed, d, dff, Hkv, hd, full_rank):
             "g2": 1 + 0.1 * g.standard_normal(d)}, Wd
 
 
+def test_relu_values():
+    assert np.array_equal(oracle.relu([-3.0, -0.0, 0.0, 2.5]), [0.0, 0.0, 0.0, 2.5])
+    z = np.linspace(-4, 4, 81)
+    # relu(z) - relu(-z) = z and relu(z) + relu(-z) = |z|
+    assert np.array_equal(oracle.relu(z) - oracle.relu(-z), z)
+    assert np.array_equal(oracle.relu(z) + oracle.relu(-z), np.abs(z))
+
+
 def _dense_layer(h, Wd, w, lat_x, L, cfg):
     """Textbook dense decoder layer from the token-level normed inputs of all
     L+1 positions (lat_x: rows that produced the cache): K = RoPE(x W_k)."""
@@ -272,13 +280,15 @@ def _dense_layer(h, Wd, w, lat_x, L, cfg):
     o = oracle.attention_one(q, K, Vv).reshape(-1)
     h = h + o @ Wd["o"]
     x2 = oracle.rmsnorm(h, w["g2"])
+    if cfg.get("mlp") == "relu":       # OPT-style: fc2(max(fc1 x, 0))
+        return h + np.maximum(x2 @ Wd["gate"], 0.0) @ Wd["down"]
     return h + (oracle.silu(x2 @ Wd["gate"]) * (x2 @ Wd["up"])) @ Wd["down"]
 
 
-@pytest.mark.parametrize("Hkv", [4, 2, 1])
-def test_decode_layer_full_rank_equals_dense(Hkv):
+@pytest.mark.parametrize("Hkv,mlp", [(4, "swiglu"), (2, "swiglu"), (1, "swiglu"), (2, "relu")])
+def test_decode_layer_full_rank_equals_dense(Hkv, mlp):
     d, dff, H, hd, L = 32, 48, 4, 8, 6
-    cfg = {"n_heads": H, "n_kv_heads": Hkv, "head_dim": hd}
+    cfg = {"n_heads": H, "n_kv_heads": Hkv, "head_dim": hd, "mlp": mlp}
     w, Wd = _tiny_layer_weights(100 * Hkv, d, dff, Hkv, hd, full_rank=True)
     g = np.random.default_rng(9)
     prev_x = g.standard_normal((L, d))          # normed inputs of earlier tokens
