@@ -243,6 +243,31 @@ lr_status lowrank_prepare_decode(int64_t B, const int32_t* lengths, const int32_
                                  int64_t max_runs);
 
 /*
+ * lowrank_prepare_prefill -- the same preparation stage for a chunked-prefill
+ * step (DeInfer/en §2.C applied to the prompt side): sequence i has
+ * lengths[i] cached tokens and appends chunk[i] >= 1 new tokens at positions
+ * lengths[i] .. lengths[i] + chunk[i] - 1, so its compact segment holds
+ * lengths[i] + chunk[i] rows.  The new tokens are numbered in sequence order,
+ * then position order.
+ *
+ * Outputs as lowrank_prepare_decode (seq_off now the prefix sums of
+ * lengths[i] + chunk[i]), with per new token t < *n_tokens:
+ *   tok_seq[t]        its sequence
+ *   pos[t]            its position
+ *   slot_mapping[t]   physical row its latents are written to
+ * pos, tok_seq and slot_mapping hold max_tokens entries.
+ * Errors: as lowrank_prepare_decode, plus LR_ERR_ARG for chunk[i] < 1 or a
+ * null chunk / tok_seq / n_tokens, LR_ERR_CAPACITY for more than max_tokens
+ * new tokens.  lowrank_prepare_decode is this call with every chunk[i] = 1.
+ */
+lr_status lowrank_prepare_prefill(int64_t S, const int32_t* lengths, const int32_t* chunk,
+                                  const int32_t* tables, int64_t table_ld, int64_t block,
+                                  int64_t cap, int64_t max_tokens, int32_t* remap,
+                                  int32_t* seq_off, int32_t* tok_seq, int32_t* pos,
+                                  int32_t* slot_mapping, int32_t* n_tokens, int32_t* n_valid,
+                                  int32_t* n_runs, int32_t* runs, int64_t max_runs);
+
+/*
  * lowrank_rope_table -- rotary-embedding table for the decode step:
  * table[p][i] = (cos(p w_i), sin(p w_i)), w_i = theta^(-2i/head_dim),
  * p < max_pos, i < head_dim/2, computed on the device in double precision and

@@ -21,7 +21,7 @@ full-rank decoder layer against a dense textbook layer.  No function here is
 """
 from .lowrank import (rank_for_ratio, truncated_factors, linear, linear_loops,
                       tp_share_stage1, tp_share_stage2)
-from .paging import (logical_to_physical, contiguous_runs, prepare_decode,
+from .paging import (logical_to_physical, contiguous_runs, prepare_decode, prepare_prefill,
                      remap_gather, remap_gather_loops)
 from .decoder import (rmsnorm, rope, attention_one, silu, relu, decode_layer_seq,
                       decode_layer, decode_step)
@@ -29,7 +29,7 @@ from .decoder import (rmsnorm, rope, attention_one, silu, relu, decode_layer_seq
 __all__ = [
     "rank_for_ratio", "truncated_factors", "linear", "linear_loops",
     "tp_share_stage1", "tp_share_stage2",
-    "logical_to_physical", "contiguous_runs", "prepare_decode", "remap_gather",
+    "logical_to_physical", "contiguous_runs", "prepare_decode", "prepare_prefill", "remap_gather",
     "remap_gather_loops",
     "rmsnorm", "rope", "attention_one", "silu", "relu", "decode_layer_seq",
     "decode_layer", "decode_step",

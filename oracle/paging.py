@@ -79,6 +79,45 @@ def prepare_decode(tables, lengths, block: int, cap: int):
     }
 
 
+def prepare_prefill(tables, lengths, chunks, block: int, cap: int):
+    """Preparation stage for one chunked-prefill step: sequence i has
+    lengths[i] cached tokens and appends chunks[i] >= 1 new tokens at
+    positions lengths[i] .. lengths[i] + chunks[i] - 1, so its compact
+    segment holds lengths[i] + chunks[i] rows.  New tokens are numbered
+    sequence by sequence in position order.
+
+    Returns int32 arrays remap[cap], seq_off[S+1], tok_seq[n], pos[n],
+    slot_mapping[n] and the ints n_valid, n_tokens, n_runs, plus 'runs'."""
+    S = len(lengths)
+    rows = [int(lengths[i]) + int(chunks[i]) for i in range(S)]
+    seq_off = np.concatenate([[0], np.cumsum(rows, dtype=np.int64)]).astype(np.int64)
+    n_valid = int(seq_off[-1])
+    if n_valid > cap:
+        raise ValueError("packed rows %d exceed capacity %d" % (n_valid, cap))
+    remap = np.full(cap, -1, dtype=np.int64)
+    runs = []
+    tok_seq, pos, slots = [], [], []
+    for i in range(S):
+        for (src, lo, cnt) in contiguous_runs(tables[i], rows[i], block):
+            runs.append((src, int(seq_off[i]) + lo, cnt))
+            remap[seq_off[i] + lo: seq_off[i] + lo + cnt] = np.arange(src, src + cnt)
+        for p in range(int(lengths[i]), rows[i]):
+            tok_seq.append(i)
+            pos.append(p)
+            slots.append(logical_to_physical(tables[i], p, block))
+    return {
+        "remap": remap.astype(np.int32),
+        "seq_off": seq_off.astype(np.int32),
+        "tok_seq": np.array(tok_seq, dtype=np.int32),
+        "pos": np.array(pos, dtype=np.int32),
+        "slot_mapping": np.array(slots, dtype=np.int32),
+        "n_valid": n_valid,
+        "n_tokens": len(pos),
+        "n_runs": len(runs),
+        "runs": runs,
+    }
+
+
 def remap_gather(src: np.ndarray, remap: np.ndarray, n_valid=None, dst_init=None):
     """dst[j] = src[remap[j]] when 0 <= remap[j] < rows(src), else a zero
     row, for j < n_valid (all of remap when n_valid is None); rows at and

@@ -22,7 +22,7 @@ from ._lib import (LR_BF16, LR_F32, LR_FULL, LR_PACKED_WEIGHTS, LR_STAGE1_ONLY, 
                    LowrankError, load, status_string)
 
 __all__ = [
-    "lowrank_linear_forward", "kv_remap_gather", "lowrank_prepare_decode",
+    "lowrank_linear_forward", "kv_remap_gather", "lowrank_prepare_decode", "lowrank_prepare_prefill",
     "lowrank_workspace_bytes", "lowrank_status_string", "lowrank_version",
     "LR_F32", "LR_BF16", "LR_FULL", "LR_STAGE1_ONLY", "LR_STAGE2_ONLY", "LR_PACKED_WEIGHTS",
     "LowrankError", "load", "PackedFactor", "pack_factor", "lowrank_packed_bytes",
@@ -258,6 +258,51 @@ def lowrank_prepare_decode(lengths, tables, block: int, cap: int, want_runs: boo
     _lib.check(st, "lowrank_prepare_decode")
     out = {"remap": remap, "seq_off": seq_off, "pos": pos[:B], "slot_mapping": slots[:B],
            "n_valid": int(nv[0]), "n_runs": int(nr[0])}
+    if want_runs:
+        out["runs"] = runs[:out["n_runs"]].copy()
+    return out
+
+
+def lowrank_prepare_prefill(lengths, chunks, tables, block: int, cap: int, max_tokens=None,
+                            want_runs: bool = False):
+    """Host preparation stage of a chunked-prefill step: sequence i has
+    lengths[i] cached tokens and appends chunks[i] new ones.  Returns a dict
+    of numpy int32 arrays remap[cap], seq_off[S+1], tok_seq[n], pos[n],
+    slot_mapping[n] (n = sum of chunks) and ints n_valid, n_tokens, n_runs
+    (plus runs[n_runs, 3] when want_runs)."""
+    lib = load()
+    lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+    chunks = np.ascontiguousarray(chunks, dtype=np.int32)
+    S = lengths.shape[0]
+    if isinstance(tables, np.ndarray) and tables.ndim == 2:
+        tab = np.ascontiguousarray(tables, dtype=np.int32)
+    else:
+        width = max((len(t) for t in tables), default=1)
+        tab = np.full((S, max(width, 1)), -1, dtype=np.int32)
+        for i, t in enumerate(tables):
+            tab[i, :len(t)] = t
+    mt = int(chunks.sum()) if max_tokens is None else int(max_tokens)
+    remap = np.empty(cap, np.int32)
+    seq_off = np.empty(S + 1, np.int32)
+    tok_seq = np.empty(max(mt, 1), np.int32)
+    pos = np.empty(max(mt, 1), np.int32)
+    slots = np.empty(max(mt, 1), np.int32)
+    nt, nv, nr = (np.zeros(1, np.int32) for _ in range(3))
+    max_runs = int(tab.size) if want_runs else 0
+    runs = np.empty((max(max_runs, 1), 3), np.int32)
+
+    def P(a):
+        return a.ctypes.data_as(C.c_void_p)
+
+    st = lib.lowrank_prepare_prefill(S, P(lengths), P(chunks), P(tab), tab.shape[1], block, cap,
+                                     mt, P(remap), P(seq_off), P(tok_seq), P(pos), P(slots),
+                                     P(nt), P(nv), P(nr), P(runs) if want_runs else None,
+                                     max_runs)
+    _lib.check(st, "lowrank_prepare_prefill")
+    n = int(nt[0])
+    out = {"remap": remap, "seq_off": seq_off, "tok_seq": tok_seq[:n], "pos": pos[:n],
+           "slot_mapping": slots[:n], "n_valid": int(nv[0]), "n_tokens": n,
+           "n_runs": int(nr[0])}
     if want_runs:
         out["runs"] = runs[:out["n_runs"]].copy()
     return out

@@ -26,6 +26,9 @@ SIGNATURES = {
                                   _p]),
     "lowrank_prepare_decode": (C.c_int, [_i64, _pi32, _pi32, _i64, _i64, _i64, _pi32, _pi32,
                                          _pi32, _pi32, _pi32, _pi32, _pi32, _i64]),
+    "lowrank_prepare_prefill": (C.c_int, [_i64, _pi32, _pi32, _pi32, _i64, _i64, _i64, _i64,
+                                          _pi32, _pi32, _pi32, _pi32, _pi32, _pi32, _pi32,
+                                          _pi32, _pi32, _i64]),
     "lowrank_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int, _i64, _i64, _i64, _i64, _i64]),
     "lowrank_status_string": (C.c_char_p, [C.c_int]),
     "lowrank_version": (C.c_int, []),

@@ -60,3 +60,60 @@ def test_errors():
     with pytest.raises(lr.LowrankError) as e:          # negative block index
         lr.lowrank_prepare_decode(np.array([3]), [np.array([-2])], 16, 100)
     assert e.value.status == 1
+
+
+# ---------------------------------------------------------------- chunked prefill
+def _prefill_case(seed, S, block, max_chunk):
+    g = synth.rng(seed)
+    lengths = g.integers(0, 300, S)
+    chunks = g.integers(1, max_chunk + 1, S)
+    # tables cover lengths + chunks rows (block_tables covers its lengths + 1)
+    tables, _ = synth.block_tables(seed, lengths + chunks - 1, block=block, max_extent=4)
+    return lengths, chunks, tables
+
+
+@pytest.mark.parametrize("seed,block,max_chunk", [(0, 16, 64), (1, 3, 1), (2, 1, 9), (3, 64, 300)])
+def test_prefill_against_oracle(seed, block, max_chunk):
+    lengths, chunks, tables = _prefill_case(seed, 9, block, max_chunk)
+    cap = int((lengths + chunks).sum()) + 7
+    ref = oracle.prepare_prefill(tables, lengths, chunks, block, cap)
+    got = lr.lowrank_prepare_prefill(lengths, chunks, tables, block, cap, want_runs=True)
+    for k in ("remap", "seq_off", "tok_seq", "pos", "slot_mapping"):
+        assert np.array_equal(got[k], ref[k]), k
+    for k in ("n_valid", "n_tokens", "n_runs"):
+        assert got[k] == ref[k], k
+    assert [tuple(r) for r in got["runs"]] == ref["runs"]
+
+
+def test_prefill_oracle_against_decode_oracle():
+    # two oracle functions written independently: a chunk of c tokens lays out
+    # the rows of a decode step at length L + c - 1, and its last token is that
+    # step's new token; chunks of one are exactly a decode step
+    lengths, chunks, tables = _prefill_case(11, 7, 16, 40)
+    cap = int((lengths + chunks).sum())
+    pf = oracle.prepare_prefill(tables, lengths, chunks, 16, cap)
+    dc = oracle.prepare_decode(tables, lengths + chunks - 1, 16, cap)
+    for k in ("remap", "seq_off"):
+        assert np.array_equal(pf[k], dc[k]), k
+    assert pf["runs"] == dc["runs"]
+    last = np.cumsum(chunks) - 1
+    assert np.array_equal(pf["pos"][last], dc["pos"])
+    assert np.array_equal(pf["slot_mapping"][last], dc["slot_mapping"])
+    assert np.array_equal(pf["tok_seq"], np.repeat(np.arange(7), chunks))
+    one = oracle.prepare_prefill(tables, lengths, np.ones(7, np.int64), 16, cap)
+    dec = oracle.prepare_decode(tables, lengths, 16, cap)
+    for k in ("remap", "seq_off", "pos", "slot_mapping"):
+        assert np.array_equal(one[k], dec[k]), k
+
+
+def test_prefill_errors():
+    tables = [np.array([0, 1, 2])]
+    with pytest.raises(lr.LowrankError) as e:          # a chunk must hold a token
+        lr.lowrank_prepare_prefill(np.array([3]), np.array([0]), tables, 16, 100)
+    assert e.value.status == 1
+    with pytest.raises(lr.LowrankError) as e:          # more new tokens than max_tokens
+        lr.lowrank_prepare_prefill(np.array([3]), np.array([5]), tables, 16, 100, max_tokens=4)
+    assert e.value.status == 5
+    with pytest.raises(lr.LowrankError) as e:          # table too short for 3 + 46 rows
+        lr.lowrank_prepare_prefill(np.array([3]), np.array([46]), tables, 16, 100)
+    assert e.value.status == 1
