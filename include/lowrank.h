@@ -358,6 +358,44 @@ lr_status lowrank_layer_decode_step(const lr_layer_weights* w, const lr_decode_s
                                     float* h, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/*
+ * State of one chunked-prefill step (see lowrank_prepare_prefill): T new
+ * tokens in S sequences; sequence i's compact segment holds its cached rows
+ * and its new tokens' rows.  Device arrays, as in lr_decode_state.
+ */
+typedef struct {
+  void* k_pool;
+  void* v_pool;                  /* [pool_rows, pool_ld] bf16, pool_ld >= r_k, r_v */
+  int64_t pool_rows, pool_ld;
+  const int32_t* slot_mapping;   /* [T] slot of each new token's latents */
+  const int32_t* remap;          /* [cap] source slot of each packed row */
+  const int32_t* seq_off;        /* [S + 1] packed-row offsets */
+  const int32_t* tok_seq;        /* [T] sequence of each new token */
+  const int32_t* pos;            /* [T] position of each new token */
+  const int32_t* n_valid;        /* scalar: packed rows in use (= seq_off[S]) */
+  int64_t T, S, cap, max_seq_rows; /* max_seq_rows >= rows of the longest segment */
+} lr_prefill_state;
+
+/* Device scratch of lowrank_layer_prefill_step for these shapes. */
+size_t lowrank_prefill_step_workspace_bytes(const lr_layer_weights* w, const lr_prefill_state* s);
+
+/*
+ * lowrank_layer_prefill_step -- one decoder layer over a chunk of prompt
+ * tokens (the prefill side of DeInfer/en §2.C: the chunk's latents join the
+ * paged cache that later decode steps reconstruct), in place on h [T,
+ * d_model] fp32, tokens in sequence order.  The same layer as
+ * lowrank_layer_decode_step, with causal attention: new token t attends to
+ * its sequence's rows 0 .. pos[t] (the cached ones and the chunk's tokens up
+ * to itself).  Projections of at most 64 tokens run on the decode path,
+ * larger chunks on the prefill path (their o and down outputs are rounded to
+ * bf16 before they are added to h).  S <= 255.
+ * Errors: as lowrank_layer_decode_step (without the B <= 64 limit), plus
+ * LR_ERR_ARG for a null tok_seq and LR_ERR_UNSUPPORTED for S > 255.
+ */
+lr_status lowrank_layer_prefill_step(const lr_layer_weights* w, const lr_prefill_state* s,
+                                     float* h, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* Device scratch of lowrank_linear_forward (which = 0; cap unused).  Other
  * values of which return 0: the decode step has its own sizing call. */
 size_t lowrank_workspace_bytes(int which, lr_dtype dt, int64_t T_or_B, int64_t d_in, int64_t r,
@@ -366,8 +404,8 @@ size_t lowrank_workspace_bytes(int which, lr_dtype dt, int64_t T_or_B, int64_t d
 const char* lowrank_status_string(lr_status s);
 
 /* sizeof(lr_layer_weights) for which = 0, sizeof(lr_decode_state) for
- * which = 1, sizeof(lr_linear) for which = 2 (lets bindings verify their
- * struct layout); 0 otherwise. */
+ * which = 1, sizeof(lr_linear) for which = 2, sizeof(lr_prefill_state) for
+ * which = 3 (lets bindings verify their struct layout); 0 otherwise. */
 size_t lowrank_abi_sizeof(int which);
 
 /* Library ABI version (major * 100 + minor). */

@@ -24,7 +24,8 @@ from .lowrank import (rank_for_ratio, truncated_factors, linear, linear_loops,
 from .paging import (logical_to_physical, contiguous_runs, prepare_decode, prepare_prefill,
                      remap_gather, remap_gather_loops)
 from .decoder import (rmsnorm, rope, attention_one, silu, relu, decode_layer_seq,
-                      decode_layer, decode_step)
+                      decode_layer, decode_step, prefill_layer_seq, prefill_layer,
+                      prefill_step)
 
 __all__ = [
     "rank_for_ratio", "truncated_factors", "linear", "linear_loops",
@@ -32,5 +33,5 @@ __all__ = [
     "logical_to_physical", "contiguous_runs", "prepare_decode", "prepare_prefill", "remap_gather",
     "remap_gather_loops",
     "rmsnorm", "rope", "attention_one", "silu", "relu", "decode_layer_seq",
-    "decode_layer", "decode_step",
+    "decode_layer", "decode_step", "prefill_layer_seq", "prefill_layer", "prefill_step",
 ]

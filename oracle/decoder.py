@@ -146,3 +146,66 @@ def decode_step(h, layers, pools_k, pools_v, tables, lengths, block: int, cfg, s
         hcur, _, _ = decode_layer(hcur, w, pools_k[li], pools_v[li], sub_tab, sub_len,
                                   block, cfg)
     return hcur
+
+
+def prefill_layer_seq(H, w, lat_k, lat_v, L: int, cfg):
+    """One decoder layer for a chunk of c new tokens of one sequence (the
+    chunked-prefill step): H[c, d] residual rows of the tokens at positions
+    L .. L + c - 1; lat_k[L, r_k], lat_v[L, r_v] the cached latents.  Token j
+    attends causally to rows 0 .. L + j: the cached rows and the chunk's
+    tokens up to itself.  Returns (H_out[c, d], new_k[c, r_k], new_v[c, r_v]).
+    """
+    Hn, Hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    eps, theta = cfg.get("eps", 1e-5), cfg.get("rope_theta", 10000.0)
+    H = np.asarray(H, np.float64)
+    c = H.shape[0]
+    X = np.stack([rmsnorm(H[j], w["g1"], eps) for j in range(c)])
+    Q = (X @ w["U"]["q"]) @ w["V"]["q"]                      # [c, Hn * hd]
+    lk = X @ w["U"]["k"]
+    lv = X @ w["U"]["v"]
+    LK = np.vstack([np.asarray(lat_k, np.float64).reshape(L, lk.shape[1]), lk])
+    LV = np.vstack([np.asarray(lat_v, np.float64).reshape(L, lv.shape[1]), lv])
+    K = (LK @ w["V"]["k"]).reshape(L + c, Hkv, hd)
+    K = np.stack([rope(K[:, i, :], np.arange(L + c), theta) for i in range(Hkv)], axis=1)
+    V = (LV @ w["V"]["v"]).reshape(L + c, Hkv, hd)
+    out = np.empty_like(H)
+    for j in range(c):
+        q = rope(Q[j].reshape(Hn, hd), np.full(Hn, L + j), theta)
+        o = attention_one(q, K[:L + j + 1], V[:L + j + 1]).reshape(Hn * hd)
+        h = H[j] + _lin(o, w, "o")
+        x2 = rmsnorm(h, w["g2"], eps)
+        if cfg.get("mlp", "swiglu") == "relu":
+            m = relu(_lin(x2, w, "gate"))
+        else:
+            m = silu(_lin(x2, w, "gate")) * _lin(x2, w, "up")
+        out[j] = h + _lin(m, w, "down")
+    return out, lk, lv
+
+
+def prefill_layer(h, w, pool_k, pool_v, tables, lengths, chunks, block: int, cfg):
+    """One layer of a chunked-prefill step over S sequences: h[n, d] holds the
+    new tokens sequence by sequence (chunks[i] of them for sequence i, at
+    positions lengths[i] ..).  Pools as in decode_layer.  Returns
+    (h_out[n, d], new_k[n, r_k], new_v[n, r_v])."""
+    rk = w["U"]["k"].shape[1]
+    rv = w["U"]["v"].shape[1]
+    hs, nk, nv = [], [], []
+    t = 0
+    for i in range(len(lengths)):
+        L, c = int(lengths[i]), int(chunks[i])
+        lat_k = _logical_rows(pool_k, tables[i], L, block)[:, :rk]
+        lat_v = _logical_rows(pool_v, tables[i], L, block)[:, :rv]
+        ho, lk, lv = prefill_layer_seq(np.asarray(h, np.float64)[t:t + c], w, lat_k, lat_v, L,
+                                       cfg)
+        hs.append(ho); nk.append(lk); nv.append(lv)
+        t += c
+    return np.vstack(hs), np.vstack(nk), np.vstack(nv)
+
+
+def prefill_step(h, layers, pools_k, pools_v, tables, lengths, chunks, block: int, cfg):
+    """All layers in order for one chunked-prefill step: h[n, d] -> h[n, d]."""
+    hcur = np.asarray(h, np.float64)
+    for li, w in enumerate(layers):
+        hcur, _, _ = prefill_layer(hcur, w, pools_k[li], pools_v[li], tables, lengths, chunks,
+                                   block, cfg)
+    return hcur

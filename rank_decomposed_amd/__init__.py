@@ -309,11 +309,12 @@ def lowrank_prepare_prefill(lengths, chunks, tables, block: int, cap: int, max_t
 
 
 # ------------------------------------------------------------------ decode step
-from ._lib import DecodeState, LayerWeights  # noqa: E402
+from ._lib import DecodeState, LayerWeights, PrefillState  # noqa: E402
 
 LR_MLP_SWIGLU, LR_MLP_RELU = 0, 1  # lr_layer_weights.mlp
 LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
-__all__ += ["LayerWeights", "DecodeState", "layer_weights", "decode_state",
+__all__ += ["LayerWeights", "DecodeState", "PrefillState", "layer_weights", "decode_state",
+            "prefill_state", "lowrank_prefill_step_workspace_bytes", "lowrank_layer_prefill_step",
             "lowrank_rope_table", "lowrank_decode_step_workspace_bytes",
             "lowrank_layer_decode_step", "LINEARS", "LR_MLP_SWIGLU", "LR_MLP_RELU"]
 
@@ -372,4 +373,35 @@ def lowrank_layer_decode_step(w: LayerWeights, s: DecodeState, h, workspace, str
     _lib.check(load().lowrank_layer_decode_step(C.byref(w), C.byref(s), _ptr(h), _ptr(workspace),
                                                 nbytes, _stream(stream, h.device)),
                "lowrank_layer_decode_step")
+    return h
+
+
+def prefill_state(k_pool, v_pool, slot_mapping, remap, seq_off, tok_seq, pos, n_valid,
+                  max_seq_rows: int):
+    """Build lr_prefill_state from device tensors (pools [pool_rows, pool_ld]
+    bf16; int32 prep arrays of lowrank_prepare_prefill; n_valid a 1-element
+    int32 tensor)."""
+    s = PrefillState()
+    s.k_pool, s.v_pool = k_pool.data_ptr(), v_pool.data_ptr()
+    s.pool_rows, s.pool_ld = k_pool.shape[0], _ld(k_pool)
+    s.slot_mapping, s.remap, s.seq_off = slot_mapping.data_ptr(), remap.data_ptr(), seq_off.data_ptr()
+    s.tok_seq, s.pos, s.n_valid = tok_seq.data_ptr(), pos.data_ptr(), n_valid.data_ptr()
+    s.T, s.S, s.cap = slot_mapping.numel(), seq_off.numel() - 1, remap.numel()
+    s.max_seq_rows = max_seq_rows
+    s._keep = (k_pool, v_pool, slot_mapping, remap, seq_off, tok_seq, pos, n_valid)
+    return s
+
+
+def lowrank_prefill_step_workspace_bytes(w: LayerWeights, s: PrefillState) -> int:
+    return int(load().lowrank_prefill_step_workspace_bytes(C.byref(w), C.byref(s)))
+
+
+def lowrank_layer_prefill_step(w: LayerWeights, s: PrefillState, h, workspace, stream=None):
+    """One decoder layer over a chunk of prompt tokens, in place on h [T, d]
+    (fp32, tokens in sequence order); causal attention over each token's
+    cached and earlier chunk rows."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _lib.check(load().lowrank_layer_prefill_step(C.byref(w), C.byref(s), _ptr(h), _ptr(workspace),
+                                                 nbytes, _stream(stream, h.device)),
+               "lowrank_layer_prefill_step")
     return h

@@ -36,6 +36,8 @@ SIGNATURES = {
     "lowrank_rope_table": (C.c_int, [_i64, _i64, C.c_float, _p, _p]),
     "lowrank_decode_step_workspace_bytes": (C.c_size_t, [_p, _p]),
     "lowrank_layer_decode_step": (C.c_int, [_p, _p, _p, _p, _sz, _p]),
+    "lowrank_prefill_step_workspace_bytes": (C.c_size_t, [_p, _p]),
+    "lowrank_layer_prefill_step": (C.c_int, [_p, _p, _p, _p, _sz, _p]),
     "lowrank_packed_bytes": (C.c_size_t, [_i64, _i64]),
     "lowrank_group_workspace_bytes": (C.c_size_t, [_i64, C.c_int, _p]),
     "lowrank_linear_forward_group": (C.c_int, [_i64, C.c_int, _p, _u, _p, _sz, _p]),
@@ -51,6 +53,15 @@ class LayerWeights(C.Structure):
                 ("ldv", C.c_int64 * 7), ("r", C.c_int64 * 7), ("attn_norm", C.c_void_p),
                 ("ffn_norm", C.c_void_p), ("rope", C.c_void_p), ("rope_max_pos", C.c_int64),
                 ("mlp", C.c_int64)]
+
+
+class PrefillState(C.Structure):
+    """lr_prefill_state (include/lowrank.h)."""
+    _fields_ = [("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("pool_rows", C.c_int64),
+                ("pool_ld", C.c_int64), ("slot_mapping", C.c_void_p), ("remap", C.c_void_p),
+                ("seq_off", C.c_void_p), ("tok_seq", C.c_void_p), ("pos", C.c_void_p),
+                ("n_valid", C.c_void_p), ("T", C.c_int64), ("S", C.c_int64), ("cap", C.c_int64),
+                ("max_seq_rows", C.c_int64)]
 
 
 class Linear(C.Structure):

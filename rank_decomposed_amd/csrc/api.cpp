@@ -19,6 +19,7 @@ extern "C" size_t lowrank_abi_sizeof(int which) {
     case 0: return sizeof(lr_layer_weights);
     case 1: return sizeof(lr_decode_state);
     case 2: return sizeof(lr_linear);
+    case 3: return sizeof(lr_prefill_state);
     default: return 0;
   }
 }

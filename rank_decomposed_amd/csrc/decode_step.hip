@@ -78,6 +78,15 @@ __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ l
     pool[s * pool_ld + j] = (uint16_t)f2bf(lat[(int64_t)b * ldl + j]);
 }
 
+// ---------------------------------------------------------------- residual add
+// h[t, :] += y[t, :] (bf16 projection output into the fp32 residual).
+__global__ __launch_bounds__(256) void add_residual_kernel(float* __restrict__ h,
+                                                           const uint16_t* __restrict__ y,
+                                                           int64_t n) {
+  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
+    h[e] += bf2f(y[e]);
+}
+
 // ---------------------------------------------------------------- ReLU
 // m = max(z, 0) on bf16, the non-GLU MLP's activation (NaN passes through).
 __global__ __launch_bounds__(256) void relu_kernel(const uint16_t* __restrict__ z,
@@ -107,12 +116,32 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
 // per row group.  A lane's slice of q stays in registers; a row's score is
 // summed over its lanes by cross-lane shuffles, and the p-weighted V rows are
 // summed per lane and then over the row groups in LDS.
+// Rows the query of token i attends to: [beg, beg + n) of the packed
+// buffer.  With tok_seq (a chunk of several tokens per sequence) token i
+// belongs to sequence tok_seq[i] and sees its rows up to its own position
+// (causal); without, token i is sequence i's new token and sees all its rows.
+__device__ __forceinline__ void query_rows(const int32_t* seq_off, const int32_t* tok_seq,
+                                           const int32_t* pos, int S, int i, int cap, int* beg,
+                                           int* n) {
+  int sq = tok_seq ? tok_seq[i] : i;
+  sq = sq < 0 ? 0 : (sq >= S ? S - 1 : sq);
+  const int b = seq_off[sq];
+  *beg = b;
+  *n = 0;
+  if (b < 0 || b >= cap) return;          // offsets are device data: stay inside cap
+  int len = seq_off[sq + 1] - b;
+  if (tok_seq) len = min(len, pos[i] + 1);
+  len = len < cap - b ? len : cap - b;
+  *n = len < 0 ? 0 : len;
+}
+
 template <int HD>
 __global__ __launch_bounds__(256) void attn_partial_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int64_t ldkv, const int32_t* __restrict__ seq_off,
-    const int32_t* __restrict__ pos, const float* __restrict__ rope, int64_t max_pos, int H,
-    int Hkv, int nch, int cap, float* __restrict__ part) {
+    const int32_t* __restrict__ tok_seq, int S, const int32_t* __restrict__ pos,
+    const float* __restrict__ rope, int64_t max_pos, int H, int Hkv, int nch, int cap,
+    float* __restrict__ part) {
   constexpr int HALF = HD / 2;
   constexpr int LPR = HD / 8;          // lanes per row
   constexpr int RG = 256 / LPR;        // row groups in the workgroup
@@ -121,10 +150,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   __shared__ float red[256];
   __shared__ float opart[RG][HD + 4];
   const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
-  const int beg = seq_off[i];
-  int n = seq_off[i + 1] - beg;
-  if (beg < 0 || beg >= cap) return;      // offsets are device data: stay inside cap
-  n = n < cap - beg ? n : cap - beg;
+  int beg, n;
+  query_rows(seq_off, tok_seq, pos, S, i, cap, &beg, &n);
   const int r0 = c * kAttnChunk;
   if (r0 >= n) return;
   const int cnt = min(kAttnChunk, n - r0);
@@ -218,13 +245,13 @@ template <int HD>
 __global__ __launch_bounds__(HD) void attn_combine_kernel(const float* __restrict__ part, int H,
                                                           int nch,
                                                           const int32_t* __restrict__ seq_off,
+                                                          const int32_t* __restrict__ tok_seq,
+                                                          int S, const int32_t* __restrict__ pos,
                                                           int cap, uint16_t* __restrict__ o,
                                                           int64_t ldo) {
   const int h = blockIdx.x, i = blockIdx.y;
-  const int beg = seq_off[i];
-  int n = seq_off[i + 1] - beg;
-  if (beg < 0 || beg >= cap) n = 0;
-  n = n < cap - beg ? n : cap - beg;
+  int beg, n;
+  query_rows(seq_off, tok_seq, pos, S, i, cap, &beg, &n);
   int used = (n + kAttnChunk - 1) / kAttnChunk;
   used = used < 0 ? 0 : (used > nch ? nch : used);
   const float* base = part + ((int64_t)i * H + h) * nch * (HD + 2);
@@ -241,28 +268,66 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------- workspace
+// One layer step over T new tokens in S sequences: the decode step (one new
+// token per sequence, tok_seq null) and the chunked-prefill step share it.
+struct StepIn {
+  void* k_pool;
+  void* v_pool;
+  int64_t pool_rows, pool_ld;
+  const int32_t* slot_mapping;  // [T]
+  const int32_t* remap;         // [cap]
+  const int32_t* seq_off;       // [S + 1]
+  const int32_t* tok_seq;       // [T] or null (token i is sequence i's)
+  const int32_t* pos;           // [T]
+  const int32_t* n_valid;
+  int64_t T, S, cap, max_seq_rows;
+};
+
+StepIn from_decode(const lr_decode_state* s) {
+  return StepIn{s->k_pool, s->v_pool,  s->pool_rows, s->pool_ld, s->slot_mapping, s->remap,
+                s->seq_off, nullptr,   s->pos,       s->n_valid, s->B,            s->B,
+                s->cap,     s->max_seq_rows};
+}
+
+StepIn from_prefill(const lr_prefill_state* s) {
+  return StepIn{s->k_pool,   s->v_pool, s->pool_rows, s->pool_ld, s->slot_mapping, s->remap,
+                s->seq_off,  s->tok_seq, s->pos,      s->n_valid, s->T,            s->S,
+                s->cap,      s->max_seq_rows};
+}
+
+// Projections of up to 64 tokens run on the decode path (streamed weights,
+// grouped launches); more tokens take the prefill path.
+constexpr int64_t kDecodeTokens = 64;
+
 struct StepLayout {
-  size_t lin, x, q, latk, latv, kbuf, vbuf, krec, vrec, part, o, gate, up, m, total;
+  size_t lin, x, q, latk, latv, kbuf, vbuf, krec, vrec, part, o, gate, up, m, yb, total;
   int64_t rk_ld, rv_ld, dkv, nch;
 };
 
-StepLayout step_layout(const lr_layer_weights* w, const lr_decode_state* s) {
+StepLayout step_layout(const lr_layer_weights* w, const StepIn& s) {
   StepLayout L{};
-  const int64_t B = s->B, d = w->d_model, dq = w->n_heads * w->head_dim;
+  const int64_t T = s.T, d = w->d_model, dq = w->n_heads * w->head_dim;
+  const bool dec = T <= kDecodeTokens;
   L.dkv = w->n_kv_heads * w->head_dim;
   L.rk_ld = rup(w->r[1], 8);
   L.rv_ld = rup(w->r[2], 8);
-  L.nch = (s->max_seq_rows + kAttnChunk - 1) / kAttnChunk;
+  L.nch = (s.max_seq_rows + kAttnChunk - 1) / kAttnChunk;
   const int64_t din[7] = {d, d, d, dq, d, d, w->d_ffn};
   const int64_t dout[7] = {dq, L.dkv, L.dkv, d, w->d_ffn, w->d_ffn, d};
-  // the projections' scratch: q,k,v and gate,up go out as groups
-  DecodeLinear g[7];
-  for (int k = 0; k < 7; ++k) g[k] = DecodeLinear{B, din[k], w->r[k], dout[k]};
-  size_t lin = decode_group_workspace_bytes(g, 3);
-  lin = std::max(lin, w->mlp == LR_MLP_RELU ? decode_workspace_bytes(B, din[4], w->r[4], dout[4])
-                                            : decode_group_workspace_bytes(g + 4, 2));
-  lin = std::max(lin, decode_workspace_bytes(B, din[3], w->r[3], dout[3]));
-  lin = std::max(lin, decode_workspace_bytes(B, din[6], w->r[6], dout[6]));
+  size_t lin = 0;
+  if (dec) {
+    // the projections' scratch: q,k,v and gate,up go out as groups
+    DecodeLinear g[7];
+    for (int k = 0; k < 7; ++k) g[k] = DecodeLinear{T, din[k], w->r[k], dout[k]};
+    lin = decode_group_workspace_bytes(g, 3);
+    lin = std::max(lin, w->mlp == LR_MLP_RELU ? decode_workspace_bytes(T, din[4], w->r[4], dout[4])
+                                              : decode_group_workspace_bytes(g + 4, 2));
+    lin = std::max(lin, decode_workspace_bytes(T, din[3], w->r[3], dout[3]));
+    lin = std::max(lin, decode_workspace_bytes(T, din[6], w->r[6], dout[6]));
+  } else {
+    for (int k = 0; k < 7; ++k)
+      if (!(k == 5 && w->mlp == LR_MLP_RELU)) lin = std::max(lin, prefill_workspace_bytes(T, w->r[k]));
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -270,50 +335,52 @@ StepLayout step_layout(const lr_layer_weights* w, const lr_decode_state* s) {
     return at;
   };
   L.lin = take(lin);  // first: zero-filled once by the caller, kept zero by the kernels
-  L.x = take(B * d * 2);
-  L.q = take(B * dq * 2);
-  L.latk = take(B * w->r[1] * 4);
-  L.latv = take(B * w->r[2] * 4);
-  L.kbuf = take(s->cap * L.rk_ld * 2);
-  L.vbuf = take(s->cap * L.rv_ld * 2);
-  L.krec = take(s->cap * L.dkv * 2);
-  L.vrec = take(s->cap * L.dkv * 2);
-  L.part = take(B * w->n_heads * L.nch * (w->head_dim + 2) * 4);
-  L.o = take(B * dq * 2);
-  L.gate = take(B * w->d_ffn * 2);
-  L.up = w->mlp == LR_MLP_RELU ? L.gate : take(B * w->d_ffn * 2);
-  L.m = take(B * w->d_ffn * 2);
+  L.x = take(T * d * 2);
+  L.q = take(T * dq * 2);
+  L.latk = take(T * w->r[1] * 4);
+  L.latv = take(T * w->r[2] * 4);
+  L.kbuf = take(s.cap * L.rk_ld * 2);
+  L.vbuf = take(s.cap * L.rv_ld * 2);
+  L.krec = take(s.cap * L.dkv * 2);
+  L.vrec = take(s.cap * L.dkv * 2);
+  L.part = take(T * w->n_heads * L.nch * (w->head_dim + 2) * 4);
+  L.o = take(T * dq * 2);
+  L.gate = take(T * w->d_ffn * 2);
+  L.up = w->mlp == LR_MLP_RELU ? L.gate : take(T * w->d_ffn * 2);
+  L.m = take(T * w->d_ffn * 2);
+  L.yb = dec ? L.m : take(T * d * 2);  // prefill path: o / down output before the residual add
   L.total = off;
   return L;
 }
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-lr_status check_step(const lr_layer_weights* w, const lr_decode_state* s, const float* h) {
-  if (!w || !s || !h) return LR_ERR_ARG;
+lr_status check_step(const lr_layer_weights* w, const StepIn& s, const float* h) {
+  if (!w || !h) return LR_ERR_ARG;
   if (w->d_model <= 0 || w->n_heads <= 0 || w->n_kv_heads <= 0 || w->d_ffn <= 0) return LR_ERR_ARG;
   if (w->head_dim != 64 && w->head_dim != 128) return LR_ERR_UNSUPPORTED;
   if (w->n_heads % w->n_kv_heads) return LR_ERR_ARG;
-  if (s->B <= 0 || s->cap <= 0 || s->max_seq_rows <= 0 || s->pool_rows <= 0) return LR_ERR_ARG;
-  if (s->cap > INT32_MAX) return LR_ERR_ARG;
-  if (s->B > 64) return LR_ERR_UNSUPPORTED;  // projections run on the decode path
+  if (s.T <= 0 || s.S <= 0 || s.cap <= 0 || s.max_seq_rows <= 0 || s.pool_rows <= 0)
+    return LR_ERR_ARG;
+  if (s.cap > INT32_MAX || s.T > INT32_MAX) return LR_ERR_ARG;
+  if (s.S > 255) return LR_ERR_UNSUPPORTED;  // the rotary epilogue stages S + 1 offsets
   if (!w->rope || w->rope_max_pos <= 0 || !w->attn_norm || !w->ffn_norm) return LR_ERR_ARG;
-  if (!s->k_pool || !s->v_pool || !s->slot_mapping || !s->remap || !s->seq_off || !s->pos ||
-      !s->n_valid)
+  if (!s.k_pool || !s.v_pool || !s.slot_mapping || !s.remap || !s.seq_off || !s.pos ||
+      !s.n_valid)
     return LR_ERR_ARG;
   const int64_t dq = w->n_heads * w->head_dim, dkv = w->n_kv_heads * w->head_dim;
   const int64_t din[7] = {w->d_model, w->d_model, w->d_model, dq, w->d_model, w->d_model, w->d_ffn};
-  const int64_t dout[7] = {dq, dkv, dkv, w->d_model, w->d_ffn, w->d_ffn, w->d_model};
   if (w->mlp != LR_MLP_SWIGLU && w->mlp != LR_MLP_RELU) return LR_ERR_ARG;
   for (int k = 0; k < 7; ++k) {
     if (k == 5 && w->mlp == LR_MLP_RELU) continue;  // no up projection
     if (!w->Ut[k] || !w->Vt[k] || w->r[k] <= 0) return LR_ERR_ARG;
     if (w->ldu[k] < din[k] || w->ldv[k] < w->r[k]) return LR_ERR_ARG;
     if (!al16(w->Ut[k]) || !al16(w->Vt[k]) || w->ldu[k] % 8 || w->ldv[k] % 8) return LR_ERR_ALIGN;
-    if (w->ldu[k] >= (1 << 24) || w->ldv[k] >= (1 << 24) || din[k] >= (1 << 24))
+    if (w->ldu[k] >= (1 << 22) || w->ldv[k] >= (1 << 22) || din[k] >= (1 << 22))
       return LR_ERR_UNSUPPORTED;
   }
-  if (s->pool_ld < w->r[1] || s->pool_ld < w->r[2]) return LR_ERR_ARG;
+  (void)dkv;
+  if (s.pool_ld < w->r[1] || s.pool_ld < w->r[2]) return LR_ERR_ARG;
   // the reconstruction's rotary epilogue copies (cos, sin) rows in 16-byte
   // chunks, addressed with 32-bit offsets
   if (!al16(w->rope)) return LR_ERR_ALIGN;
@@ -322,8 +389,155 @@ lr_status check_step(const lr_layer_weights* w, const lr_decode_state* s, const 
   if (!gemm_big_supported(rup(w->r[1], 8), w->ldv[1]) ||
       !gemm_big_supported(rup(w->r[2], 8), w->ldv[2]))
     return LR_ERR_UNSUPPORTED;
-  if (!al16(s->k_pool) || !al16(s->v_pool) || s->pool_ld % 8) return LR_ERR_ALIGN;
+  if (!al16(s.k_pool) || !al16(s.v_pool) || s.pool_ld % 8) return LR_ERR_ALIGN;
   if (w->d_model % 8 || w->d_ffn % 8) return LR_ERR_ALIGN;
+  return LR_OK;
+}
+
+lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void* workspace,
+                     size_t workspace_bytes, hipStream_t st) {
+  const StepLayout L = step_layout(w, s);
+  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return LR_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const int T = (int)s.T;
+  const bool dec = s.T <= kDecodeTokens;
+  const int64_t d = w->d_model, dq = w->n_heads * w->head_dim, ffn = w->d_ffn;
+  uint16_t* x = reinterpret_cast<uint16_t*>(ws + L.x);
+  uint16_t* q = reinterpret_cast<uint16_t*>(ws + L.q);
+  float* latk = reinterpret_cast<float*>(ws + L.latk);
+  float* latv = reinterpret_cast<float*>(ws + L.latv);
+  uint16_t* kbuf = reinterpret_cast<uint16_t*>(ws + L.kbuf);
+  uint16_t* vbuf = reinterpret_cast<uint16_t*>(ws + L.vbuf);
+  uint16_t* krec = reinterpret_cast<uint16_t*>(ws + L.krec);
+  uint16_t* vrec = reinterpret_cast<uint16_t*>(ws + L.vrec);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  uint16_t* o = reinterpret_cast<uint16_t*>(ws + L.o);
+  uint16_t* gate = reinterpret_cast<uint16_t*>(ws + L.gate);
+  uint16_t* up = reinterpret_cast<uint16_t*>(ws + L.up);
+  uint16_t* m = reinterpret_cast<uint16_t*>(ws + L.m);
+  uint16_t* yb = reinterpret_cast<uint16_t*>(ws + L.yb);
+  void* lin = ws + L.lin;
+  hipError_t e = hipSuccess;
+#define LR_CHECK(expr)                \
+  do {                                \
+    e = (expr);                       \
+    if (e != hipSuccess) return LR_ERR_HIP; \
+  } while (0)
+
+  auto linear = [&](int k, const void* in, int64_t din, int64_t ldin, int64_t dout, void* y,
+                    float* yacc, float* t_out) -> DecodeLinear {
+    DecodeLinear dl{};
+    dl.T = T;
+    dl.d_in = din;
+    dl.r = w->r[k];
+    dl.d_out = dout;
+    dl.x = in;
+    dl.ldx = ldin;
+    dl.Ut = w->Ut[k];
+    dl.ldu = w->ldu[k];
+    dl.Vt = w->Vt[k];
+    dl.ldv = w->ldv[k];
+    dl.y = y;
+    dl.ldy = dout;
+    dl.t_io = t_out;
+    dl.ldt = w->r[k];
+    dl.flags = t_out ? 1u : 0u;
+    dl.workspace = lin;
+    dl.y_acc = yacc;
+    dl.ld_acc = d;
+    return dl;
+  };
+  const unsigned eb = (unsigned)((T * d + 255) / 256 < 4096 ? (T * d + 255) / 256 : 4096);
+  // y = in . U_r V_r added into the residual h: in the decode kernel's
+  // epilogue, or (prefill path) through a bf16 y and an add
+  auto residual_linear = [&](int k, const void* in, int64_t din) -> hipError_t {
+    if (dec) return decode_linear_bf16(linear(k, in, din, din, d, nullptr, h, nullptr), st);
+    hipError_t r = prefill_linear_bf16(linear(k, in, din, din, d, yb, nullptr, nullptr), st);
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL(add_residual_kernel, dim3(eb), dim3(256), 0, st, h, yb, (int64_t)T * d);
+    return hipGetLastError();
+  };
+
+  // attention block
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, st, h, d,
+                     static_cast<const uint16_t*>(w->attn_norm), x, d, (int)d, w->eps);
+  LR_CHECK(hipGetLastError());
+  {
+    // q (full) and the k, v latents (stage 1 only) read the same x
+    const DecodeLinear qkv[3] = {linear(0, x, d, d, dq, q, nullptr, nullptr),
+                                 linear(1, x, d, d, L.dkv, nullptr, nullptr, latk),
+                                 linear(2, x, d, d, L.dkv, nullptr, nullptr, latv)};
+    if (dec) {
+      LR_CHECK(decode_group_bf16(qkv, 3, st));  // one launch
+    } else {
+      for (int k = 0; k < 3; ++k) LR_CHECK(prefill_linear_bf16(qkv[k], st));
+    }
+  }
+  hipLaunchKernelGGL(append_kernel, dim3(T), dim3(256), 0, st, latk, w->r[1], (int)w->r[1],
+                     s.slot_mapping, s.pool_rows, static_cast<uint16_t*>(s.k_pool), s.pool_ld);
+  LR_CHECK(hipGetLastError());
+  hipLaunchKernelGGL(append_kernel, dim3(T), dim3(256), 0, st, latv, w->r[2], (int)w->r[2],
+                     s.slot_mapping, s.pool_rows, static_cast<uint16_t*>(s.v_pool), s.pool_ld);
+  LR_CHECK(hipGetLastError());
+  LR_CHECK(remap_gather(2, s.k_pool, s.pool_rows, s.pool_ld, s.remap, s.cap, s.n_valid,
+                        w->r[1], kbuf, L.rk_ld, st));
+  LR_CHECK(remap_gather(2, s.v_pool, s.pool_rows, s.pool_ld, s.remap, s.cap, s.n_valid,
+                        w->r[2], vbuf, L.rv_ld, st));
+  // rec[j, :] = buf[j, 0:r] . Vt^T for the live rows j < *n_valid: the
+  // fixed-size GEMM of the replay stage (grid from the capacity), K rows
+  // rotated by their positions in the epilogue.
+  {
+    const BigRope rope{w->rope, w->rope_max_pos, s.seq_off, (int)s.S, (int)w->head_dim};
+    LR_CHECK(gemm_nt_big_rows(kbuf, L.rk_ld, w->Vt[1], w->ldv[1], krec, L.dkv, s.cap, s.n_valid,
+                              L.dkv, w->r[1], &rope, st));
+    LR_CHECK(gemm_nt_big_rows(vbuf, L.rv_ld, w->Vt[2], w->ldv[2], vrec, L.dkv, s.cap, s.n_valid,
+                              L.dkv, w->r[2], nullptr, st));
+  }
+  const dim3 agrid((unsigned)L.nch, (unsigned)w->n_heads, (unsigned)T);
+  const int S = (int)s.S;
+  if (w->head_dim == 128) {
+    hipLaunchKernelGGL(attn_partial_kernel<128>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
+                       L.dkv, s.seq_off, s.tok_seq, S, s.pos, w->rope, w->rope_max_pos,
+                       (int)w->n_heads, (int)w->n_kv_heads, (int)L.nch, (int)s.cap, part);
+    LR_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)w->n_heads, (unsigned)T),
+                       dim3(128), 0, st, part, (int)w->n_heads, (int)L.nch, s.seq_off, s.tok_seq,
+                       S, s.pos, (int)s.cap, o, dq);
+  } else {
+    hipLaunchKernelGGL(attn_partial_kernel<64>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
+                       L.dkv, s.seq_off, s.tok_seq, S, s.pos, w->rope, w->rope_max_pos,
+                       (int)w->n_heads, (int)w->n_kv_heads, (int)L.nch, (int)s.cap, part);
+    LR_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)w->n_heads, (unsigned)T),
+                       dim3(64), 0, st, part, (int)w->n_heads, (int)L.nch, s.seq_off, s.tok_seq,
+                       S, s.pos, (int)s.cap, o, dq);
+  }
+  LR_CHECK(hipGetLastError());
+  LR_CHECK(residual_linear(3, o, dq));
+  // MLP block
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, st, h, d,
+                     static_cast<const uint16_t*>(w->ffn_norm), x, d, (int)d, w->eps);
+  LR_CHECK(hipGetLastError());
+  const dim3 egrid((unsigned)((T * ffn + 255) / 256 < 4096 ? (T * ffn + 255) / 256 : 4096));
+  if (w->mlp == LR_MLP_RELU) {
+    const DecodeLinear fc1 = linear(4, x, d, d, ffn, gate, nullptr, nullptr);
+    LR_CHECK(dec ? decode_linear_bf16(fc1, st) : prefill_linear_bf16(fc1, st));
+    hipLaunchKernelGGL(relu_kernel, egrid, dim3(256), 0, st, gate, m, (int64_t)T * ffn);
+  } else {
+    const DecodeLinear gu[2] = {linear(4, x, d, d, ffn, gate, nullptr, nullptr),
+                                linear(5, x, d, d, ffn, up, nullptr, nullptr)};
+    if (dec) {
+      LR_CHECK(decode_group_bf16(gu, 2, st));
+    } else {
+      LR_CHECK(prefill_linear_bf16(gu[0], st));
+      LR_CHECK(prefill_linear_bf16(gu[1], st));
+    }
+    hipLaunchKernelGGL(silu_mul_kernel, egrid, dim3(256), 0, st, gate, up, m, (int64_t)T * ffn);
+  }
+  LR_CHECK(hipGetLastError());
+  LR_CHECK(residual_linear(6, m, ffn));
+#undef LR_CHECK
   return LR_OK;
 }
 
@@ -347,131 +561,35 @@ extern "C" lr_status lowrank_rope_table(int64_t head_dim, int64_t max_pos, float
 extern "C" size_t lowrank_decode_step_workspace_bytes(const lr_layer_weights* w,
                                                       const lr_decode_state* s) {
   if (!w || !s || s->B <= 0 || s->cap <= 0 || s->max_seq_rows <= 0) return 0;
-  return step_layout(w, s).total;
+  return step_layout(w, from_decode(s)).total;
 }
 
 extern "C" lr_status lowrank_layer_decode_step(const lr_layer_weights* w,
                                                const lr_decode_state* s, float* h,
                                                void* workspace, size_t workspace_bytes,
                                                hipStream_t st) {
-  const lr_status chk = check_step(w, s, h);
+  if (!s) return LR_ERR_ARG;
+  if (s->B > 64) return LR_ERR_UNSUPPORTED;  // projections run on the decode path
+  const StepIn in = from_decode(s);
+  const lr_status chk = check_step(w, in, h);
   if (chk != LR_OK) return chk;
-  const StepLayout L = step_layout(w, s);
-  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
-    return LR_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  const int B = (int)s->B;
-  const int64_t d = w->d_model, dq = w->n_heads * w->head_dim, ffn = w->d_ffn;
-  uint16_t* x = reinterpret_cast<uint16_t*>(ws + L.x);
-  uint16_t* q = reinterpret_cast<uint16_t*>(ws + L.q);
-  float* latk = reinterpret_cast<float*>(ws + L.latk);
-  float* latv = reinterpret_cast<float*>(ws + L.latv);
-  uint16_t* kbuf = reinterpret_cast<uint16_t*>(ws + L.kbuf);
-  uint16_t* vbuf = reinterpret_cast<uint16_t*>(ws + L.vbuf);
-  uint16_t* krec = reinterpret_cast<uint16_t*>(ws + L.krec);
-  uint16_t* vrec = reinterpret_cast<uint16_t*>(ws + L.vrec);
-  float* part = reinterpret_cast<float*>(ws + L.part);
-  uint16_t* o = reinterpret_cast<uint16_t*>(ws + L.o);
-  uint16_t* gate = reinterpret_cast<uint16_t*>(ws + L.gate);
-  uint16_t* up = reinterpret_cast<uint16_t*>(ws + L.up);
-  uint16_t* m = reinterpret_cast<uint16_t*>(ws + L.m);
-  void* lin = ws + L.lin;
-  hipError_t e = hipSuccess;
-#define LR_CHECK(expr)                \
-  do {                                \
-    e = (expr);                       \
-    if (e != hipSuccess) return LR_ERR_HIP; \
-  } while (0)
+  return layer_step(w, in, h, workspace, workspace_bytes, st);
+}
 
-  auto linear = [&](int k, const void* in, int64_t din, int64_t ldin, int64_t dout, void* y,
-                    float* yacc, float* t_out) -> DecodeLinear {
-    DecodeLinear dl{};
-    dl.T = B;
-    dl.d_in = din;
-    dl.r = w->r[k];
-    dl.d_out = dout;
-    dl.x = in;
-    dl.ldx = ldin;
-    dl.Ut = w->Ut[k];
-    dl.ldu = w->ldu[k];
-    dl.Vt = w->Vt[k];
-    dl.ldv = w->ldv[k];
-    dl.y = y;
-    dl.ldy = dout;
-    dl.t_io = t_out;
-    dl.ldt = w->r[k];
-    dl.flags = t_out ? 1u : 0u;
-    dl.workspace = lin;
-    dl.y_acc = yacc;
-    dl.ld_acc = d;
-    return dl;
-  };
+extern "C" size_t lowrank_prefill_step_workspace_bytes(const lr_layer_weights* w,
+                                                       const lr_prefill_state* s) {
+  if (!w || !s || s->T <= 0 || s->S <= 0 || s->cap <= 0 || s->max_seq_rows <= 0) return 0;
+  return step_layout(w, from_prefill(s)).total;
+}
 
-  // attention block
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(B), dim3(256), 0, st, h, d,
-                     static_cast<const uint16_t*>(w->attn_norm), x, d, (int)d, w->eps);
-  LR_CHECK(hipGetLastError());
-  {
-    // q (full) and the k, v latents (stage 1 only) read the same x: one launch
-    const DecodeLinear qkv[3] = {linear(0, x, d, d, dq, q, nullptr, nullptr),
-                                 linear(1, x, d, d, L.dkv, nullptr, nullptr, latk),
-                                 linear(2, x, d, d, L.dkv, nullptr, nullptr, latv)};
-    LR_CHECK(decode_group_bf16(qkv, 3, st));
-  }
-  hipLaunchKernelGGL(append_kernel, dim3(B), dim3(256), 0, st, latk, w->r[1], (int)w->r[1],
-                     s->slot_mapping, s->pool_rows, static_cast<uint16_t*>(s->k_pool), s->pool_ld);
-  LR_CHECK(hipGetLastError());
-  hipLaunchKernelGGL(append_kernel, dim3(B), dim3(256), 0, st, latv, w->r[2], (int)w->r[2],
-                     s->slot_mapping, s->pool_rows, static_cast<uint16_t*>(s->v_pool), s->pool_ld);
-  LR_CHECK(hipGetLastError());
-  LR_CHECK(remap_gather(2, s->k_pool, s->pool_rows, s->pool_ld, s->remap, s->cap, s->n_valid,
-                        w->r[1], kbuf, L.rk_ld, st));
-  LR_CHECK(remap_gather(2, s->v_pool, s->pool_rows, s->pool_ld, s->remap, s->cap, s->n_valid,
-                        w->r[2], vbuf, L.rv_ld, st));
-  // rec[j, :] = buf[j, 0:r] . Vt^T for the live rows j < *n_valid: the
-  // fixed-size GEMM of the replay stage (grid from the capacity), K rows
-  // rotated by their positions in the epilogue.
-  {
-    const BigRope rope{w->rope, w->rope_max_pos, s->seq_off, (int)B, (int)w->head_dim};
-    LR_CHECK(gemm_nt_big_rows(kbuf, L.rk_ld, w->Vt[1], w->ldv[1], krec, L.dkv, s->cap, s->n_valid,
-                              L.dkv, w->r[1], &rope, st));
-    LR_CHECK(gemm_nt_big_rows(vbuf, L.rv_ld, w->Vt[2], w->ldv[2], vrec, L.dkv, s->cap, s->n_valid,
-                              L.dkv, w->r[2], nullptr, st));
-  }
-  const dim3 agrid((unsigned)L.nch, (unsigned)w->n_heads, (unsigned)B);
-  if (w->head_dim == 128) {
-    hipLaunchKernelGGL(attn_partial_kernel<128>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
-                       L.dkv, s->seq_off, s->pos, w->rope, w->rope_max_pos, (int)w->n_heads,
-                       (int)w->n_kv_heads, (int)L.nch, (int)s->cap, part);
-    LR_CHECK(hipGetLastError());
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)w->n_heads, (unsigned)B),
-                       dim3(128), 0, st, part, (int)w->n_heads, (int)L.nch, s->seq_off, (int)s->cap, o, dq);
-  } else {
-    hipLaunchKernelGGL(attn_partial_kernel<64>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
-                       L.dkv, s->seq_off, s->pos, w->rope, w->rope_max_pos, (int)w->n_heads,
-                       (int)w->n_kv_heads, (int)L.nch, (int)s->cap, part);
-    LR_CHECK(hipGetLastError());
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)w->n_heads, (unsigned)B),
-                       dim3(64), 0, st, part, (int)w->n_heads, (int)L.nch, s->seq_off, (int)s->cap, o, dq);
-  }
-  LR_CHECK(hipGetLastError());
-  LR_CHECK(decode_linear_bf16(linear(3, o, dq, dq, d, nullptr, h, nullptr), st));
-  // MLP block
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(B), dim3(256), 0, st, h, d,
-                     static_cast<const uint16_t*>(w->ffn_norm), x, d, (int)d, w->eps);
-  LR_CHECK(hipGetLastError());
-  const dim3 egrid((unsigned)((B * ffn + 255) / 256 < 4096 ? (B * ffn + 255) / 256 : 4096));
-  if (w->mlp == LR_MLP_RELU) {
-    LR_CHECK(decode_linear_bf16(linear(4, x, d, d, ffn, gate, nullptr, nullptr), st));
-    hipLaunchKernelGGL(relu_kernel, egrid, dim3(256), 0, st, gate, m, (int64_t)B * ffn);
-  } else {
-    const DecodeLinear gu[2] = {linear(4, x, d, d, ffn, gate, nullptr, nullptr),
-                                linear(5, x, d, d, ffn, up, nullptr, nullptr)};
-    LR_CHECK(decode_group_bf16(gu, 2, st));
-    hipLaunchKernelGGL(silu_mul_kernel, egrid, dim3(256), 0, st, gate, up, m, (int64_t)B * ffn);
-  }
-  LR_CHECK(hipGetLastError());
-  LR_CHECK(decode_linear_bf16(linear(6, m, ffn, ffn, d, nullptr, h, nullptr), st));
-#undef LR_CHECK
-  return LR_OK;
+extern "C" lr_status lowrank_layer_prefill_step(const lr_layer_weights* w,
+                                                const lr_prefill_state* s, float* h,
+                                                void* workspace, size_t workspace_bytes,
+                                                hipStream_t st) {
+  if (!s) return LR_ERR_ARG;
+  if (!s->tok_seq) return LR_ERR_ARG;
+  const StepIn in = from_prefill(s);
+  const lr_status chk = check_step(w, in, h);
+  if (chk != LR_OK) return chk;
+  return layer_step(w, in, h, workspace, workspace_bytes, st);
 }

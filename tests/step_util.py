@@ -111,3 +111,65 @@ class Step:
     def oracle(self, seqs=None):
         return oracle.decode_step(self.h0, self.layers, self.pools_np_k, self.pools_np_v,
                                   self.tables, self.lengths, self.block, self.cfg, seqs)
+
+
+class Prefill:
+    """One chunked-prefill step: S sequences with cached lengths append
+    chunks[i] prompt tokens each; n_layers layers; paged latent pools with
+    seeded placement (the pools hold the cached rows' latents)."""
+
+    def __init__(self, cfg_id, cfg, ranks, lengths, chunks, n_layers, block=16, fast=False):
+        self.cfg, self.block = cfg, block
+        self.lengths = np.asarray(lengths, dtype=np.int64)
+        self.chunks = np.asarray(chunks, dtype=np.int64)
+        rows = self.lengths + self.chunks
+        # block_tables covers its lengths + 1 rows
+        self.tables, nblocks = synth.block_tables(synth.seed_of(cfg_id, 0, 1, synth.KIND_PLACE),
+                                                  rows - 1, block, slack_blocks=3)
+        self.pool_rows = nblocks * block
+        self.max_seq_rows = int(rows.max())
+        self.cap = int(rows.sum() + 37)
+        self.pool_ld = ld8(max(ranks["k"], ranks["v"]), 8)
+        d = dev()
+        self.rope = torch.empty((self.max_seq_rows, cfg["head_dim"] // 2, 2), dtype=torch.float32,
+                                device=d)
+        lr.lowrank_rope_table(cfg["head_dim"], self.max_seq_rows, 10000.0, self.rope)
+        self.layers, self.weights = [], []
+        self.pools_np_k, self.pools_np_v, self.pools_k, self.pools_v = [], [], [], []
+        for li in range(n_layers):
+            vals, Ut, Vt, g1, g2 = make_layer(cfg_id, li, cfg, ranks, fast)
+            self.layers.append(vals)
+            self.weights.append(lr.layer_weights(cfg, Ut, Vt, g1, g2, self.rope,
+                                                 self.max_seq_rows))
+            for kind, store_np, store in ((0, self.pools_np_k, self.pools_k),
+                                          (1, self.pools_np_v, self.pools_v)):
+                g = synth.rng(synth.seed_of(cfg_id, li, kind, synth.KIND_LAT))
+                bits = synth.bf16_bits(g.standard_normal((self.pool_rows, self.pool_ld)))
+                store_np.append(synth.bf16_value(bits))
+                store.append(to_dev(bits, "bf16"))
+        T = int(self.chunks.sum())
+        h0 = synth.tokens(synth.seed_of(cfg_id, 0, 1, synth.KIND_X), T, cfg["d_model"])
+        self.h0 = h0.astype(np.float32).astype(np.float64)
+        self.h = torch.from_numpy(self.h0.astype(np.float32)).to(d)
+        prep = lr.lowrank_prepare_prefill(self.lengths, self.chunks, self.tables, block, self.cap)
+        self.prep = prep
+        dp = {k: torch.from_numpy(np.ascontiguousarray(prep[k])).to(d)
+              for k in ("remap", "seq_off", "tok_seq", "pos", "slot_mapping")}
+        self.n_valid = torch.tensor([prep["n_valid"]], dtype=torch.int32, device=d)
+        self.states = [lr.prefill_state(self.pools_k[li], self.pools_v[li], dp["slot_mapping"],
+                                        dp["remap"], dp["seq_off"], dp["tok_seq"], dp["pos"],
+                                        self.n_valid, self.max_seq_rows)
+                       for li in range(n_layers)]
+        self._dp = dp
+        nbytes = max(lr.lowrank_prefill_step_workspace_bytes(w, s)
+                     for w, s in zip(self.weights, self.states))
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=d)
+
+    def run(self):
+        for w, s in zip(self.weights, self.states):
+            lr.lowrank_layer_prefill_step(w, s, self.h, self.ws)
+        return self.h
+
+    def oracle(self):
+        return oracle.prefill_step(self.h0, self.layers, self.pools_np_k, self.pools_np_v,
+                                   self.tables, self.lengths, self.chunks, self.block, self.cfg)

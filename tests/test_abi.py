@@ -25,6 +25,7 @@ def header_functions():
 def test_header_declares_the_boundary():
     names = header_functions()
     for n in ("lowrank_linear_forward", "kv_remap_gather", "lowrank_prepare_decode",
+              "lowrank_prepare_prefill", "lowrank_layer_prefill_step",
               "lowrank_workspace_bytes", "lowrank_status_string", "lowrank_version"):
         assert n in names
 
@@ -116,7 +117,8 @@ def test_struct_layouts_match_the_library():
     assert lib.lowrank_abi_sizeof(0) == ctypes.sizeof(lr.LayerWeights)
     assert lib.lowrank_abi_sizeof(1) == ctypes.sizeof(lr.DecodeState)
     assert lib.lowrank_abi_sizeof(2) == ctypes.sizeof(_lib.Linear)
-    assert lib.lowrank_abi_sizeof(3) == 0
+    assert lib.lowrank_abi_sizeof(3) == ctypes.sizeof(lr.PrefillState)
+    assert lib.lowrank_abi_sizeof(4) == 0
 
 
 def test_decode_step_rejects_bad_arguments():
@@ -231,3 +233,32 @@ def test_decode_step_relu_mlp_needs_no_up_projection():
                                          None) == _lib.LR_ERR_ARG     # SwiGLU needs slot 5
     w2, s2 = _valid_step_structs()
     assert 0 < relu_ws < lib.lowrank_decode_step_workspace_bytes(C.byref(w2), C.byref(s2))
+
+
+def _valid_prefill_state(T=300, S=4):
+    _, s = _valid_step_structs()
+    p = lr.PrefillState()
+    p.k_pool, p.v_pool, p.pool_rows, p.pool_ld = s.k_pool, s.v_pool, s.pool_rows, s.pool_ld
+    p.slot_mapping = p.remap = p.seq_off = p.tok_seq = p.pos = p.n_valid = A16
+    p.T, p.S, p.cap, p.max_seq_rows = T, S, 4 * 4112, 4112
+    return p
+
+
+@pytest.mark.parametrize("field,value,status", [
+    (None, None, _lib.LR_ERR_WORKSPACE),          # valid; no workspace given
+    ("tok_seq", None, _lib.LR_ERR_ARG),
+    ("S", 256, _lib.LR_ERR_UNSUPPORTED),          # rotary epilogue stages S + 1 offsets
+    ("T", 0, _lib.LR_ERR_ARG),
+])
+def test_prefill_step_host_checks(field, value, status):
+    w, _ = _valid_step_structs()
+    p = _valid_prefill_state()
+    if field is not None:
+        setattr(p, field, value)
+    lib = lr.load()
+    assert lib.lowrank_layer_prefill_step(C.byref(w), C.byref(p), C.c_void_p(A16), None, 0,
+                                          None) == status
+    if field is None:
+        # 300 tokens take the prefill path: more scratch than a 64-token chunk
+        small = lib.lowrank_prefill_step_workspace_bytes(C.byref(w), C.byref(_valid_prefill_state(64)))
+        assert lib.lowrank_prefill_step_workspace_bytes(C.byref(w), C.byref(p)) > small > 0

@@ -331,3 +331,27 @@ def test_decode_layer_placement_invariance_and_L0():
     mlp = ((oracle.silu((x2 @ w["U"]["gate"]) @ w["V"]["gate"]) *
             ((x2 @ w["U"]["up"]) @ w["V"]["up"])) @ w["U"]["down"]) @ w["V"]["down"]
     assert _rel(outs[0][1], h_attn + mlp) <= 1e-12
+
+
+@pytest.mark.parametrize("mlp,Hkv", [("swiglu", 4), ("relu", 2)])
+def test_prefill_layer_equals_token_by_token_decode(mlp, Hkv):
+    # a causal chunk is the same as decoding its tokens one after another,
+    # each appending its latents before the next one runs
+    d, dff, H, hd, L, c = 32, 48, 4, 8, 5, 4
+    cfg = {"n_heads": H, "n_kv_heads": Hkv, "head_dim": hd, "mlp": mlp}
+    w, _ = _tiny_layer_weights(300 + Hkv, d, dff, Hkv, hd, full_rank=False)
+    g = np.random.default_rng(12)
+    rk, rv = w["U"]["k"].shape[1], w["U"]["v"].shape[1]
+    lat_k, lat_v = g.standard_normal((L, rk)), g.standard_normal((L, rv))
+    Hin = g.standard_normal((c, d))
+    out, lk, lv = oracle.prefill_layer_seq(Hin, w, lat_k, lat_v, L, cfg)
+    ck, cv = lat_k, lat_v
+    for j in range(c):
+        o, k1, v1 = oracle.decode_layer_seq(Hin[j], w, ck, cv, L + j, cfg)
+        assert _rel(out[j], o) <= 1e-12
+        assert np.allclose(lk[j], k1) and np.allclose(lv[j], v1)
+        ck, cv = np.vstack([ck, k1[None]]), np.vstack([cv, v1[None]])
+    # L = 0, c = 1: attention over the token itself, as in the decode pin
+    o1, _, _ = oracle.prefill_layer_seq(Hin[:1], w, lat_k[:0], lat_v[:0], 0, cfg)
+    o2, _, _ = oracle.decode_layer_seq(Hin[0], w, lat_k[:0], lat_v[:0], 0, cfg)
+    assert _rel(o1[0], o2) <= 1e-12
