@@ -9,8 +9,10 @@ MALL), so weights stream from HBM as in a real 32-layer decode.
 
 Prints one JSON line: whole-job tokens/s (tokens x layer sets / s), the
 roofline of the dominant launch, and the fp64 CPU oracle timed on a bounded
-sample of the same workload.  Also reports the prefill configuration (16384
-rows, ratio 0.4 and 0.2) under "prefill" as context.
+sample of the same workload.  Also reports, as context: the prefill
+configuration (16384 rows, ratio 0.4 and 0.2) under "prefill", the 32-layer
+decode step under "decode_step", and the 32-layer chunked-prefill step (8
+prompts of 512 tokens) under "prefill_step".
 """
 from __future__ import annotations
 
@@ -131,6 +133,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-step", action="store_true", help="skip the 32-layer decode step")
+    ap.add_argument("--no-prefill-step", action="store_true",
+                    help="skip the 32-layer chunked-prefill step")
     ap.add_argument("--step-layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--layout", choices=("packed", "rowmajor"), default="packed",
@@ -306,6 +310,12 @@ def main():
                                             max(3, args.steps // 2))
         log("decode-step leg done")
 
+    if not args.no_prefill_step:
+        torch.cuda.empty_cache()
+        result["prefill_step"] = prefill_step(torch, lr, dev, stream, args.step_layers,
+                                              max(3, args.steps // 2))
+        log("prefill-step leg done")
+
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
         log("cpu baseline done")
@@ -442,6 +452,76 @@ def decode_step(torch, lr, dev, stream, n_layers, reps):
                                   "recon": round(1e6 * max(recon_flops / BF16_PEAK,
                                                            recon_bytes / HBM_PEAK), 2),
                                   "attention": round(1e6 * attn_bytes / HBM_PEAK, 2)}}
+
+
+def prefill_step(torch, lr, dev, stream, n_layers, reps, S=8, chunk=512):
+    """The chunked-prefill step of the same 32-layer decoder (ratio 0.2):
+    S new prompts of `chunk` tokens each (no cached rows) through every
+    layer, one lowrank_layer_prefill_step call per layer; tokens/s and the
+    MFMA roofline of the step's flops (projections, reconstruction, causal
+    attention)."""
+    from synth.decode_step import DecodeStepInputs, dims
+    si = DecodeStepInputs(n_layers=n_layers, device=dev)
+    c = si.cfg
+    lengths = np.zeros(S, np.int64)
+    chunks = np.full(S, chunk, np.int64)
+    import synth
+    tables, nblocks = synth.block_tables(synth.seed_of(5, 0, 2, synth.KIND_PLACE),
+                                         chunks - 1, si.block, slack_blocks=4)
+    pool_rows = nblocks * si.block
+    max_rows = chunk
+    cap = S * chunk
+    prep = lr.lowrank_prepare_prefill(lengths, chunks, tables, si.block, cap)
+    dp = {k: torch.from_numpy(np.ascontiguousarray(prep[k])).to(dev)
+          for k in ("remap", "seq_off", "tok_seq", "pos", "slot_mapping")}
+    nv = torch.tensor([prep["n_valid"]], dtype=torch.int32, device=dev)
+    rope = torch.empty((max_rows, c["head_dim"] // 2, 2), dtype=torch.float32, device=dev)
+    lr.lowrank_rope_table(c["head_dim"], max_rows, 10000.0, rope)
+    layers = []
+    for li in range(n_layers):
+        Ut, Vt, g1, g2 = si.device_layer(li)
+        w = lr.layer_weights(c, Ut, Vt, g1, g2, rope, max_rows)
+        pk = torch.zeros((pool_rows, si.pool_ld), dtype=torch.bfloat16, device=dev)
+        pv = torch.zeros_like(pk)
+        st = lr.prefill_state(pk, pv, dp["slot_mapping"], dp["remap"], dp["seq_off"],
+                              dp["tok_seq"], dp["pos"], nv, max_rows)
+        layers.append((w, st))
+    ws = torch.zeros(lr.lowrank_prefill_step_workspace_bytes(*layers[0]), dtype=torch.uint8,
+                     device=dev)
+    T = int(chunks.sum())
+    g = torch.Generator(device=dev).manual_seed(4_000_001)
+    h0 = torch.randn((T, c["d_model"]), generator=g, device=dev)
+    h = h0.clone()
+
+    def step():
+        h.copy_(h0)
+        for w, st in layers:
+            lr.lowrank_layer_prefill_step(w, st, h, ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    dkv = c["n_kv_heads"] * c["head_dim"]
+    lin_fl = sum(2.0 * T * si.ranks[n] * (a_ + b_) for n, (a_, b_) in dims(c).items())
+    rec_fl = 2.0 * T * (si.ranks["k"] + si.ranks["v"]) * dkv
+    att_fl = 4.0 * c["n_heads"] * c["head_dim"] * S * chunk * (chunk + 1) / 2
+    per_layer = lin_fl + rec_fl + att_fl
+    roof_ms = 1e3 * n_layers * per_layer / BF16_PEAK
+    del layers, ws
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 3),
+            "layers": n_layers, "sequences": S, "chunk": chunk,
+            "roof_ms": round(roof_ms, 3), "frac": round(roof_ms / ms, 4),
+            "per_layer_gflop": {"linears": round(lin_fl / 1e9, 2),
+                                "recon": round(rec_fl / 1e9, 2),
+                                "attention": round(att_fl / 1e9, 2)}}
 
 
 def cpu_baseline(base, seconds):
