@@ -240,6 +240,241 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   }
 }
 
+// ---------------------------------------------------------------- prefill attention
+// tok_off[i] = first new token of sequence i (tokens come sequence by
+// sequence), tok_off[S] = T; a sequence without tokens gets an empty range.
+// One workgroup.
+__global__ __launch_bounds__(256) void tok_offsets_kernel(const int32_t* __restrict__ tok_seq,
+                                                          int T, int S,
+                                                          int32_t* __restrict__ tok_off) {
+  for (int i = threadIdx.x; i <= S; i += 256) tok_off[i] = T;
+  __syncthreads();
+  for (int t = threadIdx.x; t < T; t += 256) {
+    const int sq = tok_seq[t];
+    if (sq >= 0 && sq < S && (t == 0 || tok_seq[t - 1] != sq)) tok_off[sq] = t;
+  }
+}
+
+// Causal attention of a chunk of new tokens on MFMA 16x16x32 (flash style):
+// workgroup (q-block b, head h, sequence s) takes the sequence's new tokens
+// b*64 .. b*64+63, one 16-token slice per wave, and walks the sequence's
+// reconstructed K/V rows in 64-row tiles up to the block's last position.
+// Per tile: S = Q K^T (Q rotated and scaled in registers, K rows in LDS),
+// causal mask, online softmax (running max m and sum l per query row), P
+// through LDS into the MFMA A layout, O += P V (V transposed in LDS, its
+// 16-byte key chunks XOR-swizzled by d / 8 so the transposing writes spread
+// over the banks).  The next tile's K/V rows are loaded into registers while
+// the current one multiplies.  The C layouts of S and O give a lane the same
+// 4 query rows, so the softmax rescale of O needs no exchange.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(
+    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, int64_t ldkv, const int32_t* __restrict__ seq_off,
+    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ pos,
+    const float* __restrict__ rope, int64_t max_pos, int H, int Hkv, int cap,
+    uint16_t* __restrict__ o, int64_t ldo) {
+  constexpr int KS = HD / 32;  // k-steps of Q K^T
+  constexpr int NB = HD / 16;  // 16-column blocks of O
+  constexpr int KP = HD + 8;   // K tile pitch (elements)
+  constexpr int VP = 64 + 8;   // V^T tile pitch
+  constexpr int PP = 64 + 8;   // P pitch
+  __shared__ __attribute__((aligned(16))) uint16_t ktile[64 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[HD * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t ptile[4][16 * PP];
+  const int b = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = tok_off[sq], t1 = tok_off[sq + 1];
+  const int qt0 = t0 + b * 64;
+  if (qt0 >= t1) return;
+  const int beg = seq_off[sq];
+  if (beg < 0 || beg >= cap) return;      // offsets are device data: stay inside cap
+  int rows = seq_off[sq + 1] - beg;
+  rows = rows < cap - beg ? rows : cap - beg;
+  if (rows <= 0) return;
+  int plast = pos[min(qt0 + 63, t1 - 1)];
+  plast = plast < 0 ? 0 : (plast >= rows ? rows - 1 : plast);
+  const int nkt = (plast + 64) / 64;
+  const int kvh = h / (H / Hkv);
+  const float scale = 1.0f / sqrtf((float)HD);
+
+  // Q fragments: lane supplies query row (lane & 15) of its wave's slice and
+  // elements ks*32 + 8*(lane >> 4) .. +8; rotary pairs (i, i + HD/2) sit in
+  // k-steps ks and ks + KS/2 of the same lane
+  u32x4 qa[KS];
+  {
+    const int t = qt0 + wave * 16 + (lane & 15);
+    const bool ok = t < t1;
+    int p = ok ? pos[t] : 0;
+    p = p < 0 ? 0 : (p >= max_pos ? (int)max_pos - 1 : p);
+    float v[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 w = ok ? ldg16(q + (int64_t)t * ldq + h * HD + ks * 32 + 8 * (lane >> 4))
+                         : u32x4{0, 0, 0, 0};
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[ks][2 * e] = bf2f(ww[e] & 0xffffu);
+        v[ks][2 * e + 1] = bf2f(ww[e] >> 16);
+      }
+    }
+    const float* tb = rope + (int64_t)p * HD;  // (cos, sin) of frequency i at 2i
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = ks * 32 + 8 * (lane >> 4) + e;
+        const float c = tb[2 * i], sn = tb[2 * i + 1];
+        const float a0 = v[ks][e], b0 = v[ks + KS / 2][e];
+        v[ks][e] = a0 * c - b0 * sn;
+        v[ks + KS / 2][e] = b0 * c + a0 * sn;
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qa[ks] = u32x4{pack_bf2(v[ks][0] * scale, v[ks][1] * scale),
+                     pack_bf2(v[ks][2] * scale, v[ks][3] * scale),
+                     pack_bf2(v[ks][4] * scale, v[ks][5] * scale),
+                     pack_bf2(v[ks][6] * scale, v[ks][7] * scale)};
+  }
+  // this lane's output rows: 4*(lane >> 4) + v of the wave's slice
+  int rpos[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int t = qt0 + wave * 16 + 4 * (lane >> 4) + v;
+    rpos[v] = t < t1 ? pos[t] : 0;
+  }
+  float m[4], l[4];
+  f32x4 oacc[NB];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    m[v] = -INFINITY;
+    l[v] = 0.f;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* pw = ptile[wave];
+  // V^T element (d, key) in LDS: row d, 16-byte chunk (key / 8) ^ ((d / 8) & 7)
+  auto vt_at = [&](int d, int key) {
+    return d * VP + ((((key >> 3) ^ (d >> 3)) & 7) << 3) + (key & 7);
+  };
+  // tile staging: thread c holds K chunks (row c / (HD/8) + 16*i... ) and
+  // V chunks of two adjacent rows, coalesced 16-lane row segments
+  constexpr int KN = 64 * HD / 8 / 256, VN = 32 * HD / 8 / 256;
+  u32x4 kreg[KN], vreg[VN][2];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int c = threadIdx.x + 256 * i, r = c / (HD / 8), ch = c % (HD / 8), j = kt * 64 + r;
+      kreg[i] = j < rows ? ldg16(K + (int64_t)(beg + j) * ldkv + kvh * HD + ch * 8)
+                         : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < VN; ++i) {
+      const int c = threadIdx.x + 256 * i, pr = c / (HD / 8), ch = c % (HD / 8);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = kt * 64 + 2 * pr + u;
+        vreg[i][u] = j < rows ? ldg16(V + (int64_t)(beg + j) * ldkv + kvh * HD + ch * 8)
+                              : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int c = threadIdx.x + 256 * i, r = c / (HD / 8), ch = c % (HD / 8);
+      *reinterpret_cast<u32x4*>(ktile + r * KP + ch * 8) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VN; ++i) {
+      const int c = threadIdx.x + 256 * i, pr = c / (HD / 8), ch = c % (HD / 8);
+      const uint32_t a[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
+      const uint32_t b2[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // (V[2pr][d], V[2pr+1][d]) as one 4-byte word
+        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const uint32_t hi = (b2[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        *reinterpret_cast<uint32_t*>(vtile + vt_at(ch * 8 + e, 2 * pr)) = lo | (hi << 16);
+      }
+    }
+  };
+  load_tile(0);
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < nkt) load_tile(kt + 1);  // in flight while this tile multiplies
+    // S = Q K^T over the tile's 64 keys (4 column blocks)
+    f32x4 sacc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      sacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kb =
+            *reinterpret_cast<const u32x4*>(ktile + (cb * 16 + (lane & 15)) * KP + ks * 32 +
+                                            8 * (lane >> 4));
+        sacc[cb] = mfma16x16x32(qa[ks], kb, sacc[cb]);
+      }
+    }
+    // causal mask and online softmax; a row's 64 keys: 4 blocks x the 16
+    // lanes sharing lane >> 4
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float sv[4], mx = -INFINITY;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int j = kt * 64 + cb * 16 + (lane & 15);
+        sv[cb] = (j <= rpos[v] && j < rows) ? sacc[cb][v] : -INFINITY;
+        mx = fmaxf(mx, sv[cb]);
+      }
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x, 16));
+      const float mn = fmaxf(m[v], mx);
+      const float alpha = expf(m[v] - mn);  // 0 while m is still -inf
+      float rs = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const float pv = expf(sv[cb] - mn);
+        rs += pv;
+        pw[(4 * (lane >> 4) + v) * PP + cb * 16 + (lane & 15)] = (uint16_t)f2bf(pv);
+      }
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) rs += __shfl_xor(rs, x, 16);
+      l[v] = l[v] * alpha + rs;
+      m[v] = mn;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) oacc[nb][v] *= alpha;
+    }
+    // other lanes' P entries are read below: one wave's LDS accesses run in order
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+    // O += P V
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const u32x4 pa =
+          *reinterpret_cast<const u32x4*>(pw + (lane & 15) * PP + k2 * 32 + 8 * (lane >> 4));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x4 vb = *reinterpret_cast<const u32x4*>(
+            vtile + vt_at(nb * 16 + (lane & 15), k2 * 32 + 8 * (lane >> 4)));
+        oacc[nb] = mfma16x16x32(pa, vb, oacc[nb]);
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int t = qt0 + wave * 16 + 4 * (lane >> 4) + v;
+    if (t >= t1) continue;
+    const float inv = 1.0f / l[v];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      o[(int64_t)t * ldo + h * HD + nb * 16 + (lane & 15)] = (uint16_t)f2bf(oacc[nb][v] * inv);
+  }
+}
+
 // Combine the chunks of (sequence i, head h): o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
 template <int HD>
 __global__ __launch_bounds__(HD) void attn_combine_kernel(const float* __restrict__ part, int H,
@@ -300,7 +535,7 @@ StepIn from_prefill(const lr_prefill_state* s) {
 constexpr int64_t kDecodeTokens = 64;
 
 struct StepLayout {
-  size_t lin, x, q, latk, latv, kbuf, vbuf, krec, vrec, part, o, gate, up, m, yb, total;
+  size_t lin, x, q, latk, latv, kbuf, vbuf, krec, vrec, part, o, gate, up, m, yb, tok_off, total;
   int64_t rk_ld, rv_ld, dkv, nch;
 };
 
@@ -349,6 +584,7 @@ StepLayout step_layout(const lr_layer_weights* w, const StepIn& s) {
   L.up = w->mlp == LR_MLP_RELU ? L.gate : take(T * w->d_ffn * 2);
   L.m = take(T * w->d_ffn * 2);
   L.yb = dec ? L.m : take(T * d * 2);  // prefill path: o / down output before the residual add
+  L.tok_off = take((s.S + 1) * 4);     // chunked prefill: first token of each sequence
   L.total = off;
   return L;
 }
@@ -496,7 +732,21 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
   }
   const dim3 agrid((unsigned)L.nch, (unsigned)w->n_heads, (unsigned)T);
   const int S = (int)s.S;
-  if (w->head_dim == 128) {
+  if (s.tok_seq) {
+    // chunked prefill: tiled causal attention over each sequence's rows
+    int32_t* tok_off = reinterpret_cast<int32_t*>(ws + L.tok_off);
+    hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(256), 0, st, s.tok_seq, T, S, tok_off);
+    LR_CHECK(hipGetLastError());
+    const dim3 pgrid((unsigned)((T + 63) / 64), (unsigned)w->n_heads, (unsigned)S);
+    if (w->head_dim == 128)
+      hipLaunchKernelGGL(attn_prefill_kernel<128>, pgrid, dim3(256), 0, st, q, dq, krec, vrec,
+                         L.dkv, s.seq_off, tok_off, s.pos, w->rope, w->rope_max_pos,
+                         (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
+    else
+      hipLaunchKernelGGL(attn_prefill_kernel<64>, pgrid, dim3(256), 0, st, q, dq, krec, vrec,
+                         L.dkv, s.seq_off, tok_off, s.pos, w->rope, w->rope_max_pos,
+                         (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
+  } else if (w->head_dim == 128) {
     hipLaunchKernelGGL(attn_partial_kernel<128>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
                        L.dkv, s.seq_off, s.tok_seq, S, s.pos, w->rope, w->rope_max_pos,
                        (int)w->n_heads, (int)w->n_kv_heads, (int)L.nch, (int)s.cap, part);
