@@ -204,6 +204,9 @@ struct BigArgs {
   int64_t max_pos;
   const int32_t* seq_off;  // [nseq + 1] packed-row offsets: row m sits at position m - seq_off[i]
   int nseq;
+  int ksplit;              // K ranges (> 1: each writes an fp32 partial to c + range * split_stride)
+  int kchunk;              // elements of K per range (a multiple of 64)
+  int64_t split_stride;
 };
 
 template <int BN, int BK>
@@ -242,17 +245,19 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
     const int nv = *p.m_valid;
     M = nv < 0 ? 0 : (nv > p.M ? p.M : nv);
   }
-  const int ntn = (p.N + BN - 1) / BN, ntiles = ntn * ((M + gBM - 1) / gBM);
+  const int ntn = (p.N + BN - 1) / BN, ntiles = ntn * ((M + gBM - 1) / gBM) * p.ksplit;
   const int per_xcd = (ntiles + 7) / 8;
-  const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if ((int)blockIdx.x / 8 >= per_xcd || tile >= ntiles) return;
+  const int vtile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;  // (tile, K range)
+  if ((int)blockIdx.x / 8 >= per_xcd || vtile >= ntiles) return;
+  const int tile = vtile / p.ksplit, kr = vtile % p.ksplit;
   const int m0 = (tile / ntn) * gBM, n0 = (tile % ntn) * BN;
+  const int kbeg = kr * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
   const __amdgpu_buffer_rsrc_t ra =
       make_rsrc(p.a + (int64_t)m0 * p.lda, view_bytes(min(M - m0, gBM), p.K, p.lda));
   const __amdgpu_buffer_rsrc_t rb =
       make_rsrc(p.b + (int64_t)n0 * p.ldb, view_bytes(min(p.N - n0, BN), p.K, p.ldb));
   const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
-  const int nk = (p.K + BK - 1) / BK;
+  const int nk = (kend - kbeg + BK - 1) / BK;
 
   int so = 0;  // rotary: this thread's entry of the sequence offsets, staged after the loop
   if (HD > 0 && (int)threadIdx.x <= p.nseq) so = p.seq_off[threadIdx.x];
@@ -265,8 +270,9 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
 
   auto load_stage = [&](int t) {
     uint8_t* st = smem + (t % NS) * kStage;
-    load_tile<gBM, BK, NW>(ra, p.lda, t * BK, p.K - t * BK, st, wave, lane);
-    load_tile<BN, BK, NW>(rb, p.ldb, t * BK, p.K - t * BK, st + kTileA, wave, lane);
+    const int k0 = kbeg + t * BK;
+    load_tile<gBM, BK, NW>(ra, p.lda, k0, kend - k0, st, wave, lane);
+    load_tile<BN, BK, NW>(rb, p.ldb, k0, kend - k0, st + kTileA, wave, lane);
   };
   // k-tile t's loads are done once at most the stages issued after it are
   // pending (`younger` of them; vector-memory loads complete in order)
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
   // padding of a partial last k-tile first
   auto open_stage = [&](int t) {
     lds_barrier();
-    const int kt = p.K - t * BK;
+    const int kt = kend - (kbeg + t * BK);
     if (kt < BK && (kt & 7)) {
       uint8_t* st = smem + (t % NS) * kStage;
       zero_k_tail<gBM, BK>(st, kt);
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
         const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
         const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
         if (OUT_F32) {
-          float* c = static_cast<float*>(p.c) + (int64_t)m * p.ldc + n;
+          float* c = static_cast<float*>(p.c) + kr * p.split_stride + (int64_t)m * p.ldc + n;
           uint16_t* c2 = p.c2 ? p.c2 + (int64_t)m * p.ldc2 + n : nullptr;
           if (p.vec == 2 && n + 3 < p.N) {
             *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
@@ -575,11 +581,30 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
         reinterpret_cast<const void*>(&gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD, gMBW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
-  const int tiles = ((a.N + BN - 1) / BN) * ((a.M + gBM - 1) / gBM);
+  const int tiles = ((a.N + BN - 1) / BN) * ((a.M + gBM - 1) / gBM) * a.ksplit;
   hipLaunchKernelGGL((gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD, gMBW>),
                      dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(2 * gBM / (32 * gMBW) * 64), lds,
                      st, a);
   return hipGetLastError();
+}
+
+// Sum of the K-range partials in range order: out32 (fp32, optional) and
+// out16 (bf16, optional) [M, N].
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           int ksplit, int64_t stride,
+                                                           int64_t ldp, int M, int N,
+                                                           float* __restrict__ out32,
+                                                           int64_t ld32,
+                                                           uint16_t* __restrict__ out16,
+                                                           int64_t ld16) {
+  const int64_t n = (int64_t)M * N;
+  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t m = e / N, c = e % N;
+    float v = 0.f;
+    for (int k = 0; k < ksplit; ++k) v += part[k * stride + m * ldp + c];
+    if (out32) out32[m * ld32 + c] = v;
+    if (out16) out16[m * ld16 + c] = (uint16_t)f2bf(v);
+  }
 }
 
 // 2: rows of C take 16-byte stores, 1: 8-byte stores (4 elements), 0: neither.
@@ -608,10 +633,48 @@ hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, v
                        int64_t N, int64_t K, hipStream_t st) {
   BigArgs a{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
             C2, ldc2, (int)M, (int)N, (int)K, store_width(C, ldc, c_f32 ? 4 : 2),
-            nullptr, nullptr, 0, nullptr, 0};
+            nullptr, nullptr, 0, nullptr, 0, 1, (int)K, 0};
   const bool narrow = tile_efficiency((int)M, (int)N, 128) > tile_efficiency((int)M, (int)N, 256) + 0.05;
   if (c_f32) return narrow ? launch_big<128, true>(a, st) : launch_big<256, true>(a, st);
   return narrow ? launch_big<128, false>(a, st) : launch_big<256, false>(a, st);
+}
+
+int gemm_split_ranges(int64_t M, int64_t N, int64_t K) {
+  // K ranges for a launch whose 128-column tiles leave most CUs idle: enough
+  // ranges for ~256 workgroups, each range at least 512 deep
+  const int64_t tiles = ((N + 127) / 128) * ((M + gBM - 1) / gBM);
+  if (tiles >= 128 || K < 1024) return 1;
+  int64_t s = (256 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, 8);
+  s = std::min<int64_t>(s, K / 512);
+  return (int)std::max<int64_t>(s, 1);
+}
+
+size_t gemm_split_bytes(int64_t M, int64_t N) {
+  // the largest partial buffer any K of this M, N can ask for
+  const int64_t tiles = ((N + 127) / 128) * ((M + gBM - 1) / gBM);
+  if (tiles >= 128) return 0;
+  const int64_t s = std::min<int64_t>((256 + tiles - 1) / tiles, 8);
+  return (size_t)s * M * ((N + 7) / 8 * 8) * 4;
+}
+
+hipError_t gemm_nt_big_split(const void* A, int64_t lda, const void* B, int64_t ldb, float* part,
+                             float* out32, int64_t ld32, uint16_t* out16, int64_t ld16,
+                             int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int ks = gemm_split_ranges(M, N, K);
+  const int64_t ldp = (N + 7) / 8 * 8;
+  const int kchunk = (int)(((K + ks - 1) / ks + 63) / 64 * 64);
+  const int nsplit = (int)((K + kchunk - 1) / kchunk);
+  BigArgs a{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, part, ldp,
+            nullptr, 0, (int)M, (int)N, (int)K, store_width(part, ldp, 4), nullptr, nullptr, 0,
+            nullptr, 0, nsplit, kchunk, M * ldp};
+  hipError_t e = launch_big<128, true>(a, st);
+  if (e != hipSuccess) return e;
+  const int64_t n = M * N;
+  const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(split_reduce_kernel, dim3(blocks), dim3(256), 0, st, part, nsplit, M * ldp,
+                     ldp, (int)M, (int)N, out32, ld32, out16, ld16);
+  return hipGetLastError();
 }
 
 hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t ldb, uint16_t* C,
@@ -619,7 +682,7 @@ hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t l
                             const BigRope* rope, hipStream_t st) {
   BigArgs a{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
             nullptr, 0, (int)M, (int)N, (int)K, store_width(C, ldc, 2), m_valid, nullptr, 0,
-            nullptr, 0};
+            nullptr, 0, 1, (int)K, 0};
   // without rotary: the persistent kernel (its stores drain behind the next
   // tile's products; worth it where the output is large against K)
   if (!rope) return a.vec == 2 ? launch_persist<256>(a, st) : launch_big<256, false>(a, st);

@@ -335,10 +335,12 @@ constexpr int64_t kBigT = 1024;
 
 // Calls from kBigT rows on, and calls whose rank tile does not fit on chip,
 // park t in the workspace as bf16 [T, round_up(r, 8)]; the fused kernel
-// needs none.
+// needs none.  From kBigT rows on, a stage 1 with too few tiles to fill the
+// chip splits its d_in range: the fp32 partials follow t.
 size_t prefill_workspace_bytes(int64_t T, int64_t r) {
   if (T < kBigT && fused_fits(r)) return 0;
-  return (size_t)rup(T * rup(r, 8) * 2, 256);
+  const size_t tb = (size_t)rup(T * rup(r, 8) * 2, 256);
+  return T >= kBigT ? tb + gemm_split_bytes(T, r) : tb;
 }
 
 namespace {
@@ -362,7 +364,12 @@ hipError_t prefill_big(const DecodeLinear& d, hipStream_t st) {
   uint16_t* tws = static_cast<uint16_t*>(d.workspace);
   hipError_t e = hipSuccess;
   if (d.flags != 2) {
-    if (d.t_io)
+    if (gemm_split_ranges(d.T, d.r, d.d_in) > 1) {
+      float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(d.workspace) +
+                                             rup(d.T * ldtb * 2, 256));
+      e = gemm_nt_big_split(d.x, d.ldx, d.Ut, d.ldu, part, d.t_io, d.ldt,
+                            d.t_io && d.flags == 1 ? nullptr : tws, ldtb, d.T, d.r, d.d_in, st);
+    } else if (d.t_io)
       e = gemm_nt_big(d.x, d.ldx, d.Ut, d.ldu, d.t_io, d.ldt, true, d.flags == 1 ? nullptr : tws,
                       ldtb, d.T, d.r, d.d_in, st);
     else

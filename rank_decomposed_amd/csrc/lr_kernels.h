@@ -56,6 +56,15 @@ bool gemm_big_supported(int64_t lda, int64_t ldb);
 hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                        int64_t ldc, bool c_f32, uint16_t* C2, int64_t ldc2, int64_t M,
                        int64_t N, int64_t K, hipStream_t st);
+// Split-K variant for launches whose tiles would leave most CUs idle
+// (few 128-column tiles, K >= 1024): K ranges write fp32 partials to part
+// (gemm_split_bytes(M, N) bytes), summed in range order into out32 (fp32)
+// and/or out16 (bf16).  gemm_split_ranges() == 1 means no split is needed.
+int gemm_split_ranges(int64_t M, int64_t N, int64_t K);
+size_t gemm_split_bytes(int64_t M, int64_t N);
+hipError_t gemm_nt_big_split(const void* A, int64_t lda, const void* B, int64_t ldb, float* part,
+                             float* out32, int64_t ld32, uint16_t* out16, int64_t ld16,
+                             int64_t M, int64_t N, int64_t K, hipStream_t st);
 // Rotary epilogue of gemm_nt_big_rows: rows are packed sequences (row m of
 // sequence i sits at position m - seq_off[i], 1 <= nseq <= 255); table
 // [max_pos][hd/2] holds (cos, sin) pairs, 16-byte aligned, under 2 GiB; N a

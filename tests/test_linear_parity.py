@@ -80,6 +80,27 @@ def test_bf16_prefill_large_tile_path(T, shape):
     assert np.array_equal(bits(y_t), bits(y))
 
 
+@pytest.mark.parametrize("T,shape", [(1100, (3003, 96, 320)), (1024, (4096, 409, 512)),
+                                     (2000, (11008, 597, 4096))])
+def test_bf16_prefill_split_k(T, shape):
+    # stage 1 with few 128-column tiles splits d_in into ranges summed in
+    # order: a ragged last range with a ragged last k-tile (3003), eight
+    # 512-deep ranges (4096), and the MLP down projection's d_in (11008);
+    # fused y, y through an fp32 t_io, and stage 1 alone must agree
+    d_in, r, d_out = shape
+    c = make_linear(3100 + T + r, T, d_in, r, d_out, "bf16", fast=True, ld_extra=8)
+    y, _ = _run(c, T, "bf16")
+    y_t, t = _run(c, T, "bf16", with_t=True)
+    t1 = torch.empty((T, r), dtype=torch.float32, device=dev())
+    lr.lowrank_linear_forward(c["dx"], c["dUt"], None, t_io=t1, flags=lr.LR_STAGE1_ONLY)
+    torch.cuda.synchronize()
+    tr, yr = oracle.linear(c["x"], c["U"], c["V"])
+    assert maxrel(to_f64(y), yr) <= BF16_TOL
+    assert maxrel(to_f64(t), tr) <= 1e-5
+    assert np.array_equal(t1.cpu().numpy(), t.cpu().numpy())
+    assert np.array_equal(bits(y_t), bits(y))
+
+
 @pytest.mark.parametrize("T", [5, 64, 200, 1100])
 def test_bf16_stage_flags(T):
     c = make_linear(3000 + T, T, 640, 96, 320, "bf16", fast=True)
