@@ -243,22 +243,41 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 // ---------------------------------------------------------------- prefill attention
 // tok_off[i] = first new token of sequence i (tokens come sequence by
 // sequence), tok_off[S] = T; a sequence without tokens gets an empty range.
-// One workgroup.
+// blk_off[i] = first 64-token query block of sequence i when the blocks of
+// all sequences are numbered in order, blk_off[S] = their count.  One
+// workgroup.
 __global__ __launch_bounds__(256) void tok_offsets_kernel(const int32_t* __restrict__ tok_seq,
                                                           int T, int S,
-                                                          int32_t* __restrict__ tok_off) {
-  for (int i = threadIdx.x; i <= S; i += 256) tok_off[i] = T;
+                                                          int32_t* __restrict__ tok_off,
+                                                          int32_t* __restrict__ blk_off) {
+  for (int i = threadIdx.x; i <= S; i += 256) tok_off[i] = -1;
   __syncthreads();
   for (int t = threadIdx.x; t < T; t += 256) {
     const int sq = tok_seq[t];
     if (sq >= 0 && sq < S && (t == 0 || tok_seq[t - 1] != sq)) tok_off[sq] = t;
   }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    tok_off[S] = T;
+    for (int i = S - 1; i >= 0; --i)
+      if (tok_off[i] < 0 || tok_off[i] > tok_off[i + 1]) tok_off[i] = tok_off[i + 1];
+    int nb = 0;
+    for (int i = 0; i < S; ++i) {
+      blk_off[i] = nb;
+      nb += (tok_off[i + 1] - tok_off[i] + 63) / 64;
+    }
+    blk_off[S] = nb;
+  }
 }
 
 // Causal attention of a chunk of new tokens on MFMA 16x16x32 (flash style):
-// workgroup (q-block b, head h, sequence s) takes the sequence's new tokens
-// b*64 .. b*64+63, one 16-token slice per wave, and walks the sequence's
-// reconstructed K/V rows in 64-row tiles up to the block's last position.
+// a workgroup takes one (head h, 64-token query block) pair, one 16-token
+// slice per wave, and walks its sequence's reconstructed K/V rows in 64-row
+// tiles up to the block's last position.  The pairs are listed head by head
+// (nbpad slots per head, blk_off numbering the blocks of all sequences) and
+// each XCD (workgroup id % 8) takes a contiguous range of the list, so the
+// blocks that read the same K/V rows share one L2; within a sequence the
+// later blocks, which walk more tiles, start first.
 // Per tile: S = Q K^T (Q rotated and scaled in registers, K rows in LDS),
 // causal mask, online softmax (running max m and sum l per query row), P
 // through LDS into the MFMA A layout, O += P V (V transposed in LDS, its
@@ -270,9 +289,9 @@ template <int HD>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int64_t ldkv, const int32_t* __restrict__ seq_off,
-    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ pos,
-    const float* __restrict__ rope, int64_t max_pos, int H, int Hkv, int cap,
-    uint16_t* __restrict__ o, int64_t ldo) {
+    const int32_t* __restrict__ tok_off, const int32_t* __restrict__ blk_off, int S, int nbpad,
+    const int32_t* __restrict__ pos, const float* __restrict__ rope, int64_t max_pos, int H,
+    int Hkv, int cap, uint16_t* __restrict__ o, int64_t ldo) {
   constexpr int KS = HD / 32;  // k-steps of Q K^T
   constexpr int NB = HD / 16;  // 16-column blocks of O
   constexpr int KP = HD + 8;   // K tile pitch (elements)
@@ -281,7 +300,17 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ktile[64 * KP];
   __shared__ __attribute__((aligned(16))) uint16_t vtile[HD * VP];
   __shared__ __attribute__((aligned(16))) uint16_t ptile[4][16 * PP];
-  const int b = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
+  const int nitems = H * nbpad, per_xcd = (nitems + 7) / 8;
+  const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if ((int)blockIdx.x / 8 >= per_xcd || item >= nitems) return;
+  const int h = item / nbpad, gb = item % nbpad;
+  if (gb >= blk_off[S]) return;
+  int sq = 0, hi = S;  // the sequence: the last i with blk_off[i] <= gb
+  while (hi - sq > 1) {
+    const int mid = (sq + hi) >> 1;
+    if (blk_off[mid] <= gb) sq = mid; else hi = mid;
+  }
+  const int b = blk_off[sq + 1] - 1 - gb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = tok_off[sq], t1 = tok_off[sq + 1];
   const int qt0 = t0 + b * 64;
@@ -584,7 +613,8 @@ StepLayout step_layout(const lr_layer_weights* w, const StepIn& s) {
   L.up = w->mlp == LR_MLP_RELU ? L.gate : take(T * w->d_ffn * 2);
   L.m = take(T * w->d_ffn * 2);
   L.yb = dec ? L.m : take(T * d * 2);  // prefill path: o / down output before the residual add
-  L.tok_off = take((s.S + 1) * 4);     // chunked prefill: first token of each sequence
+  L.tok_off = take(2 * (s.S + 1) * 4);  // chunked prefill: first token and first
+                                        // query block of each sequence
   L.total = off;
   return L;
 }
@@ -735,17 +765,22 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
   if (s.tok_seq) {
     // chunked prefill: tiled causal attention over each sequence's rows
     int32_t* tok_off = reinterpret_cast<int32_t*>(ws + L.tok_off);
-    hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(256), 0, st, s.tok_seq, T, S, tok_off);
+    int32_t* blk_off = tok_off + (S + 1);
+    hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(256), 0, st, s.tok_seq, T, S, tok_off,
+                       blk_off);
     LR_CHECK(hipGetLastError());
-    const dim3 pgrid((unsigned)((T + 63) / 64), (unsigned)w->n_heads, (unsigned)S);
+    // at most T/64 + S query blocks over all sequences
+    const int nbpad = (int)((T + 63) / 64) + S;
+    const int64_t nitems = (int64_t)w->n_heads * nbpad;
+    const dim3 pgrid((unsigned)((nitems + 7) / 8 * 8));
     if (w->head_dim == 128)
       hipLaunchKernelGGL(attn_prefill_kernel<128>, pgrid, dim3(256), 0, st, q, dq, krec, vrec,
-                         L.dkv, s.seq_off, tok_off, s.pos, w->rope, w->rope_max_pos,
-                         (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
+                         L.dkv, s.seq_off, tok_off, blk_off, S, nbpad, s.pos, w->rope,
+                         w->rope_max_pos, (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
     else
       hipLaunchKernelGGL(attn_prefill_kernel<64>, pgrid, dim3(256), 0, st, q, dq, krec, vrec,
-                         L.dkv, s.seq_off, tok_off, s.pos, w->rope, w->rope_max_pos,
-                         (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
+                         L.dkv, s.seq_off, tok_off, blk_off, S, nbpad, s.pos, w->rope,
+                         w->rope_max_pos, (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
   } else if (w->head_dim == 128) {
     hipLaunchKernelGGL(attn_partial_kernel<128>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
                        L.dkv, s.seq_off, s.tok_seq, S, s.pos, w->rope, w->rope_max_pos,
