@@ -25,6 +25,7 @@ namespace lr {
 namespace {
 
 constexpr int kAttnChunk = 256;  // cached rows per attention workgroup
+constexpr int kPrefQB = 128;     // query tokens per prefill-attention workgroup (32 per wave)
 
 int64_t rup(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
 // ---------------------------------------------------------------- prefill attention
 // tok_off[i] = first new token of sequence i (tokens come sequence by
 // sequence), tok_off[S] = T; a sequence without tokens gets an empty range.
-// blk_off[i] = first 64-token query block of sequence i when the blocks of
+// blk_off[i] = first kPrefQB-token query block of sequence i when the blocks of
 // all sequences are numbered in order, blk_off[S] = their count.  One
 // workgroup.
 __global__ __launch_bounds__(256) void tok_offsets_kernel(const int32_t* __restrict__ tok_seq,
@@ -264,42 +265,55 @@ __global__ __launch_bounds__(256) void tok_offsets_kernel(const int32_t* __restr
     int nb = 0;
     for (int i = 0; i < S; ++i) {
       blk_off[i] = nb;
-      nb += (tok_off[i + 1] - tok_off[i] + 63) / 64;
+      nb += (tok_off[i + 1] - tok_off[i] + kPrefQB - 1) / kPrefQB;
     }
     blk_off[S] = nb;
   }
 }
 
-// Causal attention of a chunk of new tokens on MFMA 16x16x32 (flash style):
-// a workgroup takes one (head h, 64-token query block) pair, one 16-token
-// slice per wave, and walks its sequence's reconstructed K/V rows in 64-row
-// tiles up to the block's last position.  The pairs are listed head by head
-// (nbpad slots per head, blk_off numbering the blocks of all sequences) and
-// each XCD (workgroup id % 8) takes a contiguous range of the list, so the
-// blocks that read the same K/V rows share one L2; within a sequence the
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D = A(32x16) * B(16x32) + C on bf16 inputs: lane l supplies row (l % 32)
+// of A / column (l % 32) of B with the k-group 8 * (l / 32) .. + 7; lane l
+// holds D[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32], v = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Causal attention of a chunk of new tokens on MFMA 32x32x16 (flash style).
+//
+// Work split: a workgroup takes one (head h, 128-token query block) pair,
+// 32 tokens per wave, and walks its sequence's reconstructed K/V rows in
+// 64-row tiles up to the block's last position.  The pairs are listed head
+// by head (nbpad slots per head; blk_off numbers the blocks of all sequences)
+// and each XCD (workgroup id % 8) takes a contiguous range of the list, so
+// the blocks that read the same K/V rows share one L2; within a sequence the
 // later blocks, which walk more tiles, start first.
-// Per tile: S = Q K^T (Q rotated and scaled in registers, K rows in LDS),
-// causal mask, online softmax (running max m and sum l per query row), P
-// through LDS into the MFMA A layout, O += P V (V transposed in LDS, its
-// 16-byte key chunks XOR-swizzled by d / 8 so the transposing writes spread
-// over the banks).  The next tile's K/V rows are loaded into registers while
-// the current one multiplies.  The C layouts of S and O give a lane the same
-// 4 query rows, so the softmax rescale of O needs no exchange.
+//
+// Per tile a wave forms S^T = K Q^T, so that a lane holds 32 keys of its own
+// query: the causal mask, the running max m and sum l (base-2 softmax, the
+// scale log2(e)/sqrt(hd) folded into Q) stay in the lane but for one
+// exchange between the two lane halves.  The probabilities P^T then serve
+// directly as the B operand of O^T += V^T P^T: the MFMA's contraction runs
+// over the keys in the order the S^T layout leaves them in the lane (4
+// consecutive keys, a gap of 4, 4 more), and V^T is staged in LDS in 8-byte
+// units of 4 consecutive keys of one column, so each A fragment is two
+// 8-byte reads.  K stays row-major in LDS (one 16-byte read per fragment).
+// The next tile's K/V rows are loaded into registers while the current one
+// multiplies.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int64_t ldkv, const int32_t* __restrict__ seq_off,
     const int32_t* __restrict__ tok_off, const int32_t* __restrict__ blk_off, int S, int nbpad,
     const int32_t* __restrict__ pos, const float* __restrict__ rope, int64_t max_pos, int H,
     int Hkv, int cap, uint16_t* __restrict__ o, int64_t ldo) {
-  constexpr int KS = HD / 32;  // k-steps of Q K^T
-  constexpr int NB = HD / 16;  // 16-column blocks of O
-  constexpr int KP = HD + 8;   // K tile pitch (elements)
-  constexpr int VP = 64 + 8;   // V^T tile pitch
-  constexpr int PP = 64 + 8;   // P pitch
+  constexpr int KS = HD / 16;        // k-steps of S^T = K Q^T
+  constexpr int DB = HD / 32;        // 32-row blocks of O^T
+  constexpr int KP = HD + 8;         // K tile pitch (elements)
+  constexpr int VROW = HD + HD / 8;  // 8-byte V^T units per key group (column d at d + d / 8)
   __shared__ __attribute__((aligned(16))) uint16_t ktile[64 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[HD * VP];
-  __shared__ __attribute__((aligned(16))) uint16_t ptile[4][16 * PP];
+  __shared__ __attribute__((aligned(16))) u32x2 vtile[16 * VROW];
   const int nitems = H * nbpad, per_xcd = (nitems + 7) / 8;
   const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if ((int)blockIdx.x / 8 >= per_xcd || item >= nitems) return;
@@ -311,34 +325,36 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     if (blk_off[mid] <= gb) sq = mid; else hi = mid;
   }
   const int b = blk_off[sq + 1] - 1 - gb;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
   const int t0 = tok_off[sq], t1 = tok_off[sq + 1];
-  const int qt0 = t0 + b * 64;
+  const int qt0 = t0 + b * kPrefQB;
   if (qt0 >= t1) return;
   const int beg = seq_off[sq];
   if (beg < 0 || beg >= cap) return;      // offsets are device data: stay inside cap
   int rows = seq_off[sq + 1] - beg;
   rows = rows < cap - beg ? rows : cap - beg;
   if (rows <= 0) return;
-  int plast = pos[min(qt0 + 63, t1 - 1)];
+  int plast = pos[min(qt0 + kPrefQB - 1, t1 - 1)];
   plast = plast < 0 ? 0 : (plast >= rows ? rows - 1 : plast);
   const int nkt = (plast + 64) / 64;
   const int kvh = h / (H / Hkv);
-  const float scale = 1.0f / sqrtf((float)HD);
+  const float qscale = 1.4426950408889634f / sqrtf((float)HD);
 
-  // Q fragments: lane supplies query row (lane & 15) of its wave's slice and
-  // elements ks*32 + 8*(lane >> 4) .. +8; rotary pairs (i, i + HD/2) sit in
-  // k-steps ks and ks + KS/2 of the same lane
-  u32x4 qa[KS];
+  // this lane's query (column of S^T and O^T); rows past the chunk see key 0
+  const int tq = qt0 + 32 * wave + (lane & 31);
+  int rp = tq < t1 ? pos[tq] : 0;
+  rp = rp < 0 ? 0 : rp;
+  // Q fragments: elements 16 ks + 8 half .. + 7 of the lane's query; rotary
+  // pairs (i, i + HD/2) sit in k-steps ks and ks + KS/2 of the same lane
+  u32x4 qf[KS];
   {
-    const int t = qt0 + wave * 16 + (lane & 15);
-    const bool ok = t < t1;
-    int p = ok ? pos[t] : 0;
+    const bool ok = tq < t1;
+    int p = ok ? pos[tq] : 0;
     p = p < 0 ? 0 : (p >= max_pos ? (int)max_pos - 1 : p);
     float v[KS][8];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 w = ok ? ldg16(q + (int64_t)t * ldq + h * HD + ks * 32 + 8 * (lane >> 4))
+      const u32x4 w = ok ? ldg16(q + (int64_t)tq * ldq + h * HD + ks * 16 + 8 * half)
                          : u32x4{0, 0, 0, 0};
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -352,7 +368,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     for (int ks = 0; ks < KS / 2; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int i = ks * 32 + 8 * (lane >> 4) + e;
+        const int i = ks * 16 + 8 * half + e;
         const float c = tb[2 * i], sn = tb[2 * i + 1];
         const float a0 = v[ks][e], b0 = v[ks + KS / 2][e];
         v[ks][e] = a0 * c - b0 * sn;
@@ -360,36 +376,21 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
       }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qa[ks] = u32x4{pack_bf2(v[ks][0] * scale, v[ks][1] * scale),
-                     pack_bf2(v[ks][2] * scale, v[ks][3] * scale),
-                     pack_bf2(v[ks][4] * scale, v[ks][5] * scale),
-                     pack_bf2(v[ks][6] * scale, v[ks][7] * scale)};
+      qf[ks] = u32x4{pack_bf2(v[ks][0] * qscale, v[ks][1] * qscale),
+                     pack_bf2(v[ks][2] * qscale, v[ks][3] * qscale),
+                     pack_bf2(v[ks][4] * qscale, v[ks][5] * qscale),
+                     pack_bf2(v[ks][6] * qscale, v[ks][7] * qscale)};
   }
-  // this lane's output rows: 4*(lane >> 4) + v of the wave's slice
-  int rpos[4];
+  float m = -INFINITY, l = 0.f;
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int t = qt0 + wave * 16 + 4 * (lane >> 4) + v;
-    rpos[v] = t < t1 ? pos[t] : 0;
-  }
-  float m[4], l[4];
-  f32x4 oacc[NB];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    m[v] = -INFINITY;
-    l[v] = 0.f;
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint16_t* pw = ptile[wave];
-  // V^T element (d, key) in LDS: row d, 16-byte chunk (key / 8) ^ ((d / 8) & 7)
-  auto vt_at = [&](int d, int key) {
-    return d * VP + ((((key >> 3) ^ (d >> 3)) & 7) << 3) + (key & 7);
-  };
-  // tile staging: thread c holds K chunks (row c / (HD/8) + 16*i... ) and
-  // V chunks of two adjacent rows, coalesced 16-lane row segments
-  constexpr int KN = 64 * HD / 8 / 256, VN = 32 * HD / 8 / 256;
-  u32x4 kreg[KN], vreg[VN][2];
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+
+  // tile staging: K as 16-byte row chunks; V as (key group of 4 rows, 8-column
+  // chunk) items, each transposed into 8 units on the way to LDS
+  constexpr int KN = 64 * HD / 8 / 256, VITEMS = 16 * (HD / 8);
+  const int vg = threadIdx.x / (HD / 8), vch = threadIdx.x % (HD / 8);
+  u32x4 kreg[KN], vreg[4];
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
@@ -397,14 +398,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
       kreg[i] = j < rows ? ldg16(K + (int64_t)(beg + j) * ldkv + kvh * HD + ch * 8)
                          : u32x4{0, 0, 0, 0};
     }
+    if ((int)threadIdx.x < VITEMS) {
 #pragma unroll
-    for (int i = 0; i < VN; ++i) {
-      const int c = threadIdx.x + 256 * i, pr = c / (HD / 8), ch = c % (HD / 8);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int j = kt * 64 + 2 * pr + u;
-        vreg[i][u] = j < rows ? ldg16(V + (int64_t)(beg + j) * ldkv + kvh * HD + ch * 8)
-                              : u32x4{0, 0, 0, 0};
+      for (int u = 0; u < 4; ++u) {
+        const int j = kt * 64 + 4 * vg + u;
+        vreg[u] = j < rows ? ldg16(V + (int64_t)(beg + j) * ldkv + kvh * HD + vch * 8)
+                           : u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -414,16 +413,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
       const int c = threadIdx.x + 256 * i, r = c / (HD / 8), ch = c % (HD / 8);
       *reinterpret_cast<u32x4*>(ktile + r * KP + ch * 8) = kreg[i];
     }
+    if ((int)threadIdx.x < VITEMS) {
 #pragma unroll
-    for (int i = 0; i < VN; ++i) {
-      const int c = threadIdx.x + 256 * i, pr = c / (HD / 8), ch = c % (HD / 8);
-      const uint32_t a[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-      const uint32_t b2[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {  // (V[2pr][d], V[2pr+1][d]) as one 4-byte word
-        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t hi = (b2[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        *reinterpret_cast<uint32_t*>(vtile + vt_at(ch * 8 + e, 2 * pr)) = lo | (hi << 16);
+      for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        const uint32_t k0 = (vreg[0][e >> 1] >> sh) & 0xffffu, k1 = (vreg[1][e >> 1] >> sh) & 0xffffu;
+        const uint32_t k2 = (vreg[2][e >> 1] >> sh) & 0xffffu, k3 = (vreg[3][e >> 1] >> sh) & 0xffffu;
+        const int d = vch * 8 + e;
+        vtile[vg * VROW + d + (d >> 3)] = u32x2{k0 | (k1 << 16), k2 | (k3 << 16)};
       }
     }
   };
@@ -434,74 +431,81 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     store_tile();
     __syncthreads();
     if (kt + 1 < nkt) load_tile(kt + 1);  // in flight while this tile multiplies
-    // S = Q K^T over the tile's 64 keys (4 column blocks)
-    f32x4 sacc[4];
+    // S^T over the tile's 64 keys: two 32-key blocks
+    f32x16 sacc[2];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      sacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kb =
-            *reinterpret_cast<const u32x4*>(ktile + (cb * 16 + (lane & 15)) * KP + ks * 32 +
-                                            8 * (lane >> 4));
-        sacc[cb] = mfma16x16x32(qa[ks], kb, sacc[cb]);
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(ktile + (kb * 32 + (lane & 31)) * KP +
+                                                         ks * 16 + 8 * half);
+        sacc[kb] = mfma32x32x16(kf, qf[ks], sacc[kb]);
       }
     }
-    // causal mask and online softmax; a row's 64 keys: 4 blocks x the 16
-    // lanes sharing lane >> 4
+    // causal mask and online softmax: register v of block kb is key
+    // kt*64 + 32 kb + 8 (v / 4) + 4 half + v % 4 of the lane's query
+    float mx = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float sv[4], mx = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int j = kt * 64 + cb * 16 + (lane & 15);
-        sv[cb] = (j <= rpos[v] && j < rows) ? sacc[cb][v] : -INFINITY;
-        mx = fmaxf(mx, sv[cb]);
+      for (int v = 0; v < 16; ++v) {
+        const int j = kt * 64 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        const float s = (j <= rp && j < rows) ? sacc[kb][v] : -INFINITY;
+        sacc[kb][v] = s;
+        mx = fmaxf(mx, s);
       }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 while m is still -inf
+    float rs = 0.f;
 #pragma unroll
-      for (int x = 1; x < 16; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x, 16));
-      const float mn = fmaxf(m[v], mx);
-      const float alpha = expf(m[v] - mn);  // 0 while m is still -inf
-      float rs = 0.f;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const float pv = expf(sv[cb] - mn);
-        rs += pv;
-        pw[(4 * (lane >> 4) + v) * PP + cb * 16 + (lane & 15)] = (uint16_t)f2bf(pv);
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kb][v] - mn);
+        sacc[kb][v] = p;
+        rs += p;
       }
+    rs += __shfl_xor(rs, 32);
+    l = l * alpha + rs;
+    m = mn;
 #pragma unroll
-      for (int x = 1; x < 16; x <<= 1) rs += __shfl_xor(rs, x, 16);
-      l[v] = l[v] * alpha + rs;
-      m[v] = mn;
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    // O^T += V^T P^T, 16 keys per step: P^T registers 8 kk .. 8 kk + 7 of a
+    // block are keys 16 kk + {0..3, 8..11} + 4 half, the V^T units of key
+    // groups 4 kk + half and 4 kk + 2 + half of the block
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) oacc[nb][v] *= alpha;
-    }
-    // other lanes' P entries are read below: one wave's LDS accesses run in order
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    asm volatile("" ::: "memory");
-    // O += P V
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const u32x4 pa =
-          *reinterpret_cast<const u32x4*>(pw + (lane & 15) * PP + k2 * 32 + 8 * (lane >> 4));
+      for (int kk = 0; kk < 2; ++kk) {
+        const f32x16& pv = sacc[kb];
+        const u32x4 pf = u32x4{pack_bf2(pv[8 * kk + 0], pv[8 * kk + 1]),
+                               pack_bf2(pv[8 * kk + 2], pv[8 * kk + 3]),
+                               pack_bf2(pv[8 * kk + 4], pv[8 * kk + 5]),
+                               pack_bf2(pv[8 * kk + 6], pv[8 * kk + 7])};
+        const int g0 = 8 * kb + 4 * kk + half;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 vb = *reinterpret_cast<const u32x4*>(
-            vtile + vt_at(nb * 16 + (lane & 15), k2 * 32 + 8 * (lane >> 4)));
-        oacc[nb] = mfma16x16x32(pa, vb, oacc[nb]);
+        for (int db = 0; db < DB; ++db) {
+          const int d = db * 32 + (lane & 31);
+          const u32x2 lo = vtile[g0 * VROW + d + (d >> 3)];
+          const u32x2 hi2 = vtile[(g0 + 2) * VROW + d + (d >> 3)];
+          oacc[db] = mfma32x32x16(u32x4{lo.x, lo.y, hi2.x, hi2.y}, pf, oacc[db]);
+        }
       }
-    }
-    asm volatile("" ::: "memory");
   }
+  if (tq >= t1) return;
+  const float inv = 1.0f / l;
+  uint16_t* orow = o + (int64_t)tq * ldo + h * HD;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int t = qt0 + wave * 16 + 4 * (lane >> 4) + v;
-    if (t >= t1) continue;
-    const float inv = 1.0f / l[v];
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      o[(int64_t)t * ldo + h * HD + nb * 16 + (lane & 15)] = (uint16_t)f2bf(oacc[nb][v] * inv);
-  }
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d = db * 32 + 8 * rq + 4 * half;
+      *reinterpret_cast<u32x2*>(orow + d) =
+          u32x2{pack_bf2(oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv),
+                pack_bf2(oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv)};
+    }
 }
 
 // Combine the chunks of (sequence i, head h): o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
@@ -719,6 +723,8 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
   // epilogue, or (prefill path) through a bf16 y and an add
   auto residual_linear = [&](int k, const void* in, int64_t din) -> hipError_t {
     if (dec) return decode_linear_bf16(linear(k, in, din, din, d, nullptr, h, nullptr), st);
+    const DecodeLinear acc = linear(k, in, din, din, d, nullptr, h, nullptr);
+    if (prefill_accumulates(acc)) return prefill_linear_bf16(acc, st);  // in the GEMM epilogue
     hipError_t r = prefill_linear_bf16(linear(k, in, din, din, d, yb, nullptr, nullptr), st);
     if (r != hipSuccess) return r;
     hipLaunchKernelGGL(add_residual_kernel, dim3(eb), dim3(256), 0, st, h, yb, (int64_t)T * d);
@@ -769,8 +775,8 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
     hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(256), 0, st, s.tok_seq, T, S, tok_off,
                        blk_off);
     LR_CHECK(hipGetLastError());
-    // at most T/64 + S query blocks over all sequences
-    const int nbpad = (int)((T + 63) / 64) + S;
+    // at most T/kPrefQB + S query blocks over all sequences
+    const int nbpad = (int)((T + kPrefQB - 1) / kPrefQB) + S;
     const int64_t nitems = (int64_t)w->n_heads * nbpad;
     const dim3 pgrid((unsigned)((nitems + 7) / 8 * 8));
     if (w->head_dim == 128)

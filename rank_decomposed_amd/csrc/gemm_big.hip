@@ -207,6 +207,7 @@ struct BigArgs {
   int ksplit;              // K ranges (> 1: each writes an fp32 partial to c + range * split_stride)
   int kchunk;              // elements of K per range (a multiple of 64)
   int64_t split_stride;
+  int accum;               // fp32 C += the product (C read and written)
 };
 
 template <int BN, int BK>
@@ -410,7 +411,15 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
         if (OUT_F32) {
           float* c = static_cast<float*>(p.c) + kr * p.split_stride + (int64_t)m * p.ldc + n;
           uint16_t* c2 = p.c2 ? p.c2 + (int64_t)m * p.ldc2 + n : nullptr;
-          if (p.vec == 2 && n + 3 < p.N) {
+          if (p.accum) {
+            const float v[4] = {v0, v1, v2, v3};
+            if (p.vec == 2 && n + 3 < p.N) {
+              const f32x4 o = *reinterpret_cast<const f32x4*>(c);
+              *reinterpret_cast<f32x4*>(c) = f32x4{o.x + v0, o.y + v1, o.z + v2, o.w + v3};
+            } else {
+              for (int e = 0; e < 4 && n + e < p.N; ++e) c[e] += v[e];
+            }
+          } else if (p.vec == 2 && n + 3 < p.N) {
             *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
             if (c2) *reinterpret_cast<u32x2*>(c2) = u32x2{pack_bf2(v0, v1), pack_bf2(v2, v3)};
           } else {
@@ -644,7 +653,8 @@ int gemm_split_ranges(int64_t M, int64_t N, int64_t K) {
   // ranges for ~256 workgroups, each range at least 512 deep
   const int64_t tiles = ((N + 127) / 128) * ((M + gBM - 1) / gBM);
   if (tiles >= 128 || K < 1024) return 1;
-  int64_t s = (256 + tiles - 1) / tiles;
+  // one workgroup per CU: more ranges would leave some CUs with two
+  int64_t s = 256 / tiles;
   s = std::min<int64_t>(s, 8);
   s = std::min<int64_t>(s, K / 512);
   return (int)std::max<int64_t>(s, 1);
@@ -654,8 +664,17 @@ size_t gemm_split_bytes(int64_t M, int64_t N) {
   // the largest partial buffer any K of this M, N can ask for
   const int64_t tiles = ((N + 127) / 128) * ((M + gBM - 1) / gBM);
   if (tiles >= 128) return 0;
-  const int64_t s = std::min<int64_t>((256 + tiles - 1) / tiles, 8);
+  const int64_t s = std::min<int64_t>(256 / tiles, 8);
   return (size_t)s * M * ((N + 7) / 8 * 8) * 4;
+}
+
+hipError_t gemm_nt_big_acc(const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                           int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  BigArgs a{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
+            nullptr, 0, (int)M, (int)N, (int)K, store_width(C, ldc, 4), nullptr, nullptr, 0,
+            nullptr, 0, 1, (int)K, 0, 1};
+  const bool narrow = tile_efficiency((int)M, (int)N, 128) > tile_efficiency((int)M, (int)N, 256) + 0.05;
+  return narrow ? launch_big<128, true>(a, st) : launch_big<256, true>(a, st);
 }
 
 hipError_t gemm_nt_big_split(const void* A, int64_t lda, const void* B, int64_t ldb, float* part,

@@ -382,14 +382,20 @@ hipError_t prefill_big(const DecodeLinear& d, hipStream_t st) {
                        d.T, d.r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  if (d.y_acc)
+    return gemm_nt_big_acc(tws, ldtb, d.Vt, d.ldv, d.y_acc, d.ld_acc, d.T, d.d_out, d.r, st);
   return gemm_nt_big(tws, ldtb, d.Vt, d.ldv, d.y, d.ldy, false, nullptr, 0, d.T, d.d_out, d.r, st);
 }
 
 }  // namespace
 
+bool prefill_accumulates(const DecodeLinear& d) {
+  return d.T >= kBigT && gemm_big_supported(d.ldx, d.ldu) && gemm_big_supported(rup(d.r, 8), d.ldv);
+}
+
 hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st) {
-  if (d.T >= kBigT && gemm_big_supported(d.ldx, d.ldu) && gemm_big_supported(rup(d.r, 8), d.ldv))
-    return prefill_big(d, st);
+  if (prefill_accumulates(d)) return prefill_big(d, st);
+  if (d.y_acc) return hipErrorInvalidValue;
   // buffer-load offsets are 32-bit: the fused kernel needs every operand
   // (plus one tile of rows past its end) under 2 GiB
   const bool small = (d.T + kBM) * d.ldx * 2 < (1ll << 31) && (d.r + 128) * d.ldu * 2 < (1ll << 31) &&

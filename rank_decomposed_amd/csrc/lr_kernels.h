@@ -56,6 +56,9 @@ bool gemm_big_supported(int64_t lda, int64_t ldb);
 hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                        int64_t ldc, bool c_f32, uint16_t* C2, int64_t ldc2, int64_t M,
                        int64_t N, int64_t K, hipStream_t st);
+// C[M, ldc] (fp32) += A . B^T, same operand rules as gemm_nt_big.
+hipError_t gemm_nt_big_acc(const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                           int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st);
 // Split-K variant for launches whose tiles would leave most CUs idle
 // (few 128-column tiles, K >= 1024): K ranges write fp32 partials to part
 // (gemm_split_bytes(M, N) bytes), summed in range order into out32 (fp32)
@@ -83,6 +86,9 @@ hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t l
                             const BigRope* rope, hipStream_t st);
 size_t prefill_workspace_bytes(int64_t T, int64_t r);
 hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st);
+// Whether prefill_linear_bf16 takes the large-tile path for d, the one that
+// can add y into an fp32 y_acc (other paths reject y_acc).
+bool prefill_accumulates(const DecodeLinear& d);
 
 // fp32, any T: tiled SIMT path.
 size_t f32_workspace_bytes(int64_t T, int64_t r);

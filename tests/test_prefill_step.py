@@ -36,3 +36,18 @@ def test_prefill_step_against_oracle(lengths, chunks, n_layers, mlp):
     slots = torch.from_numpy(st.prep["slot_mapping"].astype(np.int64)).cuda()
     got = st.pools_k[0][slots, :lk.shape[1]]
     assert maxrel(to_f64(got), lk) <= 1e-2
+
+
+@pytest.mark.parametrize("H,Hkv,hd", [(4, 4, 128), (8, 1, 64), (2, 2, 128)])
+def test_prefill_attention_head_shapes(H, Hkv, hd):
+    # head_dim 128 and 64, MHA and MQA; chunks spanning several 128-token
+    # query blocks (200, 129) and cached rows spanning several 64-row key
+    # tiles with ragged ends (130, 257)
+    cfg = dict(small_cfg(H, Hkv, hd, d_ffn=384), mlp="swiglu")
+    lengths, chunks = [0, 130, 257], [200, 129, 70]
+    st = Prefill(90 + H + hd, cfg, ranks_for(cfg), lengths, chunks, 1)
+    h = st.run()
+    torch.cuda.synchronize()
+    err = maxrel(to_f64(h), st.oracle())
+    print("prefill H=%d Hkv=%d hd=%d: max rel err %.2e" % (H, Hkv, hd, err))
+    assert err <= TOL
