@@ -11,8 +11,10 @@ Prints one JSON line: whole-job tokens/s (tokens x layer sets / s), the
 roofline of the dominant launch, and the fp64 CPU oracle timed on a bounded
 sample of the same workload.  Also reports, as context: the prefill
 configuration (16384 rows, ratio 0.4 and 0.2) under "prefill", the 32-layer
-decode step under "decode_step", and the 32-layer chunked-prefill step (8
-prompts of 512 tokens) under "prefill_step".
+decode step under "decode_step", the 32-layer chunked-prefill step (8
+prompts of 512 tokens) under "prefill_step", and one of 8 tensor-parallel
+shares of the LLaMA-13B projections (ratio 0.4, T = 64 and 4096) under
+"tp_share".
 """
 from __future__ import annotations
 
@@ -133,6 +135,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-step", action="store_true", help="skip the 32-layer decode step")
+    ap.add_argument("--no-tp", action="store_true",
+                    help="skip the 13B tensor-parallel share leg")
     ap.add_argument("--no-prefill-step", action="store_true",
                     help="skip the 32-layer chunked-prefill step")
     ap.add_argument("--step-layers", type=int, default=32)
@@ -316,6 +320,11 @@ def main():
                                               max(3, args.steps // 2))
         log("prefill-step leg done")
 
+    if not args.no_tp:
+        torch.cuda.empty_cache()
+        result["tp_share"] = tp_share(torch, lr, dev, stream, max(3, args.steps // 2))
+        log("tp-share leg done")
+
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
         log("cpu baseline done")
@@ -374,6 +383,95 @@ def prefill(torch, lr, dev, stream, M=16384, reps=3):
             "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
             "gate_us": round(gate_us, 2),
             "gate_frac": round(gate_fl / (gate_us * 1e-6) / BF16_PEAK, 4)}
+    return out
+
+
+SHAPES_13B = {"q": (5120, 5120), "k": (5120, 5120), "v": (5120, 5120), "o": (5120, 5120),
+              "gate": (5120, 13824), "up": (5120, 13824), "down": (13824, 5120)}
+
+
+def tp_share(torch, lr, dev, stream, reps, n_sets=32, P=8):
+    """One of 8 tensor-parallel shares of the LLaMA-13B projections at ratio
+    0.4 (r = 1024 / 1494): U_r split by input rows, so stage 1 forms the
+    share's partial rank-space t_s [T, r], materialized in fp32 (the tensor
+    the shares would all-reduce); V_r split by output columns, so stage 2
+    writes [T, d_out / 8].  32 distinct share sets (1 GB of factors) stream
+    from HBM; each pass over them is one HIP graph.  T = 64 is HBM-bound
+    (fragment-packed factors, as in the decode leg), T = 4096 MFMA-bound
+    (row-major factors on the large-tile GEMMs)."""
+    import math
+    gen = torch.Generator(device=dev).manual_seed(4_000_001)
+    sets = []
+    for _ in range(n_sets):
+        layer = {}
+        for role in ROLES:
+            d_in, d_out = SHAPES_13B[role]
+            r, wi, wo = rank(0.4, d_in, d_out), d_in // P, d_out // P
+            ut = torch.zeros((r, ld8(wi)), dtype=torch.bfloat16, device=dev)
+            vt = torch.zeros((wo, ld8(r)), dtype=torch.bfloat16, device=dev)
+            ut[:, :wi] = torch.randn((r, wi), generator=gen, device=dev) / math.sqrt(d_in)
+            vt[:, :r] = torch.randn((wo, r), generator=gen, device=dev) / math.sqrt(r)
+            layer[role] = (ut[:, :wi], vt[:, :r], r)
+        sets.append(layer)
+    out = {}
+    for T in (64, 4096):
+        use = sets
+        if T <= 64:
+            use = [{role: (lr.pack_factor(ut), lr.pack_factor(vt), r)
+                    for role, (ut, vt, r) in layer.items()} for layer in sets]
+        xs = {w: torch.randn((T, w), generator=gen, device=dev).to(torch.bfloat16)
+              for w in (640, 1728)}
+        ts = {r: torch.empty((T, r), dtype=torch.float32, device=dev) for r in (1024, 1494)}
+        ys = {w: torch.empty((T, w), dtype=torch.bfloat16, device=dev) for w in (640, 1728)}
+        need = 0
+        nbytes = flops = 0
+        for role in ROLES:
+            d_in, d_out = SHAPES_13B[role]
+            r, wi, wo = rank(0.4, d_in, d_out), d_in // P, d_out // P
+            need = max(need, lr.lowrank_workspace_bytes(0, lr.LR_BF16, T, wi, r, wo))
+            # shares, x_s, y_s, and t written and read once (counted at 2 bytes)
+            nbytes += 2 * r * (wi + wo) + 2 * T * (wi + wo) + 2 * 2 * T * r
+            flops += 2 * T * r * (wi + wo)
+        ws = torch.zeros(need + 256, dtype=torch.uint8, device=dev)
+
+        def run():
+            for layer in use:
+                for role in ROLES:
+                    ut, vt, r = layer[role]
+                    d_in, d_out = SHAPES_13B[role]
+                    lr.lowrank_linear_forward(xs[d_in // P], ut, None, t_io=ts[r],
+                                              flags=lr.LR_STAGE1_ONLY, workspace=ws)
+                    lr.lowrank_linear_forward(None, None, vt, y=ys[d_out // P], t_io=ts[r],
+                                              flags=lr.LR_STAGE2_ONLY, workspace=ws)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms_set = a.elapsed_time(b) / reps / len(use)
+        del g
+        s = ms_set * 1e-3
+        out["T%d" % T] = {
+            "tokens_per_s": round(T / s, 1), "us_per_layer_set": round(ms_set * 1e3, 2),
+            "bytes_per_layer_set": nbytes, "GBps": round(nbytes / s / 1e9, 1),
+            "hbm_frac": round(nbytes / s / HBM_PEAK, 4),
+            "flop_per_layer_set": flops, "TFLOPs": round(flops / s / 1e12, 2),
+            "mfma_frac": round(flops / s / BF16_PEAK, 4),
+            "bound": "hbm" if T <= 64 else "mfma",
+            "factor_layout": "packed" if T <= 64 else "rowmajor"}
     return out
 
 

@@ -50,20 +50,41 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
                                                       const uint16_t* __restrict__ g,
                                                       uint16_t* __restrict__ x, int64_t ldx, int d,
                                                       float eps) {
-  __shared__ float red[256];
+  __shared__ float red[4];
   const float* row = h + (int64_t)blockIdx.x * ldh;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) ss = fmaf(row[i], row[i], ss);
-  red[threadIdx.x] = ss;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const float scale = 1.0f / sqrtf(red[0] / (float)d + eps);
   uint16_t* out = x + (int64_t)blockIdx.x * ldx;
-  for (int i = threadIdx.x; i < d; i += 256)
-    out[i] = (uint16_t)f2bf(row[i] * scale * bf2f(g[i]));
+  // rows of whole 4-element groups (d, ldh, ldx multiples of 4, aligned
+  // pointers): 16-byte loads and 8-byte stores; otherwise element by element
+  const bool vec = (d & 3) == 0 && (ldh & 3) == 0 && (ldx & 3) == 0 &&
+                   (reinterpret_cast<uintptr_t>(h) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(x) & 7) == 0 &&
+                   (reinterpret_cast<uintptr_t>(g) & 7) == 0;
+  float ss = 0.f;
+  if (vec) {
+    for (int c = threadIdx.x; c < d / 4; c += 256) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(row)[c];
+      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    }
+  } else {
+    for (int i = threadIdx.x; i < d; i += 256) ss = fmaf(row[i], row[i], ss);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float scale = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+  if (vec) {
+    for (int c = threadIdx.x; c < d / 4; c += 256) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(row)[c];
+      const u32x2 gw = reinterpret_cast<const u32x2*>(g)[c];
+      reinterpret_cast<u32x2*>(out)[c] =
+          u32x2{pack_bf2(v.x * scale * bf2f(gw.x & 0xffffu), v.y * scale * bf2f(gw.x >> 16)),
+                pack_bf2(v.z * scale * bf2f(gw.y & 0xffffu), v.w * scale * bf2f(gw.y >> 16))};
+    }
+  } else {
+    for (int i = threadIdx.x; i < d; i += 256)
+      out[i] = (uint16_t)f2bf(row[i] * scale * bf2f(g[i]));
+  }
 }
 
 // ---------------------------------------------------------------- append
@@ -811,20 +832,36 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
                      static_cast<const uint16_t*>(w->ffn_norm), x, d, (int)d, w->eps);
   LR_CHECK(hipGetLastError());
   const dim3 egrid((unsigned)((T * ffn + 255) / 256 < 4096 ? (T * ffn + 255) / 256 : 4096));
+  // on the large-tile prefill path the activation runs in the epilogue of
+  // the last MLP GEMM (relu of fc1; silu(gate) * up in the up projection)
   if (w->mlp == LR_MLP_RELU) {
-    const DecodeLinear fc1 = linear(4, x, d, d, ffn, gate, nullptr, nullptr);
-    LR_CHECK(dec ? decode_linear_bf16(fc1, st) : prefill_linear_bf16(fc1, st));
-    hipLaunchKernelGGL(relu_kernel, egrid, dim3(256), 0, st, gate, m, (int64_t)T * ffn);
+    DecodeLinear fc1 = linear(4, x, d, d, ffn, m, nullptr, nullptr);
+    fc1.act = 2;
+    if (!dec && prefill_act_ok(fc1)) {
+      LR_CHECK(prefill_linear_bf16(fc1, st));
+    } else {
+      fc1 = linear(4, x, d, d, ffn, gate, nullptr, nullptr);
+      LR_CHECK(dec ? decode_linear_bf16(fc1, st) : prefill_linear_bf16(fc1, st));
+      hipLaunchKernelGGL(relu_kernel, egrid, dim3(256), 0, st, gate, m, (int64_t)T * ffn);
+    }
   } else {
     const DecodeLinear gu[2] = {linear(4, x, d, d, ffn, gate, nullptr, nullptr),
                                 linear(5, x, d, d, ffn, up, nullptr, nullptr)};
+    DecodeLinear upm = linear(5, x, d, d, ffn, m, nullptr, nullptr);
+    upm.act = 1;
+    upm.glu = gate;
+    upm.ldglu = ffn;
     if (dec) {
       LR_CHECK(decode_group_bf16(gu, 2, st));
+      hipLaunchKernelGGL(silu_mul_kernel, egrid, dim3(256), 0, st, gate, up, m, (int64_t)T * ffn);
+    } else if (prefill_act_ok(upm)) {
+      LR_CHECK(prefill_linear_bf16(gu[0], st));
+      LR_CHECK(prefill_linear_bf16(upm, st));
     } else {
       LR_CHECK(prefill_linear_bf16(gu[0], st));
       LR_CHECK(prefill_linear_bf16(gu[1], st));
+      hipLaunchKernelGGL(silu_mul_kernel, egrid, dim3(256), 0, st, gate, up, m, (int64_t)T * ffn);
     }
-    hipLaunchKernelGGL(silu_mul_kernel, egrid, dim3(256), 0, st, gate, up, m, (int64_t)T * ffn);
   }
   LR_CHECK(hipGetLastError());
   LR_CHECK(residual_linear(6, m, ffn));

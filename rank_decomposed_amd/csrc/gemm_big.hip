@@ -113,10 +113,38 @@ __device__ __forceinline__ void zero_k_tail(uint8_t* lds, int kt) {
 // row-contiguous, so each global store instruction writes whole 128-byte
 // lines instead of 16 bytes of 32 different rows.  The operand tiles are
 // dead by then (the caller has passed a barrier after the last product).
+// bf16 v (8 values, packed) through the epilogue activation: act 1 gives
+// silu(g) * v with g the matching 8 values of G, act 2 relu(v).  The product
+// is rounded to bf16 first, as a separate activation pass would see it.
+__device__ __forceinline__ u32x4 epi_act(u32x4 v, int act, const uint16_t* gp) {
+  if (act == 0) return v;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t gw[4] = {0, 0, 0, 0};
+  if (act == 1) {
+    const u32x4 g = *reinterpret_cast<const u32x4*>(gp);
+    gw[0] = g.x; gw[1] = g.y; gw[2] = g.z; gw[3] = g.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float lo = bf2f(w[e] & 0xffffu), hi = bf2f(w[e] >> 16);
+    if (act == 1) {
+      const float glo = bf2f(gw[e] & 0xffffu), ghi = bf2f(gw[e] >> 16);
+      lo *= glo / (1.0f + expf(-glo));
+      hi *= ghi / (1.0f + expf(-ghi));
+    } else {
+      lo = lo < 0.f ? 0.f : lo;
+      hi = hi < 0.f ? 0.f : hi;
+    }
+    w[e] = pack_bf2(lo, hi);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 template <int BN, int MBW>
 __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], uint16_t* C,
                                              int64_t ldc, int mw, int nw, int M, int N,
-                                             uint8_t* smem, int wave, int lane) {
+                                             uint8_t* smem, int wave, int lane, int act = 0,
+                                             const uint16_t* glu = nullptr, int64_t ldglu = 0) {
   constexpr int NBW = BN / 64, WN = BN / 2, RB = WN * 2, CPR = WN / 8, RPI = 64 / CPR;
   constexpr int WR = 32 * MBW;  // wave rows
   uint8_t* ep = smem + wave * (WR * RB);
@@ -143,9 +171,16 @@ __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], 
     if (m >= M) continue;
     uint16_t* c = C + (int64_t)m * ldc + n;
     if (n + 7 < N) {
-      *reinterpret_cast<u32x4*>(c) = v;
+      *reinterpret_cast<u32x4*>(c) = epi_act(v, act, glu + (int64_t)m * ldglu + n);
     } else {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      if (act) {  // ragged tail: G's row may end before 8 elements
+        uint16_t g8[8] __attribute__((aligned(16))) = {};
+        if (act == 1)
+          for (int e = 0; e < 8 && n + e < N; ++e) g8[e] = glu[(int64_t)m * ldglu + n + e];
+        const u32x4 r = epi_act(v, act, g8);
+        w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w;
+      }
       for (int e = 0; e < 8 && n + e < N; ++e) c[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
   }
@@ -208,6 +243,9 @@ struct BigArgs {
   int kchunk;              // elements of K per range (a multiple of 64)
   int64_t split_stride;
   int accum;               // fp32 C += the product (C read and written)
+  int act;                 // bf16 C, staged stores: 1 = silu(G) * product, 2 = relu(product)
+  const uint16_t* glu;     // G [M, ldglu] bf16 (act 1), 16-byte aligned rows
+  int64_t ldglu;
 };
 
 template <int BN, int BK>
@@ -394,7 +432,7 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
   }
   if (!OUT_F32 && p.vec == 2) {
     store_staged<BN, MBW>(acc, static_cast<uint16_t*>(p.c), p.ldc, m0 + wm, n0 + wn, M, p.N,
-                          smem, wave, lane);
+                          smem, wave, lane, p.act, p.glu, p.ldglu);
     return;
   }
 #pragma unroll
@@ -666,6 +704,18 @@ size_t gemm_split_bytes(int64_t M, int64_t N) {
   if (tiles >= 128) return 0;
   const int64_t s = std::min<int64_t>(256 / tiles, 8);
   return (size_t)s * M * ((N + 7) / 8 * 8) * 4;
+}
+
+hipError_t gemm_nt_big_act(const void* A, int64_t lda, const void* B, int64_t ldb, uint16_t* C,
+                           int64_t ldc, int act, const uint16_t* G, int64_t ldg, int64_t M,
+                           int64_t N, int64_t K, hipStream_t st) {
+  const bool g_ok = act != 1 || (G && reinterpret_cast<uintptr_t>(G) % 16 == 0 && ldg % 8 == 0);
+  if (act < 1 || act > 2 || store_width(C, ldc, 2) != 2 || !g_ok) return hipErrorInvalidValue;
+  BigArgs a{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
+            nullptr, 0, (int)M, (int)N, (int)K, 2, nullptr, nullptr, 0, nullptr, 0, 1, (int)K, 0,
+            0, act, G, ldg};
+  const bool narrow = tile_efficiency((int)M, (int)N, 128) > tile_efficiency((int)M, (int)N, 256) + 0.05;
+  return narrow ? launch_big<128, false>(a, st) : launch_big<256, false>(a, st);
 }
 
 hipError_t gemm_nt_big_acc(const void* A, int64_t lda, const void* B, int64_t ldb, float* C,

@@ -384,6 +384,9 @@ hipError_t prefill_big(const DecodeLinear& d, hipStream_t st) {
   }
   if (d.y_acc)
     return gemm_nt_big_acc(tws, ldtb, d.Vt, d.ldv, d.y_acc, d.ld_acc, d.T, d.d_out, d.r, st);
+  if (d.act)
+    return gemm_nt_big_act(tws, ldtb, d.Vt, d.ldv, static_cast<uint16_t*>(d.y), d.ldy, d.act,
+                           static_cast<const uint16_t*>(d.glu), d.ldglu, d.T, d.d_out, d.r, st);
   return gemm_nt_big(tws, ldtb, d.Vt, d.ldv, d.y, d.ldy, false, nullptr, 0, d.T, d.d_out, d.r, st);
 }
 
@@ -393,7 +396,14 @@ bool prefill_accumulates(const DecodeLinear& d) {
   return d.T >= kBigT && gemm_big_supported(d.ldx, d.ldu) && gemm_big_supported(rup(d.r, 8), d.ldv);
 }
 
+bool prefill_act_ok(const DecodeLinear& d) {
+  const auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  return prefill_accumulates(d) && d.y && a16(d.y) && d.ldy % 8 == 0 &&
+         (d.act != 1 || (d.glu && a16(d.glu) && d.ldglu % 8 == 0));
+}
+
 hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st) {
+  if (d.act && !prefill_act_ok(d)) return hipErrorInvalidValue;
   if (prefill_accumulates(d)) return prefill_big(d, st);
   if (d.y_acc) return hipErrorInvalidValue;
   // buffer-load offsets are 32-bit: the fused kernel needs every operand

@@ -28,6 +28,12 @@ struct DecodeLinear {
   int64_t ld_acc = 0;
   // bf16 paths: Ut/Vt fragment-packed, ldu/ldv = block pitch in 32-column steps
   bool packed = false;
+  // optional (large-tile prefill path only, see prefill_act_ok): y =
+  // act(x U_r V_r), act 1 = silu(glu) * product with glu bf16 [T, ldglu],
+  // act 2 = relu(product)
+  int act = 0;
+  const void* glu = nullptr;
+  int64_t ldglu = 0;
 };
 
 // bf16, T <= 64: streamed skinny MFMA path.
@@ -56,6 +62,12 @@ bool gemm_big_supported(int64_t lda, int64_t ldb);
 hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                        int64_t ldc, bool c_f32, uint16_t* C2, int64_t ldc2, int64_t M,
                        int64_t N, int64_t K, hipStream_t st);
+// C (bf16, 16-byte aligned rows) = act(A . B^T): act 1 = silu(G) * (A . B^T)
+// with G bf16 [M, ldg] (16-byte aligned rows), act 2 = relu(A . B^T); the
+// product is rounded to bf16 before the activation.
+hipError_t gemm_nt_big_act(const void* A, int64_t lda, const void* B, int64_t ldb, uint16_t* C,
+                           int64_t ldc, int act, const uint16_t* G, int64_t ldg, int64_t M,
+                           int64_t N, int64_t K, hipStream_t st);
 // C[M, ldc] (fp32) += A . B^T, same operand rules as gemm_nt_big.
 hipError_t gemm_nt_big_acc(const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
                            int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st);
@@ -89,6 +101,8 @@ hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st);
 // Whether prefill_linear_bf16 takes the large-tile path for d, the one that
 // can add y into an fp32 y_acc (other paths reject y_acc).
 bool prefill_accumulates(const DecodeLinear& d);
+// Whether prefill_linear_bf16 can apply d.act in the stage-2 epilogue.
+bool prefill_act_ok(const DecodeLinear& d);
 
 // fp32, any T: tiled SIMT path.
 size_t f32_workspace_bytes(int64_t T, int64_t r);

@@ -2,7 +2,8 @@
 prompt tokens appended to a paged cache of rank-r latents, causal attention
 over each token's cached and earlier chunk rows.  Chunks of at most 64
 tokens take the decode path, larger ones the prefill path (fused kernel
-below 1024 rows, large-tile GEMMs from 1024 on).  Bar: max|gpu - ref| /
+below 1024 rows, large-tile GEMMs from 1024 on, with the residual add and
+the MLP activation in their epilogues).  Bar: max|gpu - ref| /
 max|ref| <= 2e-2 on the residual stream."""
 import numpy as np
 import pytest
@@ -21,6 +22,7 @@ pytestmark = pytest.mark.gpu
     ([10, 0, 300], [100, 64, 150], 2, "swiglu"),         # 314 tokens: fused prefill kernel
     ([7, 0, 120], [33, 90, 10], 1, "relu"),              # 133 tokens, non-GLU MLP
     ([50], [1100], 1, "swiglu"),                         # 1100 tokens: large-tile GEMMs
+    ([20, 3], [700, 330], 1, "relu"),                    # 1030 tokens: relu in the epilogue
 ])
 def test_prefill_step_against_oracle(lengths, chunks, n_layers, mlp):
     cfg = dict(small_cfg(4, 2, 64, d_ffn=512), mlp=mlp)
