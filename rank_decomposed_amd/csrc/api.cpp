@@ -41,7 +41,7 @@ extern "C" const char* lowrank_status_string(lr_status s) {
 static size_t linear_ws(lr_dtype dt, int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
   if (dt == LR_F32) return lr::f32_workspace_bytes(T, r);
   if (T <= 64) return lr::decode_workspace_bytes(T, d_in, r, d_out);
-  return lr::prefill_workspace_bytes(T, r);
+  return lr::prefill_workspace_bytes(T, r, d_out);
 }
 
 extern "C" size_t lowrank_workspace_bytes(int which, lr_dtype dt, int64_t T_or_B, int64_t d_in,

@@ -615,7 +615,8 @@ StepLayout step_layout(const lr_layer_weights* w, const StepIn& s) {
     lin = std::max(lin, decode_workspace_bytes(T, din[6], w->r[6], dout[6]));
   } else {
     for (int k = 0; k < 7; ++k)
-      if (!(k == 5 && w->mlp == LR_MLP_RELU)) lin = std::max(lin, prefill_workspace_bytes(T, w->r[k]));
+      if (!(k == 5 && w->mlp == LR_MLP_RELU))
+        lin = std::max(lin, prefill_workspace_bytes(T, w->r[k], dout[k]));
   }
   size_t off = 0;
   auto take = [&](size_t bytes) {

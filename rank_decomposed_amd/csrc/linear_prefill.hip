@@ -337,7 +337,8 @@ constexpr int64_t kBigT = 1024;
 // park t in the workspace as bf16 [T, round_up(r, 8)]; the fused kernel
 // needs none.  From kBigT rows on, a stage 1 with too few tiles to fill the
 // chip splits its d_in range: the fp32 partials follow t.
-size_t prefill_workspace_bytes(int64_t T, int64_t r) {
+size_t prefill_workspace_bytes(int64_t T, int64_t r, int64_t d_out) {
+  (void)d_out;
   if (T < kBigT && fused_fits(r)) return 0;
   const size_t tb = (size_t)rup(T * rup(r, 8) * 2, 256);
   return T >= kBigT ? tb + gemm_split_bytes(T, r) : tb;

@@ -96,7 +96,7 @@ struct BigRope {
 hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t ldb, uint16_t* C,
                             int64_t ldc, int64_t M, const int32_t* m_valid, int64_t N, int64_t K,
                             const BigRope* rope, hipStream_t st);
-size_t prefill_workspace_bytes(int64_t T, int64_t r);
+size_t prefill_workspace_bytes(int64_t T, int64_t r, int64_t d_out);
 hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st);
 // Whether prefill_linear_bf16 takes the large-tile path for d, the one that
 // can add y into an fp32 y_acc (other paths reject y_acc).

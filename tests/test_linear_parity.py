@@ -81,12 +81,13 @@ def test_bf16_prefill_large_tile_path(T, shape):
 
 
 @pytest.mark.parametrize("T,shape", [(1100, (3003, 96, 320)), (1024, (4096, 409, 512)),
-                                     (2000, (11008, 597, 4096))])
+                                     (2000, (11008, 597, 4096)), (1024, (1200, 1100, 1300))])
 def test_bf16_prefill_split_k(T, shape):
-    # stage 1 with few 128-column tiles splits d_in into ranges summed in
+    # a stage 1 with few 128-column tiles splits d_in into ranges summed in
     # order: a ragged last range with a ragged last k-tile (3003), eight
-    # 512-deep ranges (4096), and the MLP down projection's d_in (11008);
-    # fused y, y through an fp32 t_io, and stage 1 alone must agree
+    # 512-deep ranges (4096), the MLP down projection's d_in (11008), two
+    # ranges before a wide rank (1200 -> 1100).  Fused y, y through an fp32
+    # t_io, and stage 1 alone must agree
     d_in, r, d_out = shape
     c = make_linear(3100 + T + r, T, d_in, r, d_out, "bf16", fast=True, ld_extra=8)
     y, _ = _run(c, T, "bf16")
