@@ -274,9 +274,14 @@ __global__ __launch_bounds__(256) void tok_offsets_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ blk_off) {
   for (int i = threadIdx.x; i <= S; i += 256) tok_off[i] = -1;
   __syncthreads();
-  for (int t = threadIdx.x; t < T; t += 256) {
+  // a contiguous run of tokens per thread, its loads unrolled
+  const int per = (T + 255) / 256, tb = threadIdx.x * per, te = min(T, tb + per);
+  int prev = tb > 0 && tb < T ? tok_seq[tb - 1] : -1;
+#pragma unroll 8
+  for (int t = tb; t < te; ++t) {
     const int sq = tok_seq[t];
-    if (sq >= 0 && sq < S && (t == 0 || tok_seq[t - 1] != sq)) tok_off[sq] = t;
+    if (sq >= 0 && sq < S && (t == 0 || prev != sq)) tok_off[sq] = t;
+    prev = sq;
   }
   __syncthreads();
   if (threadIdx.x == 0) {

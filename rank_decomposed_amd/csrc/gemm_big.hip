@@ -116,21 +116,17 @@ __device__ __forceinline__ void zero_k_tail(uint8_t* lds, int kt) {
 // bf16 v (8 values, packed) through the epilogue activation: act 1 gives
 // silu(g) * v with g the matching 8 values of G, act 2 relu(v).  The product
 // is rounded to bf16 first, as a separate activation pass would see it.
-__device__ __forceinline__ u32x4 epi_act(u32x4 v, int act, const uint16_t* gp) {
+__device__ __forceinline__ u32x4 epi_act(u32x4 v, int act, u32x4 g) {
   if (act == 0) return v;
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t gw[4] = {0, 0, 0, 0};
-  if (act == 1) {
-    const u32x4 g = *reinterpret_cast<const u32x4*>(gp);
-    gw[0] = g.x; gw[1] = g.y; gw[2] = g.z; gw[3] = g.w;
-  }
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     float lo = bf2f(w[e] & 0xffffu), hi = bf2f(w[e] >> 16);
-    if (act == 1) {
+    if (act == 1) {  // silu(g) = g / (1 + 2^(-g log2 e)), hardware exp2 and reciprocal
       const float glo = bf2f(gw[e] & 0xffffu), ghi = bf2f(gw[e] >> 16);
-      lo *= glo / (1.0f + expf(-glo));
-      hi *= ghi / (1.0f + expf(-ghi));
+      lo *= glo * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * glo));
+      hi *= ghi * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * ghi));
     } else {
       lo = lo < 0.f ? 0.f : lo;
       hi = hi < 0.f ? 0.f : hi;
@@ -164,23 +160,35 @@ __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], 
   __builtin_amdgcn_s_waitcnt(0xc07f);
   asm volatile("" ::: "memory");
   const int chl = lane % CPR, n = nw + chl * 8;
-#pragma unroll 4
-  for (int r0 = 0; r0 < WR; r0 += RPI) {
-    const int rl = r0 + lane / CPR, m = mw + rl;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ep + rl * RB + ((chl ^ (rl & (CPR - 1))) * 16));
+  // act 1: every row's 8 values of G in flight at once before the stores
+  constexpr int NIT = WR / RPI;
+  u32x4 gv[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    gv[it] = u32x4{0, 0, 0, 0};
+    const int m = mw + it * RPI + lane / CPR;
+    if (act != 1 || m >= M) continue;
+    const uint16_t* g = glu + (int64_t)m * ldglu + n;
+    if (n + 7 < N) {
+      gv[it] = *reinterpret_cast<const u32x4*>(g);
+    } else {  // ragged tail: G's row may end before 8 elements
+      uint32_t w[4] = {0, 0, 0, 0};
+      for (int e = 0; e < 8 && n + e < N; ++e) w[e >> 1] |= (uint32_t)g[e] << (16 * (e & 1));
+      gv[it] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int rl = it * RPI + lane / CPR, m = mw + rl;
+    const u32x4 v = epi_act(
+        *reinterpret_cast<const u32x4*>(ep + rl * RB + ((chl ^ (rl & (CPR - 1))) * 16)), act,
+        gv[it]);
     if (m >= M) continue;
     uint16_t* c = C + (int64_t)m * ldc + n;
     if (n + 7 < N) {
-      *reinterpret_cast<u32x4*>(c) = epi_act(v, act, glu + (int64_t)m * ldglu + n);
+      *reinterpret_cast<u32x4*>(c) = v;
     } else {
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      if (act) {  // ragged tail: G's row may end before 8 elements
-        uint16_t g8[8] __attribute__((aligned(16))) = {};
-        if (act == 1)
-          for (int e = 0; e < 8 && n + e < N; ++e) g8[e] = glu[(int64_t)m * ldglu + n + e];
-        const u32x4 r = epi_act(v, act, g8);
-        w[0] = r.x; w[1] = r.y; w[2] = r.z; w[3] = r.w;
-      }
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       for (int e = 0; e < 8 && n + e < N; ++e) c[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
   }
@@ -636,7 +644,9 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
 }
 
 // Sum of the K-range partials in range order: out32 (fp32, optional) and
-// out16 (bf16, optional) [M, N].
+// out16 (bf16, optional) [M, N].  A thread takes 4 consecutive columns of
+// the partials' rows (ldp, a multiple of 8, wide: columns past N are read,
+// never written).
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
                                                            int ksplit, int64_t stride,
                                                            int64_t ldp, int M, int N,
@@ -644,13 +654,17 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
                                                            int64_t ld32,
                                                            uint16_t* __restrict__ out16,
                                                            int64_t ld16) {
-  const int64_t n = (int64_t)M * N;
+  const int64_t q = ldp / 4, n = (int64_t)M * q;
   for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
-    const int64_t m = e / N, c = e % N;
-    float v = 0.f;
-    for (int k = 0; k < ksplit; ++k) v += part[k * stride + m * ldp + c];
-    if (out32) out32[m * ld32 + c] = v;
-    if (out16) out16[m * ld16 + c] = (uint16_t)f2bf(v);
+    const int64_t m = e / q, c = (e % q) * 4;
+    if (c >= N) continue;
+    f32x4 v = *reinterpret_cast<const f32x4*>(part + m * ldp + c);
+    for (int k = 1; k < ksplit; ++k) v += *reinterpret_cast<const f32x4*>(part + k * stride + m * ldp + c);
+    const float w[4] = {v.x, v.y, v.z, v.w};
+    for (int e2 = 0; e2 < 4 && c + e2 < N; ++e2) {
+      if (out32) out32[m * ld32 + c + e2] = w[e2];
+      if (out16) out16[m * ld16 + c + e2] = (uint16_t)f2bf(w[e2]);
+    }
   }
 }
 
@@ -739,7 +753,7 @@ hipError_t gemm_nt_big_split(const void* A, int64_t lda, const void* B, int64_t 
             nullptr, 0, nsplit, kchunk, M * ldp};
   hipError_t e = launch_big<128, true>(a, st);
   if (e != hipSuccess) return e;
-  const int64_t n = M * N;
+  const int64_t n = M * (ldp / 4);
   const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
   hipLaunchKernelGGL(split_reduce_kernel, dim3(blocks), dim3(256), 0, st, part, nsplit, M * ldp,
                      ldp, (int)M, (int)N, out32, ld32, out16, ld16);
