@@ -160,6 +160,24 @@ __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], 
   __builtin_amdgcn_s_waitcnt(0xc07f);
   asm volatile("" ::: "memory");
   const int chl = lane % CPR, n = nw + chl * 8;
+  if (act != 1) {
+#pragma unroll 4
+    for (int r0 = 0; r0 < WR; r0 += RPI) {
+      const int rl = r0 + lane / CPR, m = mw + rl;
+      const u32x4 v = epi_act(
+          *reinterpret_cast<const u32x4*>(ep + rl * RB + ((chl ^ (rl & (CPR - 1))) * 16)), act,
+          u32x4{0, 0, 0, 0});
+      if (m >= M) continue;
+      uint16_t* c = C + (int64_t)m * ldc + n;
+      if (n + 7 < N) {
+        *reinterpret_cast<u32x4*>(c) = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int e = 0; e < 8 && n + e < N; ++e) c[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    return;
+  }
   // act 1: every row's 8 values of G in flight at once before the stores
   constexpr int NIT = WR / RPI;
   u32x4 gv[NIT];
@@ -167,7 +185,7 @@ __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], 
   for (int it = 0; it < NIT; ++it) {
     gv[it] = u32x4{0, 0, 0, 0};
     const int m = mw + it * RPI + lane / CPR;
-    if (act != 1 || m >= M) continue;
+    if (m >= M) continue;
     const uint16_t* g = glu + (int64_t)m * ldglu + n;
     if (n + 7 < N) {
       gv[it] = *reinterpret_cast<const u32x4*>(g);
@@ -181,7 +199,7 @@ __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], 
   for (int it = 0; it < NIT; ++it) {
     const int rl = it * RPI + lane / CPR, m = mw + rl;
     const u32x4 v = epi_act(
-        *reinterpret_cast<const u32x4*>(ep + rl * RB + ((chl ^ (rl & (CPR - 1))) * 16)), act,
+        *reinterpret_cast<const u32x4*>(ep + rl * RB + ((chl ^ (rl & (CPR - 1))) * 16)), 1,
         gv[it]);
     if (m >= M) continue;
     uint16_t* c = C + (int64_t)m * ldc + n;
@@ -440,7 +458,7 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
   }
   if (!OUT_F32 && p.vec == 2) {
     store_staged<BN, MBW>(acc, static_cast<uint16_t*>(p.c), p.ldc, m0 + wm, n0 + wn, M, p.N,
-                          smem, wave, lane, p.act, p.glu, p.ldglu);
+                          smem, wave, lane, HD > 0 ? 0 : p.act, p.glu, p.ldglu);
     return;
   }
 #pragma unroll
