@@ -358,6 +358,30 @@ lr_status lowrank_layer_decode_step(const lr_layer_weights* w, const lr_decode_s
                                     float* h, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* Device scratch of lowrank_layer_decode_step_fused (no reconstructed K/V
+ * buffers).  Zero-fill it before its first use. */
+size_t lowrank_decode_step_fused_workspace_bytes(const lr_layer_weights* w,
+                                                 const lr_decode_state* s);
+
+/*
+ * lowrank_layer_decode_step_fused -- the layer of lowrank_layer_decode_step
+ * with the reconstruction folded into the attention: per 256-row block of a
+ * sequence's compact latents and 256 K/V columns, one workgroup expands K =
+ * RoPE(buf_k V_k) and V = buf_v V_v on chip (both rounded to bf16, as the
+ * reconstruction stores them), scores the block against the sequence's query
+ * heads and writes the block's softmax partials, which a second kernel
+ * combines per head.  The reconstructed rows (2 * cap * n_kv_heads *
+ * head_dim bf16 in lowrank_layer_decode_step) never reach memory.  The
+ * result equals lowrank_layer_decode_step's up to the order of the fp32
+ * sums.  Same arguments, ownership and graph rules.
+ * Errors: as lowrank_layer_decode_step, plus LR_ERR_UNSUPPORTED when
+ * (256 / head_dim) * (n_heads / n_kv_heads) > 16 (query heads per 256
+ * K/V columns).
+ */
+lr_status lowrank_layer_decode_step_fused(const lr_layer_weights* w, const lr_decode_state* s,
+                                          float* h, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
 /*
  * State of one chunked-prefill step (see lowrank_prepare_prefill): T new
  * tokens in S sequences; sequence i's compact segment holds its cached rows
@@ -387,8 +411,9 @@ size_t lowrank_prefill_step_workspace_bytes(const lr_layer_weights* w, const lr_
  * lowrank_layer_decode_step, with causal attention: new token t attends to
  * its sequence's rows 0 .. pos[t] (the cached ones and the chunk's tokens up
  * to itself).  Projections of at most 64 tokens run on the decode path,
- * larger chunks on the prefill path (their o and down outputs are rounded to
- * bf16 before they are added to h).  S <= 255.
+ * larger chunks on the prefill path (below 1024 tokens their o and down
+ * outputs are rounded to bf16 before they are added to h; from 1024 tokens on
+ * they are added in fp32 by the GEMM).  S <= 255.
  * Errors: as lowrank_layer_decode_step (without the B <= 64 limit), plus
  * LR_ERR_ARG for a null tok_seq and LR_ERR_UNSUPPORTED for S > 255.
  */

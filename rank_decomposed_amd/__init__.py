@@ -316,7 +316,8 @@ LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
 __all__ += ["LayerWeights", "DecodeState", "PrefillState", "layer_weights", "decode_state",
             "prefill_state", "lowrank_prefill_step_workspace_bytes", "lowrank_layer_prefill_step",
             "lowrank_rope_table", "lowrank_decode_step_workspace_bytes",
-            "lowrank_layer_decode_step", "LINEARS", "LR_MLP_SWIGLU", "LR_MLP_RELU"]
+            "lowrank_layer_decode_step", "lowrank_decode_step_fused_workspace_bytes",
+            "lowrank_layer_decode_step_fused", "LINEARS", "LR_MLP_SWIGLU", "LR_MLP_RELU"]
 
 
 def lowrank_rope_table(head_dim: int, max_pos: int, theta: float, table, stream=None):
@@ -373,6 +374,21 @@ def lowrank_layer_decode_step(w: LayerWeights, s: DecodeState, h, workspace, str
     _lib.check(load().lowrank_layer_decode_step(C.byref(w), C.byref(s), _ptr(h), _ptr(workspace),
                                                 nbytes, _stream(stream, h.device)),
                "lowrank_layer_decode_step")
+    return h
+
+
+def lowrank_decode_step_fused_workspace_bytes(w: LayerWeights, s: DecodeState) -> int:
+    return int(load().lowrank_decode_step_fused_workspace_bytes(C.byref(w), C.byref(s)))
+
+
+def lowrank_layer_decode_step_fused(w: LayerWeights, s: DecodeState, h, workspace, stream=None):
+    """lowrank_layer_decode_step with the reconstruction folded into the
+    attention, in place on h (fp32 [B, d_model])."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _lib.check(load().lowrank_layer_decode_step_fused(C.byref(w), C.byref(s), _ptr(h),
+                                                      _ptr(workspace), nbytes,
+                                                      _stream(stream, h.device)),
+               "lowrank_layer_decode_step_fused")
     return h
 
 

@@ -36,6 +36,8 @@ SIGNATURES = {
     "lowrank_rope_table": (C.c_int, [_i64, _i64, C.c_float, _p, _p]),
     "lowrank_decode_step_workspace_bytes": (C.c_size_t, [_p, _p]),
     "lowrank_layer_decode_step": (C.c_int, [_p, _p, _p, _p, _sz, _p]),
+    "lowrank_decode_step_fused_workspace_bytes": (C.c_size_t, [_p, _p]),
+    "lowrank_layer_decode_step_fused": (C.c_int, [_p, _p, _p, _p, _sz, _p]),
     "lowrank_prefill_step_workspace_bytes": (C.c_size_t, [_p, _p]),
     "lowrank_layer_prefill_step": (C.c_int, [_p, _p, _p, _p, _sz, _p]),
     "lowrank_packed_bytes": (C.c_size_t, [_i64, _i64]),

@@ -12,7 +12,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 }  // namespace
 
-extern "C" int lowrank_version(void) { return 101; }
+extern "C" int lowrank_version(void) { return 102; }
 
 extern "C" size_t lowrank_abi_sizeof(int which) {
   switch (which) {

@@ -561,6 +561,45 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(const float* __restric
   o[(int64_t)i * ldo + h * HD + threadIdx.x] = (uint16_t)f2bf(used > 0 ? acc / L : 0.f);
 }
 
+// ---------------------------------------------------------------- fused decode attention
+// blk_off[i] = first 256-row block of sequence i's rows [seq_off[i],
+// seq_off[i+1]) (clamped to cap), blocks numbered sequence by sequence;
+// blk_off[S] = their count.  One thread.
+__global__ void row_blocks_kernel(const int32_t* __restrict__ seq_off, int S, int cap,
+                                  int32_t* __restrict__ blk_off) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int nb = 0;
+  for (int i = 0; i < S; ++i) {
+    blk_off[i] = nb;
+    const int b = seq_off[i], e = min(seq_off[i + 1], cap);
+    const int n = (b < 0 || b >= cap || e < b) ? 0 : e - b;
+    nb += (n + 255) / 256;
+  }
+  blk_off[S] = nb;
+}
+
+// o[i, h] from the block partials of sequence i: o = sum_b e^(m_b - M) o_b /
+// sum_b e^(m_b - M) l_b.  Blocks past nbpad (only from corrupt offsets) are
+// skipped.
+template <int HD>
+__global__ __launch_bounds__(HD) void fused_combine_kernel(const float* __restrict__ part, int H,
+                                                           const int32_t* __restrict__ blk_off,
+                                                           int nbpad, uint16_t* __restrict__ o,
+                                                           int64_t ldo) {
+  const int h = blockIdx.x, i = blockIdx.y;
+  const int b0 = max(0, blk_off[i]), b1 = min(nbpad, blk_off[i + 1]);
+  float M = -INFINITY;
+  for (int b = b0; b < b1; ++b) M = fmaxf(M, part[((int64_t)b * H + h) * (HD + 2)]);
+  float L = 0.f, acc = 0.f;
+  for (int b = b0; b < b1; ++b) {
+    const float* pb = part + ((int64_t)b * H + h) * (HD + 2);
+    const float w = expf(pb[0] - M);
+    L = fmaf(w, pb[1], L);
+    acc = fmaf(w, pb[2 + threadIdx.x], acc);
+  }
+  o[(int64_t)i * ldo + h * HD + threadIdx.x] = (uint16_t)f2bf(b1 > b0 ? acc / L : 0.f);
+}
+
 // ---------------------------------------------------------------- workspace
 // One layer step over T new tokens in S sequences: the decode step (one new
 // token per sequence, tok_seq null) and the chunked-prefill step share it.
@@ -595,10 +634,12 @@ constexpr int64_t kDecodeTokens = 64;
 
 struct StepLayout {
   size_t lin, x, q, latk, latv, kbuf, vbuf, krec, vrec, part, o, gate, up, m, yb, tok_off, total;
-  int64_t rk_ld, rv_ld, dkv, nch;
+  int64_t rk_ld, rv_ld, dkv, nch, nbpad;
 };
 
-StepLayout step_layout(const lr_layer_weights* w, const StepIn& s) {
+// fused: decode attention with the reconstruction on chip (no reconstructed
+// K/V buffers; block partials instead of chunk partials)
+StepLayout step_layout(const lr_layer_weights* w, const StepIn& s, bool fused = false) {
   StepLayout L{};
   const int64_t T = s.T, d = w->d_model, dq = w->n_heads * w->head_dim;
   const bool dec = T <= kDecodeTokens;
@@ -636,9 +677,11 @@ StepLayout step_layout(const lr_layer_weights* w, const StepIn& s) {
   L.latv = take(T * w->r[2] * 4);
   L.kbuf = take(s.cap * L.rk_ld * 2);
   L.vbuf = take(s.cap * L.rv_ld * 2);
-  L.krec = take(s.cap * L.dkv * 2);
-  L.vrec = take(s.cap * L.dkv * 2);
-  L.part = take(T * w->n_heads * L.nch * (w->head_dim + 2) * 4);
+  L.nbpad = (s.cap + 255) / 256 + s.S;
+  L.krec = fused ? 0 : take(s.cap * L.dkv * 2);
+  L.vrec = fused ? 0 : take(s.cap * L.dkv * 2);
+  L.part = fused ? take(L.nbpad * w->n_heads * (w->head_dim + 2) * 4)
+                 : take(T * w->n_heads * L.nch * (w->head_dim + 2) * 4);
   L.o = take(T * dq * 2);
   L.gate = take(T * w->d_ffn * 2);
   L.up = w->mlp == LR_MLP_RELU ? L.gate : take(T * w->d_ffn * 2);
@@ -692,8 +735,8 @@ lr_status check_step(const lr_layer_weights* w, const StepIn& s, const float* h)
 }
 
 lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void* workspace,
-                     size_t workspace_bytes, hipStream_t st) {
-  const StepLayout L = step_layout(w, s);
+                     size_t workspace_bytes, hipStream_t st, bool fused = false) {
+  const StepLayout L = step_layout(w, s, fused);
   if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return LR_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -783,53 +826,94 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
                         w->r[1], kbuf, L.rk_ld, st));
   LR_CHECK(remap_gather(2, s.v_pool, s.pool_rows, s.pool_ld, s.remap, s.cap, s.n_valid,
                         w->r[2], vbuf, L.rv_ld, st));
-  // rec[j, :] = buf[j, 0:r] . Vt^T for the live rows j < *n_valid: the
-  // fixed-size GEMM of the replay stage (grid from the capacity), K rows
-  // rotated by their positions in the epilogue.
-  {
-    const BigRope rope{w->rope, w->rope_max_pos, s.seq_off, (int)s.S, (int)w->head_dim};
-    LR_CHECK(gemm_nt_big_rows(kbuf, L.rk_ld, w->Vt[1], w->ldv[1], krec, L.dkv, s.cap, s.n_valid,
-                              L.dkv, w->r[1], &rope, st));
-    LR_CHECK(gemm_nt_big_rows(vbuf, L.rv_ld, w->Vt[2], w->ldv[2], vrec, L.dkv, s.cap, s.n_valid,
-                              L.dkv, w->r[2], nullptr, st));
-  }
-  const dim3 agrid((unsigned)L.nch, (unsigned)w->n_heads, (unsigned)T);
   const int S = (int)s.S;
-  if (s.tok_seq) {
-    // chunked prefill: tiled causal attention over each sequence's rows
-    int32_t* tok_off = reinterpret_cast<int32_t*>(ws + L.tok_off);
-    int32_t* blk_off = tok_off + (S + 1);
-    hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(256), 0, st, s.tok_seq, T, S, tok_off,
+  if (fused) {
+    // attention straight from the gathered latents: K and V expanded per
+    // 256-row block on chip, block partials, then their combine per head
+    int32_t* blk_off = reinterpret_cast<int32_t*>(ws + L.tok_off);
+    float* fpart = reinterpret_cast<float*>(ws + L.part);
+    hipLaunchKernelGGL(row_blocks_kernel, dim3(1), dim3(64), 0, st, s.seq_off, S, (int)s.cap,
                        blk_off);
     LR_CHECK(hipGetLastError());
-    // at most T/kPrefQB + S query blocks over all sequences
-    const int nbpad = (int)((T + kPrefQB - 1) / kPrefQB) + S;
-    const int64_t nitems = (int64_t)w->n_heads * nbpad;
-    const dim3 pgrid((unsigned)((nitems + 7) / 8 * 8));
+    FusedAttnArgs fa{};
+    fa.kl = kbuf;
+    fa.ldkl = L.rk_ld;
+    fa.rk = (int)w->r[1];
+    fa.vl = vbuf;
+    fa.ldvl = L.rv_ld;
+    fa.rv = (int)w->r[2];
+    fa.vk = static_cast<const uint16_t*>(w->Vt[1]);
+    fa.ldvk = w->ldv[1];
+    fa.vv = static_cast<const uint16_t*>(w->Vt[2]);
+    fa.ldvv = w->ldv[2];
+    fa.q = q;
+    fa.ldq = dq;
+    fa.rope = w->rope;
+    fa.max_pos = w->rope_max_pos;
+    fa.seq_off = s.seq_off;
+    fa.pos = s.pos;
+    fa.blk_off = blk_off;
+    fa.S = S;
+    fa.cap = (int)s.cap;
+    fa.H = (int)w->n_heads;
+    fa.Hkv = (int)w->n_kv_heads;
+    fa.nbpad = (int)L.nbpad;
+    fa.part = fpart;
+    LR_CHECK(attn_fused_decode(fa, (int)w->head_dim, st));
     if (w->head_dim == 128)
-      hipLaunchKernelGGL(attn_prefill_kernel<128>, pgrid, dim3(256), 0, st, q, dq, krec, vrec,
-                         L.dkv, s.seq_off, tok_off, blk_off, S, nbpad, s.pos, w->rope,
-                         w->rope_max_pos, (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
+      hipLaunchKernelGGL(fused_combine_kernel<128>, dim3((unsigned)w->n_heads, (unsigned)S),
+                         dim3(128), 0, st, fpart, (int)w->n_heads, blk_off, (int)L.nbpad, o, dq);
     else
-      hipLaunchKernelGGL(attn_prefill_kernel<64>, pgrid, dim3(256), 0, st, q, dq, krec, vrec,
-                         L.dkv, s.seq_off, tok_off, blk_off, S, nbpad, s.pos, w->rope,
-                         w->rope_max_pos, (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
-  } else if (w->head_dim == 128) {
-    hipLaunchKernelGGL(attn_partial_kernel<128>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
-                       L.dkv, s.seq_off, s.tok_seq, S, s.pos, w->rope, w->rope_max_pos,
-                       (int)w->n_heads, (int)w->n_kv_heads, (int)L.nch, (int)s.cap, part);
-    LR_CHECK(hipGetLastError());
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)w->n_heads, (unsigned)T),
-                       dim3(128), 0, st, part, (int)w->n_heads, (int)L.nch, s.seq_off, s.tok_seq,
-                       S, s.pos, (int)s.cap, o, dq);
+      hipLaunchKernelGGL(fused_combine_kernel<64>, dim3((unsigned)w->n_heads, (unsigned)S),
+                         dim3(64), 0, st, fpart, (int)w->n_heads, blk_off, (int)L.nbpad, o, dq);
   } else {
-    hipLaunchKernelGGL(attn_partial_kernel<64>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
-                       L.dkv, s.seq_off, s.tok_seq, S, s.pos, w->rope, w->rope_max_pos,
-                       (int)w->n_heads, (int)w->n_kv_heads, (int)L.nch, (int)s.cap, part);
-    LR_CHECK(hipGetLastError());
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)w->n_heads, (unsigned)T),
-                       dim3(64), 0, st, part, (int)w->n_heads, (int)L.nch, s.seq_off, s.tok_seq,
-                       S, s.pos, (int)s.cap, o, dq);
+    // rec[j, :] = buf[j, 0:r] . Vt^T for the live rows j < *n_valid: the
+    // fixed-size GEMM of the replay stage (grid from the capacity), K rows
+    // rotated by their positions in the epilogue.
+    {
+      const BigRope rope{w->rope, w->rope_max_pos, s.seq_off, (int)s.S, (int)w->head_dim};
+      LR_CHECK(gemm_nt_big_rows(kbuf, L.rk_ld, w->Vt[1], w->ldv[1], krec, L.dkv, s.cap, s.n_valid,
+                                L.dkv, w->r[1], &rope, st));
+      LR_CHECK(gemm_nt_big_rows(vbuf, L.rv_ld, w->Vt[2], w->ldv[2], vrec, L.dkv, s.cap, s.n_valid,
+                                L.dkv, w->r[2], nullptr, st));
+    }
+    const dim3 agrid((unsigned)L.nch, (unsigned)w->n_heads, (unsigned)T);
+    if (s.tok_seq) {
+      // chunked prefill: tiled causal attention over each sequence's rows
+      int32_t* tok_off = reinterpret_cast<int32_t*>(ws + L.tok_off);
+      int32_t* blk_off = tok_off + (S + 1);
+      hipLaunchKernelGGL(tok_offsets_kernel, dim3(1), dim3(256), 0, st, s.tok_seq, T, S, tok_off,
+                         blk_off);
+      LR_CHECK(hipGetLastError());
+      // at most T/kPrefQB + S query blocks over all sequences
+      const int nbpad = (int)((T + kPrefQB - 1) / kPrefQB) + S;
+      const int64_t nitems = (int64_t)w->n_heads * nbpad;
+      const dim3 pgrid((unsigned)((nitems + 7) / 8 * 8));
+      if (w->head_dim == 128)
+        hipLaunchKernelGGL(attn_prefill_kernel<128>, pgrid, dim3(256), 0, st, q, dq, krec, vrec,
+                           L.dkv, s.seq_off, tok_off, blk_off, S, nbpad, s.pos, w->rope,
+                           w->rope_max_pos, (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
+      else
+        hipLaunchKernelGGL(attn_prefill_kernel<64>, pgrid, dim3(256), 0, st, q, dq, krec, vrec,
+                           L.dkv, s.seq_off, tok_off, blk_off, S, nbpad, s.pos, w->rope,
+                           w->rope_max_pos, (int)w->n_heads, (int)w->n_kv_heads, (int)s.cap, o, dq);
+    } else if (w->head_dim == 128) {
+      hipLaunchKernelGGL(attn_partial_kernel<128>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
+                         L.dkv, s.seq_off, s.tok_seq, S, s.pos, w->rope, w->rope_max_pos,
+                         (int)w->n_heads, (int)w->n_kv_heads, (int)L.nch, (int)s.cap, part);
+      LR_CHECK(hipGetLastError());
+      hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((unsigned)w->n_heads, (unsigned)T),
+                         dim3(128), 0, st, part, (int)w->n_heads, (int)L.nch, s.seq_off, s.tok_seq,
+                         S, s.pos, (int)s.cap, o, dq);
+    } else {
+      hipLaunchKernelGGL(attn_partial_kernel<64>, agrid, dim3(256), 0, st, q, dq, krec, vrec,
+                         L.dkv, s.seq_off, s.tok_seq, S, s.pos, w->rope, w->rope_max_pos,
+                         (int)w->n_heads, (int)w->n_kv_heads, (int)L.nch, (int)s.cap, part);
+      LR_CHECK(hipGetLastError());
+      hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((unsigned)w->n_heads, (unsigned)T),
+                         dim3(64), 0, st, part, (int)w->n_heads, (int)L.nch, s.seq_off, s.tok_seq,
+                         S, s.pos, (int)s.cap, o, dq);
+    }
   }
   LR_CHECK(hipGetLastError());
   LR_CHECK(residual_linear(3, o, dq));
@@ -908,6 +992,26 @@ extern "C" lr_status lowrank_layer_decode_step(const lr_layer_weights* w,
   const lr_status chk = check_step(w, in, h);
   if (chk != LR_OK) return chk;
   return layer_step(w, in, h, workspace, workspace_bytes, st);
+}
+
+extern "C" size_t lowrank_decode_step_fused_workspace_bytes(const lr_layer_weights* w,
+                                                            const lr_decode_state* s) {
+  if (!w || !s || s->B <= 0 || s->cap <= 0 || s->max_seq_rows <= 0) return 0;
+  return step_layout(w, from_decode(s), true).total;
+}
+
+extern "C" lr_status lowrank_layer_decode_step_fused(const lr_layer_weights* w,
+                                                     const lr_decode_state* s, float* h,
+                                                     void* workspace, size_t workspace_bytes,
+                                                     hipStream_t st) {
+  if (!s) return LR_ERR_ARG;
+  if (s->B > 64) return LR_ERR_UNSUPPORTED;  // projections run on the decode path
+  const StepIn in = from_decode(s);
+  const lr_status chk = check_step(w, in, h);
+  if (chk != LR_OK) return chk;
+  // the fused kernel stages at most 16 query heads per 256 K/V columns
+  if ((256 / w->head_dim) * (w->n_heads / w->n_kv_heads) > 16) return LR_ERR_UNSUPPORTED;
+  return layer_step(w, in, h, workspace, workspace_bytes, st, true);
 }
 
 extern "C" size_t lowrank_prefill_step_workspace_bytes(const lr_layer_weights* w,

@@ -661,6 +661,310 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- fused decode attention
+// Decode attention with the reconstruction on chip: one workgroup takes a
+// 256-row block of one sequence's cached rows and the 256 K/V columns of
+// 256/HD kv heads.  It expands the block's K latents into K (the large-tile
+// k-loop over r_k), rotates and rounds them to bf16 as the reconstruction
+// would store them, and scores them against the sequence's query heads of
+// those kv heads.  Then it forms the tile's softmax partials (max m, sum l),
+// expands the V latents the same way (bf16, through LDS), and writes
+// o = sum_rows p V per query head with m and l: the combine over a
+// sequence's blocks follows.  The reconstructed rows never reach HBM.
+// Blocks come from blk_off (blk_off[i] = first block of sequence i); the
+// (block, column tile) pairs are dealt to the XCDs in contiguous runs with
+// the column tiles of a block together, so they share its latent rows in L2.
+constexpr int kFusedQH = 16;  // query heads per column tile at most
+
+template <int BN, int BK, int NS, int MBW>
+__device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
+                                              __amdgpu_buffer_rsrc_t ra, int64_t lda,
+                                              __amdgpu_buffer_rsrc_t rb, int64_t ldb, int K,
+                                              uint8_t* smem, int wave, int lane) {
+  constexpr int NW = 2 * gBM / (32 * MBW), NBW = BN / 64, KS = BK / 16;
+  constexpr int kTileA = gBM * BK * 2;
+  constexpr int kStage = big_stage_bytes<BN, BK>();
+  constexpr int IPW = kStage / 1024 / NW;
+  const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int i = 0; i < NBW; ++i)
+#pragma unroll
+    for (int j = 0; j < MBW; ++j) acc[i][j] = f32x16{};
+  auto load_stage = [&](int t) {
+    uint8_t* st = smem + (t % NS) * kStage;
+    load_tile<gBM, BK, NW>(ra, lda, t * BK, K - t * BK, st, wave, lane);
+    load_tile<BN, BK, NW>(rb, ldb, t * BK, K - t * BK, st + kTileA, wave, lane);
+  };
+  auto wait_stage = [&](int younger) {
+    if (younger >= NS - 1) wait_vm<(NS - 1) * IPW>();
+    else if (NS > 3 && younger == 2) wait_vm<(NS > 3 ? 2 : 0) * IPW>();
+    else if (NS > 2 && younger == 1) wait_vm<(NS > 2 ? 1 : 0) * IPW>();
+    else wait_vm<0>();
+  };
+  auto open_stage = [&](int t) {
+    lds_barrier();
+    const int kt = K - t * BK;
+    if (kt < BK && (kt & 7)) {
+      uint8_t* st = smem + (t % NS) * kStage;
+      zero_k_tail<gBM, BK>(st, kt);
+      zero_k_tail<BN, BK>(st + kTileA, kt);
+      lds_barrier();
+    }
+  };
+  u32x4 af[2][MBW], bfr[2][NBW];
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nk) load_stage(t);
+  wait_stage(min(NS - 2, nk - 1));
+  open_stage(0);
+  load_frags<NBW, MBW, BK>(af[0], bfr[0], smem, smem + kTileA, wm, wn, lane, 0);
+  // one barrier per k-tile, the last k-tile peeled (as in gemm_big_kernel)
+  auto k_tile = [&](int t, auto has_next) {
+    if (t + NS - 1 < nk) load_stage(t + NS - 1);
+    const uint8_t* cur = smem + (t % NS) * kStage;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int nb = (ks + 1) & 1;
+      if (ks + 1 < KS) {
+        load_frags<NBW, MBW, BK>(af[nb], bfr[nb], cur, cur + kTileA, wm, wn, lane, ks + 1);
+      } else if constexpr (decltype(has_next)::value) {
+        wait_stage(min(NS - 2, nk - 2 - t));
+        open_stage(t + 1);
+        const uint8_t* nxt = smem + ((t + 1) % NS) * kStage;
+        load_frags<NBW, MBW, BK>(af[nb], bfr[nb], nxt, nxt + kTileA, wm, wn, lane, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int j = 0; j < MBW; ++j)
+          acc[i][j] = mfma32(bfr[ks & 1][i], af[ks & 1][j], acc[i][j]);
+    }
+  };
+  for (int t = 0; t + 1 < nk; ++t) k_tile(t, std::true_type{});
+  k_tile(nk - 1, std::false_type{});
+  lds_barrier();  // operand tiles dead
+}
+
+template <int HD>
+constexpr int fused_lds_bytes() {
+  return gBM * (256 * 2 + 8) + kFusedQH * HD * 4 + kFusedQH * 256 * 4 + kFusedQH * 2 * 4;
+}
+
+template <int HD>
+__global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
+  constexpr int BN = 256, MBW = gMBW, NBW = BN / 64;
+  constexpr int VP = BN * 2 + 8;  // V staging pitch (bytes): rows land 2 banks apart
+  constexpr int QH = kFusedQH;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* qs = reinterpret_cast<float*>(smem + gBM * VP);  // [QH][HD] rotated, scaled queries
+  float* ps = qs + QH * HD;                               // [QH][256] scores, then p
+  float* ml = ps + QH * 256;                              // [QH][2] tile max and sum
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int dkv = p.Hkv * HD, ntn = (dkv + BN - 1) / BN;
+  const int nitems = p.nbpad * ntn, per_xcd = (nitems + 7) / 8;
+  const int item = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+  if ((int)blockIdx.x / 8 >= per_xcd || item >= nitems) return;
+  const int gb = item / ntn, nt = item % ntn;
+  if (gb >= p.blk_off[p.S]) return;
+  int i = 0, hi = p.S;  // the sequence: the last i with blk_off[i] <= gb
+  while (hi - i > 1) {
+    const int mid = (i + hi) >> 1;
+    if (p.blk_off[mid] <= gb) i = mid; else hi = mid;
+  }
+  const int beg = p.seq_off[i];
+  if (beg < 0 || beg >= p.cap) return;  // offsets are device data: stay inside cap
+  const int n = min(p.seq_off[i + 1], p.cap) - beg;
+  const int r0 = (gb - p.blk_off[i]) * gBM;
+  if (r0 < 0 || r0 >= n) return;
+  const int nrows = min(gBM, n - r0), m0 = beg + r0, n0 = nt * BN;
+  const int grp = p.H / p.Hkv, kv0 = n0 / HD;
+  const int nkv = min(BN / HD, p.Hkv - kv0), nq = nkv * grp;
+  const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
+
+  // the tile's query heads, rotated at the new token's position and scaled
+  {
+    int qp = p.pos[i];
+    qp = qp < 0 ? 0 : (qp >= p.max_pos ? (int)p.max_pos - 1 : qp);
+    const float scale = 1.0f / sqrtf((float)HD);
+    for (int t = threadIdx.x; t < nq * (HD / 2); t += blockDim.x) {
+      const int ql = t / (HD / 2), e = t % (HD / 2), h = kv0 * grp + ql;
+      const float cs = p.rope[((int64_t)qp * (HD / 2) + e) * 2];
+      const float sn = p.rope[((int64_t)qp * (HD / 2) + e) * 2 + 1];
+      const float a = bf2f(p.q[(int64_t)i * p.ldq + h * HD + e]);
+      const float b = bf2f(p.q[(int64_t)i * p.ldq + h * HD + e + HD / 2]);
+      qs[ql * HD + e] = (a * cs - b * sn) * scale;
+      qs[ql * HD + e + HD / 2] = (b * cs + a * sn) * scale;
+    }
+  }
+  f32x16 acc[NBW][MBW];
+  // K = latents . V_k^T (the k-loop's barriers also publish qs)
+  tile_mainloop<BN, gBK, gNS, MBW>(
+      acc, make_rsrc(p.kl + (int64_t)m0 * p.ldkl, view_bytes(nrows, p.rk, p.ldkl)), p.ldkl,
+      make_rsrc(p.vk + (int64_t)n0 * p.ldvk, view_bytes(min(dkv - n0, BN), p.rk, p.ldvk)),
+      p.ldvk, p.rk, smem, wave, lane);
+  // rotate each head's column pairs (c, c + HD/2) by the row's position (its
+  // index in the sequence), then round to bf16.  acc[i][j] reg v: column
+  // wn + 32i + 8(v/4) + 4(lane/32) + v%4, row wm + 32j + lane%32.
+  constexpr int hb = HD / 64;
+#pragma unroll
+  for (int j = 0; j < MBW; ++j) {
+    int rp = r0 + wm + 32 * j + (lane & 31);
+    rp = rp >= p.max_pos ? (int)p.max_pos - 1 : rp;
+    const float* tr = p.rope + (int64_t)rp * HD;
+#pragma unroll
+    for (int ib = 0; ib < NBW; ++ib) {
+      if ((32 * ib) % HD >= HD / 2) continue;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int fi = (32 * ib) % HD + 8 * qq + 4 * (lane >> 5);  // 4 frequencies from fi
+        const f32x4 cs01 = *reinterpret_cast<const f32x4*>(tr + 2 * fi);
+        const f32x4 cs23 = *reinterpret_cast<const f32x4*>(tr + 2 * fi + 4);
+        const float c[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
+        const float sn[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a0 = acc[ib][j][4 * qq + e], b0 = acc[ib + hb][j][4 * qq + e];
+          acc[ib][j][4 * qq + e] = a0 * c[e] - b0 * sn[e];
+          acc[ib + hb][j][4 * qq + e] = b0 * c[e] + a0 * sn[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int ib = 0; ib < NBW; ++ib)
+#pragma unroll
+    for (int j = 0; j < MBW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[ib][j][v] = bf2f(f2bf(acc[ib][j][v]));
+  // scores: the wave's 128 columns hold HD-wide heads; a lane has half of a
+  // head's columns for its rows, the partner lane (lane ^ 32) the other half
+#pragma unroll
+  for (int hk = 0; hk < 128 / HD; ++hk) {
+    const int kvl = (wn + hk * HD) / HD;  // kv head within the tile
+    if (kvl >= nkv) continue;
+    for (int g = 0; g < grp; ++g) {
+      const float* qrow = qs + (kvl * grp + g) * HD;
+#pragma unroll
+      for (int j = 0; j < MBW; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int ib = hk * (HD / 32); ib < (hk + 1) * (HD / 32); ++ib)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int d = (32 * ib) % HD + 8 * qq + 4 * (lane >> 5);
+            const f32x4 qv = *reinterpret_cast<const f32x4*>(qrow + d);
+            s = fmaf(acc[ib][j][4 * qq], qv.x, s);
+            s = fmaf(acc[ib][j][4 * qq + 1], qv.y, s);
+            s = fmaf(acc[ib][j][4 * qq + 2], qv.z, s);
+            s = fmaf(acc[ib][j][4 * qq + 3], qv.w, s);
+          }
+        s += __shfl_xor(s, 32);
+        const int row = wm + 32 * j + (lane & 31);
+        if (lane < 32) ps[(kvl * grp + g) * 256 + row] = row < nrows ? s : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+  // softmax partials of the tile: wave w takes query heads w, w + 8
+  for (int qh = wave; qh < nq; qh += 8) {
+    float* pr = ps + qh * 256;
+    float sv[4], mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sv[u] = pr[lane + 64 * u];
+      mx = fmaxf(mx, sv[u]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float pv = expf(sv[u] - mx);  // rows past the block: exp(-inf) = 0
+      pr[lane + 64 * u] = pv;
+      sum += pv;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0) {
+      ml[2 * qh] = mx;
+      ml[2 * qh + 1] = sum;
+    }
+  }
+  // V = latents . V_v^T (its first barrier publishes p, m, l)
+  tile_mainloop<BN, gBK, gNS, MBW>(
+      acc, make_rsrc(p.vl + (int64_t)m0 * p.ldvl, view_bytes(nrows, p.rv, p.ldvl)), p.ldvl,
+      make_rsrc(p.vv + (int64_t)n0 * p.ldvv, view_bytes(min(dkv - n0, BN), p.rv, p.ldvv)),
+      p.ldvv, p.rv, smem, wave, lane);
+  // V tile in bf16 into LDS, row-major (pitch VP)
+#pragma unroll
+  for (int ib = 0; ib < NBW; ++ib)
+#pragma unroll
+    for (int j = 0; j < MBW; ++j)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int row = wm + 32 * j + (lane & 31), col = wn + 32 * ib + 8 * qq + 4 * (lane >> 5);
+        *reinterpret_cast<u32x2*>(smem + row * VP + col * 2) =
+            u32x2{pack_bf2(acc[ib][j][4 * qq], acc[ib][j][4 * qq + 1]),
+                  pack_bf2(acc[ib][j][4 * qq + 2], acc[ib][j][4 * qq + 3])};
+      }
+  __syncthreads();
+  // o[qh][d] = sum_rows p[qh][row] V[row][d]: thread (column, half of the rows)
+  const int col = threadIdx.x & 255, half = threadIdx.x >> 8;
+  const int kvl = col / HD, d = col % HD;
+  float* ob = qs;  // the second half's sums ([QH][HD]); the queries are dead
+  float o[8];
+  const bool live = kvl < nkv;
+  const int rb = half * 128, re = min(nrows, rb + 128);
+  for (int g0 = 0; g0 < grp; g0 += 8) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) o[g] = 0.f;
+    if (live) {
+      for (int r = rb; r < re; ++r) {
+        const float v = bf2f(*reinterpret_cast<const uint16_t*>(smem + r * VP + col * 2));
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+          if (g0 + g < grp) o[g] = fmaf(ps[(kvl * grp + g0 + g) * 256 + r], v, o[g]);
+      }
+    }
+    if (half == 1 && live)
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        if (g0 + g < grp) ob[(kvl * grp + g0 + g) * HD + d] = o[g];
+    __syncthreads();
+    if (half == 0 && live) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if (g0 + g >= grp) continue;
+        const int ql = kvl * grp + g0 + g, h = kv0 * grp + ql;
+        float* out = p.part + ((int64_t)gb * p.H + h) * (HD + 2);
+        out[2 + d] = o[g] + ob[ql * HD + d];
+        if (d == 0) {
+          out[0] = ml[2 * ql];
+          out[1] = ml[2 * ql + 1];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int HD>
+hipError_t launch_fused(const FusedAttnArgs& a, hipStream_t st) {
+  constexpr int lds = fused_lds_bytes<HD>();
+  static_assert(lds <= 160 * 1024, "LDS");
+  static_assert(gNS * big_stage_bytes<256, gBK>() <= gBM * (256 * 2 + 8), "ring inside staging");
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused_kernel<HD>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  });
+  const int64_t ntn = (a.Hkv * HD + 255) / 256, items = (int64_t)a.nbpad * ntn;
+  hipLaunchKernelGGL((attn_fused_kernel<HD>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(512),
+                     lds, st, a);
+  return hipGetLastError();
+}
+
 // Sum of the K-range partials in range order: out32 (fp32, optional) and
 // out16 (bf16, optional) [M, N].  A thread takes 4 consecutive columns of
 // the partials' rows (ldp, a multiple of 8, wide: columns past N are read,
@@ -736,6 +1040,12 @@ size_t gemm_split_bytes(int64_t M, int64_t N) {
   if (tiles >= 128) return 0;
   const int64_t s = std::min<int64_t>(256 / tiles, 8);
   return (size_t)s * M * ((N + 7) / 8 * 8) * 4;
+}
+
+hipError_t attn_fused_decode(const FusedAttnArgs& a, int hd, hipStream_t st) {
+  if (hd == 128) return launch_fused<128>(a, st);
+  if (hd == 64) return launch_fused<64>(a, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t gemm_nt_big_act(const void* A, int64_t lda, const void* B, int64_t ldb, uint16_t* C,

@@ -96,6 +96,34 @@ struct BigRope {
 hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t ldb, uint16_t* C,
                             int64_t ldc, int64_t M, const int32_t* m_valid, int64_t N, int64_t K,
                             const BigRope* rope, hipStream_t st);
+// Decode attention with the reconstruction on chip (one new token per
+// sequence): per 256-row block of a sequence and 256 K/V columns, K and V are
+// expanded from the gathered latents (rotary on K, both rounded to bf16) and
+// the block's softmax partials part[block][h] = {m, l, o[hd]} are written.
+// blk_off[i]: first block of sequence i (blk_off[S] = blocks); nbpad bounds
+// the blocks (cap / 256 + S).  At most 16 query heads per 256 columns.
+struct FusedAttnArgs {
+  const uint16_t* kl;  // K latents [cap, ldkl], rk columns
+  int64_t ldkl;
+  int rk;
+  const uint16_t* vl;  // V latents [cap, ldvl], rv columns
+  int64_t ldvl;
+  int rv;
+  const uint16_t* vk;  // V_k^T [Hkv * hd, ldvk]
+  int64_t ldvk;
+  const uint16_t* vv;  // V_v^T [Hkv * hd, ldvv]
+  int64_t ldvv;
+  const uint16_t* q;   // [S, ldq] bf16 queries before rotary
+  int64_t ldq;
+  const float* rope;   // [max_pos][hd/2] (cos, sin)
+  int64_t max_pos;
+  const int32_t* seq_off;
+  const int32_t* pos;
+  const int32_t* blk_off;
+  int S, cap, H, Hkv, nbpad;
+  float* part;         // [nbpad][H][hd + 2]
+};
+hipError_t attn_fused_decode(const FusedAttnArgs& a, int hd, hipStream_t st);
 size_t prefill_workspace_bytes(int64_t T, int64_t r, int64_t d_out);
 hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st);
 // Whether prefill_linear_bf16 takes the large-tile path for d, the one that

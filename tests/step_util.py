@@ -54,11 +54,12 @@ def pad_dev(bits, ld):
 class Step:
     """B sequences with given cached lengths, n_layers layers, paged latent
     pools with seeded placement.  ranks: one {name: r} for every layer, or a
-    list with one per layer (per-layer ratios)."""
+    list with one per layer (per-layer ratios).  fused: run
+    lowrank_layer_decode_step_fused (reconstruction inside the attention)."""
 
     def __init__(self, cfg_id, cfg, ranks, lengths, n_layers, block=16, fast=False,
-                 max_seq_rows=None, cap=None, slack_blocks=3):
-        self.cfg, self.block = cfg, block
+                 max_seq_rows=None, cap=None, slack_blocks=3, fused=False):
+        self.cfg, self.block, self.fused = cfg, block, fused
         self.lengths = np.asarray(lengths, dtype=np.int64)
         B = len(lengths)
         self.tables, nblocks = synth.block_tables(synth.seed_of(cfg_id, 0, 0, synth.KIND_PLACE),
@@ -99,13 +100,15 @@ class Step:
                                        self.dev_prep["seq_off"], self.dev_prep["pos"],
                                        self.n_valid, self.max_seq_rows)
                        for li in range(n_layers)]
-        nbytes = max(lr.lowrank_decode_step_workspace_bytes(w, s)
-                     for w, s in zip(self.weights, self.states))
+        size = (lr.lowrank_decode_step_fused_workspace_bytes if fused
+                else lr.lowrank_decode_step_workspace_bytes)
+        nbytes = max(size(w, s) for w, s in zip(self.weights, self.states))
         self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=d)
 
     def run(self):
+        step = lr.lowrank_layer_decode_step_fused if self.fused else lr.lowrank_layer_decode_step
         for w, s in zip(self.weights, self.states):
-            lr.lowrank_layer_decode_step(w, s, self.h, self.ws)
+            step(w, s, self.h, self.ws)
         return self.h
 
     def oracle(self, seqs=None):

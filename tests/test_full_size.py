@@ -158,7 +158,9 @@ def test_remap_gather_decode_step_shape_bit_exact():
     assert np.all(got[sample, r:] == 0xABCD)              # past row_elems: untouched
 
 
-def test_decode_step_32_layers_sampled_sequences():
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_step_32_layers_sampled_sequences(fused):
+    # fused: the reconstruction inside the attention (lowrank_layer_decode_step_fused)
     si = step_inputs()
     c = si.cfg
     d = dev()
@@ -177,9 +179,10 @@ def test_decode_step_32_layers_sampled_sequences():
         st = lr.decode_state(pk, pv, dp["slot_mapping"], dp["remap"], dp["seq_off"], dp["pos"],
                              nv, si.max_seq_rows)
         if ws is None:
-            ws = torch.zeros(lr.lowrank_decode_step_workspace_bytes(w, st), dtype=torch.uint8,
-                             device=d)
-        lr.lowrank_layer_decode_step(w, st, h, ws)
+            size = (lr.lowrank_decode_step_fused_workspace_bytes if fused
+                    else lr.lowrank_decode_step_workspace_bytes)
+            ws = torch.zeros(size(w, st), dtype=torch.uint8, device=d)
+        (lr.lowrank_layer_decode_step_fused if fused else lr.lowrank_layer_decode_step)(w, st, h, ws)
         torch.cuda.synchronize()
         print("layer %d done" % li, flush=True)
         del pk, pv, w, st, Ut, Vt
@@ -193,6 +196,6 @@ def test_decode_step_32_layers_sampled_sequences():
                              si.lengths[seqs], si.block, c)
     for k, i in enumerate(seqs):
         err = maxrel(got[i], ref[k])
-        print("32-layer decode step, sequence %d (L=%d): max rel err %.2e"
-              % (i, si.lengths[i], err))
+        print("32-layer decode step%s, sequence %d (L=%d): max rel err %.2e"
+              % (" (fused)" if fused else "", i, si.lengths[i], err))
         assert err <= BF16_TOL
