@@ -11,7 +11,8 @@ Prints one JSON line: whole-job tokens/s (tokens x layer sets / s), the
 roofline of the dominant launch, and the fp64 CPU oracle timed on a bounded
 sample of the same workload.  Also reports, as context: the prefill
 configuration (16384 rows, ratio 0.4 and 0.2) under "prefill", the 32-layer
-decode step under "decode_step", the 32-layer chunked-prefill step (8
+decode step under "decode_step" (and with the reconstruction inside the
+attention under "decode_step_fused"), the 32-layer chunked-prefill step (8
 prompts of 512 tokens) under "prefill_step", and one of 8 tensor-parallel
 shares of the LLaMA-13B projections (ratio 0.4, T = 64 and 4096) under
 "tp_share".
@@ -313,6 +314,10 @@ def main():
         result["decode_step"] = decode_step(torch, lr, dev, stream, args.step_layers,
                                             max(3, args.steps // 2))
         log("decode-step leg done")
+        torch.cuda.empty_cache()
+        result["decode_step_fused"] = decode_step(torch, lr, dev, stream, args.step_layers,
+                                                  max(3, args.steps // 2), fused=True)
+        log("fused decode-step leg done")
 
     if not args.no_prefill_step:
         torch.cuda.empty_cache()
@@ -475,10 +480,12 @@ def tp_share(torch, lr, dev, stream, reps, n_sets=32, P=8):
     return out
 
 
-def decode_step(torch, lr, dev, stream, n_layers, reps):
+def decode_step(torch, lr, dev, stream, n_layers, reps, fused=False):
     """The 32-layer decode step of a LLaMA-7B-shaped decoder decomposed at
     ratio 0.2 (64 sequences, cached lengths uniform in [128, 4096]) captured
-    once in a HIP graph and replayed; preparation stage timed separately."""
+    once in a HIP graph and replayed; preparation stage timed separately.
+    fused: lowrank_layer_decode_step_fused (the reconstruction expanded per
+    256-row block inside the attention; no reconstructed K/V in memory)."""
     from synth.decode_step import DecodeStepInputs
     si = DecodeStepInputs(n_layers=n_layers, device=dev)
     c = si.cfg
@@ -497,15 +504,17 @@ def decode_step(torch, lr, dev, stream, n_layers, reps):
         st = lr.decode_state(si.device_pool(li, 0), si.device_pool(li, 1), dp["slot_mapping"],
                              dp["remap"], dp["seq_off"], dp["pos"], nv, si.max_seq_rows)
         layers.append((w, st))
-    ws = torch.zeros(lr.lowrank_decode_step_workspace_bytes(*layers[0]), dtype=torch.uint8,
-                     device=dev)
+    size = (lr.lowrank_decode_step_fused_workspace_bytes if fused
+            else lr.lowrank_decode_step_workspace_bytes)
+    layer_step = lr.lowrank_layer_decode_step_fused if fused else lr.lowrank_layer_decode_step
+    ws = torch.zeros(size(*layers[0]), dtype=torch.uint8, device=dev)
     h0 = torch.from_numpy(si.h0.astype(np.float32)).to(dev)
     h = h0.clone()
 
     def step():
         h.copy_(h0)
         for w, st in layers:
-            lr.lowrank_layer_decode_step(w, st, h, ws)
+            layer_step(w, st, h, ws)
 
     side = torch.cuda.Stream(dev)
     side.wait_stream(torch.cuda.current_stream(dev))
@@ -534,8 +543,9 @@ def decode_step(torch, lr, dev, stream, n_layers, reps):
                     for n, (a_, b_) in dims(c).items())
     gather_bytes = 2 * nvr * (rk + rv) * 2
     recon_flops = 2.0 * nvr * (rk + rv) * dkv
-    recon_bytes = nvr * (rk + rv) * 2 + 2 * nvr * dkv * 2
-    attn_bytes = 2 * nvr * dkv * 2
+    # fused: the reconstructed rows stay on chip (latents read once)
+    recon_bytes = nvr * (rk + rv) * 2 + (0 if fused else 2 * nvr * dkv * 2)
+    attn_bytes = 0 if fused else 2 * nvr * dkv * 2
     roof_s = (lin_bytes / HBM_PEAK + gather_bytes / HBM_PEAK
               + max(recon_flops / BF16_PEAK, recon_bytes / HBM_PEAK) + attn_bytes / HBM_PEAK)
     roof_ms = 1e3 * roof_s * n_layers

@@ -668,12 +668,14 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
 // k-loop over r_k), rotates and rounds them to bf16 as the reconstruction
 // would store them, and scores them against the sequence's query heads of
 // those kv heads.  Then it forms the tile's softmax partials (max m, sum l),
-// expands the V latents the same way (bf16, through LDS), and writes
-// o = sum_rows p V per query head with m and l: the combine over a
-// sequence's blocks follows.  The reconstructed rows never reach HBM.
-// Blocks come from blk_off (blk_off[i] = first block of sequence i); the
-// (block, column tile) pairs are dealt to the XCDs in contiguous runs with
-// the column tiles of a block together, so they share its latent rows in L2.
+// expands the V latents the same way (bf16), and sums o = sum_rows p V per
+// query head in registers (a butterfly across the row lanes), writing it
+// with m and l: the combine over a sequence's blocks follows.  The reconstructed rows never reach HBM.
+// Blocks come from blk_off (blk_off[i] = first block of sequence i).  With
+// a multiple of 8 column tiles each XCD keeps its share of them for every
+// block, so the two up-projection tiles it reads stay in its L2 (both
+// factors together exceed one L2); otherwise the (block, column tile) pairs
+// go to the XCDs in contiguous runs.
 constexpr int kFusedQH = 16;  // query heads per column tile at most
 
 template <int BN, int BK, int NS, int MBW>
@@ -746,26 +748,59 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
   lds_barrier();  // operand tiles dead
 }
 
+// LDS: the operand ring (reused for the row waves' output sums), then the
+// queries, scores and tile (max, sum) pairs.
+template <int HD>
+constexpr int fused_ring_bytes() {
+  return gNS * big_stage_bytes<256, gBK>() > 4 * kFusedQH * HD * 4
+             ? gNS * big_stage_bytes<256, gBK>() : 4 * kFusedQH * HD * 4;
+}
 template <int HD>
 constexpr int fused_lds_bytes() {
-  return gBM * (256 * 2 + 8) + kFusedQH * HD * 4 + kFusedQH * 256 * 4 + kFusedQH * 2 * 4;
+  return fused_ring_bytes<HD>() + kFusedQH * HD * 4 + kFusedQH * 256 * 4 + kFusedQH * 2 * 4;
+}
+
+// One butterfly step over the lanes that differ in bit sh: N values become
+// N / 2, the upper half kept where that lane bit is set, the lower half
+// elsewhere, each plus the partner's copy of the same half.
+template <int N>
+__device__ __forceinline__ void bfly_step(float* val, int lane, int sh) {
+  const bool up = (lane & sh) != 0;
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float keep = up ? val[k + N / 2] : val[k];
+    const float send = up ? val[k] : val[k + N / 2];
+    val[k] = keep + __shfl_xor(send, sh);
+  }
 }
 
 template <int HD>
 __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   constexpr int BN = 256, MBW = gMBW, NBW = BN / 64;
-  constexpr int VP = BN * 2 + 8;  // V staging pitch (bytes): rows land 2 banks apart
   constexpr int QH = kFusedQH;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float* qs = reinterpret_cast<float*>(smem + gBM * VP);  // [QH][HD] rotated, scaled queries
+  float* qs = reinterpret_cast<float*>(smem + fused_ring_bytes<HD>());  // [QH][HD] queries
   float* ps = qs + QH * HD;                               // [QH][256] scores, then p
   float* ml = ps + QH * 256;                              // [QH][2] tile max and sum
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int dkv = p.Hkv * HD, ntn = (dkv + BN - 1) / BN;
-  const int nitems = p.nbpad * ntn, per_xcd = (nitems + 7) / 8;
-  const int item = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
-  if ((int)blockIdx.x / 8 >= per_xcd || item >= nitems) return;
-  const int gb = item / ntn, nt = item % ntn;
+  int gb, nt;
+  if (ntn % 8 == 0) {
+    // each XCD keeps ntn / 8 column tiles (their V_k and V_v rows stay in its
+    // L2) and walks the blocks in order, its column tiles of a block together
+    const int npx = ntn / 8, w = (int)blockIdx.x / 8;
+    if (w >= p.nbpad * npx) return;
+    gb = w / npx;
+    nt = ((int)blockIdx.x % 8) * npx + w % npx;
+  } else {
+    // the (block, column tile) list in contiguous runs per XCD, a block's
+    // column tiles together
+    const int nitems = p.nbpad * ntn, per_xcd = (nitems + 7) / 8;
+    const int item = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+    if ((int)blockIdx.x / 8 >= per_xcd || item >= nitems) return;
+    gb = item / ntn;
+    nt = item % ntn;
+  }
   if (gb >= p.blk_off[p.S]) return;
   int i = 0, hi = p.S;  // the sequence: the last i with blk_off[i] <= gb
   while (hi - i > 1) {
@@ -896,56 +931,80 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
       acc, make_rsrc(p.vl + (int64_t)m0 * p.ldvl, view_bytes(nrows, p.rv, p.ldvl)), p.ldvl,
       make_rsrc(p.vv + (int64_t)n0 * p.ldvv, view_bytes(min(dkv - n0, BN), p.rv, p.ldvv)),
       p.ldvv, p.rv, smem, wave, lane);
-  // V tile in bf16 into LDS, row-major (pitch VP)
+  // o[qh][c] = sum_rows p[qh][row] V[row][c] from the registers: a lane
+  // weights its two rows' bf16 values of the head's columns by p and sums
+  // them, then a butterfly over the 32 row lanes (each step keeps half the
+  // columns and adds the partner's half) leaves every lane with two
+  // columns' sums; the four row waves meet in LDS.
+  constexpr int NV = HD / 2;  // a lane's values of one head (two rows summed)
+  float* red = reinterpret_cast<float*>(smem);  // [4][QH][HD], the ring is dead
+  const int rw = wave >> 1;
+  uint32_t vpk[NBW][MBW][8];  // V rounded to bf16, register pairs packed
 #pragma unroll
   for (int ib = 0; ib < NBW; ++ib)
 #pragma unroll
     for (int j = 0; j < MBW; ++j)
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int row = wm + 32 * j + (lane & 31), col = wn + 32 * ib + 8 * qq + 4 * (lane >> 5);
-        *reinterpret_cast<u32x2*>(smem + row * VP + col * 2) =
-            u32x2{pack_bf2(acc[ib][j][4 * qq], acc[ib][j][4 * qq + 1]),
-                  pack_bf2(acc[ib][j][4 * qq + 2], acc[ib][j][4 * qq + 3])};
+      for (int v2 = 0; v2 < 8; ++v2)
+        vpk[ib][j][v2] = pack_bf2(acc[ib][j][2 * v2], acc[ib][j][2 * v2 + 1]);
+#pragma unroll
+  for (int hk = 0; hk < 128 / HD; ++hk) {
+    const int kvl = (wn + hk * HD) / HD;
+    if (kvl >= nkv) continue;
+    for (int g = 0; g < grp; ++g) {
+      const int ql = kvl * grp + g;
+      const float p0 = ps[ql * 256 + wm + (lane & 31)], p1 = ps[ql * 256 + wm + 32 + (lane & 31)];
+      // value k: p0 V[row 0][column k] + p1 V[row 1][column k]; the first
+      // butterfly step (lane bit 16) is taken as the values are formed
+      auto pv = [&](int k) {
+        const int ib = hk * (HD / 32) + k / 16, v = k % 16, sh = 16 * (v & 1);
+        return p0 * bf2f((vpk[ib][0][v >> 1] >> sh) & 0xffffu) +
+               p1 * bf2f((vpk[ib][1][v >> 1] >> sh) & 0xffffu);
+      };
+      float val[NV / 2];
+      const bool up16 = (lane & 16) != 0;
+#pragma unroll
+      for (int k = 0; k < NV / 2; ++k) {
+        const float a = pv(k), b = pv(k + NV / 2);
+        val[k] = (up16 ? b : a) + __shfl_xor(up16 ? a : b, 16);
       }
-  __syncthreads();
-  // o[qh][d] = sum_rows p[qh][row] V[row][d]: thread (column, half of the rows)
-  const int col = threadIdx.x & 255, half = threadIdx.x >> 8;
-  const int kvl = col / HD, d = col % HD;
-  float* ob = qs;  // the second half's sums ([QH][HD]); the queries are dead
-  float o[8];
-  const bool live = kvl < nkv;
-  const int rb = half * 128, re = min(nrows, rb + 128);
-  for (int g0 = 0; g0 < grp; g0 += 8) {
-#pragma unroll
-    for (int g = 0; g < 8; ++g) o[g] = 0.f;
-    if (live) {
-      for (int r = rb; r < re; ++r) {
-        const float v = bf2f(*reinterpret_cast<const uint16_t*>(smem + r * VP + col * 2));
-#pragma unroll
-        for (int g = 0; g < 8; ++g)
-          if (g0 + g < grp) o[g] = fmaf(ps[(kvl * grp + g0 + g) * 256 + r], v, o[g]);
+      bfly_step<NV / 2>(val, lane, 8);
+      bfly_step<NV / 4>(val, lane, 4);
+      bfly_step<NV / 8>(val, lane, 2);
+      if (NV == 64) {
+        bfly_step<4>(val, lane, 1);
+      } else {  // the xor-1 lanes hold the same two columns: add them
+        val[0] += __shfl_xor(val[0], 1);
+        val[1] += __shfl_xor(val[1], 1);
       }
-    }
-    if (half == 1 && live)
+      // the lane's two columns: index k = 32 b4 + 16 b3 + 8 b2 + 4 b1 + 2 b0 + e
+      // (b: lane bits; for NV == 32 without b0) -> (block k / 16, register k % 16)
+      if (NV == 64 || (lane & 1) == 0) {
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
-        if (g0 + g < grp) ob[(kvl * grp + g0 + g) * HD + d] = o[g];
-    __syncthreads();
-    if (half == 0 && live) {
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        if (g0 + g >= grp) continue;
-        const int ql = kvl * grp + g0 + g, h = kv0 * grp + ql;
-        float* out = p.part + ((int64_t)gb * p.H + h) * (HD + 2);
-        out[2 + d] = o[g] + ob[ql * HD + d];
-        if (d == 0) {
-          out[0] = ml[2 * ql];
-          out[1] = ml[2 * ql + 1];
+        for (int e = 0; e < 2; ++e) {
+          const int kk = NV == 64 ? (((lane >> 4) & 1) * 32 + ((lane >> 3) & 1) * 16 +
+                                     ((lane >> 2) & 1) * 8 + ((lane >> 1) & 1) * 4 +
+                                     (lane & 1) * 2 + e)
+                                  : (((lane >> 4) & 1) * 16 + ((lane >> 3) & 1) * 8 +
+                                     ((lane >> 2) & 1) * 4 + ((lane >> 1) & 1) * 2 + e);
+          const int v = kk % 16;
+          const int c = 32 * (kk / 16) + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);  // in the head
+          red[(rw * QH + ql) * HD + c] = val[e];
         }
       }
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < nq * HD; t += blockDim.x) {
+    const int ql = t / HD, c = t % HD, h = kv0 * grp + ql;
+    const float o = red[(0 * QH + ql) * HD + c] + red[(1 * QH + ql) * HD + c] +
+                    red[(2 * QH + ql) * HD + c] + red[(3 * QH + ql) * HD + c];
+    float* out = p.part + ((int64_t)gb * p.H + h) * (HD + 2);
+    out[2 + c] = o;
+    if (c == 0) {
+      out[0] = ml[2 * ql];
+      out[1] = ml[2 * ql + 1];
+    }
   }
 }
 
@@ -953,7 +1012,6 @@ template <int HD>
 hipError_t launch_fused(const FusedAttnArgs& a, hipStream_t st) {
   constexpr int lds = fused_lds_bytes<HD>();
   static_assert(lds <= 160 * 1024, "LDS");
-  static_assert(gNS * big_stage_bytes<256, gBK>() <= gBM * (256 * 2 + 8), "ring inside staging");
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused_kernel<HD>),
