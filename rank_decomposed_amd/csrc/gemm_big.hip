@@ -280,6 +280,19 @@ constexpr int big_stage_bytes() { return (gBM + BN) * BK * 2; }
 // LDS of one launch: the operand ring, reused by the epilogue (bf16 result
 // staging 256 * BN * 2 bytes; rotary tables 256 rows * HD * 4 bytes), then
 // (rotary) 2 KB of sequence offsets and row positions.
+// Tile order: tiles are listed kGroupM row tiles at a time, column by column
+// (tile q of the group of rows [g, g + kGroupM) is row g + q % rows, column
+// q / rows).  An XCD's contiguous run of tiles is then a block of rows x
+// columns, so the tiles it runs at once share both their A rows and their B
+// rows in its L2 (row by row, every column tile of a row ran at once and the
+// B operand streamed through the L2 again for every row).
+constexpr int kGroupM = 4;
+__device__ __forceinline__ int group_rows(int t, int ntn, int ntm) {
+  const int first = t / (kGroupM * ntn) * kGroupM;
+  const int rows = min(kGroupM, ntm - first), q = t % (kGroupM * ntn);
+  return (first + q % rows) * ntn + q / rows;
+}
+
 template <int BN, int BK, int NS, int HD>
 constexpr int big_lds_bytes() {
   constexpr int ring = NS * big_stage_bytes<BN, BK>();
@@ -314,7 +327,8 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
   const int per_xcd = (ntiles + 7) / 8;
   const int vtile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;  // (tile, K range)
   if ((int)blockIdx.x / 8 >= per_xcd || vtile >= ntiles) return;
-  const int tile = vtile / p.ksplit, kr = vtile % p.ksplit;
+  const int tile = group_rows(vtile / p.ksplit, ntn, (M + gBM - 1) / gBM);
+  const int kr = vtile % p.ksplit;
   const int m0 = (tile / ntn) * gBM, n0 = (tile % ntn) * BN;
   const int kbeg = kr * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
   const __amdgpu_buffer_rsrc_t ra =
