@@ -639,6 +639,12 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_persist_kernel
 // tile 32 * gMBW rows
 constexpr int gBK = 32, gNS = 3, gMBW = 2;
 
+// k-tile depth of the one-tile-per-workgroup launches: 128-column tiles take
+// 64-deep k-tiles (three of them fit the LDS), so each operand row of a load
+// is one whole 128-byte line; 256-column tiles keep 32-deep k-tiles.
+template <int BN>
+constexpr int big_bk() { return BN == 128 ? 64 : gBK; }
+
 // Persistent launch: one workgroup per CU (the grid is a multiple of 8 and
 // at most 256), for bf16 output with 16-byte row stores and no rotary.
 template <int BN>
@@ -660,16 +666,17 @@ hipError_t launch_persist(const BigArgs& a, hipStream_t st) {
 
 template <int BN, bool OUT_F32, int HD = 0>
 hipError_t launch_big(const BigArgs& a, hipStream_t st) {
-  constexpr int lds = big_lds_bytes<BN, gBK, gNS, HD>();
+  constexpr int kBK = big_bk<BN>();
+  constexpr int lds = big_lds_bytes<BN, kBK, gNS, HD>();
   static_assert(lds <= 160 * 1024, "LDS");
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD, gMBW>),
+        reinterpret_cast<const void*>(&gemm_big_kernel<BN, kBK, gNS, OUT_F32, HD, gMBW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + gBM - 1) / gBM) * a.ksplit;
-  hipLaunchKernelGGL((gemm_big_kernel<BN, gBK, gNS, OUT_F32, HD, gMBW>),
+  hipLaunchKernelGGL((gemm_big_kernel<BN, kBK, gNS, OUT_F32, HD, gMBW>),
                      dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(2 * gBM / (32 * gMBW) * 64), lds,
                      st, a);
   return hipGetLastError();

@@ -80,6 +80,24 @@ def test_bf16_prefill_large_tile_path(T, shape):
     assert np.array_equal(bits(y_t), bits(y))
 
 
+@pytest.mark.parametrize("T,shape", [(2600, (512, 300, 2100)), (3333, (1040, 700, 1000))])
+def test_bf16_prefill_grouped_tile_order(T, shape):
+    # the large-tile GEMM lists tiles four row tiles at a time: 11 and 14 row
+    # tiles (two full groups and a partial one of 3 or 2 rows) against 9 / 4
+    # output column tiles and 2 / 3-6 rank column tiles, with a ragged last
+    # 64-deep k-tile in stage 1 (d_in 1040); every output tile must be
+    # computed exactly once (outputs start as NaN)
+    d_in, r, d_out = shape
+    c = make_linear(3900 + T + r, T, d_in, r, d_out, "bf16", fast=True, ld_extra=8)
+    y = torch.full((T, d_out), float("nan"), dtype=torch.bfloat16, device=dev())
+    t = torch.full((T, r), float("nan"), dtype=torch.float32, device=dev())
+    lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"], y=y, t_io=t)
+    torch.cuda.synchronize()
+    tr, yr = oracle.linear(c["x"], c["U"], c["V"])
+    assert maxrel(to_f64(t), tr) <= 1e-5
+    assert maxrel(to_f64(y), yr) <= BF16_TOL
+
+
 @pytest.mark.parametrize("T,shape", [(1100, (3003, 96, 320)), (1024, (4096, 409, 512)),
                                      (2000, (11008, 597, 4096)), (1024, (1200, 1100, 1300))])
 def test_bf16_prefill_split_k(T, shape):
