@@ -3,16 +3,17 @@
 // Used for the many-token (prefill) decomposed linear: both stages, x U_r and
 // t V_r, have this form with the factors stored transposed.
 //
-// Tile 256 x BN x BK (BN = 256 or 128), one workgroup of 4 waves, each wave
-// 128 x BN/2.  Operand tiles move global -> LDS with direct-to-LDS buffer
+// Tile 256 x BN x BK (BN = 256 or 128), one workgroup of 8 waves, each wave
+// 64 x BN/2.  Operand tiles move global -> LDS with direct-to-LDS buffer
 // loads (no registers in between) through a ring of NS stages: the loads of
 // the next NS - 1 k-tiles are in flight while one multiplies.  LDS rows are
 // BK * 2 bytes with the 16-byte chunk index XOR-swizzled by row, so the
 // fragment reads (32 rows at one chunk) spread over the banks.  The MFMA
 // takes the B fragment as its first operand, so each lane ends with 4
 // consecutive output columns of one row; bf16 results are staged through LDS
-// and written as whole 128-byte lines.  Tiles go to the 8 XCDs in contiguous
-// runs (workgroups are dealt to XCDs round robin), so an XCD's tiles share A
+// and written as whole 128-byte lines.  Tiles are listed four row tiles at a
+// time and go to the 8 XCDs in contiguous runs of that list (workgroups are
+// dealt to XCDs round robin), so the tiles an XCD runs at once share A and B
 // rows in its L2.  Rows past M or N and k-chunks past K read zero from
 // outside the buffers; the padding in the last partial chunk is zeroed in
 // LDS.
@@ -635,15 +636,18 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_persist_kernel
   k_tile(total - 1, std::false_type{});
 }
 
-// k-pipeline of every launch: 32-deep k-tiles in a ring of 3 stages; wave
-// tile 32 * gMBW rows
+// k-pipeline of the persistent launch and the fused attention: 32-deep
+// k-tiles in a ring of 3 stages; wave tile 32 * gMBW rows (every launch)
 constexpr int gBK = 32, gNS = 3, gMBW = 2;
 
-// k-tile depth of the one-tile-per-workgroup launches: 128-column tiles take
-// 64-deep k-tiles (three of them fit the LDS), so each operand row of a load
-// is one whole 128-byte line; 256-column tiles keep 32-deep k-tiles.
+// k-pipeline of the one-tile-per-workgroup launches: 64-deep k-tiles, so each
+// operand row of a direct-to-LDS load is one whole 128-byte line (32-deep
+// tiles fetch every line in two halves, one k-tile apart).  Three stages of
+// 384 x 64 fit the LDS for 128-column tiles, two of 512 x 64 for 256-column
+// tiles.
+constexpr int kBigBK = 64;
 template <int BN>
-constexpr int big_bk() { return BN == 128 ? 64 : gBK; }
+constexpr int big_ns() { return BN == 128 ? 3 : 2; }
 
 // Persistent launch: one workgroup per CU (the grid is a multiple of 8 and
 // at most 256), for bf16 output with 16-byte row stores and no rotary.
@@ -666,17 +670,17 @@ hipError_t launch_persist(const BigArgs& a, hipStream_t st) {
 
 template <int BN, bool OUT_F32, int HD = 0>
 hipError_t launch_big(const BigArgs& a, hipStream_t st) {
-  constexpr int kBK = big_bk<BN>();
-  constexpr int lds = big_lds_bytes<BN, kBK, gNS, HD>();
+  constexpr int kBK = kBigBK, kNS = big_ns<BN>();
+  constexpr int lds = big_lds_bytes<BN, kBK, kNS, HD>();
   static_assert(lds <= 160 * 1024, "LDS");
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_big_kernel<BN, kBK, gNS, OUT_F32, HD, gMBW>),
+        reinterpret_cast<const void*>(&gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + gBM - 1) / gBM) * a.ksplit;
-  hipLaunchKernelGGL((gemm_big_kernel<BN, kBK, gNS, OUT_F32, HD, gMBW>),
+  hipLaunchKernelGGL((gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW>),
                      dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(2 * gBM / (32 * gMBW) * 64), lds,
                      st, a);
   return hipGetLastError();
