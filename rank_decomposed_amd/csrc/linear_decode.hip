@@ -25,9 +25,10 @@
 //     streams quickly).  With S1 > 1 the partials meet in the workspace and
 //     the last tile of the row block to arrive sums them in K-range order.
 //     The finishing tile publishes its rows of t (fp32 for t_io, bf16 for
-//     stage 2; for T <= 16 also the bf16 residual t - bf16(t), so stage 2
-//     sees ~16 mantissa bits at the cost of a second MFMA) and bumps the
-//     "t ready" counter; the last one raises the GO flag.
+//     stage 2 in the fragment-packed layout the weights use; for T <= 16 also
+//     the bf16 residual t - bf16(t), so stage 2 sees ~16 mantissa bits at the
+//     cost of a second MFMA) and bumps the "t ready" counter; the last one
+//     raises the GO flag.
 //   stage-2 tile: 16*RB2 rows of V_r^T over all of r.  Each wave issues the
 //     loads of its first PF steps of V_r *before* waiting for GO, so the V_r
 //     stream overlaps stage 1; then it reads t and finishes, writing y in
@@ -88,7 +89,7 @@ struct LinArgs {
   int64_t ldacc;
   float* t32;  // optional fp32 t [T, ldt32] (stage-1 output)
   int64_t ldt32;
-  uint16_t* thi;  // bf16 t [T, ldtb]
+  uint16_t* thi;  // bf16 t, fragment-packed (tpack), ldtb k-steps per token block
   uint16_t* tlo;  // bf16 residual (T <= 16)
   int64_t ldtb;
   float* part;    // stage-1 split-K partials
@@ -109,6 +110,16 @@ struct DecArgs {
   int n, T, n1;  // linears, tokens, stage-1 tiles in all
 };
 
+// Element (tok, n) of the bf16 t handed to stage 2, which is stored
+// fragment-packed like the weights: 16-token blocks of nst 32-wide steps, the
+// 16 bytes of lane (tok % 16) + 16 * (n % 32 / 8) of step n / 32 holding
+// n % 8.  A stage-2 fragment load is then 1 KB of contiguous memory; t in
+// token rows would give 16 rows x 64 bytes, every cache line fetched in two
+// halves one k-step apart.
+__device__ __forceinline__ int64_t tpack(int tok, int n, int64_t nst) {
+  return ((((int64_t)(tok >> 4) * nst + (n >> 5)) * 64 + (tok & 15) + 16 * ((n & 31) >> 3)) << 3) +
+         (n & 7);
+}
 // Relaxed device-scope atomics: on gfx950 these are plain loads/stores with
 // device coherence (no cache maintenance); ordering is made explicit with a
 // wait for outstanding memory operations before a counter is bumped.
@@ -206,12 +217,18 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
   const int kq = (lane >> 4) * 8;
   const int K = kend - kbeg;
   const WeightTile<RB> w(B, ldb, packed, N, row0, kbeg, kend, lane);
-  const uint64_t abytes = view_bytes(min(T, 16 * TB), K, lda);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + kbeg, abytes);
-  const __amdgpu_buffer_rsrc_t ral = make_rsrc((SPLIT ? Alo : A) + kbeg, abytes);
+  // stage 2 (WAIT) reads t fragment-packed (lda = steps per token block, the
+  // K range starts at 0): one k-step is 1 KB per token block
+  constexpr int ASTEP = WAIT ? 1024 : 64;
+  const uint64_t abytes =
+      WAIT ? (uint64_t)TB * lda * 1024 : view_bytes(min(T, 16 * TB), K, lda);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(WAIT ? A : A + kbeg, abytes);
+  const __amdgpu_buffer_rsrc_t ral = make_rsrc((SPLIT ? Alo : A) + (WAIT ? 0 : kbeg), abytes);
   uint32_t aoff[TB];
 #pragma unroll
-  for (int tb = 0; tb < TB; ++tb) aoff[tb] = (uint32_t)(((tb * 16 + (lane & 15)) * lda + kq) * 2);
+  for (int tb = 0; tb < TB; ++tb)
+    aoff[tb] = WAIT ? (uint32_t)((tb * lda * 64 + lane) * 16)
+                    : (uint32_t)(((tb * 16 + (lane & 15)) * lda + kq) * 2);
 
   const int nsteps = (K + 31) / 32;
   const int nfull = K / 32;
@@ -230,8 +247,8 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
     u32x4 av[KSW][TB], alv[KSW][TB];
 #pragma unroll
     for (int i = 0; i < KSW; ++i) {
-      frag_load_at<TB, WAIT>(av[i], ra, aoff, (sb + i) * 64, sb + i < s_full);
-      if (SPLIT) frag_load_at<TB, WAIT>(alv[i], ral, aoff, (sb + i) * 64, sb + i < s_full);
+      frag_load_at<TB, WAIT>(av[i], ra, aoff, (sb + i) * ASTEP, sb + i < s_full);
+      if (SPLIT) frag_load_at<TB, WAIT>(alv[i], ral, aoff, (sb + i) * ASTEP, sb + i < s_full);
     }
 #pragma unroll
     for (int i = 0; i < KSW; ++i)
@@ -277,8 +294,8 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
     const int kk = nfull * 32 + kq;
     u32x4 bv[RB], av[TB], alv[TB];
     frag_load_at<RB, false>(bv, w.rs, w.off, nfull * w.step, true);
-    frag_load_at<TB, WAIT>(av, ra, aoff, nfull * 64, true);
-    if (SPLIT) frag_load_at<TB, WAIT>(alv, ral, aoff, nfull * 64, true);
+    frag_load_at<TB, WAIT>(av, ra, aoff, nfull * ASTEP, true);
+    if (SPLIT) frag_load_at<TB, WAIT>(alv, ral, aoff, nfull * ASTEP, true);
 #pragma unroll
     for (int r = 0; r < RB; ++r) bv[r] = mask_tail_nb(bv[r], kk, K);
 #pragma unroll
@@ -477,8 +494,9 @@ void decode_kernel(DecArgs args) {
       if (e >= NE || tok >= T || n >= p.r) continue;
       if (p.t32) p.t32[(int64_t)tok * p.ldt32 + n] = val[i];
       const uint32_t hi = f2bf(val[i]);
-      store_coherent(p.thi + (int64_t)tok * p.ldtb + n, (uint16_t)hi);
-      if (SPLIT) store_coherent(p.tlo + (int64_t)tok * p.ldtb + n, (uint16_t)f2bf(val[i] - bf2f(hi)));
+      const int64_t pi = tpack(tok, n, p.ldtb);
+      store_coherent(p.thi + pi, (uint16_t)hi);
+      if (SPLIT) store_coherent(p.tlo + pi, (uint16_t)f2bf(val[i] - bf2f(hi)));
     }
     wait_memory();  // this block's t is visible device-wide before it is counted
     __syncthreads();
@@ -501,18 +519,19 @@ void decode_kernel(DecArgs args) {
     stage2_tile<TB, RB2, KSW2, PF, SPLIT, kBudget>(p, T, tile, red);
 }
 
-// t (fp32, caller's layout) -> bf16 (and bf16 residual) for a stage-2-only call.
+// t (fp32, caller's layout) -> fragment-packed bf16 (and bf16 residual) for a
+// stage-2-only call.
 __global__ __launch_bounds__(256) void split_t_kernel(const float* __restrict__ t, int64_t ldt,
                                                       int T, int N, uint16_t* thi, uint16_t* tlo,
                                                       int64_t ldtb) {
-  const int64_t total = (int64_t)T * ldtb;
+  const int64_t total = (int64_t)T * N;
   for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int tok = (int)(e / ldtb), n = (int)(e % ldtb);
-    if (n >= N) continue;
+    const int tok = (int)(e / N), n = (int)(e % N);
     const float v = t[(int64_t)tok * ldt + n];
     const uint32_t hi = f2bf(v);
-    thi[e] = (uint16_t)hi;
-    if (tlo) tlo[e] = (uint16_t)f2bf(v - bf2f(hi));
+    const int64_t pi = tpack(tok, n, ldtb);
+    thi[pi] = (uint16_t)hi;
+    if (tlo) tlo[pi] = (uint16_t)f2bf(v - bf2f(hi));
   }
 }
 
@@ -550,12 +569,12 @@ Plan make_plan(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
   if (CTL_CNT + pl.nb1 > CTL_WORDS) pl.S1 = 1;  // no counters for that many row blocks
   pl.kc1 = (int)((steps + pl.S1 - 1) / pl.S1 * 32);
   pl.S1 = (int)((d_in + pl.kc1 - 1) / pl.kc1);
-  pl.ldtb = round_up(r, 8);
+  pl.ldtb = (r + 31) / 32;  // t fragment-packed: k-steps per 16-token block
   const size_t nr1 = (size_t)pl.TB * pl.RB1 * 4 * 64;  // floats per stage-1 tile
   const size_t part = pl.S1 > 1 ? (size_t)pl.nb1 * pl.S1 * nr1 * 4 : 0;
   pl.off_part = 0;
   pl.off_thi = round_up(part, 256);
-  const size_t tb_bytes = round_up(T * pl.ldtb * 2, 256);
+  const size_t tb_bytes = round_up((int64_t)pl.TB * pl.ldtb * 1024, 256);
   pl.off_tlo = pl.off_thi + tb_bytes;
   pl.bytes = pl.off_tlo + tb_bytes;
   return pl;
@@ -668,7 +687,7 @@ hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
       L.n2 = 0;
       L.wait = 0;
     } else if (d.flags == 2) {  // stage 2 only: t from t_io
-      const int64_t total = T * pl.ldtb;
+      const int64_t total = T * d.r;
       int blocks = (int)((total + 255) / 256);
       if (blocks > 1024) blocks = 1024;
       hipLaunchKernelGGL(split_t_kernel, dim3(blocks), dim3(256), 0, st, d.t_io, d.ldt, (int)T,
