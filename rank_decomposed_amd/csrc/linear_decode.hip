@@ -210,7 +210,8 @@ template <int TB, int RB, int KSW, int PF, bool SPLIT, bool WAIT>
 __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ A,
                              const uint16_t* __restrict__ Alo, int64_t lda,
                              const uint16_t* __restrict__ B, int64_t ldb, bool packed, int T,
-                             int N, int row0, int kbeg, int kend, uint32_t* ctl, bool wait) {
+                             int N, int row0, int kbeg, int kend, uint32_t* ctl, bool wait,
+                             float* stage = nullptr) {
   static_assert(!WAIT || PF % KSW == 0, "the prefetched steps are consumed KSW at a time");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -232,7 +233,14 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
 
   const int nsteps = (K + 31) / 32;
   const int nfull = K / 32;
-  const int per = (nsteps + kWaves - 1) / kWaves;  // contiguous k-steps per wave
+  // Stage-1 activations go through LDS (XL) for T > 16: a round of two
+  // k-steps is one whole 128-byte line per token row, so waves take even
+  // runs of steps.  (The MFMA fragment of one k-step is 16 token rows x 64
+  // bytes; loaded straight from the caller's row-major x, every line was
+  // fetched in two halves.)
+  constexpr bool XL = !WAIT && !SPLIT && TB >= 2 && KSW % 2 == 0;
+  const int per = XL ? 2 * ((nsteps + 2 * kWaves - 1) / (2 * kWaves))
+                     : (nsteps + kWaves - 1) / kWaves;  // contiguous k-steps per wave
   const int s_lo = min(nsteps, wave * per);
   const int s_hi = min(nsteps, s_lo + per);
   const int s_full = min(s_hi, nfull);
@@ -245,10 +253,43 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
   // KSW steps whose weights are in bv: load the activations, multiply
   auto round = [&](const u32x4 (*bv)[RB], int sb) {
     u32x4 av[KSW][TB], alv[KSW][TB];
+    if constexpr (XL) {
+      // per pair of steps: 2*TB loads of 8 token rows x 128 bytes (whole
+      // lines) into the wave's own LDS region (the slot it later parks its
+      // partial products in), the rows' 16-byte chunks XOR-swizzled by row;
+      // then the MFMA fragments read back from it.  Only this wave touches
+      // the region, so LDS ordering within the wave is all it needs.
+      uint8_t* xs = reinterpret_cast<uint8_t*>(stage) + wave * (TB * 2048);
 #pragma unroll
-    for (int i = 0; i < KSW; ++i) {
-      frag_load_at<TB, WAIT>(av[i], ra, aoff, (sb + i) * ASTEP, sb + i < s_full);
-      if (SPLIT) frag_load_at<TB, WAIT>(alv[i], ral, aoff, (sb + i) * ASTEP, sb + i < s_full);
+      for (int pr = 0; pr < KSW / 2; ++pr) {
+        const int sp = sb + 2 * pr;
+        u32x4 ld[2 * TB];
+#pragma unroll
+        for (int q = 0; q < 2 * TB; ++q) {
+          const int row = 8 * q + (lane >> 3), c = lane & 7;
+          const bool live = sp + (c >> 2) < s_full;
+          ld[q] = bload(ra, live ? (uint32_t)((row * lda + sp * 32 + c * 8) * 2) : kOutside);
+        }
+#pragma unroll
+        for (int q = 0; q < 2 * TB; ++q) {
+          const int row = 8 * q + (lane >> 3), c = lane & 7;
+          *reinterpret_cast<u32x4*>(xs + row * 128 + ((c ^ (row & 7)) << 4)) = ld[q];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) {
+            const int row = tb * 16 + (lane & 15), c = 4 * i + (lane >> 4);
+            av[2 * pr + i][tb] =
+                *reinterpret_cast<const u32x4*>(xs + row * 128 + ((c ^ (row & 7)) << 4));
+          }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KSW; ++i) {
+        frag_load_at<TB, WAIT>(av[i], ra, aoff, (sb + i) * ASTEP, sb + i < s_full);
+        if (SPLIT) frag_load_at<TB, WAIT>(alv[i], ral, aoff, (sb + i) * ASTEP, sb + i < s_full);
+      }
     }
 #pragma unroll
     for (int i = 0; i < KSW; ++i)
@@ -441,7 +482,7 @@ void decode_kernel(DecArgs args) {
     f32x4 acc[TB][RB1];
     tile_product<TB, RB1, KSW1, KSW1, false, false>(acc, p.x, nullptr, p.ldx, p.ut, p.ldu,
                                                     p.packed != 0, T, p.r, row0, kbeg, kend,
-                                                    p.ctl, false);
+                                                    p.ctl, false, red);
     constexpr int NS = park_slots(NR, kBudget);
     park<TB, RB1, NS>(acc, red);
     float val[EPT];
@@ -568,6 +609,7 @@ Plan make_plan(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
   if (pl.TB == 2 && pl.S1 > 6) pl.S1 = 6;
   if (CTL_CNT + pl.nb1 > CTL_WORDS) pl.S1 = 1;  // no counters for that many row blocks
   pl.kc1 = (int)((steps + pl.S1 - 1) / pl.S1 * 32);
+  if (pl.TB >= 2) pl.kc1 = (pl.kc1 + 63) / 64 * 64;  // ranges start on 128-byte lines
   pl.S1 = (int)((d_in + pl.kc1 - 1) / pl.kc1);
   pl.ldtb = (r + 31) / 32;  // t fragment-packed: k-steps per 16-token block
   const size_t nr1 = (size_t)pl.TB * pl.RB1 * 4 * 64;  // floats per stage-1 tile
@@ -601,6 +643,11 @@ hipError_t launch_one(const DecArgs& a, int grid, hipStream_t st) {
   constexpr size_t red2 = (size_t)park_slots(NR2, budget) * NR2 * 256;
   constexpr size_t red_bytes = red1 > red2 ? red1 : red2;
   static_assert(red_bytes <= (size_t)budget, "parked partials exceed the LDS budget");
+  // stage-1 activation staging (T > 16): TB * 2 KiB per wave, inside the LDS
+  constexpr size_t lds_min = WPC == 1 ? (size_t)kLdsMax / 2 + 1024 : 0;
+  static_assert(TB < 2 || KSW1 % 2 != 0 ||
+                    (red_bytes > lds_min ? red_bytes : lds_min) >= (size_t)kWaves * TB * 2048,
+                "activation staging exceeds the dynamic LDS");
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
