@@ -227,8 +227,9 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
   const __amdgpu_buffer_rsrc_t ral = make_rsrc((SPLIT ? Alo : A) + (WAIT ? 0 : kbeg), abytes);
   uint32_t aoff[TB];
 #pragma unroll
-  for (int tb = 0; tb < TB; ++tb)
-    aoff[tb] = WAIT ? (uint32_t)((tb * lda * 64 + lane) * 16)
+  for (int tb = 0; tb < TB; ++tb)  // (packed t: lanes of tokens >= T read zero, no memory)
+    aoff[tb] = WAIT ? (tb * 16 + (lane & 15) < T ? (uint32_t)((tb * lda * 64 + lane) * 16)
+                                                  : kOutside)
                     : (uint32_t)(((tb * 16 + (lane & 15)) * lda + kq) * 2);
 
   const int nsteps = (K + 31) / 32;
