@@ -120,11 +120,16 @@ def test_bf16_prefill_split_k(T, shape):
     assert np.array_equal(bits(y_t), bits(y))
 
 
-@pytest.mark.parametrize("T", [5, 64, 200, 1100])
-def test_bf16_stage_flags(T):
-    c = make_linear(3000 + T, T, 640, 96, 320, "bf16", fast=True)
+@pytest.mark.parametrize("T", [5, 24, 64, 200, 1100])
+@pytest.mark.parametrize("shape", [(640, 96, 320), (650, 100, 330)])
+def test_bf16_stage_flags(T, shape):
+    # stage 1 alone into an fp32 t, then stage 2 alone from it (on the decode
+    # path t is re-laid in the packed bf16 operand layout in between); the
+    # second shape has a ragged last k-step in both stages
+    d_in, r, d_out = shape
+    c = make_linear(3000 + T + r, T, d_in, r, d_out, "bf16", fast=True)
     d = dev()
-    t = torch.empty((T, 96), dtype=torch.float32, device=d)
+    t = torch.empty((T, r), dtype=torch.float32, device=d)
     lr.lowrank_linear_forward(c["dx"], c["dUt"], None, t_io=t, flags=lr.LR_STAGE1_ONLY)
     y = lr.lowrank_linear_forward(None, None, c["dVt"], t_io=t, flags=lr.LR_STAGE2_ONLY)
     torch.cuda.synchronize()
