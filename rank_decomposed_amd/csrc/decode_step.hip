@@ -822,10 +822,16 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
   hipLaunchKernelGGL(append_kernel, dim3(T), dim3(256), 0, st, latv, w->r[2], (int)w->r[2],
                      s.slot_mapping, s.pool_rows, static_cast<uint16_t*>(s.v_pool), s.pool_ld);
   LR_CHECK(hipGetLastError());
-  LR_CHECK(remap_gather(2, s.k_pool, s.pool_rows, s.pool_ld, s.remap, s.cap, s.n_valid,
-                        w->r[1], kbuf, L.rk_ld, st));
-  LR_CHECK(remap_gather(2, s.v_pool, s.pool_rows, s.pool_ld, s.remap, s.cap, s.n_valid,
-                        w->r[2], vbuf, L.rv_ld, st));
+  // The fused attention reads the latents in place through the remap list
+  // (32-bit offsets into a pool under 2 GiB); otherwise they are first
+  // gathered into the compact buffers.
+  const bool in_place = fused && s.pool_rows * s.pool_ld * 2 < (int64_t(1) << 31);
+  if (!in_place) {
+    LR_CHECK(remap_gather(2, s.k_pool, s.pool_rows, s.pool_ld, s.remap, s.cap, s.n_valid,
+                          w->r[1], kbuf, L.rk_ld, st));
+    LR_CHECK(remap_gather(2, s.v_pool, s.pool_rows, s.pool_ld, s.remap, s.cap, s.n_valid,
+                          w->r[2], vbuf, L.rv_ld, st));
+  }
   const int S = (int)s.S;
   if (fused) {
     // attention straight from the gathered latents: K and V expanded per
@@ -836,12 +842,14 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
                        blk_off);
     LR_CHECK(hipGetLastError());
     FusedAttnArgs fa{};
-    fa.kl = kbuf;
-    fa.ldkl = L.rk_ld;
+    fa.kl = in_place ? static_cast<const uint16_t*>(s.k_pool) : kbuf;
+    fa.ldkl = in_place ? s.pool_ld : L.rk_ld;
     fa.rk = (int)w->r[1];
-    fa.vl = vbuf;
-    fa.ldvl = L.rv_ld;
+    fa.vl = in_place ? static_cast<const uint16_t*>(s.v_pool) : vbuf;
+    fa.ldvl = in_place ? s.pool_ld : L.rv_ld;
     fa.rv = (int)w->r[2];
+    fa.remap = in_place ? s.remap : nullptr;
+    fa.pool_rows = s.pool_rows;
     fa.vk = static_cast<const uint16_t*>(w->Vt[1]);
     fa.ldvk = w->ldv[1];
     fa.vv = static_cast<const uint16_t*>(w->Vt[2]);

@@ -79,6 +79,28 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, int64_t ld,
   }
 }
 
+// load_tile for an operand whose tile rows are scattered: lane row r of
+// instruction i reads source row prow[i] (negative: a zero row), the LDS
+// placement staying that of tile row r.
+template <int ROWS, int BK, int NW>
+__device__ __forceinline__ void load_tile_rows(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0,
+                                               int kt, uint8_t* lds, int wave, int lane,
+                                               const int (&prow)[ROWS / (64 / (BK / 8)) / NW]) {
+  constexpr int CPR = BK / 8, RPI = 64 / CPR;
+  const int rr = lane / CPR, slot = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < ROWS / RPI / NW; ++i) {
+    const int inst = wave + NW * i;
+    const int row = inst * RPI + rr;
+    const int chunk = swz<BK>(row, slot);
+    const int off = prow[i] >= 0 && chunk * 8 < kt
+                        ? (int)(((int64_t)prow[i] * ld + k0 + chunk * 8) * 2)
+                        : (int)0x80000000;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(lds + inst * 1024), 16, off, 0, 0, 0);
+  }
+}
+
 template <int NBW, int MBW, int BK>
 __device__ __forceinline__ void load_frags(u32x4 (&af)[MBW], u32x4 (&bfr)[NBW], const uint8_t* ta,
                                            const uint8_t* tb, int wm, int wn, int lane, int ks) {
@@ -703,12 +725,27 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
 // go to the XCDs in contiguous runs.
 constexpr int kFusedQH = 16;  // query heads per column tile at most
 
+// amap (optional): the A rows of the tile are rows amap[am0 + r] of the A
+// buffer (r < anrows; entries outside [0, arows) and rows r >= anrows read
+// zero), so the operand is read in place through a row list.
 template <int BN, int BK, int NS, int MBW>
 __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
                                               __amdgpu_buffer_rsrc_t ra, int64_t lda,
                                               __amdgpu_buffer_rsrc_t rb, int64_t ldb, int K,
-                                              uint8_t* smem, int wave, int lane) {
+                                              uint8_t* smem, int wave, int lane,
+                                              const int32_t* amap = nullptr, int am0 = 0,
+                                              int anrows = 0, int64_t arows = 0) {
   constexpr int NW = 2 * gBM / (32 * MBW), NBW = BN / 64, KS = BK / 16;
+  constexpr int RPI = 64 / (BK / 8), NAI = gBM / RPI / NW;
+  int prow[NAI];
+  if (amap) {
+#pragma unroll
+    for (int i = 0; i < NAI; ++i) {
+      const int row = (wave + NW * i) * RPI + lane / (BK / 8);
+      const int src = row < anrows ? amap[am0 + row] : -1;
+      prow[i] = src >= 0 && src < arows ? src : -1;
+    }
+  }
   constexpr int kTileA = gBM * BK * 2;
   constexpr int kStage = big_stage_bytes<BN, BK>();
   constexpr int IPW = kStage / 1024 / NW;
@@ -720,7 +757,10 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
     for (int j = 0; j < MBW; ++j) acc[i][j] = f32x16{};
   auto load_stage = [&](int t) {
     uint8_t* st = smem + (t % NS) * kStage;
-    load_tile<gBM, BK, NW>(ra, lda, t * BK, K - t * BK, st, wave, lane);
+    if (amap)
+      load_tile_rows<gBM, BK, NW>(ra, lda, t * BK, K - t * BK, st, wave, lane, prow);
+    else
+      load_tile<gBM, BK, NW>(ra, lda, t * BK, K - t * BK, st, wave, lane);
     load_tile<BN, BK, NW>(rb, ldb, t * BK, K - t * BK, st + kTileA, wave, lane);
   };
   auto wait_stage = [&](int younger) {
@@ -860,9 +900,12 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   f32x16 acc[NBW][MBW];
   // K = latents . V_k^T (the k-loop's barriers also publish qs)
   tile_mainloop<BN, gBK, gNS, MBW>(
-      acc, make_rsrc(p.kl + (int64_t)m0 * p.ldkl, view_bytes(nrows, p.rk, p.ldkl)), p.ldkl,
+      acc,
+      p.remap ? make_rsrc(p.kl, view_bytes(p.pool_rows, p.rk, p.ldkl))
+              : make_rsrc(p.kl + (int64_t)m0 * p.ldkl, view_bytes(nrows, p.rk, p.ldkl)),
+      p.ldkl,
       make_rsrc(p.vk + (int64_t)n0 * p.ldvk, view_bytes(min(dkv - n0, BN), p.rk, p.ldvk)),
-      p.ldvk, p.rk, smem, wave, lane);
+      p.ldvk, p.rk, smem, wave, lane, p.remap, m0, nrows, p.pool_rows);
   // rotate each head's column pairs (c, c + HD/2) by the row's position (its
   // index in the sequence), then round to bf16.  acc[i][j] reg v: column
   // wn + 32i + 8(v/4) + 4(lane/32) + v%4, row wm + 32j + lane%32.
@@ -953,9 +996,12 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   }
   // V = latents . V_v^T (its first barrier publishes p, m, l)
   tile_mainloop<BN, gBK, gNS, MBW>(
-      acc, make_rsrc(p.vl + (int64_t)m0 * p.ldvl, view_bytes(nrows, p.rv, p.ldvl)), p.ldvl,
+      acc,
+      p.remap ? make_rsrc(p.vl, view_bytes(p.pool_rows, p.rv, p.ldvl))
+              : make_rsrc(p.vl + (int64_t)m0 * p.ldvl, view_bytes(nrows, p.rv, p.ldvl)),
+      p.ldvl,
       make_rsrc(p.vv + (int64_t)n0 * p.ldvv, view_bytes(min(dkv - n0, BN), p.rv, p.ldvv)),
-      p.ldvv, p.rv, smem, wave, lane);
+      p.ldvv, p.rv, smem, wave, lane, p.remap, m0, nrows, p.pool_rows);
   // o[qh][c] = sum_rows p[qh][row] V[row][c] from the registers: a lane
   // weights its two rows' bf16 values of the head's columns by p and sums
   // them, then a butterfly over the 32 row lanes (each step keeps half the

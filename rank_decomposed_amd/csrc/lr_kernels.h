@@ -103,12 +103,16 @@ hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t l
 // blk_off[i]: first block of sequence i (blk_off[S] = blocks); nbpad bounds
 // the blocks (cap / 256 + S).  At most 16 query heads per 256 columns.
 struct FusedAttnArgs {
-  const uint16_t* kl;  // K latents [cap, ldkl], rk columns
+  const uint16_t* kl;  // K latents [cap, ldkl], rk columns (or the pool, see remap)
   int64_t ldkl;
   int rk;
-  const uint16_t* vl;  // V latents [cap, ldvl], rv columns
+  const uint16_t* vl;  // V latents [cap, ldvl], rv columns (or the pool, see remap)
   int64_t ldvl;
   int rv;
+  // optional: kl / vl are the paged pools [pool_rows, ld] and compact row j is
+  // pool row remap[j] (-1 or out of range: a zero row), read in place
+  const int32_t* remap;
+  int64_t pool_rows;
   const uint16_t* vk;  // V_k^T [Hkv * hd, ldvk]
   int64_t ldvk;
   const uint16_t* vv;  // V_v^T [Hkv * hd, ldvv]
