@@ -725,27 +725,39 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
 // go to the XCDs in contiguous runs.
 constexpr int kFusedQH = 16;  // query heads per column tile at most
 
-// amap (optional): the A rows of the tile are rows amap[am0 + r] of the A
-// buffer (r < anrows; entries outside [0, arows) and rows r >= anrows read
-// zero), so the operand is read in place through a row list.
+// A load instructions per lane for a 256-row tile of BK-deep k-tiles
+template <int BK, int MBW>
+constexpr int tile_a_loads() { return gBM / (64 / (BK / 8)) / (2 * gBM / (32 * MBW)); }
+
+// Source rows of this lane's A load instructions for a tile of rows
+// [0, nrows): row r itself, or with a row list, map[m0 + r] when that lies in
+// [0, rows) (else a zero row).  Issued early, the list's loads overlap other work.
+template <int BK, int MBW>
+__device__ __forceinline__ void tile_rows(int (&prow)[gBM / (64 / (BK / 8)) / (2 * gBM / (32 * MBW))], const int32_t* map,
+                                          int m0, int nrows, int64_t rows, int wave, int lane) {
+  constexpr int NW = 2 * gBM / (32 * MBW), RPI = 64 / (BK / 8);
+#pragma unroll
+  for (int i = 0; i < tile_a_loads<BK, MBW>(); ++i) {
+    const int row = (wave + NW * i) * RPI + lane / (BK / 8);
+    int src = row < nrows ? row : -1;
+    if (map && src >= 0) {
+      src = map[m0 + row];
+      src = src >= 0 && src < rows ? src : -1;
+    }
+    prow[i] = src;
+  }
+}
+
+// The A rows of the tile are rows prow[i] of the A buffer for this lane's
+// i-th A load instruction (tile_rows; negative: a zero row), so the operand can
+// be read in place through a row list.
 template <int BN, int BK, int NS, int MBW>
 __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
                                               __amdgpu_buffer_rsrc_t ra, int64_t lda,
                                               __amdgpu_buffer_rsrc_t rb, int64_t ldb, int K,
                                               uint8_t* smem, int wave, int lane,
-                                              const int32_t* amap = nullptr, int am0 = 0,
-                                              int anrows = 0, int64_t arows = 0) {
+                                              const int (&prow)[gBM / (64 / (BK / 8)) / (2 * gBM / (32 * MBW))]) {
   constexpr int NW = 2 * gBM / (32 * MBW), NBW = BN / 64, KS = BK / 16;
-  constexpr int RPI = 64 / (BK / 8), NAI = gBM / RPI / NW;
-  int prow[NAI];
-  if (amap) {
-#pragma unroll
-    for (int i = 0; i < NAI; ++i) {
-      const int row = (wave + NW * i) * RPI + lane / (BK / 8);
-      const int src = row < anrows ? amap[am0 + row] : -1;
-      prow[i] = src >= 0 && src < arows ? src : -1;
-    }
-  }
   constexpr int kTileA = gBM * BK * 2;
   constexpr int kStage = big_stage_bytes<BN, BK>();
   constexpr int IPW = kStage / 1024 / NW;
@@ -757,10 +769,7 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
     for (int j = 0; j < MBW; ++j) acc[i][j] = f32x16{};
   auto load_stage = [&](int t) {
     uint8_t* st = smem + (t % NS) * kStage;
-    if (amap)
-      load_tile_rows<gBM, BK, NW>(ra, lda, t * BK, K - t * BK, st, wave, lane, prow);
-    else
-      load_tile<gBM, BK, NW>(ra, lda, t * BK, K - t * BK, st, wave, lane);
+    load_tile_rows<gBM, BK, NW>(ra, lda, t * BK, K - t * BK, st, wave, lane, prow);
     load_tile<BN, BK, NW>(rb, ldb, t * BK, K - t * BK, st + kTileA, wave, lane);
   };
   auto wait_stage = [&](int younger) {
@@ -882,6 +891,11 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   const int nkv = min(BN / HD, p.Hkv - kv0), nq = nkv * grp;
   const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
 
+  // this lane's latent rows (pool rows through the remap list, or rows of the
+  // compact copy), shared by the K and V expansions
+  int prow[tile_a_loads<gBK, MBW>()];
+  tile_rows<gBK, MBW>(prow, p.remap, m0, nrows, p.pool_rows, wave, lane);
+
   // the tile's query heads, rotated at the new token's position and scaled
   {
     int qp = p.pos[i];
@@ -905,7 +919,7 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
               : make_rsrc(p.kl + (int64_t)m0 * p.ldkl, view_bytes(nrows, p.rk, p.ldkl)),
       p.ldkl,
       make_rsrc(p.vk + (int64_t)n0 * p.ldvk, view_bytes(min(dkv - n0, BN), p.rk, p.ldvk)),
-      p.ldvk, p.rk, smem, wave, lane, p.remap, m0, nrows, p.pool_rows);
+      p.ldvk, p.rk, smem, wave, lane, prow);
   // rotate each head's column pairs (c, c + HD/2) by the row's position (its
   // index in the sequence), then round to bf16.  acc[i][j] reg v: column
   // wn + 32i + 8(v/4) + 4(lane/32) + v%4, row wm + 32j + lane%32.
@@ -1001,7 +1015,7 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
               : make_rsrc(p.vl + (int64_t)m0 * p.ldvl, view_bytes(nrows, p.rv, p.ldvl)),
       p.ldvl,
       make_rsrc(p.vv + (int64_t)n0 * p.ldvv, view_bytes(min(dkv - n0, BN), p.rv, p.ldvv)),
-      p.ldvv, p.rv, smem, wave, lane, p.remap, m0, nrows, p.pool_rows);
+      p.ldvv, p.rv, smem, wave, lane, prow);
   // o[qh][c] = sum_rows p[qh][row] V[row][c] from the registers: a lane
   // weights its two rows' bf16 values of the head's columns by p and sums
   // them, then a butterfly over the 32 row lanes (each step keeps half the
