@@ -83,3 +83,32 @@ def test_fused_rejects_too_many_query_heads_per_tile():
     cfg = small_cfg(8, 1, 64)
     with pytest.raises(Exception):
         Step(181, cfg, ranks_for(cfg), [4, 9], n_layers=1, fused=True).run()
+
+
+def test_fused_pools_over_2gib_take_the_gather_path_bit_exactly():
+    # pools under 2 GiB are read in place through the remap list; larger ones
+    # are first gathered into the compact buffers.  The same rows embedded at
+    # the start of >= 2 GiB pools must give the same output bit for bit
+    cfg = small_cfg(4, 2, 128)
+    st = Step(191, cfg, ranks_for(cfg), [3, 260, 0, 511, 90, 17], n_layers=1, fused=True)
+    h_in = st.h.clone()
+    small = st.run().clone()
+    torch.cuda.synchronize()
+    assert maxrel(to_f64(small), st.oracle()) <= TOL
+    pk, pv = st.pools_k[0], st.pools_v[0]
+    rows = (1 << 31) // (2 * pk.stride(0)) + 16
+    big_k = torch.zeros((rows, pk.shape[1]), dtype=pk.dtype, device=pk.device)
+    big_v = torch.zeros_like(big_k)
+    big_k[: pk.shape[0]] = pk   # the cached rows, and the new token's row the first run appended
+    big_v[: pv.shape[0]] = pv
+    assert big_k.numel() * 2 >= 1 << 31
+    s = st.states[0]
+    dp = st.dev_prep
+    st.states = [lr.decode_state(big_k, big_v, dp["slot_mapping"], dp["remap"], dp["seq_off"],
+                                 dp["pos"], st.n_valid, st.max_seq_rows)]
+    st.h.copy_(h_in)
+    big = st.run()
+    torch.cuda.synchronize()
+    assert torch.equal(big, small)
+    del big_k, big_v, s
+    torch.cuda.empty_cache()
