@@ -485,7 +485,8 @@ def decode_step(torch, lr, dev, stream, n_layers, reps, fused=False):
     ratio 0.2 (64 sequences, cached lengths uniform in [128, 4096]) captured
     once in a HIP graph and replayed; preparation stage timed separately.
     fused: lowrank_layer_decode_step_fused (the reconstruction expanded per
-    256-row block inside the attention; no reconstructed K/V in memory)."""
+    256-row block inside the attention from the latents read in place; no
+    reconstructed K/V and no compact latent copy in memory)."""
     from synth.decode_step import DecodeStepInputs
     si = DecodeStepInputs(n_layers=n_layers, device=dev)
     c = si.cfg
@@ -541,7 +542,9 @@ def decode_step(torch, lr, dev, stream, n_layers, reps, fused=False):
     from synth.decode_step import dims
     lin_bytes = sum(2 * si.ranks[n] * (a_ + b_) + 2 * B * (a_ + b_)
                     for n, (a_, b_) in dims(c).items())
-    gather_bytes = 2 * nvr * (rk + rv) * 2
+    # the fused step reads the latents in place through the remap list (no
+    # compact copy); the unfused one copies them first (read + write)
+    gather_bytes = 0 if fused else 2 * nvr * (rk + rv) * 2
     recon_flops = 2.0 * nvr * (rk + rv) * dkv
     # fused: the reconstructed rows stay on chip (latents read once)
     recon_bytes = nvr * (rk + rv) * 2 + (0 if fused else 2 * nvr * dkv * 2)
