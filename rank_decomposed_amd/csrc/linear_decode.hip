@@ -588,6 +588,8 @@ struct Plan {
 };
 
 constexpr size_t kCtlBytes = (size_t)kMaxGroup * CTL_WORDS * 4;
+// Stage-2 tiles a group must have at 64 rows each before it takes them (T > 32)
+constexpr int kTallGroupTiles = 192;
 
 Plan make_plan(int64_t T, int64_t d_in, int64_t r, int64_t d_out) {
   Plan pl{};
@@ -747,6 +749,20 @@ hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
     }
     L.first1 = n1;
     n1 += L.nb1 * L.S1;
+  }
+  // 64-row stage-2 tiles for a whole group at T > 32 when it still has tiles
+  // enough to keep most CUs streaming V: on the 7B shapes at 64 tokens q,k,v
+  // together (3 x 64 tiles) gain, o or down alone (64 tiles) lose.
+  if (TB == 4) {
+    int tall = 0;
+    for (int i = 0; i < n; ++i)
+      if (a.lin[i].n2) tall += (a.lin[i].d_out + 63) / 64;
+    if (tall >= kTallGroupTiles)
+      for (int i = 0; i < n; ++i)
+        if (a.lin[i].n2) {
+          a.lin[i].rb2 = 4;
+          a.lin[i].n2 = (a.lin[i].d_out + 63) / 64;
+        }
   }
   a.n1 = n1;
   int grid = n1;

@@ -62,6 +62,33 @@ def test_group_mixed_members(T):
     assert maxrel(added, oracle.linear(xv, cs[2]["U"], cs[2]["V"])[1]) <= BF16_TOL
 
 
+@pytest.mark.parametrize("T", [40, 64])
+def test_group_tall_stage2_tiles(T):
+    # three members of 65 stage-2 tiles at 64 rows (the last one ragged) are
+    # enough for the group to take 64-row tiles at T > 32; member 1
+    # accumulates into an fp32 residual.  Outputs start as NaN.
+    cs = _cases(T, 8200 + T, [(512, 100, 4100), (512, 60, 4100), (512, 130, 4100)])
+    x = cs[0]["dx"]
+    d = dev()
+    y0 = torch.full((T, 4100), float("nan"), dtype=torch.bfloat16, device=d)
+    y2 = torch.full((T, 4100), float("nan"), dtype=torch.bfloat16, device=d)
+    g = torch.Generator(device="cpu").manual_seed(T)
+    acc0 = torch.randn((T, 4100), generator=g, dtype=torch.float32)
+    acc = acc0.clone().to(d)
+    lr.lowrank_linear_forward_group([dict(x=x, Ut=cs[0]["dUt"], Vt=cs[0]["dVt"], y=y0),
+                                     dict(x=x, Ut=cs[1]["dUt"], Vt=cs[1]["dVt"], y_acc=acc),
+                                     dict(x=x, Ut=cs[2]["dUt"], Vt=cs[2]["dVt"], y=y2)])
+    sep = [lr.lowrank_linear_forward(x, c["dUt"], c["dVt"]) for c in (cs[0], cs[2])]
+    torch.cuda.synchronize()
+    xv = cs[0]["x"]
+    for c, y, s in zip((cs[0], cs[2]), (y0, y2), sep):
+        yr = oracle.linear(xv, c["U"], c["V"])[1]
+        assert maxrel(to_f64(y), yr) <= BF16_TOL
+        assert maxrel(to_f64(y), to_f64(s)) <= BF16_TOL
+    added = to_f64(acc) - acc0.double().numpy()
+    assert maxrel(added, oracle.linear(xv, cs[1]["U"], cs[1]["V"])[1]) <= BF16_TOL
+
+
 @pytest.mark.parametrize("T", [1, 32])
 def test_group_packed_matches_row_major(T):
     cs = _cases(T, 8200 + T)
