@@ -641,12 +641,15 @@ def cpu_baseline(base, seconds):
     per second, as the GPU value."""
     import oracle
     import synth
+    threads, vendor = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count()), "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            threads = max(i.get("num_threads", 1) for i in blas)
+            vendor = ",".join(sorted({str(i.get("internal_api", "?")) for i in blas}))
     except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+        pass
     xs = {T: {d: synth.tokens(synth.seed_of(2, 0, 0, synth.KIND_X) + T, T, d)
               for d in (4096, 11008)} for T in TOKENS}
     tokens, passes = 0, 0
@@ -662,7 +665,8 @@ def cpu_baseline(base, seconds):
             break
     el = time.perf_counter() - t0
     return {"value": round(tokens / el, 2), "unit": "tokens/s (x 7-projection layer set)",
-            "cores": int(threads), "kind": "oracle",
+            "cores": int(threads), "host_cpu_count": os.cpu_count(), "blas_vendor": vendor,
+            "blas_threads": int(threads), "kind": "oracle",
             "sample": "%d passes of layer set 0 (7 projections) at T=1,8,32,64, fp64 numpy, "
                       "%.1f s" % (passes, el)}
 

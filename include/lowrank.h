@@ -61,7 +61,8 @@ typedef enum {
   LR_ERR_WORKSPACE = 4,   /* workspace missing or smaller than lowrank_workspace_bytes */
   LR_ERR_CAPACITY = 5,    /* packed rows exceed the fixed capacity */
   LR_ERR_HIP = 6,         /* the HIP runtime rejected a launch */
-  LR_ERR_UNSUPPORTED = 7  /* valid request outside what this build implements */
+  LR_ERR_UNSUPPORTED = 7, /* valid request outside what this build implements */
+  LR_ERR_WAIT = 8         /* lowrank_workspace_check: a bounded wait in a kernel gave up */
 } lr_status;
 
 typedef enum { LR_F32 = 0, LR_BF16 = 1 } lr_dtype;
@@ -155,8 +156,11 @@ lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in, int64_t r
  * one launch: bf16 decode path only (1 <= T <= 64, 1 <= n <= 8).  Meant for
  * the projections of a decoder layer that read the same input (q, k, v;
  * gate, up): one launch instead of n, and one linear's hand-over from stage
- * 1 to stage 2 overlaps the others' weight streams.  Results are bit for bit
- * those of n separate lowrank_linear_forward calls.
+ * 1 to stage 2 overlaps the others' weight streams.  The launch splits the
+ * stage-1 reduction over d_in into as many K ranges as keep about one
+ * stage-1 tile per CU for the whole group, so a member's t (and y) may
+ * differ from a separate call's in fp32 summation order; it is bit for bit
+ * the separate call's whenever both split d_in alike.
  *
  *   lin[i]   one linear, operands as in lowrank_linear_forward (bf16 x, Ut,
  *            Vt, y; fp32 t_io):
@@ -427,6 +431,38 @@ size_t lowrank_workspace_bytes(int which, lr_dtype dt, int64_t T_or_B, int64_t d
                                int64_t d_out, int64_t cap);
 
 const char* lowrank_status_string(lr_status s);
+
+/*
+ * lowrank_workspace_check -- after the decode path (lowrank_linear_forward
+ * with bf16 and T <= 64, lowrank_linear_forward_group, and the decode and
+ * prefill layer steps, whose workspaces start with the same control area):
+ * did a bounded wait inside a kernel give up?  A stage-2 tile waits for the
+ * rank-r intermediate of DeInfer/en §2.A to be complete; the wait is bounded
+ * (lowrank_set_wait_limit) so that no input can hang the GPU, and a wait that
+ * gives up leaves an error word in the workspace and lets the call finish
+ * with stale data.
+ *
+ *   Synchronises `stream`, reads the error words of the workspace's eight
+ *   control blocks (the first 128 KiB) and stores in *failed (when non-NULL)
+ *   a bit mask of the blocks (linears of a launch) whose wait gave up.
+ *   Returns LR_OK when none did.  Otherwise it zero-fills the control area
+ *   (so later calls start from clean counters) and returns LR_ERR_WAIT: the
+ *   outputs of the calls since the previous check are unreliable.
+ *   Not capturable in a graph (it synchronises).  Errors: LR_ERR_ARG (NULL
+ *   or misaligned workspace), LR_ERR_WORKSPACE (under 128 KiB), LR_ERR_HIP.
+ */
+lr_status lowrank_workspace_check(void* workspace, size_t workspace_bytes, uint32_t* failed,
+                                  hipStream_t stream);
+
+/*
+ * lowrank_set_wait_limit -- polls (each about a microsecond) a bounded wait
+ * of the decode path makes before it gives up, for launches issued (or
+ * captured) from now on, process-wide.  LR_DEFAULT_WAIT_LIMIT is the default;
+ * tiny values are a test hook that forces the give-up path while every
+ * kernel still runs to its end.
+ */
+#define LR_DEFAULT_WAIT_LIMIT (1u << 20)
+void lowrank_set_wait_limit(uint32_t polls);
 
 /* sizeof(lr_layer_weights) for which = 0, sizeof(lr_decode_state) for
  * which = 1, sizeof(lr_linear) for which = 2, sizeof(lr_prefill_state) for

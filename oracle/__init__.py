@@ -15,9 +15,12 @@ no blocking, fusion or reordering beyond the definitions.
 Pins (``tests/test_oracle_pins.py`` and friends, ``-m "not gpu"``):
 associativity, full-rank reconstruction, Eckart-Young, brute-force loops on
 tiny shapes, hand-computed golden cases, shard-sum, gather identities,
-paging coverage/maximality, RMSNorm/rotary/softmax closed forms, and the
-full-rank decoder layer against a dense textbook layer.  No function here is
-"parity unpinned".
+paging coverage/maximality, RMSNorm/rotary/softmax closed forms, the
+full-rank decoder layer against a dense textbook layer, a chunk of prefill
+against token-by-token decode, and the multi-layer, multi-sequence
+compositions (decode_step, prefill_layer, prefill_step) against a dense
+textbook decoder stack at full rank plus prefill_step with single-token
+chunks against decode_step.  Each function has at least one such pin.
 """
 from .lowrank import (rank_for_ratio, truncated_factors, linear, linear_loops,
                       tp_share_stage1, tp_share_stage2)

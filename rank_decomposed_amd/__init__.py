@@ -14,19 +14,22 @@ leading dimensions, so tensor-parallel shares are plain slices
 from __future__ import annotations
 
 import ctypes as C
+import weakref
 
 import numpy as np
 
 from . import _lib
-from ._lib import (LR_BF16, LR_F32, LR_FULL, LR_PACKED_WEIGHTS, LR_STAGE1_ONLY, LR_STAGE2_ONLY,
-                   LowrankError, load, status_string)
+from ._lib import (LR_BF16, LR_DEFAULT_WAIT_LIMIT, LR_ERR_WAIT, LR_F32, LR_FULL,
+                   LR_PACKED_WEIGHTS, LR_STAGE1_ONLY, LR_STAGE2_ONLY, LowrankError, load,
+                   status_string)
 
 __all__ = [
     "lowrank_linear_forward", "kv_remap_gather", "lowrank_prepare_decode", "lowrank_prepare_prefill",
     "lowrank_workspace_bytes", "lowrank_status_string", "lowrank_version",
     "LR_F32", "LR_BF16", "LR_FULL", "LR_STAGE1_ONLY", "LR_STAGE2_ONLY", "LR_PACKED_WEIGHTS",
     "LowrankError", "load", "PackedFactor", "pack_factor", "lowrank_packed_bytes",
-    "lowrank_linear_forward_group", "lowrank_group_workspace_bytes",
+    "lowrank_linear_forward_group", "lowrank_group_workspace_bytes", "lowrank_workspace_check",
+    "lowrank_set_wait_limit", "LR_DEFAULT_WAIT_LIMIT", "LR_ERR_WAIT",
 ]
 
 
@@ -71,6 +74,53 @@ def lowrank_status_string(s: int) -> str:
 
 def lowrank_version() -> int:
     return int(load().lowrank_version())
+
+
+def lowrank_workspace_check(workspace, stream=None, raise_on_wait=True) -> int:
+    """Synchronise the stream and read the decode path's wait-error words of
+    a workspace (see lowrank.h).  Returns the bit mask of control blocks whose
+    bounded wait gave up (0 when none; the control area is then cleared);
+    raises LowrankError(LR_ERR_WAIT) for a nonzero mask unless
+    raise_on_wait is False."""
+    mask = C.c_uint32(0)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load().lowrank_workspace_check(_ptr(workspace), nbytes, C.byref(mask),
+                                        _stream(stream, workspace.device))
+    if st == LR_ERR_WAIT and not raise_on_wait:
+        return int(mask.value)
+    _lib.check(st, "lowrank_workspace_check")
+    return int(mask.value)
+
+
+_watched = None  # decode-path workspaces seen while watching (test hook)
+
+
+def watch_workspaces(on: bool = True) -> None:
+    """Record every workspace a decode-path call uses from now on (weakly),
+    so that check_watched_workspaces() can run lowrank_workspace_check on
+    each; off drops the record."""
+    global _watched
+    _watched = weakref.WeakValueDictionary() if on else None
+
+
+def _note(workspace) -> None:
+    if _watched is not None and workspace is not None:
+        _watched[workspace.data_ptr()] = workspace
+
+
+def check_watched_workspaces() -> None:
+    """lowrank_workspace_check on every recorded workspace still alive
+    (raises LowrankError(LR_ERR_WAIT) if a bounded wait gave up)."""
+    if _watched is None:
+        return
+    for ws in list(_watched.values()):
+        lowrank_workspace_check(ws)
+
+
+def lowrank_set_wait_limit(polls: int) -> None:
+    """Polls a bounded wait of the decode path makes before it gives up, for
+    launches issued from now on (LR_DEFAULT_WAIT_LIMIT restores the default)."""
+    load().lowrank_set_wait_limit(int(polls))
 
 
 class PackedFactor:
@@ -159,6 +209,8 @@ def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, w
         _ptr(t_io), _ld(t_io) if t_io is not None else 0,
         flags, _ptr(workspace), ws_bytes, _stream(stream, dev))
     _lib.check(st, "lowrank_linear_forward")
+    if dt == LR_BF16 and T <= 64:
+        _note(workspace)
     return y
 
 
@@ -211,6 +263,7 @@ def lowrank_linear_forward_group(linears, workspace=None, stream=None):
                                           LR_PACKED_WEIGHTS if packed else 0, _ptr(workspace),
                                           ws_bytes, _stream(stream, dev))
     _lib.check(st, "lowrank_linear_forward_group")
+    _note(workspace)
     return [L.get("y") for L in linears]
 
 
@@ -374,6 +427,7 @@ def lowrank_layer_decode_step(w: LayerWeights, s: DecodeState, h, workspace, str
     _lib.check(load().lowrank_layer_decode_step(C.byref(w), C.byref(s), _ptr(h), _ptr(workspace),
                                                 nbytes, _stream(stream, h.device)),
                "lowrank_layer_decode_step")
+    _note(workspace)
     return h
 
 
@@ -389,6 +443,7 @@ def lowrank_layer_decode_step_fused(w: LayerWeights, s: DecodeState, h, workspac
                                                       _ptr(workspace), nbytes,
                                                       _stream(stream, h.device)),
                "lowrank_layer_decode_step_fused")
+    _note(workspace)
     return h
 
 
@@ -420,4 +475,6 @@ def lowrank_layer_prefill_step(w: LayerWeights, s: PrefillState, h, workspace, s
     _lib.check(load().lowrank_layer_prefill_step(C.byref(w), C.byref(s), _ptr(h), _ptr(workspace),
                                                  nbytes, _stream(stream, h.device)),
                "lowrank_layer_prefill_step")
+    if s.T <= 64:  # projections on the decode path: its control area leads the workspace
+        _note(workspace)
     return h

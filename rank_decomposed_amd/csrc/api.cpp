@@ -34,6 +34,7 @@ extern "C" const char* lowrank_status_string(lr_status s) {
     case LR_ERR_CAPACITY: return "capacity exceeded";
     case LR_ERR_HIP: return "HIP runtime error";
     case LR_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LR_ERR_WAIT: return "a bounded wait inside a decode kernel gave up";
   }
   return "unknown status";
 }
@@ -188,4 +189,29 @@ extern "C" lr_status kv_remap_gather(lr_dtype dt, const void* src, int64_t src_r
   hipError_t e = lr::remap_gather(eb, src, src_rows, src_ld, remap, cap, n_valid, row_elems, dst,
                                   dst_ld, stream);
   return e == hipSuccess ? LR_OK : LR_ERR_HIP;
+}
+
+extern "C" void lowrank_set_wait_limit(uint32_t polls) { lr::set_spin_limit(polls); }
+
+extern "C" lr_status lowrank_workspace_check(void* workspace, size_t workspace_bytes,
+                                             uint32_t* failed, hipStream_t stream) {
+  const size_t ctl = (size_t)lr::kCtlBlocks * lr::kCtlBlockWords * 4;
+  if (!workspace || !aligned(workspace, 256)) return LR_ERR_ARG;
+  if (workspace_bytes < ctl) return LR_ERR_WORKSPACE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return LR_ERR_HIP;
+  uint32_t mask = 0;
+  for (int b = 0; b < lr::kCtlBlocks; ++b) {
+    uint32_t w = 0;
+    const char* at = static_cast<const char*>(workspace) +
+                     ((size_t)b * lr::kCtlBlockWords + lr::kCtlErrWord) * 4;
+    if (hipMemcpy(&w, at, 4, hipMemcpyDeviceToHost) != hipSuccess) return LR_ERR_HIP;
+    if (w == lr::kWaitErrorMagic) mask |= 1u << b;
+  }
+  if (failed) *failed = mask;
+  if (!mask) return LR_OK;
+  // a wait gave up: every counter of the control area goes back to zero
+  if (hipMemsetAsync(workspace, 0, ctl, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return LR_ERR_HIP;
+  return LR_ERR_WAIT;
 }

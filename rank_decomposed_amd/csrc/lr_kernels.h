@@ -36,6 +36,19 @@ struct DecodeLinear {
   int64_t ldglu = 0;
 };
 
+// Control area of a decode-path workspace: kCtlBlocks blocks of
+// kCtlBlockWords uint32 words at its start, one per linear of a launch.  Word
+// kCtlErrWord of a block holds kWaitErrorMagic once a bounded wait of that
+// linear gave up (lowrank_workspace_check reads and clears it).
+constexpr int kCtlBlocks = 8;
+constexpr int kCtlBlockWords = 4096;
+constexpr int kCtlErrWord = 1216;
+constexpr uint32_t kWaitErrorMagic = 0x4c525754u;
+constexpr uint32_t kDefaultSpinLimit = 1u << 20;  // polls (~1 us each) before a wait gives up
+// Polls of a bounded wait in decode launches issued from now on (a test hook:
+// a tiny limit forces the give-up path while every kernel still exits).
+void set_spin_limit(uint32_t polls);
+
 // bf16, T <= 64: streamed skinny MFMA path.
 // The decode kernel addresses each 64-row tile with 32-bit offsets: every
 // leading dimension (and r) must stay below 2^24 elements.

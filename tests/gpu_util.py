@@ -71,3 +71,10 @@ def make_linear(seed: int, T: int, d_in: int, r: int, d_out: int, dtype: str, fa
     du = padded(us, ld_for(d_in, ld_extra), dtype)
     dv = padded(vs, ld_for(r, ld_extra), dtype)
     return {"x": xv, "U": uv.T, "V": vv.T, "dx": dx, "dUt": du, "dVt": dv}
+
+
+def control_counters(ws):
+    """Every word of a decode-path workspace's eight control blocks (4096
+    uint32 words each): counters, flags and error words, all back at zero
+    after every call."""
+    return ws[:8 * 16384].view(torch.int32).cpu().numpy().reshape(8, 4096)

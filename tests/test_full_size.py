@@ -158,6 +158,29 @@ def test_remap_gather_decode_step_shape_bit_exact():
     assert np.all(got[sample, r:] == 0xABCD)              # past row_elems: untouched
 
 
+def sampled_sequences(lengths):
+    """8 seeded sequences of the 64, the shortest and the longest among them."""
+    rest = np.setdiff1d(np.arange(len(lengths)), [np.argmin(lengths), np.argmax(lengths)])
+    pick = np.random.default_rng(2024).choice(rest, 6, replace=False)
+    return [int(np.argmin(lengths)), int(np.argmax(lengths))] + sorted(int(i) for i in pick)
+
+
+@functools.lru_cache(maxsize=1)
+def decode_step_reference():
+    """fp64 oracle of the 32-layer step on the sampled sequences (computed
+    once for both step variants; a few minutes of host time)."""
+    si = DecodeStepInputs(device=None)
+    c = si.cfg
+    seqs = sampled_sequences(si.lengths)
+    layers = (si.layer_values(li) for li in range(c["n_layers"]))
+    pools_k = [si.pool_rows_for(li, 0, seqs) for li in range(c["n_layers"])]
+    pools_v = [si.pool_rows_for(li, 1, seqs) for li in range(c["n_layers"])]
+    sub_tables = [si.tables[i] for i in seqs]
+    return seqs, oracle.decode_step(si.h0[seqs], layers, pools_k, pools_v, sub_tables,
+                                    si.lengths[seqs], si.block, c)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("fused", [False, True])
 def test_decode_step_32_layers_sampled_sequences(fused):
     # fused: the reconstruction inside the attention (lowrank_layer_decode_step_fused)
@@ -187,13 +210,7 @@ def test_decode_step_32_layers_sampled_sequences(fused):
         print("layer %d done" % li, flush=True)
         del pk, pv, w, st, Ut, Vt
     got = to_f64(h)
-    seqs = [int(np.argmin(si.lengths)), int(np.argmax(si.lengths))]
-    layers = (si.layer_values(li) for li in range(c["n_layers"]))
-    pools_k = [si.pool_rows_for(li, 0, seqs) for li in range(c["n_layers"])]
-    pools_v = [si.pool_rows_for(li, 1, seqs) for li in range(c["n_layers"])]
-    sub_tables = [si.tables[i] for i in seqs]
-    ref = oracle.decode_step(si.h0[seqs], layers, pools_k, pools_v, sub_tables,
-                             si.lengths[seqs], si.block, c)
+    seqs, ref = decode_step_reference()
     for k, i in enumerate(seqs):
         err = maxrel(got[i], ref[k])
         print("32-layer decode step%s, sequence %d (L=%d): max rel err %.2e"

@@ -1,13 +1,15 @@
 """lowrank_linear_forward_group on the GPU: several independent decode
-linears in one launch give bit for bit what separate calls give, and match
-the fp64 oracle (stage-1-only and accumulate members included)."""
+linears in one launch match the fp64 oracle (stage-1-only and accumulate
+members included), and give bit for bit what separate calls give where both
+split the stage-1 reduction alike (d_in under 1024 here: one or two K ranges
+either way)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import rank_decomposed_amd as lr
-from gpu_util import bits, dev, make_linear, maxrel, to_f64
+from gpu_util import bits, control_counters, dev, make_linear, maxrel, to_f64
 
 pytestmark = pytest.mark.gpu
 BF16_TOL = 2e-2
@@ -84,7 +86,9 @@ def test_group_tall_stage2_tiles(T):
     for c, y, s in zip((cs[0], cs[2]), (y0, y2), sep):
         yr = oracle.linear(xv, c["U"], c["V"])[1]
         assert maxrel(to_f64(y), yr) <= BF16_TOL
-        assert maxrel(to_f64(y), to_f64(s)) <= BF16_TOL
+        # 64- and 32-row stage-2 tiles split k over the waves alike and sum
+        # the waves in one fixed order: grouped equals separate bit for bit
+        assert np.array_equal(bits(y), bits(s))
     added = to_f64(acc) - acc0.double().numpy()
     assert maxrel(added, oracle.linear(xv, cs[1]["U"], cs[1]["V"])[1]) <= BF16_TOL
 
@@ -121,8 +125,7 @@ def test_group_and_single_calls_share_a_workspace():
             assert np.array_equal(bits(a), bits(b))
         for L in lin:
             L.pop("y", None)
-    ctl = ws[:8 * 16384].view(torch.int32).cpu().numpy()
-    assert not ctl.any()
+    assert not control_counters(ws).any()      # every counter back at zero
 
 
 def test_group_graph_replay():

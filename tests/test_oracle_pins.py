@@ -355,3 +355,170 @@ def test_prefill_layer_equals_token_by_token_decode(mlp, Hkv):
     o1, _, _ = oracle.prefill_layer_seq(Hin[:1], w, lat_k[:0], lat_v[:0], 0, cfg)
     o2, _, _ = oracle.decode_layer_seq(Hin[0], w, lat_k[:0], lat_v[:0], 0, cfg)
     assert _rel(o1[0], o2) <= 1e-12
+
+
+# ------------------------------------------------- multi-layer compositions
+# decode_step, prefill_layer and prefill_step compose the single-layer
+# functions pinned above over layers (the residual stream threaded from one
+# layer to the next, each layer reading its own latent pools) and over
+# sequences (each sequence's rows at its own offset).  Their pins: at full
+# rank a stack of layers equals a dense textbook decoder run sequence by
+# sequence, and a prefill step whose chunks are single tokens equals a
+# decode step.  Every layer has distinct weights and distinct pools, and the
+# pools' unused rows hold NaN, so a slip in the threading of h, the layer
+# order, the pool of a layer or a sequence's row offset fails these tests
+# (the last test below shows it does).
+
+def _phys(table, p, block):
+    return int(table[p // block]) * block + p % block
+
+
+def _scatter_pool(rows_per_seq, tables, nblocks, block, width):
+    """Pool [nblocks * block, width] holding each sequence's logical rows at
+    their physical rows (NaN elsewhere)."""
+    pool = np.full((nblocks * block, width), np.nan)
+    for i, rows in enumerate(rows_per_seq):
+        for p in range(rows.shape[0]):
+            pool[_phys(tables[i], p, block)] = rows[p]
+    return pool
+
+
+def _decoder_case(seed, n_layers, lengths, cfg, full_rank, d=32, dff=48, block=4,
+                  extra_rows=None):
+    """Layers (factors + dense weights), per-layer normed inputs of the cached
+    tokens, paged pools of their latents and the block tables.  extra_rows[i]
+    rows beyond the cached ones are placed too (chunked prefill)."""
+    H, Hkv, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    lengths = np.asarray(lengths)
+    covered = lengths if extra_rows is None else lengths + np.asarray(extra_rows) - 1
+    tables, nblocks = synth.block_tables(seed, np.maximum(covered, 0), block=block,
+                                         slack_blocks=2)
+    g = np.random.default_rng(seed)
+    layers, dense, prev_x, pools_k, pools_v = [], [], [], [], []
+    for li in range(n_layers):
+        w, Wd = _tiny_layer_weights(seed + 31 * li + 1, d, dff, Hkv, hd, full_rank)
+        px = [g.standard_normal((int(L), d)) for L in lengths]
+        layers.append(w)
+        dense.append(Wd)
+        prev_x.append(px)
+        rk, rv = w["U"]["k"].shape[1], w["U"]["v"].shape[1]
+        pools_k.append(_scatter_pool([x @ w["U"]["k"] for x in px], tables, nblocks, block, rk))
+        pools_v.append(_scatter_pool([x @ w["U"]["v"] for x in px], tables, nblocks, block, rv))
+    return layers, dense, prev_x, pools_k, pools_v, tables
+
+
+def _dense_decoder_token(h, dense, layers, prev_x_seq, L, cfg):
+    """One new token through every layer of a dense textbook decoder."""
+    for Wd, w, px in zip(dense, layers, prev_x_seq):
+        h = _dense_layer(h, Wd, w, px, L, cfg)
+    return h
+
+
+@pytest.mark.parametrize("Hkv,mlp", [(4, "swiglu"), (2, "swiglu"), (1, "relu")])
+def test_decode_step_full_rank_equals_dense_stack(Hkv, mlp):
+    cfg = {"n_heads": 4, "n_kv_heads": Hkv, "head_dim": 8, "mlp": mlp}
+    lengths = [6, 0, 11, 3]
+    layers, dense, prev_x, pk, pv, tables = _decoder_case(700 + Hkv, 3, lengths, cfg, True)
+    h0 = np.random.default_rng(70).standard_normal((len(lengths), 32))
+    got = oracle.decode_step(h0, layers, pk, pv, tables, lengths, 4, cfg)
+    for i, L in enumerate(lengths):
+        ref = _dense_decoder_token(h0[i], dense, layers, [px[i] for px in prev_x], L, cfg)
+        assert _rel(got[i], ref) <= 1e-11, i
+    # a subset of sequences, in any order, gives those sequences' rows
+    sub = oracle.decode_step(h0, layers, pk, pv, tables, lengths, 4, cfg, seqs=[2, 0])
+    assert np.array_equal(sub, got[[2, 0]])
+
+
+@pytest.mark.parametrize("Hkv,mlp", [(4, "swiglu"), (2, "relu")])
+def test_prefill_step_full_rank_equals_dense_causal_stack(Hkv, mlp):
+    # several sequences with different cached lengths and chunk lengths; in
+    # the dense decoder, chunk token j of a sequence is one more decoded
+    # token whose cache holds the cached rows and chunk tokens 0 .. j-1 of
+    # the same layer
+    cfg = {"n_heads": 4, "n_kv_heads": Hkv, "head_dim": 8, "mlp": mlp}
+    lengths, chunks = [5, 0, 2], [3, 1, 4]
+    layers, dense, prev_x, pk, pv, tables = _decoder_case(800 + Hkv, 3, lengths, cfg, True,
+                                                          extra_rows=chunks)
+    n = sum(chunks)
+    h0 = np.random.default_rng(80).standard_normal((n, 32))
+    got = oracle.prefill_step(h0, layers, pk, pv, tables, lengths, chunks, 4, cfg)
+    t = 0
+    for i, (L, c) in enumerate(zip(lengths, chunks)):
+        Hc = h0[t:t + c].copy()
+        for Wd, w, px in zip(dense, layers, prev_x):
+            X = np.stack([oracle.rmsnorm(Hc[j], w["g1"]) for j in range(c)])
+            Hc = np.stack([_dense_layer(Hc[j], Wd, w, np.vstack([px[i], X[:j]]), L + j, cfg)
+                           for j in range(c)])
+        assert _rel(got[t:t + c], Hc) <= 1e-11, i
+        t += c
+    # prefill_layer returns the new latents of each token: x U_k / x U_v of
+    # its normed input, sequence by sequence
+    _, nk, nv = oracle.prefill_layer(h0, layers[0], pk[0], pv[0], tables, lengths, chunks, 4, cfg)
+    X0 = oracle.rmsnorm(h0, layers[0]["g1"])
+    assert _rel(nk, X0 @ layers[0]["U"]["k"]) <= 1e-13
+    assert _rel(nv, X0 @ layers[0]["U"]["v"]) <= 1e-13
+
+
+@pytest.mark.parametrize("mlp", ["swiglu", "relu"])
+def test_prefill_step_single_token_chunks_equal_decode_step(mlp):
+    # low rank, 3 layers: with one new token per sequence a prefill step is a
+    # decode step (two independently written paths)
+    cfg = {"n_heads": 4, "n_kv_heads": 2, "head_dim": 8, "mlp": mlp}
+    lengths = [9, 1, 0, 14, 4]
+    layers, _, _, pk, pv, tables = _decoder_case(900, 3, lengths, cfg, False)
+    h0 = np.random.default_rng(90).standard_normal((len(lengths), 32))
+    a = oracle.prefill_step(h0, layers, pk, pv, tables, lengths, [1] * len(lengths), 4, cfg)
+    b = oracle.decode_step(h0, layers, pk, pv, tables, lengths, 4, cfg)
+    assert _rel(a, b) <= 1e-12
+    assert np.all(np.isfinite(a))
+
+
+def test_composition_pins_catch_planted_slips():
+    # the comparisons above fail for plausible slips in the compositions,
+    # planted here in local copies (the oracle itself is untouched)
+    cfg = {"n_heads": 4, "n_kv_heads": 2, "head_dim": 8}
+    lengths = [6, 2, 9]
+    layers, dense, prev_x, pk, pv, tables = _decoder_case(950, 3, lengths, cfg, True)
+    h0 = np.random.default_rng(95).standard_normal((len(lengths), 32))
+    ref = np.stack([_dense_decoder_token(h0[i], dense, layers, [px[i] for px in prev_x], L, cfg)
+                    for i, L in enumerate(lengths)])
+    assert _rel(oracle.decode_step(h0, layers, pk, pv, tables, lengths, 4, cfg), ref) <= 1e-11
+
+    def unthreaded():
+        for li, w in enumerate(layers):
+            out, _, _ = oracle.decode_layer(h0, w, pk[li], pv[li], tables, lengths, 4, cfg)
+        return out
+
+    def reversed_layers():
+        h = h0
+        for li in reversed(range(len(layers))):
+            h, _, _ = oracle.decode_layer(h, layers[li], pk[li], pv[li], tables, lengths, 4, cfg)
+        return h
+
+    def rotated_pools():
+        h = h0
+        for li, w in enumerate(layers):
+            lj = (li + 1) % len(layers)
+            h, _, _ = oracle.decode_layer(h, w, pk[lj], pv[lj], tables, lengths, 4, cfg)
+        return h
+
+    for slip in (unthreaded, reversed_layers, rotated_pools):
+        assert not _rel(slip(), ref) <= 1e-3, slip.__name__
+
+    # prefill: every sequence reading the first rows (offset never advanced)
+    chunks = [2, 3, 1]
+    layers2, _, _, pk2, pv2, tables2 = _decoder_case(960, 2, lengths, cfg, False,
+                                                     extra_rows=chunks)
+    hp = np.random.default_rng(96).standard_normal((sum(chunks), 32))
+    good = oracle.prefill_step(hp, layers2, pk2, pv2, tables2, lengths, chunks, 4, cfg)
+    per_seq = []
+    t = 0
+    for i, (L, c) in enumerate(zip(lengths, chunks)):
+        one = oracle.prefill_step(hp[t:t + c], layers2, pk2, pv2, [tables2[i]], [L], [c], 4, cfg)
+        per_seq.append(one)
+        t += c
+    assert _rel(good, np.vstack(per_seq)) <= 1e-13
+    slipped = np.vstack([oracle.prefill_step(hp[:c], layers2, pk2, pv2, [tables2[i]], [L], [c], 4,
+                                             cfg)
+                         for i, (L, c) in enumerate(zip(lengths, chunks))])
+    assert not _rel(slipped, good) <= 1e-3
