@@ -151,6 +151,30 @@ lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in, int64_t r
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * lowrank_linear_forward_noalloc -- lowrank_linear_forward for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, which is instead a fixed scratch array of this library, one per
+ * GPU, LR_NOALLOC_SCRATCH_BYTES bytes, held until the process ends.  The call
+ * allocates nothing and frees nothing.
+ *
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (other streams, other threads) race and must not be
+ *   issued.  The scratch keeps the last call's contents; the decode path's
+ *   counters return to zero at the end of every call, as in a workspace.
+ *   Errors: as lowrank_linear_forward, and LR_ERR_CAPACITY when the call needs
+ *   more scratch than LR_NOALLOC_SCRATCH_BYTES (lowrank_workspace_bytes(0, ...)
+ *   gives the need); LR_ERR_HIP if the scratch address cannot be looked up.
+ *   A bounded wait that gives up is not reported by this variant.
+ */
+#define LR_NOALLOC_SCRATCH_BYTES (8u << 20)
+lr_status lowrank_linear_forward_noalloc(lr_dtype dt, int64_t T, int64_t d_in, int64_t r,
+                                         int64_t d_out, const void* x, int64_t ldx,
+                                         const void* Ut, int64_t ldu, const void* Vt,
+                                         int64_t ldv, void* y, int64_t ldy, float* t_io,
+                                         int64_t ldt, unsigned flags, hipStream_t stream);
+
+/*
  * lowrank_linear_forward_group -- n independent decomposed linears
  * (DeInfer/en §2.A, as lowrank_linear_forward) over the same T token rows in
  * one launch: bf16 decode path only (1 <= T <= 64, 1 <= n <= 8).  Meant for

@@ -20,7 +20,7 @@ import numpy as np
 
 from . import _lib
 from ._lib import (LR_BF16, LR_DEFAULT_WAIT_LIMIT, LR_ERR_WAIT, LR_F32, LR_FULL,
-                   LR_PACKED_WEIGHTS, LR_STAGE1_ONLY, LR_STAGE2_ONLY, LowrankError, load,
+                   LR_NOALLOC_SCRATCH_BYTES, LR_PACKED_WEIGHTS, LR_STAGE1_ONLY, LR_STAGE2_ONLY, LowrankError, load,
                    status_string)
 
 __all__ = [
@@ -30,6 +30,7 @@ __all__ = [
     "LowrankError", "load", "PackedFactor", "pack_factor", "lowrank_packed_bytes",
     "lowrank_linear_forward_group", "lowrank_group_workspace_bytes", "lowrank_workspace_check",
     "lowrank_set_wait_limit", "LR_DEFAULT_WAIT_LIMIT", "LR_ERR_WAIT",
+    "lowrank_linear_forward_noalloc", "LR_NOALLOC_SCRATCH_BYTES",
 ]
 
 
@@ -211,6 +212,41 @@ def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, w
     _lib.check(st, "lowrank_linear_forward")
     if dt == LR_BF16 and T <= 64:
         _note(workspace)
+    return y
+
+
+def lowrank_linear_forward_noalloc(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL,
+                                   stream=None):
+    """lowrank_linear_forward with the library's fixed scratch instead of a
+    workspace (no device allocation by the library; y must then be given or
+    is allocated here by the caller's framework).  See lowrank.h."""
+    torch = _torch()
+    lib = load()
+    ref = x if x is not None else t_io
+    dev = ref.device
+    if isinstance(Ut, PackedFactor) or isinstance(Vt, PackedFactor):
+        flags |= LR_PACKED_WEIGHTS
+    mode = flags & ~LR_PACKED_WEIGHTS
+    if mode == LR_STAGE2_ONLY:
+        T, r = t_io.shape
+        d_in = int(Ut.shape[1]) if Ut is not None else 1
+        dt = _dtype_code(Vt)
+    else:
+        T, d_in = x.shape
+        r = int(Ut.shape[0])
+        dt = _dtype_code(x)
+    d_out = int(Vt.shape[0]) if Vt is not None else 1
+    if y is None and mode != LR_STAGE1_ONLY:
+        y = torch.empty((T, d_out), dtype=Vt.dtype, device=dev)
+    st = lib.lowrank_linear_forward_noalloc(
+        dt, T, d_in, r, d_out,
+        _ptr(x), _ld(x) if x is not None else 0,
+        _ptr(Ut), _wld(Ut) if Ut is not None else 0,
+        _ptr(Vt), _wld(Vt) if Vt is not None else 0,
+        _ptr(y), _ld(y) if y is not None else 0,
+        _ptr(t_io), _ld(t_io) if t_io is not None else 0,
+        flags, _stream(stream, dev))
+    _lib.check(st, "lowrank_linear_forward_noalloc")
     return y
 
 

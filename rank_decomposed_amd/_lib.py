@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "liblowrank.so")
 LR_OK, LR_ERR_ARG, LR_ERR_DTYPE, LR_ERR_ALIGN, LR_ERR_WORKSPACE, LR_ERR_CAPACITY, \
     LR_ERR_HIP, LR_ERR_UNSUPPORTED, LR_ERR_WAIT = range(9)
 LR_DEFAULT_WAIT_LIMIT = 1 << 20
+LR_NOALLOC_SCRATCH_BYTES = 8 << 20
 LR_F32, LR_BF16 = 0, 1
 LR_FULL, LR_STAGE1_ONLY, LR_STAGE2_ONLY = 0, 1, 2
 LR_PACKED_WEIGHTS = 4
@@ -46,6 +47,8 @@ SIGNATURES = {
     "lowrank_linear_forward_group": (C.c_int, [_i64, C.c_int, _p, _u, _p, _sz, _p]),
     "lowrank_pack_factor": (C.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p]),
     "lowrank_workspace_check": (C.c_int, [_p, _sz, _p, _p]),
+    "lowrank_linear_forward_noalloc": (C.c_int, [C.c_int, _i64, _i64, _i64, _i64, _p, _i64, _p,
+                                                 _i64, _p, _i64, _p, _i64, _p, _i64, _u, _p]),
     "lowrank_set_wait_limit": (None, [C.c_uint32]),
 }
 
