@@ -338,7 +338,10 @@ def main():
 
 def prefill(torch, lr, dev, stream, M=16384, reps=3):
     """16384 rows (8 x 2048) through the seven projections at ratio 0.4 and
-    0.2 on the fused kernel; MFMA-bound, so one layer set suffices."""
+    0.2, each on its two large-tile GEMMs with t through HBM (the path the
+    library takes from 1024 rows on); MFMA-bound, so one layer set suffices.
+    A context entry times the fused kernel (t kept in LDS) on the same rows
+    for three projections."""
     import synth
     out = {}
     gen = torch.Generator(device=dev).manual_seed(3_000_001)
@@ -382,12 +385,34 @@ def prefill(torch, lr, dev, stream, M=16384, reps=3):
         torch.cuda.synchronize()
         gate_us = 1e3 * a.elapsed_time(b) / reps
         gate_fl = 2 * M * r * (4096 + 11008)
+        # context: the fused kernel (rank tile kept in LDS, 64-row tiles) at
+        # the same 16384 rows, per projection, against the two-GEMM path
+        cmp = {}
+        for role in ("q", "gate", "down"):
+            ut, vt, r_ = fac[role]
+            d_in, d_out = SHAPES[role]
+            us = {}
+            for name, fl in (("two_gemm", lr.LR_FULL), ("fused", lr.LR_PREFILL_FUSED)):
+                lr.lowrank_linear_forward(x[d_in], ut, vt, y=y[d_out], flags=fl, workspace=ws)
+                a.record(stream)
+                for _ in range(reps):
+                    lr.lowrank_linear_forward(x[d_in], ut, vt, y=y[d_out], flags=fl,
+                                              workspace=ws)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us[name] = 1e3 * a.elapsed_time(b) / reps
+            fl_ = 2 * M * r_ * (d_in + d_out)
+            cmp[role] = {"r": r_, "two_gemm_us": round(us["two_gemm"], 2),
+                         "fused_us": round(us["fused"], 2),
+                         "two_gemm_frac": round(fl_ / (us["two_gemm"] * 1e-6) / BF16_PEAK, 4),
+                         "fused_frac": round(fl_ / (us["fused"] * 1e-6) / BF16_PEAK, 4)}
         out["rho%.1f" % rho] = {
             "tokens_per_s": round(M / (ms * 1e-3), 1), "ms_per_layer_set": round(ms, 4),
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
             "frac": round(flops / (ms * 1e-3) / BF16_PEAK, 4),
             "gate_us": round(gate_us, 2),
-            "gate_frac": round(gate_fl / (gate_us * 1e-6) / BF16_PEAK, 4)}
+            "gate_frac": round(gate_fl / (gate_us * 1e-6) / BF16_PEAK, 4),
+            "fused_vs_two_gemm": cmp}
     return out
 
 
@@ -402,7 +427,8 @@ def tp_share(torch, lr, dev, stream, reps, n_sets=32, P=8):
     the shares would all-reduce); V_r split by output columns, so stage 2
     writes [T, d_out / 8].  32 distinct share sets (1 GB of factors) stream
     from HBM; each pass over them is one HIP graph.  T = 64 is HBM-bound
-    (fragment-packed factors, as in the decode leg), T = 4096 MFMA-bound
+    (fragment-packed factors, as in the decode leg; projections that read the
+    same x_s grouped into one launch per stage), T = 4096 MFMA-bound
     (row-major factors on the large-tile GEMMs)."""
     import math
     gen = torch.Generator(device=dev).manual_seed(4_000_001)
@@ -426,8 +452,10 @@ def tp_share(torch, lr, dev, stream, reps, n_sets=32, P=8):
                     for role, (ut, vt, r) in layer.items()} for layer in sets]
         xs = {w: torch.randn((T, w), generator=gen, device=dev).to(torch.bfloat16)
               for w in (640, 1728)}
-        ts = {r: torch.empty((T, r), dtype=torch.float32, device=dev) for r in (1024, 1494)}
-        ys = {w: torch.empty((T, w), dtype=torch.bfloat16, device=dev) for w in (640, 1728)}
+        ts = {role: torch.empty((T, rank(0.4, *SHAPES_13B[role])), dtype=torch.float32,
+                                device=dev) for role in ROLES}
+        ys = {role: torch.empty((T, SHAPES_13B[role][1] // P), dtype=torch.bfloat16,
+                                device=dev) for role in ROLES}
         need = 0
         nbytes = flops = 0
         for role in ROLES:
@@ -437,16 +465,35 @@ def tp_share(torch, lr, dev, stream, reps, n_sets=32, P=8):
             # shares, x_s, y_s, and t written and read once (counted at 2 bytes)
             nbytes += 2 * r * (wi + wo) + 2 * T * (wi + wo) + 2 * 2 * T * r
             flops += 2 * T * r * (wi + wo)
+        if T <= 64:
+            # the layer's dependency order: q,k,v read one x_s, gate,up
+            # another; each group is one stage-1 launch, then (after the
+            # shares' all-reduce of t_s) one stage-2 launch
+            groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+            layer0 = use[0]
+            s1 = [[dict(x=xs[SHAPES_13B[m][0] // P], Ut=layer0[m][0], t_io=ts[m]) for m in grp]
+                  for grp in groups]
+            s2 = [[dict(Vt=layer0[m][1], t_io=ts[m], y=ys[m]) for m in grp] for grp in groups]
+            need = max(need, max(lr.lowrank_group_workspace_bytes(T, lin) for lin in s1 + s2))
         ws = torch.zeros(need + 256, dtype=torch.uint8, device=dev)
 
         def run():
             for layer in use:
+                if T <= 64:
+                    for grp in groups:
+                        lr.lowrank_linear_forward_group(
+                            [dict(x=xs[SHAPES_13B[m][0] // P], Ut=layer[m][0], t_io=ts[m])
+                             for m in grp], workspace=ws)
+                        lr.lowrank_linear_forward_group(
+                            [dict(Vt=layer[m][1], t_io=ts[m], y=ys[m]) for m in grp],
+                            workspace=ws)
+                    continue
                 for role in ROLES:
                     ut, vt, r = layer[role]
-                    d_in, d_out = SHAPES_13B[role]
-                    lr.lowrank_linear_forward(xs[d_in // P], ut, None, t_io=ts[r],
-                                              flags=lr.LR_STAGE1_ONLY, workspace=ws)
-                    lr.lowrank_linear_forward(None, None, vt, y=ys[d_out // P], t_io=ts[r],
+                    lr.lowrank_linear_forward(xs[SHAPES_13B[role][0] // P], ut, None,
+                                              t_io=ts[role], flags=lr.LR_STAGE1_ONLY,
+                                              workspace=ws)
+                    lr.lowrank_linear_forward(None, None, vt, y=ys[role], t_io=ts[role],
                                               flags=lr.LR_STAGE2_ONLY, workspace=ws)
         side = torch.cuda.Stream(dev)
         side.wait_stream(torch.cuda.current_stream(dev))

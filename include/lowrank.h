@@ -67,13 +67,20 @@ typedef enum {
 
 typedef enum { LR_F32 = 0, LR_BF16 = 1 } lr_dtype;
 
-/* flags of lowrank_linear_forward: one mode, optionally | LR_PACKED_WEIGHTS */
+/* flags of lowrank_linear_forward: one mode, optionally | LR_PACKED_WEIGHTS
+   or | LR_PREFILL_FUSED */
 enum {
   LR_FULL = 0,         /* y = (x U_r) V_r; t_io written too when non-NULL          */
   LR_STAGE1_ONLY = 1,  /* t_io = x U_r (t_io required; Vt, y unused)              */
   LR_STAGE2_ONLY = 2,  /* y = t_io V_r (t_io read; x, Ut unused)                   */
-  LR_PACKED_WEIGHTS = 4 /* bf16, T <= 64: Ut and Vt are fragment-packed (below);
+  LR_PACKED_WEIGHTS = 4, /* bf16, T <= 64: Ut and Vt are fragment-packed (below);
                            ldu / ldv are their block pitches in steps           */
+  LR_PREFILL_FUSED = 8  /* bf16, T > 64, LR_FULL without t_io: the fused kernel
+                           (t kept on chip) at any row count, instead of the
+                           two large-tile GEMMs it cedes to from 1024 rows on;
+                           for comparing the two.  Needs r <= 1216 (the rank
+                           tile in LDS); LR_ERR_UNSUPPORTED otherwise.  No
+                           workspace is needed.                                */
 };
 
 /*
@@ -189,6 +196,8 @@ lr_status lowrank_linear_forward_noalloc(lr_dtype dt, int64_t T, int64_t d_in, i
  *   lin[i]   one linear, operands as in lowrank_linear_forward (bf16 x, Ut,
  *            Vt, y; fp32 t_io):
  *              Vt == NULL   stage 1 only: t_io = x U_r (t_io required)
+ *              Ut == NULL   stage 2 only: y = bf16(t_io V_r) from the fp32
+ *                           t_io [T, r] (x unused; d_in > 0 still given)
  *              y_acc != NULL  y_acc[T, ld_acc] += y in fp32 (y unused)
  *              otherwise    y = bf16((x U_r) V_r), t_io written when given
  *   flags    0 or LR_PACKED_WEIGHTS (then every Ut / Vt is fragment-packed,

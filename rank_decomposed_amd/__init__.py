@@ -20,13 +20,15 @@ import numpy as np
 
 from . import _lib
 from ._lib import (LR_BF16, LR_DEFAULT_WAIT_LIMIT, LR_ERR_WAIT, LR_F32, LR_FULL,
-                   LR_NOALLOC_SCRATCH_BYTES, LR_PACKED_WEIGHTS, LR_STAGE1_ONLY, LR_STAGE2_ONLY, LowrankError, load,
+                   LR_NOALLOC_SCRATCH_BYTES, LR_PACKED_WEIGHTS, LR_PREFILL_FUSED,
+                   LR_STAGE1_ONLY, LR_STAGE2_ONLY, LowrankError, load,
                    status_string)
 
 __all__ = [
     "lowrank_linear_forward", "kv_remap_gather", "lowrank_prepare_decode", "lowrank_prepare_prefill",
     "lowrank_workspace_bytes", "lowrank_status_string", "lowrank_version",
     "LR_F32", "LR_BF16", "LR_FULL", "LR_STAGE1_ONLY", "LR_STAGE2_ONLY", "LR_PACKED_WEIGHTS",
+    "LR_PREFILL_FUSED",
     "LowrankError", "load", "PackedFactor", "pack_factor", "lowrank_packed_bytes",
     "lowrank_linear_forward_group", "lowrank_group_workspace_bytes", "lowrank_workspace_check",
     "lowrank_set_wait_limit", "LR_DEFAULT_WAIT_LIMIT", "LR_ERR_WAIT",
@@ -183,7 +185,7 @@ def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, w
     dev = ref.device
     if isinstance(Ut, PackedFactor) or isinstance(Vt, PackedFactor):
         flags |= LR_PACKED_WEIGHTS
-    mode = flags & ~LR_PACKED_WEIGHTS
+    mode = flags & ~(LR_PACKED_WEIGHTS | LR_PREFILL_FUSED)
     if mode == LR_STAGE2_ONLY:
         T, r = t_io.shape
         d_in = int(Ut.shape[1]) if Ut is not None else 1
@@ -195,7 +197,7 @@ def lowrank_linear_forward(x, Ut, Vt, y=None, t_io=None, flags: int = LR_FULL, w
     d_out = int(Vt.shape[0]) if Vt is not None else 1
     if y is None and mode != LR_STAGE1_ONLY:
         y = torch.empty((T, d_out), dtype=Vt.dtype, device=dev)
-    need = lowrank_workspace_bytes(0, dt, T, d_in, r, d_out)
+    need = 0 if flags & LR_PREFILL_FUSED else lowrank_workspace_bytes(0, dt, T, d_in, r, d_out)
     if workspace is None and need > 0:
         # zero-filled: the decode kernel's counters must start at zero (it
         # leaves them at zero when it finishes)
@@ -226,7 +228,7 @@ def lowrank_linear_forward_noalloc(x, Ut, Vt, y=None, t_io=None, flags: int = LR
     dev = ref.device
     if isinstance(Ut, PackedFactor) or isinstance(Vt, PackedFactor):
         flags |= LR_PACKED_WEIGHTS
-    mode = flags & ~LR_PACKED_WEIGHTS
+    mode = flags & ~(LR_PACKED_WEIGHTS | LR_PREFILL_FUSED)
     if mode == LR_STAGE2_ONLY:
         T, r = t_io.shape
         d_in = int(Ut.shape[1]) if Ut is not None else 1
@@ -253,13 +255,15 @@ def lowrank_linear_forward_noalloc(x, Ut, Vt, y=None, t_io=None, flags: int = LR
 def _group_structs(linears):
     arr = (_lib.Linear * len(linears))()
     for i, L in enumerate(linears):
-        x, Ut, Vt = L["x"], L["Ut"], L.get("Vt")
+        x, Ut, Vt = L.get("x"), L.get("Ut"), L.get("Vt")
         y, y_acc, t_io = L.get("y"), L.get("y_acc"), L.get("t_io")
         a = arr[i]
-        a.d_in, a.r = int(x.shape[1]), int(Ut.shape[0])
+        a.d_in = int(x.shape[1]) if x is not None else 1
+        a.r = int(Ut.shape[0]) if Ut is not None else int(t_io.shape[1])
         a.d_out = int(Vt.shape[0]) if Vt is not None else 1
-        a.x, a.ldx = x.data_ptr(), _ld(x)
-        a.Ut, a.ldu = Ut.data_ptr(), _wld(Ut)
+        if Ut is not None:
+            a.x, a.ldx = x.data_ptr(), _ld(x)
+            a.Ut, a.ldu = Ut.data_ptr(), _wld(Ut)
         if Vt is not None:
             a.Vt, a.ldv = Vt.data_ptr(), _wld(Vt)
         if y is not None:
@@ -280,13 +284,15 @@ def lowrank_linear_forward_group(linears, workspace=None, stream=None):
     """n independent bf16 decode linears over the same T <= 64 rows in one
     launch.  Each entry: dict with x [T, d_in], Ut, Vt (None: stage 1 only),
     y (allocated when missing and neither y_acc nor stage-1-only), y_acc
-    (fp32, added to), t_io (fp32).  Ut / Vt may be PackedFactor views (then
-    all of them must be).  Returns the list of y (None where not written)."""
+    (fp32, added to), t_io (fp32).  Without x and Ut an entry is stage 2
+    only, from its t_io.  Ut / Vt may be PackedFactor views (then all of them
+    must be).  Returns the list of y (None where not written)."""
     torch = _torch()
     lib = load()
-    T = int(linears[0]["x"].shape[0])
-    dev = linears[0]["x"].device
-    packed = any(isinstance(L["Ut"], PackedFactor) for L in linears)
+    ref = next(L.get("x") if L.get("Ut") is not None else L["t_io"] for L in linears)
+    T = int(ref.shape[0])
+    dev = ref.device
+    packed = any(isinstance(L.get(k), PackedFactor) for L in linears for k in ("Ut", "Vt"))
     for L in linears:
         if L.get("Vt") is not None and L.get("y") is None and L.get("y_acc") is None:
             L["y"] = torch.empty((T, int(L["Vt"].shape[0])), dtype=torch.bfloat16, device=dev)

@@ -18,6 +18,7 @@ LR_NOALLOC_SCRATCH_BYTES = 8 << 20
 LR_F32, LR_BF16 = 0, 1
 LR_FULL, LR_STAGE1_ONLY, LR_STAGE2_ONLY = 0, 1, 2
 LR_PACKED_WEIGHTS = 4
+LR_PREFILL_FUSED = 8
 
 # every symbol include/lowrank.h declares, with (restype, argtypes)
 _i64, _u, _sz, _p, _pi32 = C.c_int64, C.c_uint, C.c_size_t, C.c_void_p, C.c_void_p

@@ -64,7 +64,8 @@ extern "C" lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in
                                             size_t workspace_bytes, hipStream_t stream) {
   if (dt != LR_F32 && dt != LR_BF16) return LR_ERR_DTYPE;
   const bool packed = (flags & LR_PACKED_WEIGHTS) != 0;
-  const unsigned mode = flags & ~(unsigned)LR_PACKED_WEIGHTS;
+  const bool fused = (flags & LR_PREFILL_FUSED) != 0;
+  const unsigned mode = flags & ~(unsigned)(LR_PACKED_WEIGHTS | LR_PREFILL_FUSED);
   if (mode > 2) return LR_ERR_ARG;
   if (T <= 0 || d_in <= 0 || r <= 0 || d_out <= 0) return LR_ERR_ARG;
   if (T > INT32_MAX || d_in > INT32_MAX || r > INT32_MAX || d_out > INT32_MAX) return LR_ERR_ARG;
@@ -85,13 +86,16 @@ extern "C" lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in
     if (s1 && (!aligned(x, 4) || !aligned(Ut, 4))) return LR_ERR_ALIGN;
     if (s2 && (!aligned(Vt, 4) || !aligned(y, 4))) return LR_ERR_ALIGN;
   }
-  const size_t need = linear_ws(dt, T, d_in, r, d_out);
+  const size_t need = fused ? 0 : linear_ws(dt, T, d_in, r, d_out);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return LR_ERR_WORKSPACE;
 
   lr::DecodeLinear d{T, d_in, r, d_out, x, ldx, Ut, ldu, Vt, ldv, y, ldy, t_io, ldt, mode,
                      workspace};
   d.packed = packed;
+  d.force_fused = fused;
+  if (fused && (dt != LR_BF16 || T <= 64 || !lr::prefill_fused_supported(d)))
+    return LR_ERR_UNSUPPORTED;
   if (dt == LR_BF16 && T <= 64 && !lr::decode_supported(d)) return LR_ERR_UNSUPPORTED;
   hipError_t e;
   if (dt == LR_F32)
@@ -106,24 +110,28 @@ extern "C" lr_status lowrank_linear_forward(lr_dtype dt, int64_t T, int64_t d_in
 namespace {
 
 // Host checks of one member of a group; fills the kernel-side description.
+// 0: both stages, 1: stage 1 only (no Vt), 2: stage 2 only (no Ut)
+unsigned member_mode(const lr_linear& L) { return !L.Vt ? 1u : (!L.Ut ? 2u : 0u); }
+
 lr_status group_member(int64_t T, const lr_linear& L, bool packed, lr::DecodeLinear* d) {
   if (L.d_in <= 0 || L.r <= 0 || L.d_out <= 0) return LR_ERR_ARG;
   if (L.d_in > INT32_MAX || L.r > INT32_MAX || L.d_out > INT32_MAX) return LR_ERR_ARG;
-  const bool s2 = L.Vt != nullptr;
+  const bool s1 = L.Ut != nullptr, s2 = L.Vt != nullptr;
   const int64_t ku = packed ? (L.d_in + 31) / 32 : L.d_in, kv = packed ? (L.r + 31) / 32 : L.r;
-  if (!L.x || !L.Ut || L.ldx < L.d_in || L.ldu < ku) return LR_ERR_ARG;
-  if (!s2 && !L.t_io) return LR_ERR_ARG;
+  if (!s1 && !s2) return LR_ERR_ARG;
+  if (s1 && (!L.x || L.ldx < L.d_in || L.ldu < ku)) return LR_ERR_ARG;
+  if ((!s1 || !s2) && !L.t_io) return LR_ERR_ARG;
   if (s2 && (L.ldv < kv || (!L.y_acc && (!L.y || L.ldy < L.d_out)) ||
              (L.y_acc && L.ld_acc < L.d_out)))
     return LR_ERR_ARG;
   if (L.t_io && L.ldt < L.r) return LR_ERR_ARG;
-  if (!aligned(L.x, 16) || !aligned(L.Ut, 16) || L.ldx % 8 || (!packed && L.ldu % 8))
+  if (s1 && (!aligned(L.x, 16) || !aligned(L.Ut, 16) || L.ldx % 8 || (!packed && L.ldu % 8)))
     return LR_ERR_ALIGN;
   if (s2 && (!aligned(L.Vt, 16) || (!packed && L.ldv % 8))) return LR_ERR_ALIGN;
   if (s2 && !L.y_acc && !aligned(L.y, 2)) return LR_ERR_ALIGN;
   if ((L.y_acc && !aligned(L.y_acc, 4)) || (L.t_io && !aligned(L.t_io, 4))) return LR_ERR_ALIGN;
   *d = lr::DecodeLinear{T, L.d_in, L.r, L.d_out, L.x, L.ldx, L.Ut, L.ldu, L.Vt, L.ldv, L.y,
-                        L.ldy, L.t_io, L.ldt, s2 ? 0u : 1u, nullptr};
+                        L.ldy, L.t_io, L.ldt, member_mode(L), nullptr};
   d->y_acc = L.y_acc;
   d->ld_acc = L.ld_acc;
   d->packed = packed;
@@ -139,6 +147,7 @@ extern "C" size_t lowrank_group_workspace_bytes(int64_t T, int n, const lr_linea
   for (int i = 0; i < n; ++i) {
     if (lin[i].d_in <= 0 || lin[i].r <= 0 || lin[i].d_out <= 0) return 0;
     d[i] = lr::DecodeLinear{T, lin[i].d_in, lin[i].r, lin[i].d_out};
+    d[i].flags = member_mode(lin[i]);
   }
   return lr::decode_group_workspace_bytes(d, n);
 }

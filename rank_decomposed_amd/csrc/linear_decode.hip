@@ -1016,17 +1016,32 @@ void decode_pers_kernel(PersArgs args) {
 
 // t (fp32, caller's layout) -> fragment-packed bf16 (and bf16 residual) for a
 // stage-2-only call.
-__global__ __launch_bounds__(256) void split_t_kernel(const float* __restrict__ t, int64_t ldt,
-                                                      int T, int N, uint16_t* thi, uint16_t* tlo,
-                                                      int64_t ldtb) {
-  const int64_t total = (int64_t)T * N;
+// Stage-2-only members of a launch: their caller's fp32 t re-laid into the
+// fragment-packed bf16 operand (plus the bf16 residual for T <= 16), all
+// members in one launch (blockIdx.y = member).
+struct SplitT {
+  const float* t;
+  int64_t ldt;
+  int N;
+  uint16_t* thi;
+  uint16_t* tlo;
+  int64_t ldtb;
+};
+struct SplitArgs {
+  SplitT m[kMaxGroup];
+  int T;
+};
+
+__global__ __launch_bounds__(256) void split_t_kernel(SplitArgs a) {
+  const SplitT& s = a.m[blockIdx.y];
+  const int64_t total = (int64_t)a.T * s.N;
   for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int tok = (int)(e / N), n = (int)(e % N);
-    const float v = t[(int64_t)tok * ldt + n];
+    const int tok = (int)(e / s.N), n = (int)(e % s.N);
+    const float v = s.t[(int64_t)tok * s.ldt + n];
     const uint32_t hi = f2bf(v);
-    const int64_t pi = tpack(tok, n, ldtb);
-    thi[pi] = (uint16_t)hi;
-    if (tlo) tlo[pi] = (uint16_t)f2bf(v - bf2f(hi));
+    const int64_t pi = tpack(tok, n, s.ldtb);
+    s.thi[pi] = (uint16_t)hi;
+    if (s.tlo) s.tlo[pi] = (uint16_t)f2bf(v - bf2f(hi));
   }
 }
 
@@ -1281,6 +1296,10 @@ hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
   const int S1 = group_ranges(ds, n);
   size_t off = kCtlBytes;
   int n1 = 0, TB = 1;
+  SplitArgs sa{};
+  sa.T = (int)T;
+  int nsplit = 0;
+  int64_t split_el = 0;
   for (int i = 0; i < n; ++i) {
     const DecodeLinear& d = ds[i];
     const Plan pl = make_plan(T, d.d_in, d.r, d.d_out, S1);
@@ -1318,18 +1337,20 @@ hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
       L.n2 = 0;
       L.wait = 0;
     } else if (d.flags == 2) {  // stage 2 only: t from t_io
-      const int64_t total = T * d.r;
-      int blocks = (int)((total + 255) / 256);
-      if (blocks > 1024) blocks = 1024;
-      hipLaunchKernelGGL(split_t_kernel, dim3(blocks), dim3(256), 0, st, d.t_io, d.ldt, (int)T,
-                         (int)d.r, L.thi, pl.TB == 1 ? L.tlo : (uint16_t*)nullptr, pl.ldtb);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      sa.m[nsplit++] = SplitT{d.t_io, d.ldt, (int)d.r, L.thi,
+                              pl.TB == 1 ? L.tlo : (uint16_t*)nullptr, pl.ldtb};
+      split_el = std::max(split_el, T * d.r);
       L.nb1 = 0;
       L.wait = 0;
     }
     L.first1 = n1;
     n1 += L.nb1 * L.S1;
+  }
+  if (nsplit) {
+    const int blocks = (int)std::min<int64_t>((split_el + 255) / 256, 1024);
+    hipLaunchKernelGGL(split_t_kernel, dim3(blocks, nsplit), dim3(256), 0, st, sa);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   a.n1 = n1;
   int grid = n1;

@@ -403,15 +403,21 @@ bool prefill_act_ok(const DecodeLinear& d) {
          (d.act != 1 || (d.glu && a16(d.glu) && d.ldglu % 8 == 0));
 }
 
-hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st) {
-  if (d.act && !prefill_act_ok(d)) return hipErrorInvalidValue;
-  if (prefill_accumulates(d)) return prefill_big(d, st);
-  if (d.y_acc) return hipErrorInvalidValue;
+bool prefill_fused_supported(const DecodeLinear& d) {
   // buffer-load offsets are 32-bit: the fused kernel needs every operand
   // (plus one tile of rows past its end) under 2 GiB
-  const bool small = (d.T + kBM) * d.ldx * 2 < (1ll << 31) && (d.r + 128) * d.ldu * 2 < (1ll << 31) &&
+  const bool small = (d.T + kBM) * d.ldx * 2 < (1ll << 31) &&
+                     (d.r + 128) * d.ldu * 2 < (1ll << 31) &&
                      (d.d_out + 512) * d.ldv * 2 < (1ll << 31);
-  if (d.flags == 0 && d.t_io == nullptr && fused_fits(d.r) && small) {
+  return d.flags == 0 && d.t_io == nullptr && !d.y_acc && !d.act && fused_fits(d.r) && small;
+}
+
+hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st) {
+  if (d.act && !prefill_act_ok(d)) return hipErrorInvalidValue;
+  if (d.force_fused && !prefill_fused_supported(d)) return hipErrorInvalidValue;
+  if (!d.force_fused && prefill_accumulates(d)) return prefill_big(d, st);
+  if (d.y_acc) return hipErrorInvalidValue;
+  if (prefill_fused_supported(d)) {
     FusedArgs f{};
     f.x = static_cast<const uint16_t*>(d.x);
     f.ldx = d.ldx;

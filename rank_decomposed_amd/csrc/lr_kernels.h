@@ -34,6 +34,8 @@ struct DecodeLinear {
   int act = 0;
   const void* glu = nullptr;
   int64_t ldglu = 0;
+  // prefill path: the fused kernel at any row count (prefill_fused_supported)
+  bool force_fused = false;
 };
 
 // Control area of a decode-path workspace: kCtlBlocks blocks of
@@ -146,6 +148,9 @@ hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st);
 // Whether prefill_linear_bf16 takes the large-tile path for d, the one that
 // can add y into an fp32 y_acc (other paths reject y_acc).
 bool prefill_accumulates(const DecodeLinear& d);
+// The fused kernel can take this call (both stages, no t_io, rank tile in
+// LDS, operands under its 32-bit offsets).
+bool prefill_fused_supported(const DecodeLinear& d);
 // Whether prefill_linear_bf16 can apply d.act in the stage-2 epilogue.
 bool prefill_act_ok(const DecodeLinear& d);
 

@@ -3,13 +3,16 @@ linears in one launch match the fp64 oracle (stage-1-only and accumulate
 members included), and give bit for bit what separate calls give where both
 split the stage-1 reduction alike (d_in under 1024 here: one or two K ranges
 either way)."""
+import functools
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import rank_decomposed_amd as lr
-from gpu_util import bits, control_counters, dev, make_linear, maxrel, to_f64
+import synth
+from gpu_util import bits, control_counters, dev, ld_for, make_linear, maxrel, padded, to_f64
 
 pytestmark = pytest.mark.gpu
 BF16_TOL = 2e-2
@@ -152,3 +155,67 @@ def test_group_graph_replay():
         torch.cuda.synchronize()
         for a, b in zip(got, ref):
             assert np.array_equal(a, b)
+
+
+@functools.lru_cache(maxsize=8)
+def _share_factors(seed, d_in, r, d_out, P):
+    U, V = synth.fast_factors(seed, d_in, d_out, r)
+    return U[:d_in // P], V[:, :d_out // P]
+
+
+def _share(seed, T, d_in, r, d_out, P):
+    """Share 0 of P of a rank-r decomposition of a d_in x d_out weight: the
+    first d_in / P rows of U_r and the first d_out / P columns of V_r (so r
+    may exceed both share widths), as make_linear returns them."""
+    U, V = _share_factors(seed, d_in, r, d_out, P)
+    wi = d_in // P
+    x = synth.tokens(seed + 1 + T, T, wi)
+    xs, xv = synth.quantize(x, "bf16")
+    us, uv = synth.quantize(np.ascontiguousarray(U.T), "bf16")
+    vs, vv = synth.quantize(np.ascontiguousarray(V.T), "bf16")
+    return {"x": xv, "U": uv.T, "V": vv.T, "dx": padded(xs, ld_for(wi, 8), "bf16"),
+            "dUt": padded(us, ld_for(wi, 8), "bf16"), "dVt": padded(vs, ld_for(r, 8), "bf16")}
+
+
+@pytest.mark.parametrize("T", [1, 16, 17, 64])
+def test_group_stage2_only_members(T):
+    # a tensor-parallel share's stage 2: each member multiplies its own fp32
+    # rank-space t (which the shares would have summed) by its V_r columns.
+    # Three stage-2-only members (one packed split for all) against separate
+    # stage-2-only calls, bit for bit, and against the oracle from that t
+    cs = [_share(8500, T, 2560, 1024, 2560, 4), _share(8510, T, 2560, 1494, 6912, 4),
+          make_linear(8520 + T, T, 640, 120, 130, "bf16", fast=True, ld_extra=8)]
+    d = dev()
+    g = torch.Generator(device="cpu").manual_seed(100 + T)
+    ts = [torch.randn((T, c["dUt"].shape[0]), generator=g, dtype=torch.float32).to(d)
+          for c in cs]
+    ys = [torch.full((T, c["dVt"].shape[0]), float("nan"), dtype=torch.bfloat16, device=d)
+          for c in cs]
+    lr.lowrank_linear_forward_group([dict(Vt=c["dVt"], t_io=t, y=y)
+                                     for c, t, y in zip(cs, ts, ys)])
+    sep = [lr.lowrank_linear_forward(None, None, c["dVt"], t_io=t, flags=lr.LR_STAGE2_ONLY)
+           for c, t in zip(cs, ts)]
+    torch.cuda.synchronize()
+    for c, t, y, s in zip(cs, ts, ys, sep):
+        assert np.array_equal(bits(y), bits(s))
+        assert maxrel(to_f64(y), to_f64(t) @ c["V"]) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T", [8, 64])
+def test_group_share_pattern_stage1_then_stage2(T):
+    # q, k, v of one share: stage 1 alone for all three (one launch, one x),
+    # then stage 2 alone for all three from the fp32 t (one launch), packed
+    # factors; equals the fused per-linear result of the oracle
+    cs = [_share(8600 + i, T, 2560, 1024, 2560, 4) for i in range(3)]
+    x = cs[0]["dx"]
+    d = dev()
+    ts = [torch.full((T, 1024), float("nan"), dtype=torch.float32, device=d) for _ in cs]
+    lr.lowrank_linear_forward_group([dict(x=x, Ut=lr.pack_factor(c["dUt"]), t_io=t)
+                                     for c, t in zip(cs, ts)])
+    ys = lr.lowrank_linear_forward_group([dict(Vt=lr.pack_factor(c["dVt"]), t_io=t)
+                                          for c, t in zip(cs, ts)])
+    torch.cuda.synchronize()
+    for c, t, y in zip(cs, ts, ys):
+        tr, yr = oracle.linear(cs[0]["x"], c["U"], c["V"])
+        assert maxrel(to_f64(t), tr) <= 1e-5
+        assert maxrel(to_f64(y), yr) <= BF16_TOL

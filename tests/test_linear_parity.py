@@ -10,7 +10,7 @@ import torch
 import oracle
 import rank_decomposed_amd as lr
 import synth
-from gpu_util import bits, control_counters, dev, make_linear, maxrel, padded, to_dev, to_f64
+from gpu_util import bits, control_counters, dev, ld_for, make_linear, maxrel, padded, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 BF16_TOL, F32_TOL = 2e-2, 1e-5
@@ -244,3 +244,41 @@ def test_decode_workspace_shared_across_shapes():
         assert maxrel(to_f64(y_shared), oracle.linear(c["x"], c["U"], c["V"])[1]) <= BF16_TOL
     counters = control_counters(ws)
     assert not counters.any(), np.nonzero(counters)   # every counter and flag back at zero
+
+
+@pytest.mark.parametrize("T,shape", [(1024, (512, 300, 700)), (2100, (1300, 1194, 1280)),
+                                     (4100, (4096, 819, 4096))])
+def test_bf16_prefill_forced_fused(T, shape):
+    # LR_PREFILL_FUSED keeps t on chip at row counts that otherwise take the
+    # two large-tile GEMMs: a ragged last 64-row tile (2100, 4100), the
+    # largest rank whose tile fits in LDS (1194 -> 1216 columns), ragged
+    # d_in and d_out; both realizations meet the oracle's tolerance
+    d_in, r, d_out = shape
+    c = make_linear(4700 + T + r, T, d_in, r, d_out, "bf16", fast=True, ld_extra=8)
+    y = torch.full((T, d_out), float("nan"), dtype=torch.bfloat16, device=dev())
+    lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"], y=y, flags=lr.LR_PREFILL_FUSED)
+    y2, _ = _run(c, T, "bf16")
+    torch.cuda.synchronize()
+    _, yr = oracle.linear(c["x"], c["U"], c["V"])
+    assert maxrel(to_f64(y), yr) <= BF16_TOL
+    assert maxrel(to_f64(y2), yr) <= BF16_TOL
+
+
+def test_bf16_prefill_forced_fused_refusals():
+    # a rank tile past LDS, a requested t_io, a stage-only call and decode
+    # row counts are refused before anything runs
+    d = dev()
+    x = torch.zeros((1024, 512), dtype=torch.bfloat16, device=d)
+    for T, r, kw in [(1024, 1300, {}), (1024, 300, {"t_io": True}),
+                     (1024, 300, {"stage1": True}), (64, 300, {})]:
+        ut = torch.zeros((r, 512), dtype=torch.bfloat16, device=d)
+        vt = torch.zeros((640, ld_for(r, 8)), dtype=torch.bfloat16, device=d)[:, :r]
+        y = torch.full((T, 640), float("nan"), dtype=torch.bfloat16, device=d)
+        t = torch.zeros((T, r), dtype=torch.float32, device=d)
+        flags = lr.LR_PREFILL_FUSED | (lr.LR_STAGE1_ONLY if kw.get("stage1") else 0)
+        with pytest.raises(lr.LowrankError) as err:
+            lr.lowrank_linear_forward(x[:T], ut, vt, y=y, flags=flags,
+                                      t_io=t if kw else None)
+        assert err.value.status == lr._lib.LR_ERR_UNSUPPORTED, (T, r, kw)
+        torch.cuda.synchronize()
+        assert torch.isnan(y.float()).all()
