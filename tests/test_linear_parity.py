@@ -282,3 +282,23 @@ def test_bf16_prefill_forced_fused_refusals():
         assert err.value.status == lr._lib.LR_ERR_UNSUPPORTED, (T, r, kw)
         torch.cuda.synchronize()
         assert torch.isnan(y.float()).all()
+
+
+@pytest.mark.parametrize("T", [1, 16, 17, 64])
+def test_bf16_stage2_only_reads_strided_fp32_t(T):
+    # stage 2 alone from a caller's fp32 t whose rows are padded with NaN past
+    # r (ragged last k-step: r = 100): the padding must never reach y.  Up to
+    # 16 tokens the tiles also form the bf16 residual of t, so y matches the
+    # fp64 product of the fp32 t nearly to fp32 accuracy
+    r, d_out = 100, 330
+    c = make_linear(5100 + T, T, 640, r, d_out, "bf16", fast=True, ld_extra=8)
+    g = torch.Generator(device="cpu").manual_seed(T)
+    t = torch.full((T, r + 12), float("nan"), dtype=torch.float32)
+    t[:, :r] = torch.randn((T, r), generator=g)
+    t = t.to(dev())[:, :r]
+    y = lr.lowrank_linear_forward(None, None, c["dVt"], t_io=t, flags=lr.LR_STAGE2_ONLY)
+    torch.cuda.synchronize()
+    yr = to_f64(t) @ c["V"]
+    assert maxrel(to_f64(y), yr) <= BF16_TOL
+    if T <= 16:   # t carried as bf16 hi + lo: only y's own bf16 rounding remains
+        assert maxrel(to_f64(y), yr) <= 1e-2
