@@ -829,9 +829,13 @@ constexpr int fused_ring_bytes() {
   return gNS * big_stage_bytes<256, gBK>() > 4 * kFusedQH * HD * 4
              ? gNS * big_stage_bytes<256, gBK>() : 4 * kFusedQH * HD * 4;
 }
+// LDS of the fused attention: the operand ring, queries, scores, tile max and
+// sum, then the block's rotary tables (32 offset rows and 8 base rows of HD
+// floats each).
 template <int HD>
 constexpr int fused_lds_bytes() {
-  return fused_ring_bytes<HD>() + kFusedQH * HD * 4 + kFusedQH * 256 * 4 + kFusedQH * 2 * 4;
+  return fused_ring_bytes<HD>() + kFusedQH * HD * 4 + kFusedQH * 256 * 4 + kFusedQH * 2 * 4 +
+         40 * HD * 4;
 }
 
 // One butterfly step over the lanes that differ in bit sh: N values become
@@ -911,8 +915,39 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
       qs[ql * HD + e + HD / 2] = (b * cs + a * sn) * scale;
     }
   }
+  // The block's rotary tables in LDS, for angle addition: the angle of
+  // position r0 + 32k + l is that of r0 + 32k (base row k < 8) plus that of l
+  // (offset row l < 32, the same for every block).  Direct-to-LDS loads,
+  // issued before the K k-loop, whose first wait and barrier cover them.
+  // Offset row l's 16-byte chunk c sits in slot l * CPR + (c ^ (l & 15)), so
+  // the 16 lanes of a read group (16 rows at one chunk) hit distinct bank
+  // slots; a base row is read by a whole half-wave at one address.  Rows past
+  // the table (only rows past the sequence, whose scores are masked) take its
+  // last row.
+  static_assert(MBW == 2, "two 32-row blocks per wave");
+  constexpr int CPR = HD / 4;  // 16-byte chunks per table row (HD / 2 (cos, sin) pairs)
+  uint8_t* rope_l = reinterpret_cast<uint8_t*>(ml + QH * 2);
+  {
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.rope, (uint64_t)p.max_pos * HD * 4);
+    constexpr int NI = 40 * CPR / 64;  // load instructions: 10 (HD 64), 20 (HD 128)
+    for (int inst = wave; inst < NI; inst += 8) {
+      const int slot = inst * 64 + lane;
+      int row, c;
+      if (slot < 32 * CPR) {
+        row = slot / CPR;
+        c = (slot % CPR) ^ (row & 15);
+      } else {
+        row = r0 + 32 * ((slot - 32 * CPR) / CPR);
+        c = slot % CPR;
+      }
+      row = min(row, (int)p.max_pos - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rt, (__attribute__((address_space(3))) void*)(rope_l + inst * 1024), 16,
+          (row * HD + c * 4) * 4, 0, 0, 0);
+    }
+  }
   f32x16 acc[NBW][MBW];
-  // K = latents . V_k^T (the k-loop's barriers also publish qs)
+  // K = latents . V_k^T (the k-loop's barriers also publish qs and the tables)
   tile_mainloop<BN, gBK, gNS, MBW>(
       acc,
       p.remap ? make_rsrc(p.kl, view_bytes(p.pool_rows, p.rk, p.ldkl))
@@ -923,27 +958,35 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   // rotate each head's column pairs (c, c + HD/2) by the row's position (its
   // index in the sequence), then round to bf16.  acc[i][j] reg v: column
   // wn + 32i + 8(v/4) + 4(lane/32) + v%4, row wm + 32j + lane%32.
+  // (cos, sin) of row wm + 32j + l from the tables: base row wm / 32 + j
+  // rotated by offset row l = lane % 32.
   constexpr int hb = HD / 64;
+  const int l = lane & 31;
+  const uint8_t* ro = rope_l + l * CPR * 16;
+  const uint8_t* rb = rope_l + (32 + wm / 32) * CPR * 16;
 #pragma unroll
-  for (int j = 0; j < MBW; ++j) {
-    int rp = r0 + wm + 32 * j + (lane & 31);
-    rp = rp >= p.max_pos ? (int)p.max_pos - 1 : rp;
-    const float* tr = p.rope + (int64_t)rp * HD;
+  for (int ib = 0; ib < NBW; ++ib) {
+    if ((32 * ib) % HD >= HD / 2) continue;
 #pragma unroll
-    for (int ib = 0; ib < NBW; ++ib) {
-      if ((32 * ib) % HD >= HD / 2) continue;
+    for (int qq = 0; qq < 4; ++qq) {
+      const int c0 = ((32 * ib) % HD + 8 * qq + 4 * (lane >> 5)) / 2;  // frequencies 2 c0 ..
+      const f32x4 o01 = *reinterpret_cast<const f32x4*>(ro + ((c0 ^ (l & 15)) << 4));
+      const f32x4 o23 = *reinterpret_cast<const f32x4*>(ro + (((c0 + 1) ^ (l & 15)) << 4));
+      const float oc[4] = {o01.x, o01.z, o23.x, o23.z};
+      const float os[4] = {o01.y, o01.w, o23.y, o23.w};
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int fi = (32 * ib) % HD + 8 * qq + 4 * (lane >> 5);  // 4 frequencies from fi
-        const f32x4 cs01 = *reinterpret_cast<const f32x4*>(tr + 2 * fi);
-        const f32x4 cs23 = *reinterpret_cast<const f32x4*>(tr + 2 * fi + 4);
-        const float c[4] = {cs01.x, cs01.z, cs23.x, cs23.z};
-        const float sn[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+      for (int j = 0; j < MBW; ++j) {
+        const f32x4 b01 = *reinterpret_cast<const f32x4*>(rb + ((j * CPR + c0) << 4));
+        const f32x4 b23 = *reinterpret_cast<const f32x4*>(rb + ((j * CPR + c0 + 1) << 4));
+        const float bc[4] = {b01.x, b01.z, b23.x, b23.z};
+        const float bs[4] = {b01.y, b01.w, b23.y, b23.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          const float c = fmaf(bc[e], oc[e], -bs[e] * os[e]);
+          const float sn = fmaf(bs[e], oc[e], bc[e] * os[e]);
           const float a0 = acc[ib][j][4 * qq + e], b0 = acc[ib + hb][j][4 * qq + e];
-          acc[ib][j][4 * qq + e] = a0 * c[e] - b0 * sn[e];
-          acc[ib + hb][j][4 * qq + e] = b0 * c[e] + a0 * sn[e];
+          acc[ib][j][4 * qq + e] = a0 * c - b0 * sn;
+          acc[ib + hb][j][4 * qq + e] = b0 * c + a0 * sn;
         }
       }
     }
