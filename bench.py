@@ -531,9 +531,10 @@ def decode_step(torch, lr, dev, stream, n_layers, reps, fused=False):
     """The 32-layer decode step of a LLaMA-7B-shaped decoder decomposed at
     ratio 0.2 (64 sequences, cached lengths uniform in [128, 4096]) captured
     once in a HIP graph and replayed; preparation stage timed separately.
-    fused: lowrank_layer_decode_step_fused (the reconstruction expanded per
-    256-row block inside the attention from the latents read in place; no
-    reconstructed K/V and no compact latent copy in memory)."""
+    fused: lowrank_layer_decode_step_fused (K expanded per 256-row block
+    inside the attention from the latents read in place, V applied after the
+    softmax-weighted sum of its latents; no reconstructed K/V and no compact
+    latent copy in memory)."""
     from synth.decode_step import DecodeStepInputs
     si = DecodeStepInputs(n_layers=n_layers, device=dev)
     c = si.cfg
@@ -592,8 +593,13 @@ def decode_step(torch, lr, dev, stream, n_layers, reps, fused=False):
     # the fused step reads the latents in place through the remap list (no
     # compact copy); the unfused one copies them first (read + write)
     gather_bytes = 0 if fused else 2 * nvr * (rk + rv) * 2
-    recon_flops = 2.0 * nvr * (rk + rv) * dkv
-    # fused: the reconstructed rows stay on chip (latents read once)
+    # unfused: K and V reconstructed; fused: K expanded on chip, V never formed
+    # (the p-weighted sum of V latent rows per block and head, then V_v once
+    # per sequence and head in the combine)
+    H, hd = c["n_heads"], c["head_dim"]
+    recon_flops = (2.0 * nvr * rk * dkv + 2.0 * nvr * rv * H + 2.0 * B * H * rv * hd
+                   if fused else 2.0 * nvr * (rk + rv) * dkv)
+    # fused: the latents read once (nothing reconstructed reaches HBM)
     recon_bytes = nvr * (rk + rv) * 2 + (0 if fused else 2 * nvr * dkv * 2)
     attn_bytes = 0 if fused else 2 * nvr * dkv * 2
     roof_s = (lin_bytes / HBM_PEAK + gather_bytes / HBM_PEAK

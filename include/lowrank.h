@@ -403,14 +403,18 @@ size_t lowrank_decode_step_fused_workspace_bytes(const lr_layer_weights* w,
 /*
  * lowrank_layer_decode_step_fused -- the layer of lowrank_layer_decode_step
  * with the reconstruction folded into the attention: per 256-row block of a
- * sequence's compact latents and 256 K/V columns, one workgroup expands K =
- * RoPE(buf_k V_k) and V = buf_v V_v on chip (both rounded to bf16, as the
- * reconstruction stores them), scores the block against the sequence's query
- * heads and writes the block's softmax partials, which a second kernel
- * combines per head.  The reconstructed rows (2 * cap * n_kv_heads *
- * head_dim bf16 in lowrank_layer_decode_step) never reach memory.  The
- * result equals lowrank_layer_decode_step's up to the order of the fp32
- * sums.  Same arguments, ownership and graph rules.
+ * sequence's latents (read in place through the remap list) and 256 K
+ * columns, one workgroup expands K = RoPE(buf_k V_k) on chip (rounded to
+ * bf16, as the reconstruction stores it), scores the block against the
+ * sequence's query heads, and writes the block's softmax max and sum and its
+ * p-weighted sum of V latent rows (r_v wide).  A second kernel combines a
+ * sequence's blocks per head and applies V_v once: by associativity
+ * sum_rows p (buf_v V_v) = (sum_rows p buf_v) V_v, so V is never formed.
+ * The reconstructed rows (2 * cap * n_kv_heads * head_dim bf16 in
+ * lowrank_layer_decode_step) never reach memory.  The result equals
+ * lowrank_layer_decode_step's up to the order of the fp32 sums and the bf16
+ * rounding of the reconstructed V (relative differences ~1e-3).  Same
+ * arguments, ownership and graph rules.
  * Errors: as lowrank_layer_decode_step, plus LR_ERR_UNSUPPORTED when
  * (256 / head_dim) * (n_heads / n_kv_heads) > 16 (query heads per 256
  * K/V columns).

@@ -578,26 +578,56 @@ __global__ void row_blocks_kernel(const int32_t* __restrict__ seq_off, int S, in
   blk_off[S] = nb;
 }
 
-// o[i, h] from the block partials of sequence i: o = sum_b e^(m_b - M) o_b /
-// sum_b e^(m_b - M) l_b.  Blocks past nbpad (only from corrupt offsets) are
-// skipped.
+// o[i, h] from the block partials of sequence i, each (m_b, l_b, w_b) with w_b
+// the block's p-weighted sum of V latent rows (r_v wide):
+//   o = (sum_b e^(m_b - M) w_b) V_v^T / sum_b e^(m_b - M) l_b
+// over the rows of kv head h / (H / Hkv) of V_v^T.  Thread t takes output
+// column t / 4 and every fourth 8-wide step of r_v (t % 4), summed by two
+// shuffles.  Blocks past nbpad (only from corrupt offsets) are skipped.
 template <int HD>
-__global__ __launch_bounds__(HD) void fused_combine_kernel(const float* __restrict__ part, int H,
-                                                           const int32_t* __restrict__ blk_off,
-                                                           int nbpad, uint16_t* __restrict__ o,
-                                                           int64_t ldo) {
-  const int h = blockIdx.x, i = blockIdx.y;
+__global__ __launch_bounds__(4 * HD) void fused_combine_kernel(
+    const float* __restrict__ part, int H, int Hkv, int rv, const int32_t* __restrict__ blk_off,
+    int nbpad, const uint16_t* __restrict__ vt, int64_t ldv, uint16_t* __restrict__ o,
+    int64_t ldo) {
+  extern __shared__ float vec[];  // [rv]
+  const int h = blockIdx.x, i = blockIdx.y, kvh = h / (H / Hkv);
   const int b0 = max(0, blk_off[i]), b1 = min(nbpad, blk_off[i + 1]);
+  const int64_t pw = rv + 2;
   float M = -INFINITY;
-  for (int b = b0; b < b1; ++b) M = fmaxf(M, part[((int64_t)b * H + h) * (HD + 2)]);
-  float L = 0.f, acc = 0.f;
+  for (int b = b0; b < b1; ++b) M = fmaxf(M, part[((int64_t)b * H + h) * pw]);
+  float L = 0.f;
   for (int b = b0; b < b1; ++b) {
-    const float* pb = part + ((int64_t)b * H + h) * (HD + 2);
-    const float w = expf(pb[0] - M);
-    L = fmaf(w, pb[1], L);
-    acc = fmaf(w, pb[2 + threadIdx.x], acc);
+    const float* pb = part + ((int64_t)b * H + h) * pw;
+    L = fmaf(expf(pb[0] - M), pb[1], L);
   }
-  o[(int64_t)i * ldo + h * HD + threadIdx.x] = (uint16_t)f2bf(b1 > b0 ? acc / L : 0.f);
+  for (int n = threadIdx.x; n < rv; n += blockDim.x) {
+    float acc = 0.f;
+    for (int b = b0; b < b1; ++b) {
+      const float* pb = part + ((int64_t)b * H + h) * pw;
+      acc = fmaf(expf(pb[0] - M), pb[2 + n], acc);
+    }
+    vec[n] = acc;
+  }
+  __syncthreads();
+  const int c = threadIdx.x >> 2, qtr = threadIdx.x & 3;
+  const uint16_t* row = vt + (int64_t)(kvh * HD + c) * ldv;
+  float acc = 0.f;
+  for (int n = qtr * 8; n < rv; n += 32) {
+    if (n + 8 <= rv) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(row + n);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(vec[n + 2 * e], bf2f(ww[e] & 0xffffu), acc);
+        acc = fmaf(vec[n + 2 * e + 1], bf2f(ww[e] >> 16), acc);
+      }
+    } else {
+      for (int e = n; e < rv; ++e) acc = fmaf(vec[e], bf2f(row[e]), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  if (qtr == 0) o[(int64_t)i * ldo + h * HD + c] = (uint16_t)f2bf(b1 > b0 ? acc / L : 0.f);
 }
 
 // ---------------------------------------------------------------- workspace
@@ -680,7 +710,7 @@ StepLayout step_layout(const lr_layer_weights* w, const StepIn& s, bool fused = 
   L.nbpad = (s.cap + 255) / 256 + s.S;
   L.krec = fused ? 0 : take(s.cap * L.dkv * 2);
   L.vrec = fused ? 0 : take(s.cap * L.dkv * 2);
-  L.part = fused ? take(L.nbpad * w->n_heads * (w->head_dim + 2) * 4)
+  L.part = fused ? take(L.nbpad * w->n_heads * (w->r[2] + 2) * 4)
                  : take(T * w->n_heads * L.nch * (w->head_dim + 2) * 4);
   L.o = take(T * dq * 2);
   L.gate = take(T * w->d_ffn * 2);
@@ -868,12 +898,16 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
     fa.nbpad = (int)L.nbpad;
     fa.part = fpart;
     LR_CHECK(attn_fused_decode(fa, (int)w->head_dim, st));
+    const size_t vec_lds = (size_t)w->r[2] * 4;
+    const uint16_t* vv = static_cast<const uint16_t*>(w->Vt[2]);
     if (w->head_dim == 128)
       hipLaunchKernelGGL(fused_combine_kernel<128>, dim3((unsigned)w->n_heads, (unsigned)S),
-                         dim3(128), 0, st, fpart, (int)w->n_heads, blk_off, (int)L.nbpad, o, dq);
+                         dim3(512), vec_lds, st, fpart, (int)w->n_heads, (int)w->n_kv_heads,
+                         (int)w->r[2], blk_off, (int)L.nbpad, vv, w->ldv[2], o, dq);
     else
       hipLaunchKernelGGL(fused_combine_kernel<64>, dim3((unsigned)w->n_heads, (unsigned)S),
-                         dim3(64), 0, st, fpart, (int)w->n_heads, blk_off, (int)L.nbpad, o, dq);
+                         dim3(256), vec_lds, st, fpart, (int)w->n_heads, (int)w->n_kv_heads,
+                         (int)w->r[2], blk_off, (int)L.nbpad, vv, w->ldv[2], o, dq);
   } else {
     // rec[j, :] = buf[j, 0:r] . Vt^T for the live rows j < *n_valid: the
     // fixed-size GEMM of the replay stage (grid from the capacity), K rows

@@ -710,14 +710,15 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------- fused decode attention
 // Decode attention with the reconstruction on chip: one workgroup takes a
-// 256-row block of one sequence's cached rows and the 256 K/V columns of
-// 256/HD kv heads.  It expands the block's K latents into K (the large-tile
-// k-loop over r_k), rotates and rounds them to bf16 as the reconstruction
-// would store them, and scores them against the sequence's query heads of
-// those kv heads.  Then it forms the tile's softmax partials (max m, sum l),
-// expands the V latents the same way (bf16), and sums o = sum_rows p V per
-// query head in registers (a butterfly across the row lanes), writing it
-// with m and l: the combine over a sequence's blocks follows.  The reconstructed rows never reach HBM.
+// 256-row block of one sequence's cached rows and the 256 K columns of 256/HD
+// kv heads.  It expands the block's K latents into K (the large-tile k-loop
+// over r_k), rotates and rounds them to bf16 as the reconstruction would
+// store them, and scores them against the sequence's query heads of those kv
+// heads.  Then it forms the block's softmax partials (max m, sum l) and, per
+// query head, the p-weighted sum of the block's V latent rows, which it
+// writes with m and l: the combine over a sequence's blocks follows and
+// applies V_v there (sum_rows p (l V_v) = (sum_rows p l) V_v), so V is
+// never formed and the reconstructed rows never reach HBM.
 // Blocks come from blk_off (blk_off[i] = first block of sequence i).  With
 // a multiple of 8 column tiles each XCD keeps its share of them for every
 // block, so the two up-projection tiles it reads stay in its L2 (both
@@ -822,7 +823,7 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
   lds_barrier();  // operand tiles dead
 }
 
-// LDS: the operand ring (reused for the row waves' output sums), then the
+// LDS: the operand ring (reused for the row waves' latent sums), then the
 // queries, scores and tile (max, sum) pairs.
 template <int HD>
 constexpr int fused_ring_bytes() {
@@ -836,20 +837,6 @@ template <int HD>
 constexpr int fused_lds_bytes() {
   return fused_ring_bytes<HD>() + kFusedQH * HD * 4 + kFusedQH * 256 * 4 + kFusedQH * 2 * 4 +
          40 * HD * 4;
-}
-
-// One butterfly step over the lanes that differ in bit sh: N values become
-// N / 2, the upper half kept where that lane bit is set, the lower half
-// elsewhere, each plus the partner's copy of the same half.
-template <int N>
-__device__ __forceinline__ void bfly_step(float* val, int lane, int sh) {
-  const bool up = (lane & sh) != 0;
-#pragma unroll
-  for (int k = 0; k < N / 2; ++k) {
-    const float keep = up ? val[k + N / 2] : val[k];
-    const float send = up ? val[k] : val[k + N / 2];
-    val[k] = keep + __shfl_xor(send, sh);
-  }
 }
 
 template <int HD>
@@ -1051,87 +1038,117 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
       ml[2 * qh + 1] = sum;
     }
   }
-  // V = latents . V_v^T (its first barrier publishes p, m, l)
-  tile_mainloop<BN, gBK, gNS, MBW>(
-      acc,
-      p.remap ? make_rsrc(p.vl, view_bytes(p.pool_rows, p.rv, p.ldvl))
-              : make_rsrc(p.vl + (int64_t)m0 * p.ldvl, view_bytes(nrows, p.rv, p.ldvl)),
-      p.ldvl,
-      make_rsrc(p.vv + (int64_t)n0 * p.ldvv, view_bytes(min(dkv - n0, BN), p.rv, p.ldvv)),
-      p.ldvv, p.rv, smem, wave, lane, prow);
-  // o[qh][c] = sum_rows p[qh][row] V[row][c] from the registers: a lane
-  // weights its two rows' bf16 values of the head's columns by p and sums
-  // them, then a butterfly over the 32 row lanes (each step keeps half the
-  // columns and adds the partner's half) leaves every lane with two
-  // columns' sums; the four row waves meet in LDS.
-  constexpr int NV = HD / 2;  // a lane's values of one head (two rows summed)
-  float* red = reinterpret_cast<float*>(smem);  // [4][QH][HD], the ring is dead
-  const int rw = wave >> 1;
-  uint32_t vpk[NBW][MBW][8];  // V rounded to bf16, register pairs packed
-#pragma unroll
-  for (int ib = 0; ib < NBW; ++ib)
-#pragma unroll
-    for (int j = 0; j < MBW; ++j)
-#pragma unroll
-      for (int v2 = 0; v2 < 8; ++v2)
-        vpk[ib][j][v2] = pack_bf2(acc[ib][j][2 * v2], acc[ib][j][2 * v2 + 1]);
-#pragma unroll
-  for (int hk = 0; hk < 128 / HD; ++hk) {
-    const int kvl = (wn + hk * HD) / HD;
-    if (kvl >= nkv) continue;
-    for (int g = 0; g < grp; ++g) {
-      const int ql = kvl * grp + g;
-      const float p0 = ps[ql * 256 + wm + (lane & 31)], p1 = ps[ql * 256 + wm + 32 + (lane & 31)];
-      // value k: p0 V[row 0][column k] + p1 V[row 1][column k]; the first
-      // butterfly step (lane bit 16) is taken as the values are formed
-      auto pv = [&](int k) {
-        const int ib = hk * (HD / 32) + k / 16, v = k % 16, sh = 16 * (v & 1);
-        return p0 * bf2f((vpk[ib][0][v >> 1] >> sh) & 0xffffu) +
-               p1 * bf2f((vpk[ib][1][v >> 1] >> sh) & 0xffffu);
-      };
-      float val[NV / 2];
-      const bool up16 = (lane & 16) != 0;
-#pragma unroll
-      for (int k = 0; k < NV / 2; ++k) {
-        const float a = pv(k), b = pv(k + NV / 2);
-        val[k] = (up16 ? b : a) + __shfl_xor(up16 ? a : b, 16);
-      }
-      bfly_step<NV / 2>(val, lane, 8);
-      bfly_step<NV / 4>(val, lane, 4);
-      bfly_step<NV / 8>(val, lane, 2);
-      if (NV == 64) {
-        bfly_step<4>(val, lane, 1);
-      } else {  // the xor-1 lanes hold the same two columns: add them
-        val[0] += __shfl_xor(val[0], 1);
-        val[1] += __shfl_xor(val[1], 1);
-      }
-      // the lane's two columns: index k = 32 b4 + 16 b3 + 8 b2 + 4 b1 + 2 b0 + e
-      // (b: lane bits; for NV == 32 without b0) -> (block k / 16, register k % 16)
-      if (NV == 64 || (lane & 1) == 0) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int kk = NV == 64 ? (((lane >> 4) & 1) * 32 + ((lane >> 3) & 1) * 16 +
-                                     ((lane >> 2) & 1) * 8 + ((lane >> 1) & 1) * 4 +
-                                     (lane & 1) * 2 + e)
-                                  : (((lane >> 4) & 1) * 16 + ((lane >> 3) & 1) * 8 +
-                                     ((lane >> 2) & 1) * 4 + ((lane >> 1) & 1) * 2 + e);
-          const int v = kk % 16;
-          const int c = 32 * (kk / 16) + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);  // in the head
-          red[(rw * QH + ql) * HD + c] = val[e];
-        }
+  // V is never formed.  sum_rows p[q][row] (l_row V_v^T) = (sum_rows p[q][row]
+  // l_row) V_v^T, so the block's partial for query head q is the p-weighted sum
+  // of its V latent rows (r_v wide), and the combine applies V_v once per
+  // sequence and head.  Wave w takes rows 32w .. 32w + 31, lane c the latent
+  // columns 8c .. 8c + 7 of a 512-column block; heads go four at a time, and
+  // the eight waves' sums meet in the ring (dead since the K k-loop).
+  __syncthreads();  // p, m and l published
+  {
+    const __amdgpu_buffer_rsrc_t rl =
+        p.remap ? make_rsrc(p.vl, view_bytes(p.pool_rows, p.rv, p.ldvl))
+                : make_rsrc(p.vl + (int64_t)m0 * p.ldvl, view_bytes(nrows, p.rv, p.ldvl));
+    float* red = reinterpret_cast<float*>(smem);  // [8 waves][4 heads][512 columns]
+    const int pw = p.rv + 2;
+    const int rlo = wave * 32;
+    // source row of row rlo + lane (lanes < 32): a pool row through the remap
+    // list (-1: none), or the row of the compact copy
+    int src = -1;
+    if (lane < 32 && rlo + lane < nrows) {
+      src = rlo + lane;
+      if (p.remap) {
+        const int pr = p.remap[m0 + rlo + lane];
+        src = pr >= 0 && pr < p.pool_rows ? pr : -1;
       }
     }
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < nq * HD; t += blockDim.x) {
-    const int ql = t / HD, c = t % HD, h = kv0 * grp + ql;
-    const float o = red[(0 * QH + ql) * HD + c] + red[(1 * QH + ql) * HD + c] +
-                    red[(2 * QH + ql) * HD + c] + red[(3 * QH + ql) * HD + c];
-    float* out = p.part + ((int64_t)gb * p.H + h) * (HD + 2);
-    out[2 + c] = o;
-    if (c == 0) {
-      out[0] = ml[2 * ql];
-      out[1] = ml[2 * ql + 1];
+    for (int cb = 0; cb < p.rv; cb += 512) {
+      const int col = cb + lane * 8;
+      // row r of the wave's 32 (zero past the block, past r_v, or when missing)
+      auto load_row = [&](int r) {
+        const int sr = __builtin_amdgcn_readlane(src, r);
+        const uint32_t off = sr >= 0 && col < p.rv
+                                 ? (uint32_t)(((int64_t)sr * p.ldvl + col) * 2)
+                                 : 0x80000000u;  // past the buffer: reads zero
+        return mask_tail_nb(bload(rl, off), col, p.rv);
+      };
+      for (int q0 = 0; q0 < nq; q0 += 4) {
+        float a[4][8];
+#pragma unroll
+        for (int qi = 0; qi < 4; ++qi)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[qi][e] = 0.f;
+        // 8 rows at a time, the next 8 in flight while these are summed
+        u32x4 cur[8], nxt[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cur[u] = load_row(u);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b < 3) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) nxt[u] = load_row(8 * (b + 1) + u);
+          }
+          // p of these 8 rows for the (up to) four heads
+          float pv[4][8];
+#pragma unroll
+          for (int qi = 0; qi < 4; ++qi) {
+            const float* pr = ps + min(q0 + qi, nq - 1) * 256 + rlo + 8 * b;
+            const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr);
+            const f32x4 p1 = *reinterpret_cast<const f32x4*>(pr + 4);
+            const bool on = q0 + qi < nq;
+            pv[qi][0] = on ? p0.x : 0.f;
+            pv[qi][1] = on ? p0.y : 0.f;
+            pv[qi][2] = on ? p0.z : 0.f;
+            pv[qi][3] = on ? p0.w : 0.f;
+            pv[qi][4] = on ? p1.x : 0.f;
+            pv[qi][5] = on ? p1.y : 0.f;
+            pv[qi][6] = on ? p1.z : 0.f;
+            pv[qi][7] = on ? p1.w : 0.f;
+          }
+          // one row at a time: its 8 values widened once, used by every head
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t ww[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              f[2 * e] = bf2f(ww[e] & 0xffffu);
+              f[2 * e + 1] = bf2f(ww[e] >> 16);
+            }
+#pragma unroll
+            for (int qi = 0; qi < 4; ++qi)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) a[qi][e] = fmaf(pv[qi][u], f[e], a[qi][e]);
+          }
+          if (b < 3) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+          }
+        }
+#pragma unroll
+        for (int qi = 0; qi < 4; ++qi) {
+          float* rr = red + (wave * 4 + qi) * 512 + lane * 8;
+          *reinterpret_cast<f32x4*>(rr) = f32x4{a[qi][0], a[qi][1], a[qi][2], a[qi][3]};
+          *reinterpret_cast<f32x4*>(rr + 4) = f32x4{a[qi][4], a[qi][5], a[qi][6], a[qi][7]};
+        }
+        __syncthreads();
+        for (int t = threadIdx.x; t < 4 * 512; t += blockDim.x) {
+          const int qi = t / 512, c = t % 512;
+          if (q0 + qi < nq && cb + c < p.rv) {
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) sum += red[(w * 4 + qi) * 512 + c];
+            const int h = kv0 * grp + q0 + qi;
+            p.part[((int64_t)gb * p.H + h) * pw + 2 + cb + c] = sum;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int t = threadIdx.x; t < nq; t += blockDim.x) {
+      float* out = p.part + ((int64_t)gb * p.H + kv0 * grp + t) * pw;
+      out[0] = ml[2 * t];
+      out[1] = ml[2 * t + 1];
     }
   }
 }
