@@ -1012,6 +1012,38 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
       }
     }
   }
+  // V is never formed.  sum_rows p[q][row] (l_row V_v^T) = (sum_rows p[q][row]
+  // l_row) V_v^T, so the block's partial for query head q is the p-weighted sum
+  // of its V latent rows (r_v wide), and the combine applies V_v once per
+  // sequence and head.  Wave w takes rows 32w .. 32w + 31, lane c the latent
+  // columns 8c .. 8c + 7 of a 512-column block; heads go four at a time, and
+  // the eight waves' sums meet in the ring (dead since the K k-loop).  The
+  // first 8 rows are loaded before the softmax, so they arrive while it runs.
+  const __amdgpu_buffer_rsrc_t rl =
+      p.remap ? make_rsrc(p.vl, view_bytes(p.pool_rows, p.rv, p.ldvl))
+              : make_rsrc(p.vl + (int64_t)m0 * p.ldvl, view_bytes(nrows, p.rv, p.ldvl));
+  const int rlo = wave * 32;
+  // source row of row rlo + lane (lanes < 32): a pool row through the remap
+  // list (-1: none), or the row of the compact copy
+  int src = -1;
+  if (lane < 32 && rlo + lane < nrows) {
+    src = rlo + lane;
+    if (p.remap) {
+      const int pr = p.remap[m0 + rlo + lane];
+      src = pr >= 0 && pr < p.pool_rows ? pr : -1;
+    }
+  }
+  // row r of the wave's 32 at latent column col (zero past the block, past
+  // r_v, or when missing)
+  auto load_row = [&](int col, int r) {
+    const int sr = __builtin_amdgcn_readlane(src, r);
+    const uint32_t off = sr >= 0 && col < p.rv ? (uint32_t)(((int64_t)sr * p.ldvl + col) * 2)
+                                               : 0x80000000u;  // past the buffer: reads zero
+    return mask_tail_nb(bload(rl, off), col, p.rv);
+  };
+  u32x4 cur[8], nxt[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) cur[u] = load_row(lane * 8, u);
   __syncthreads();
   // softmax partials of the tile: wave w takes query heads w, w + 8
   for (int qh = wave; qh < nq; qh += 8) {
@@ -1038,55 +1070,29 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
       ml[2 * qh + 1] = sum;
     }
   }
-  // V is never formed.  sum_rows p[q][row] (l_row V_v^T) = (sum_rows p[q][row]
-  // l_row) V_v^T, so the block's partial for query head q is the p-weighted sum
-  // of its V latent rows (r_v wide), and the combine applies V_v once per
-  // sequence and head.  Wave w takes rows 32w .. 32w + 31, lane c the latent
-  // columns 8c .. 8c + 7 of a 512-column block; heads go four at a time, and
-  // the eight waves' sums meet in the ring (dead since the K k-loop).
   __syncthreads();  // p, m and l published
   {
-    const __amdgpu_buffer_rsrc_t rl =
-        p.remap ? make_rsrc(p.vl, view_bytes(p.pool_rows, p.rv, p.ldvl))
-                : make_rsrc(p.vl + (int64_t)m0 * p.ldvl, view_bytes(nrows, p.rv, p.ldvl));
     float* red = reinterpret_cast<float*>(smem);  // [8 waves][4 heads][512 columns]
     const int pw = p.rv + 2;
-    const int rlo = wave * 32;
-    // source row of row rlo + lane (lanes < 32): a pool row through the remap
-    // list (-1: none), or the row of the compact copy
-    int src = -1;
-    if (lane < 32 && rlo + lane < nrows) {
-      src = rlo + lane;
-      if (p.remap) {
-        const int pr = p.remap[m0 + rlo + lane];
-        src = pr >= 0 && pr < p.pool_rows ? pr : -1;
-      }
-    }
     for (int cb = 0; cb < p.rv; cb += 512) {
       const int col = cb + lane * 8;
-      // row r of the wave's 32 (zero past the block, past r_v, or when missing)
-      auto load_row = [&](int r) {
-        const int sr = __builtin_amdgcn_readlane(src, r);
-        const uint32_t off = sr >= 0 && col < p.rv
-                                 ? (uint32_t)(((int64_t)sr * p.ldvl + col) * 2)
-                                 : 0x80000000u;  // past the buffer: reads zero
-        return mask_tail_nb(bload(rl, off), col, p.rv);
-      };
       for (int q0 = 0; q0 < nq; q0 += 4) {
         float a[4][8];
 #pragma unroll
         for (int qi = 0; qi < 4; ++qi)
 #pragma unroll
           for (int e = 0; e < 8; ++e) a[qi][e] = 0.f;
-        // 8 rows at a time, the next 8 in flight while these are summed
-        u32x4 cur[8], nxt[8];
+        // 8 rows at a time, the next 8 in flight while these are summed (the
+        // first pass's first 8 are already in flight)
+        if (cb > 0 || q0 > 0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) cur[u] = load_row(u);
+          for (int u = 0; u < 8; ++u) cur[u] = load_row(col, u);
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           if (b < 3) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) nxt[u] = load_row(8 * (b + 1) + u);
+            for (int u = 0; u < 8; ++u) nxt[u] = load_row(col, 8 * (b + 1) + u);
           }
           // p of these 8 rows for the (up to) four heads
           float pv[4][8];
