@@ -69,9 +69,9 @@ def test_group_mixed_members(T):
 
 @pytest.mark.parametrize("T", [40, 64])
 def test_group_tall_stage2_tiles(T):
-    # three members of 65 stage-2 tiles at 64 rows (the last one ragged) are
-    # enough for the group to take 64-row tiles at T > 32; member 1
-    # accumulates into an fp32 residual.  Outputs start as NaN.
+    # three members with a ragged last stage-2 tile (4100 output rows) at
+    # more than 32 tokens; member 1 accumulates into an fp32 residual.
+    # Outputs start as NaN.
     cs = _cases(T, 8200 + T, [(512, 100, 4100), (512, 60, 4100), (512, 130, 4100)])
     x = cs[0]["dx"]
     d = dev()
@@ -89,8 +89,8 @@ def test_group_tall_stage2_tiles(T):
     for c, y, s in zip((cs[0], cs[2]), (y0, y2), sep):
         yr = oracle.linear(xv, c["U"], c["V"])[1]
         assert maxrel(to_f64(y), yr) <= BF16_TOL
-        # 64- and 32-row stage-2 tiles split k over the waves alike and sum
-        # the waves in one fixed order: grouped equals separate bit for bit
+        # stage-2 tiles split k over the waves alike and sum the waves in one
+        # fixed order: grouped equals separate bit for bit
         assert np.array_equal(bits(y), bits(s))
     added = to_f64(acc) - acc0.double().numpy()
     assert maxrel(added, oracle.linear(xv, cs[1]["U"], cs[1]["V"])[1]) <= BF16_TOL
