@@ -11,7 +11,9 @@
 // fragment reads (32 rows at one chunk) spread over the banks.  The MFMA
 // takes the B fragment as its first operand, so each lane ends with 4
 // consecutive output columns of one row; bf16 results are staged through LDS
-// and written as whole 128-byte lines.  Tiles are listed four row tiles at a
+// and written as whole 128-byte lines, with non-temporal stores (the output
+// is not read again by this launch, and streaming it past the L2 leaves the
+// operands' lines there).  Tiles are listed four row tiles at a
 // time and go to the 8 XCDs in contiguous runs of that list (workgroups are
 // dealt to XCDs round robin), so the tiles an XCD runs at once share A and B
 // rows in its L2.  Rows past M or N and k-chunks past K read zero from
@@ -193,7 +195,7 @@ __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], 
       if (m >= M) continue;
       uint16_t* c = C + (int64_t)m * ldc + n;
       if (n + 7 < N) {
-        *reinterpret_cast<u32x4*>(c) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(c));
       } else {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         for (int e = 0; e < 8 && n + e < N; ++e) c[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
@@ -227,7 +229,7 @@ __device__ __forceinline__ void store_staged(const f32x16 (&acc)[BN / 64][MBW], 
     if (m >= M) continue;
     uint16_t* c = C + (int64_t)m * ldc + n;
     if (n + 7 < N) {
-      *reinterpret_cast<u32x4*>(c) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(c));
     } else {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       for (int e = 0; e < 8 && n + e < N; ++e) c[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
@@ -263,7 +265,7 @@ __device__ __forceinline__ void store_block(const f32x16 (&acc)[BN / 64][MBW], i
     if (m >= M) continue;
     uint16_t* c = C + (int64_t)m * ldc + n;
     if (n + 7 < N) {
-      *reinterpret_cast<u32x4*>(c) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(c));
     } else {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       for (int e = 0; e < 8 && n + e < N; ++e) c[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
