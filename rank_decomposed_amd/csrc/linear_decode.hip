@@ -66,6 +66,9 @@ constexpr int kNW = 8;                      // waves per workgroup
 constexpr int kThreads = 64 * kNW;
 constexpr uint32_t kOutside = 0x80000000u;  // past every buffer (tiles stay < 2 GiB)
 constexpr int kCoherentLoad = 16;           // buffer-load cache policy: device scope
+constexpr int kStreamLoad = 2;              // buffer-load cache policy: non-temporal
+                                            // (weights, streamed once per call, should
+                                            // not evict the activations and t)
 constexpr int kMaxGroup = 8;                // linears per launch
 constexpr int kRedBudget = 79 * 1024;       // LDS for parked partials: two workgroups per CU
 constexpr int kStage1Tiles = 256;           // stage-1 tiles a launch aims at (one per CU)
@@ -187,14 +190,15 @@ __device__ __forceinline__ bool count_arrival(uint32_t* ctl, int sub_base, int t
 // NB fragments of one k-step at byte offset step_off from the per-lane bases
 // off[]; a dead step goes to an offset outside the buffer (reads zero, no
 // memory access).
-template <int NB>
+// POL: the loads' cache policy (kStreamLoad for weights, read once per call).
+template <int NB, int POL = 0>
 __device__ __forceinline__ void frag_load_at(u32x4 (&f)[NB], __amdgpu_buffer_rsrc_t rs,
                                              const uint32_t (&off)[NB], uint32_t step_off,
                                              bool live) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int o = (int)(live ? off[nb] + step_off : kOutside);
-    f[nb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
+    f[nb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, POL));
   }
 }
 
@@ -355,7 +359,7 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
     u32x4 bp[PF][RB];
 #pragma unroll
     for (int i = 0; i < PF; ++i)
-      frag_load_at<RB>(bp[i], w.rs, w.off, (s_lo + i) * w.step, s_lo + i < s_full);
+      frag_load_at<RB, kStreamLoad>(bp[i], w.rs, w.off, (s_lo + i) * w.step, s_lo + i < s_full);
     if (wait) wait_go(ctl, spin_limit);
 #pragma unroll
     for (int i0 = 0; i0 < PF; i0 += KSW) round(bp + i0, s_lo + i0);
@@ -365,14 +369,14 @@ __device__ void tile_product(f32x4 (&acc)[TB][RB], const uint16_t* __restrict__ 
     u32x4 bv[KSW][RB];
 #pragma unroll
     for (int i = 0; i < KSW; ++i)
-      frag_load_at<RB>(bv[i], w.rs, w.off, (s0 + i) * w.step, s0 + i < s_full);
+      frag_load_at<RB, kStreamLoad>(bv[i], w.rs, w.off, (s0 + i) * w.step, s0 + i < s_full);
     round(bv, s0);
   }
   if (nfull < nsteps && nfull >= s_lo && nfull < s_hi) {
     // ragged last step of the K range, owned by this wave
     const int kk = nfull * 32 + kq;
     u32x4 bv[RB], av[TB], alv[TB];
-    frag_load_at<RB>(bv, w.rs, w.off, nfull * w.step, true);
+    frag_load_at<RB, kStreamLoad>(bv, w.rs, w.off, nfull * w.step, true);
     frag_load_at<TB>(av, ra, aoff, nfull * ASTEP, true);
     if (SPLIT) frag_load_at<TB>(alv, ral, aoff, nfull * ASTEP, true);
 #pragma unroll
@@ -428,7 +432,7 @@ __device__ __forceinline__ void stage1_products(f32x4 (&acc)[TB][RB],
     u32x4 wv[NS][RB];
 #pragma unroll
     for (int i = 0; i < NS; ++i)
-      frag_load_at<RB>(wv[i], w.rs, w.off, (c0 + i) * w.step, c0 + i < s_full);
+      frag_load_at<RB, kStreamLoad>(wv[i], w.rs, w.off, (c0 + i) * w.step, c0 + i < s_full);
     if constexpr (XL) {
       u32x4 ld[NS / 2][2 * TB];
 #pragma unroll
@@ -481,7 +485,7 @@ __device__ __forceinline__ void stage1_products(f32x4 (&acc)[TB][RB],
     // ragged last step of the K range, owned by this wave
     const int kk = nfull * 32 + kq;
     u32x4 bv[RB], av[TB];
-    frag_load_at<RB>(bv, w.rs, w.off, nfull * w.step, true);
+    frag_load_at<RB, kStreamLoad>(bv, w.rs, w.off, nfull * w.step, true);
     frag_load_at<TB>(av, ra, aoff, nfull * 64, true);
 #pragma unroll
     for (int r = 0; r < RB; ++r) bv[r] = mask_tail_nb(bv[r], kk, K);
@@ -825,7 +829,8 @@ struct Stage2 {
     const int j = i - src.dead;  // live step index within the run
     ring[slot][i] = __builtin_bit_cast(
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                   src.rs, (int)(j >= 0 ? src.off + (uint32_t)j * src.step : kOutside), 0, 0));
+                   src.rs, (int)(j >= 0 ? src.off + (uint32_t)j * src.step : kOutside), 0,
+                   kStreamLoad));
   }
 
   __device__ __forceinline__ void issue(const PersArgs& a, int slot, int u) {
