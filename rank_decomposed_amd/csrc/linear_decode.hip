@@ -1134,11 +1134,16 @@ hipError_t launch_one(const DecArgs& a, int grid, hipStream_t st) {
 }
 
 template <int TB>
-hipError_t launch_decode(const DecArgs& a, int grid, hipStream_t st) {
+hipError_t launch_decode(const DecArgs& a, int grid, bool thin, hipStream_t st) {
   // <TB, RB1, RB2, KSW1, KSW2, PF, SPLIT>: PF covers a wave's whole run of
-  // V_r for r up to 8 * 8 * 32 = 2048 (6 * 8 * 32 at 64 tokens)
-  if (TB == 1) return launch_one<1, 1, 2, 8, 4, 8, true>(a, grid, st);
-  if (TB == 2) return launch_one<2, 2, 2, 4, 2, 8, false>(a, grid, st);
+  // V_r for r up to 8 * 8 * 32 = 2048 (6 * 8 * 32 at 64 tokens).  thin:
+  // 16-row stage-2 tiles (launches with few output rows)
+  if (TB == 1)
+    return thin ? launch_one<1, 1, 1, 8, 4, 8, true>(a, grid, st)
+                : launch_one<1, 1, 2, 8, 4, 8, true>(a, grid, st);
+  if (TB == 2)
+    return thin ? launch_one<2, 2, 1, 4, 2, 8, false>(a, grid, st)
+                : launch_one<2, 2, 2, 4, 2, 8, false>(a, grid, st);
   return launch_one<4, 2, 2, 2, 2, 6, false>(a, grid, st);
 }
 
@@ -1385,10 +1390,24 @@ hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
       default: return launch_pers<4>(pa, per, st);
     }
   }
+  // Tiled form: a launch with fewer than kThinTiles 32-row stage-2 tiles
+  // (o alone at 4096 outputs: 128) would leave half the CUs without V_r to
+  // stream, so up to 32 tokens it takes 16-row tiles instead.
+  constexpr int kThinTiles = 192;
+  const bool thin = TB <= 2 && grid - n1 < kThinTiles;
+  if (thin) {
+    grid = n1;
+    for (int i = 0; i < n; ++i) {
+      LinArgs& L = a.lin[i];
+      if (L.n2) L.n2 = (L.d_out + 15) / 16;
+      L.first2 = grid;
+      grid += L.n2;
+    }
+  }
   switch (TB) {
-    case 1: return launch_decode<1>(a, grid, st);
-    case 2: return launch_decode<2>(a, grid, st);
-    default: return launch_decode<4>(a, grid, st);
+    case 1: return launch_decode<1>(a, grid, thin, st);
+    case 2: return launch_decode<2>(a, grid, thin, st);
+    default: return launch_decode<4>(a, grid, false, st);
   }
 }
 
