@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   for (int r = grp; r < kAttnChunk; r += RG) {
     float acc = 0.f;
     if (r < cnt) {
-      const u32x4 w = ldg16(kb + (int64_t)r * ldkv);
+      const u32x4 w = ldg16_stream(kb + (int64_t)r * ldkv);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(
   float ov[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int r = grp; r < cnt; r += RG) {
-    const u32x4 w = ldg16(vb + (int64_t)r * ldkv);
+    const u32x4 w = ldg16_stream(vb + (int64_t)r * ldkv);
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
     const float pr = sc[r];
 #pragma unroll

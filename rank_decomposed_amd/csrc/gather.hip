@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ sr
     char* drow = dst + j * dst_pitch;
     for (int64_t c = lane; c < nvec; c += 64) {
       if (VEC == 16) {
-        u32x4 v = ok ? *reinterpret_cast<const u32x4*>(srow + c * 16) : u32x4{0, 0, 0, 0};
+        u32x4 v = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(srow + c * 16))
+                     : u32x4{0, 0, 0, 0};
         *reinterpret_cast<u32x4*>(drow + c * 16) = v;
       } else if (VEC == 4) {
         uint32_t v = ok ? *reinterpret_cast<const uint32_t*>(srow + c * 4) : 0u;
