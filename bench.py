@@ -288,7 +288,7 @@ def main():
                    "tokens_per_step": tokens_per_step, "layer_sets": len(sets),
                    "factor_layout": args.layout},
         "roofline": {"bound": "hbm",
-                     "kernel": "decode_kernel (%s), %s T=%s" % (
+                     "kernel": "decode linear, one launch (%s), %s T=%s" % (
                          "lowrank_linear_forward_group" if len(dom_roles) > 1
                          else "lowrank_linear_forward",
                          " + ".join("%s %dx%dx%d" % (r, SHAPES[r][0], rank(0.6, *SHAPES[r]),

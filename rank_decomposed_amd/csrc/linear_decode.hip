@@ -1369,18 +1369,14 @@ hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
     grid += a.lin[i].n2;
   }
   if (grid == 0) return hipSuccess;
-  // The persistent form wins where stage 1 streams at least as much as
-  // stage 2 (its U_r share keeps every CU busy up to the hand-over) or, at
-  // more than 32 tokens, where stage 1 is not far below it (t read once per
-  // workgroup instead of once per stage-2 tile); the tiled form elsewhere.
-  // Measured on the 7B decode shapes: down always, q,k,v and o at 64
-  // tokens, neither gate,up nor q,k,v / o at up to 32 tokens.
-  double u_el = 0, v_el = 0;
-  for (int i = 0; i < n; ++i) {
+  // The persistent form wins wherever the launch has stage-1 work (measured
+  // on the 7B decode shapes with weights loaded non-temporally: every class
+  // at 1, 8 and 64 tokens, o at 32, gate,up even at 32; q,k,v at 32 within
+  // 3 %); stage-2-only launches keep the tiled form.
+  double u_el = 0;
+  for (int i = 0; i < n; ++i)
     if (a.lin[i].nb1) u_el += (double)a.lin[i].r * a.lin[i].d_in;
-    if (a.lin[i].n2) v_el += (double)a.lin[i].r * a.lin[i].d_out;
-  }
-  const bool pers_wins = u_el > 1.5 * v_el || (T > 32 && u_el >= 0.6 * v_el);
+  const bool pers_wins = u_el > 0;
   PersArgs pa;
   int per = 0;
   if (pers_wins && plan_persistent(a, TB, &pa, &per)) {
