@@ -744,7 +744,7 @@ void decode_kernel(DecArgs args) {
 // Every workgroup counts its completion once; the last clears every GO.
 constexpr int kMaxWG = 256;
 constexpr int kPersLds = 96 * 1024;  // over half a CU: one workgroup per CU
-constexpr int kPreUnits = 1;         // ring slots in flight across the wait for GO
+constexpr int kPreUnits = 2;         // ring slots in flight across the wait for GO
 
 struct PersArgs {
   LinArgs lin[kMaxGroup];
