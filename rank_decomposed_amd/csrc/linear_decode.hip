@@ -658,6 +658,9 @@ __device__ __forceinline__ void stage1_tile(const LinArgs& p, int T, int t1, flo
     }
   }
   const bool split = TB == 1;
+  // the bf16 operand only for a stage 2 in this launch (a stage-1-only
+  // linear's t leaves as fp32 t_io, which the end of the kernel publishes)
+  const bool pub = p.wait != 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
     const int e = threadIdx.x + i * kThreads;
@@ -666,12 +669,13 @@ __device__ __forceinline__ void stage1_tile(const LinArgs& p, int T, int t1, flo
     const int n = row0 + ro;
     if (e >= NE || tok >= T || n >= p.r) continue;
     if (p.t32) p.t32[(int64_t)tok * p.ldt32 + n] = val[i];
+    if (!pub) continue;
     const uint32_t hi = f2bf(val[i]);
     const int64_t pi = tpack(tok, n, p.ldtb);
     store_coherent(p.thi + pi, (uint16_t)hi);
     if (split) store_coherent(p.tlo + pi, (uint16_t)f2bf(val[i] - bf2f(hi)));
   }
-  wait_memory();  // this block's t is visible device-wide before it is counted
+  if (pub) wait_memory();  // this block's t is visible device-wide before it is counted
   hook.others();
   lds_barrier();  // every wave's t is complete
   if (p.wait && threadIdx.x == 0 && count_arrival(p.ctl, CTL_TSUB, CTL_TTOP, blk, p.nb1))
@@ -1013,7 +1017,10 @@ void decode_pers_kernel(PersArgs args) {
     for (int li = l0; li <= l1; ++li)
       if (a.lin[li].wait && a.lin[li].n2u) wait_go_light(a.lin[li].ctl, a.spin_limit);
   }
-  if (threadIdx.x == 0 && count_arrival(a.lin[0].ctl, CTL_DSUB, CTL_DTOP, w, a.G))
+  // (a launch where no linear waits -- stage 1 only -- has nothing to clear)
+  bool waits = false;
+  for (int li = 0; li < a.n; ++li) waits = waits || a.lin[li].wait;
+  if (waits && threadIdx.x == 0 && count_arrival(a.lin[0].ctl, CTL_DSUB, CTL_DTOP, w, a.G))
     for (int li = 0; li < a.n; ++li)
       if (a.lin[li].wait) store_relaxed(a.lin[li].ctl + CTL_GO, 0u);
   s2.run(a, red);
