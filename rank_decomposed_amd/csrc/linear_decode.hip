@@ -1376,17 +1376,15 @@ hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
     grid += a.lin[i].n2;
   }
   if (grid == 0) return hipSuccess;
-  // The persistent form wins wherever the launch has stage-1 work (measured
-  // on the 7B decode shapes with weights loaded non-temporally: every class
-  // at 1, 8 and 64 tokens, o at 32, gate,up even at 32; q,k,v at 32 within
-  // 3 %); stage-2-only launches keep the tiled form.
-  double u_el = 0;
-  for (int i = 0; i < n; ++i)
-    if (a.lin[i].nb1) u_el += (double)a.lin[i].r * a.lin[i].d_in;
-  const bool pers_wins = u_el > 0;
+  // The persistent form wherever it fits.  Measured against the tiled form
+  // with weights loaded non-temporally: faster on every 7B decode class at 1,
+  // 8 and 64 tokens, o and gate,up at 32 (q,k,v at 32 within 3 %), and on
+  // stage-2-only launches (13B tensor-parallel share at 64 tokens: each 2 us
+  // faster; it loads its slice of t once, all at once, where a tiled-form
+  // tile loads it a round at a time).
   PersArgs pa;
   int per = 0;
-  if (pers_wins && plan_persistent(a, TB, &pa, &per)) {
+  if (plan_persistent(a, TB, &pa, &per)) {
     switch (TB) {
       case 1: return launch_pers<1>(pa, per, st);
       case 2: return launch_pers<2>(pa, per, st);
