@@ -1076,83 +1076,92 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   {
     float* red = reinterpret_cast<float*>(smem);  // [8 waves][4 heads][512 columns]
     const int pw = p.rv + 2;
-    for (int cb = 0; cb < p.rv; cb += 512) {
+    // one pass: QB query heads (of those left from q0) over latent columns
+    // cb .. cb + 511; a pass of two heads (the only one of a multi-head tile)
+    // does half the multiply-adds of a pass of four
+    auto pass = [&](int cb, int q0, auto qbc) {
+      constexpr int QB = decltype(qbc)::value;
       const int col = cb + lane * 8;
-      for (int q0 = 0; q0 < nq; q0 += 4) {
-        float a[4][8];
+      float a[QB][8];
 #pragma unroll
-        for (int qi = 0; qi < 4; ++qi)
+      for (int qi = 0; qi < QB; ++qi)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a[qi][e] = 0.f;
-        // 8 rows at a time, the next 8 in flight while these are summed (the
-        // first pass's first 8 are already in flight)
-        if (cb > 0 || q0 > 0) {
+        for (int e = 0; e < 8; ++e) a[qi][e] = 0.f;
+      // 8 rows at a time, the next 8 in flight while these are summed (the
+      // first pass's first 8 are already in flight)
+      if (cb > 0 || q0 > 0) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) cur[u] = load_row(col, u);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          if (b < 3) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) nxt[u] = load_row(col, 8 * (b + 1) + u);
-          }
-          // p of these 8 rows for the (up to) four heads
-          float pv[4][8];
-#pragma unroll
-          for (int qi = 0; qi < 4; ++qi) {
-            const float* pr = ps + min(q0 + qi, nq - 1) * 256 + rlo + 8 * b;
-            const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr);
-            const f32x4 p1 = *reinterpret_cast<const f32x4*>(pr + 4);
-            const bool on = q0 + qi < nq;
-            pv[qi][0] = on ? p0.x : 0.f;
-            pv[qi][1] = on ? p0.y : 0.f;
-            pv[qi][2] = on ? p0.z : 0.f;
-            pv[qi][3] = on ? p0.w : 0.f;
-            pv[qi][4] = on ? p1.x : 0.f;
-            pv[qi][5] = on ? p1.y : 0.f;
-            pv[qi][6] = on ? p1.z : 0.f;
-            pv[qi][7] = on ? p1.w : 0.f;
-          }
-          // one row at a time: its 8 values widened once, used by every head
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const uint32_t ww[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
-            float f[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              f[2 * e] = bf2f(ww[e] & 0xffffu);
-              f[2 * e + 1] = bf2f(ww[e] >> 16);
-            }
-#pragma unroll
-            for (int qi = 0; qi < 4; ++qi)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) a[qi][e] = fmaf(pv[qi][u], f[e], a[qi][e]);
-          }
-          if (b < 3) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
-          }
-        }
-#pragma unroll
-        for (int qi = 0; qi < 4; ++qi) {
-          float* rr = red + (wave * 4 + qi) * 512 + lane * 8;
-          *reinterpret_cast<f32x4*>(rr) = f32x4{a[qi][0], a[qi][1], a[qi][2], a[qi][3]};
-          *reinterpret_cast<f32x4*>(rr + 4) = f32x4{a[qi][4], a[qi][5], a[qi][6], a[qi][7]};
-        }
-        __syncthreads();
-        for (int t = threadIdx.x; t < 4 * 512; t += blockDim.x) {
-          const int qi = t / 512, c = t % 512;
-          if (q0 + qi < nq && cb + c < p.rv) {
-            float sum = 0.f;
-#pragma unroll
-            for (int w = 0; w < 8; ++w) sum += red[(w * 4 + qi) * 512 + c];
-            const int h = kv0 * grp + q0 + qi;
-            p.part[((int64_t)gb * p.H + h) * pw + 2 + cb + c] = sum;
-          }
-        }
-        __syncthreads();
+        for (int u = 0; u < 8; ++u) cur[u] = load_row(col, u);
       }
-    }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b < 3) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) nxt[u] = load_row(col, 8 * (b + 1) + u);
+        }
+        // p of these 8 rows for the (up to) QB heads
+        float pv[QB][8];
+#pragma unroll
+        for (int qi = 0; qi < QB; ++qi) {
+          const float* pr = ps + min(q0 + qi, nq - 1) * 256 + rlo + 8 * b;
+          const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr);
+          const f32x4 p1 = *reinterpret_cast<const f32x4*>(pr + 4);
+          const bool on = q0 + qi < nq;
+          pv[qi][0] = on ? p0.x : 0.f;
+          pv[qi][1] = on ? p0.y : 0.f;
+          pv[qi][2] = on ? p0.z : 0.f;
+          pv[qi][3] = on ? p0.w : 0.f;
+          pv[qi][4] = on ? p1.x : 0.f;
+          pv[qi][5] = on ? p1.y : 0.f;
+          pv[qi][6] = on ? p1.z : 0.f;
+          pv[qi][7] = on ? p1.w : 0.f;
+        }
+        // one row at a time: its 8 values widened once, used by every head
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t ww[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            f[2 * e] = bf2f(ww[e] & 0xffffu);
+            f[2 * e + 1] = bf2f(ww[e] >> 16);
+          }
+#pragma unroll
+          for (int qi = 0; qi < QB; ++qi)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[qi][e] = fmaf(pv[qi][u], f[e], a[qi][e]);
+        }
+        if (b < 3) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+        }
+      }
+#pragma unroll
+      for (int qi = 0; qi < QB; ++qi) {
+        float* rr = red + (wave * 4 + qi) * 512 + lane * 8;
+        *reinterpret_cast<f32x4*>(rr) = f32x4{a[qi][0], a[qi][1], a[qi][2], a[qi][3]};
+        *reinterpret_cast<f32x4*>(rr + 4) = f32x4{a[qi][4], a[qi][5], a[qi][6], a[qi][7]};
+      }
+      __syncthreads();
+      for (int t = threadIdx.x; t < QB * 512; t += blockDim.x) {
+        const int qi = t / 512, c = t % 512;
+        if (q0 + qi < nq && cb + c < p.rv) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) sum += red[(w * 4 + qi) * 512 + c];
+          const int h = kv0 * grp + q0 + qi;
+          p.part[((int64_t)gb * p.H + h) * pw + 2 + cb + c] = sum;
+        }
+      }
+      __syncthreads();
+    };
+    for (int cb = 0; cb < p.rv; cb += 512)
+      for (int q0 = 0; q0 < nq; q0 += 4) {
+        if (nq - q0 <= 2)
+          pass(cb, q0, std::integral_constant<int, 2>{});
+        else
+          pass(cb, q0, std::integral_constant<int, 4>{});
+      }
     for (int t = threadIdx.x; t < nq; t += blockDim.x) {
       float* out = p.part + ((int64_t)gb * p.H + kv0 * grp + t) * pw;
       out[0] = ml[2 * t];
