@@ -841,32 +841,35 @@ constexpr int fused_lds_bytes() {
          40 * HD * 4;
 }
 
-template <int HD>
+template <int HD, int TT>
 __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   constexpr int BN = 256, MBW = gMBW, NBW = BN / 64;
   constexpr int QH = kFusedQH;
+  constexpr int KPT = BN / HD;  // kv heads per column tile
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* qs = reinterpret_cast<float*>(smem + fused_ring_bytes<HD>());  // [QH][HD] queries
   float* ps = qs + QH * HD;                               // [QH][256] scores, then p
   float* ml = ps + QH * 256;                              // [QH][2] tile max and sum
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int dkv = p.Hkv * HD, ntn = (dkv + BN - 1) / BN;
-  int gb, nt;
-  if (ntn % 8 == 0) {
-    // each XCD keeps ntn / 8 column tiles (their V_k and V_v rows stay in its
-    // L2) and walks the blocks in order, its column tiles of a block together
-    const int npx = ntn / 8, w = (int)blockIdx.x / 8;
+  // an item: one block and TT adjacent column tiles (the last item of a
+  // block may hold fewer)
+  const int dkv = p.Hkv * HD, ntn = (dkv + BN - 1) / BN, nti = (ntn + TT - 1) / TT;
+  int gb, it;
+  if (nti % 8 == 0) {
+    // each XCD keeps nti / 8 column items (their V_k and V_v rows stay in its
+    // L2) and walks the blocks in order, its column items of a block together
+    const int npx = nti / 8, w = (int)blockIdx.x / 8;
     if (w >= p.nbpad * npx) return;
     gb = w / npx;
-    nt = ((int)blockIdx.x % 8) * npx + w % npx;
+    it = ((int)blockIdx.x % 8) * npx + w % npx;
   } else {
-    // the (block, column tile) list in contiguous runs per XCD, a block's
-    // column tiles together
-    const int nitems = p.nbpad * ntn, per_xcd = (nitems + 7) / 8;
+    // the (block, column item) list in contiguous runs per XCD, a block's
+    // column items together
+    const int nitems = p.nbpad * nti, per_xcd = (nitems + 7) / 8;
     const int item = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
     if ((int)blockIdx.x / 8 >= per_xcd || item >= nitems) return;
-    gb = item / ntn;
-    nt = item % ntn;
+    gb = item / nti;
+    it = item % nti;
   }
   if (gb >= p.blk_off[p.S]) return;
   int i = 0, hi = p.S;  // the sequence: the last i with blk_off[i] <= gb
@@ -879,9 +882,9 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   const int n = min(p.seq_off[i + 1], p.cap) - beg;
   const int r0 = (gb - p.blk_off[i]) * gBM;
   if (r0 < 0 || r0 >= n) return;
-  const int nrows = min(gBM, n - r0), m0 = beg + r0, n0 = nt * BN;
-  const int grp = p.H / p.Hkv, kv0 = n0 / HD;
-  const int nkv = min(BN / HD, p.Hkv - kv0), nq = nkv * grp;
+  const int nrows = min(gBM, n - r0), m0 = beg + r0, nt0 = it * TT;
+  const int grp = p.H / p.Hkv, kv0 = nt0 * KPT;
+  const int nkv = min(TT * KPT, p.Hkv - kv0), nq = nkv * grp;  // of the item
   const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
 
   // this lane's latent rows (pool rows through the remap list, or rows of the
@@ -889,7 +892,7 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   int prow[tile_a_loads<gBK, MBW>()];
   tile_rows<gBK, MBW>(prow, p.remap, m0, nrows, p.pool_rows, wave, lane);
 
-  // the tile's query heads, rotated at the new token's position and scaled
+  // the item's query heads, rotated at the new token's position and scaled
   {
     int qp = p.pos[i];
     qp = qp < 0 ? 0 : (qp >= p.max_pos ? (int)p.max_pos - 1 : qp);
@@ -936,81 +939,91 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
     }
   }
   f32x16 acc[NBW][MBW];
-  // K = latents . V_k^T (the k-loop's barriers also publish qs and the tables)
-  tile_mainloop<BN, gBK, gNS, MBW>(
-      acc,
-      p.remap ? make_rsrc(p.kl, view_bytes(p.pool_rows, p.rk, p.ldkl))
-              : make_rsrc(p.kl + (int64_t)m0 * p.ldkl, view_bytes(nrows, p.rk, p.ldkl)),
-      p.ldkl,
-      make_rsrc(p.vk + (int64_t)n0 * p.ldvk, view_bytes(min(dkv - n0, BN), p.rk, p.ldvk)),
-      p.ldvk, p.rk, smem, wave, lane, prow);
-  // rotate each head's column pairs (c, c + HD/2) by the row's position (its
-  // index in the sequence), then round to bf16.  acc[i][j] reg v: column
-  // wn + 32i + 8(v/4) + 4(lane/32) + v%4, row wm + 32j + lane%32.
-  // (cos, sin) of row wm + 32j + l from the tables: base row wm / 32 + j
-  // rotated by offset row l = lane % 32.
-  constexpr int hb = HD / 64;
-  const int l = lane & 31;
-  const uint8_t* ro = rope_l + l * CPR * 16;
-  const uint8_t* rb = rope_l + (32 + wm / 32) * CPR * 16;
-#pragma unroll
-  for (int ib = 0; ib < NBW; ++ib) {
-    if ((32 * ib) % HD >= HD / 2) continue;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int c0 = ((32 * ib) % HD + 8 * qq + 4 * (lane >> 5)) / 2;  // frequencies 2 c0 ..
-      const f32x4 o01 = *reinterpret_cast<const f32x4*>(ro + ((c0 ^ (l & 15)) << 4));
-      const f32x4 o23 = *reinterpret_cast<const f32x4*>(ro + (((c0 + 1) ^ (l & 15)) << 4));
-      const float oc[4] = {o01.x, o01.z, o23.x, o23.z};
-      const float os[4] = {o01.y, o01.w, o23.y, o23.w};
-#pragma unroll
-      for (int j = 0; j < MBW; ++j) {
-        const f32x4 b01 = *reinterpret_cast<const f32x4*>(rb + ((j * CPR + c0) << 4));
-        const f32x4 b23 = *reinterpret_cast<const f32x4*>(rb + ((j * CPR + c0 + 1) << 4));
-        const float bc[4] = {b01.x, b01.z, b23.x, b23.z};
-        const float bs[4] = {b01.y, b01.w, b23.y, b23.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float c = fmaf(bc[e], oc[e], -bs[e] * os[e]);
-          const float sn = fmaf(bs[e], oc[e], bc[e] * os[e]);
-          const float a0 = acc[ib][j][4 * qq + e], b0 = acc[ib + hb][j][4 * qq + e];
-          acc[ib][j][4 * qq + e] = a0 * c - b0 * sn;
-          acc[ib + hb][j][4 * qq + e] = b0 * c + a0 * sn;
+  // the item's column tiles one after another (the ring, acc and the
+  // rotary tables reused); their scores gather in ps for one softmax
+#pragma nounroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int n0 = (nt0 + tt) * BN;
+    if (n0 >= dkv) break;
+    const int kt0 = tt * KPT;               // the tile's first kv head in the item
+    const int nkt = min(KPT, nkv - kt0);    // its kv heads
+    // K = latents . V_k^T (the first k-loop's barriers also publish qs and the
+    // tables)
+    tile_mainloop<BN, gBK, gNS, MBW>(
+        acc,
+        p.remap ? make_rsrc(p.kl, view_bytes(p.pool_rows, p.rk, p.ldkl))
+                : make_rsrc(p.kl + (int64_t)m0 * p.ldkl, view_bytes(nrows, p.rk, p.ldkl)),
+        p.ldkl,
+        make_rsrc(p.vk + (int64_t)n0 * p.ldvk, view_bytes(min(dkv - n0, BN), p.rk, p.ldvk)),
+        p.ldvk, p.rk, smem, wave, lane, prow);
+    // rotate each head's column pairs (c, c + HD/2) by the row's position (its
+    // index in the sequence), then round to bf16.  acc[i][j] reg v: column
+    // wn + 32i + 8(v/4) + 4(lane/32) + v%4, row wm + 32j + lane%32.
+    // (cos, sin) of row wm + 32j + l from the tables: base row wm / 32 + j
+    // rotated by offset row l = lane % 32.
+    constexpr int hb = HD / 64;
+    const int l = lane & 31;
+    const uint8_t* ro = rope_l + l * CPR * 16;
+    const uint8_t* rb = rope_l + (32 + wm / 32) * CPR * 16;
+  #pragma unroll
+    for (int ib = 0; ib < NBW; ++ib) {
+      if ((32 * ib) % HD >= HD / 2) continue;
+  #pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int c0 = ((32 * ib) % HD + 8 * qq + 4 * (lane >> 5)) / 2;  // frequencies 2 c0 ..
+        const f32x4 o01 = *reinterpret_cast<const f32x4*>(ro + ((c0 ^ (l & 15)) << 4));
+        const f32x4 o23 = *reinterpret_cast<const f32x4*>(ro + (((c0 + 1) ^ (l & 15)) << 4));
+        const float oc[4] = {o01.x, o01.z, o23.x, o23.z};
+        const float os[4] = {o01.y, o01.w, o23.y, o23.w};
+  #pragma unroll
+        for (int j = 0; j < MBW; ++j) {
+          const f32x4 b01 = *reinterpret_cast<const f32x4*>(rb + ((j * CPR + c0) << 4));
+          const f32x4 b23 = *reinterpret_cast<const f32x4*>(rb + ((j * CPR + c0 + 1) << 4));
+          const float bc[4] = {b01.x, b01.z, b23.x, b23.z};
+          const float bs[4] = {b01.y, b01.w, b23.y, b23.w};
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float c = fmaf(bc[e], oc[e], -bs[e] * os[e]);
+            const float sn = fmaf(bs[e], oc[e], bc[e] * os[e]);
+            const float a0 = acc[ib][j][4 * qq + e], b0 = acc[ib + hb][j][4 * qq + e];
+            acc[ib][j][4 * qq + e] = a0 * c - b0 * sn;
+            acc[ib + hb][j][4 * qq + e] = b0 * c + a0 * sn;
+          }
         }
       }
     }
-  }
-#pragma unroll
-  for (int ib = 0; ib < NBW; ++ib)
-#pragma unroll
-    for (int j = 0; j < MBW; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[ib][j][v] = bf2f(f2bf(acc[ib][j][v]));
-  // scores: the wave's 128 columns hold HD-wide heads; a lane has half of a
-  // head's columns for its rows, the partner lane (lane ^ 32) the other half
-#pragma unroll
-  for (int hk = 0; hk < 128 / HD; ++hk) {
-    const int kvl = (wn + hk * HD) / HD;  // kv head within the tile
-    if (kvl >= nkv) continue;
-    for (int g = 0; g < grp; ++g) {
-      const float* qrow = qs + (kvl * grp + g) * HD;
-#pragma unroll
-      for (int j = 0; j < MBW; ++j) {
-        float s = 0.f;
-#pragma unroll
-        for (int ib = hk * (HD / 32); ib < (hk + 1) * (HD / 32); ++ib)
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int d = (32 * ib) % HD + 8 * qq + 4 * (lane >> 5);
-            const f32x4 qv = *reinterpret_cast<const f32x4*>(qrow + d);
-            s = fmaf(acc[ib][j][4 * qq], qv.x, s);
-            s = fmaf(acc[ib][j][4 * qq + 1], qv.y, s);
-            s = fmaf(acc[ib][j][4 * qq + 2], qv.z, s);
-            s = fmaf(acc[ib][j][4 * qq + 3], qv.w, s);
-          }
-        s += __shfl_xor(s, 32);
-        const int row = wm + 32 * j + (lane & 31);
-        if (lane < 32) ps[(kvl * grp + g) * 256 + row] = row < nrows ? s : -INFINITY;
+  #pragma unroll
+    for (int ib = 0; ib < NBW; ++ib)
+  #pragma unroll
+      for (int j = 0; j < MBW; ++j)
+  #pragma unroll
+        for (int v = 0; v < 16; ++v) acc[ib][j][v] = bf2f(f2bf(acc[ib][j][v]));
+    // scores: the wave's 128 columns hold HD-wide heads; a lane has half of a
+    // head's columns for its rows, the partner lane (lane ^ 32) the other half
+  #pragma unroll
+    for (int hk = 0; hk < 128 / HD; ++hk) {
+      const int kvl = (wn + hk * HD) / HD;  // kv head within the tile
+      if (kvl >= nkt) continue;
+      for (int g = 0; g < grp; ++g) {
+        const float* qrow = qs + ((kt0 + kvl) * grp + g) * HD;
+  #pragma unroll
+        for (int j = 0; j < MBW; ++j) {
+          float s = 0.f;
+  #pragma unroll
+          for (int ib = hk * (HD / 32); ib < (hk + 1) * (HD / 32); ++ib)
+  #pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int d = (32 * ib) % HD + 8 * qq + 4 * (lane >> 5);
+              const f32x4 qv = *reinterpret_cast<const f32x4*>(qrow + d);
+              s = fmaf(acc[ib][j][4 * qq], qv.x, s);
+              s = fmaf(acc[ib][j][4 * qq + 1], qv.y, s);
+              s = fmaf(acc[ib][j][4 * qq + 2], qv.z, s);
+              s = fmaf(acc[ib][j][4 * qq + 3], qv.w, s);
+            }
+          s += __shfl_xor(s, 32);
+          const int row = wm + 32 * j + (lane & 31);
+          if (lane < 32) ps[((kt0 + kvl) * grp + g) * 256 + row] = row < nrows ? s : -INFINITY;
+        }
       }
     }
   }
@@ -1170,19 +1183,34 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
   }
 }
 
-template <int HD>
-hipError_t launch_fused(const FusedAttnArgs& a, hipStream_t st) {
+template <int HD, int TT>
+hipError_t launch_fused_tt(const FusedAttnArgs& a, hipStream_t st) {
   constexpr int lds = fused_lds_bytes<HD>();
   static_assert(lds <= 160 * 1024, "LDS");
   static std::once_flag once;
   std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused_kernel<HD>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused_kernel<HD, TT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
-  const int64_t ntn = (a.Hkv * HD + 255) / 256, items = (int64_t)a.nbpad * ntn;
-  hipLaunchKernelGGL((attn_fused_kernel<HD>), dim3((unsigned)((items + 7) / 8 * 8)), dim3(512),
-                     lds, st, a);
+  const int64_t ntn = (a.Hkv * HD + 255) / 256, items = (int64_t)a.nbpad * ((ntn + TT - 1) / TT);
+  hipLaunchKernelGGL((attn_fused_kernel<HD, TT>), dim3((unsigned)((items + 7) / 8 * 8)),
+                     dim3(512), lds, st, a);
   return hipGetLastError();
+}
+
+// At hd 128, two column tiles per item wherever their query heads fit the
+// item's LDS (MHA; GQA up to 4 query heads per kv head): the latent rows'
+// addresses, the queries and the rotary tables are set up once for both, one
+// softmax and one pass of latent sums serve both tiles' heads, and the V
+// latent rows are read once for them.  (At hd 64 the two-tile kernel spills.)
+template <int HD>
+hipError_t launch_fused(const FusedAttnArgs& a, hipStream_t st) {
+  if constexpr (HD == 128) {
+    const int64_t ntn = (a.Hkv * HD + 255) / 256;
+    const int grp = a.Hkv > 0 ? a.H / a.Hkv : 1;
+    if (ntn >= 2 && 2 * (256 / HD) * grp <= kFusedQH) return launch_fused_tt<HD, 2>(a, st);
+  }
+  return launch_fused_tt<HD, 1>(a, st);
 }
 
 // Sum of the K-range partials in range order: out32 (fp32, optional) and
