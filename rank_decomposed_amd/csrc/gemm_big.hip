@@ -862,6 +862,14 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
     if (w >= p.nbpad * npx) return;
     gb = w / npx;
     it = ((int)blockIdx.x % 8) * npx + w % npx;
+  } else if (8 % nti == 0) {
+    // 8 / nti XCDs per column item, each taking every (8 / nti)-th block: an
+    // XCD keeps one item's factor rows in its L2, and a block's latent rows
+    // are fetched by 8 / nti XCDs rather than by all of them
+    const int xpi = 8 / nti, x = (int)blockIdx.x % 8;
+    it = x % nti;
+    gb = ((int)blockIdx.x / 8) * xpi + x / nti;
+    if (gb >= p.nbpad) return;
   } else {
     // the (block, column item) list in contiguous runs per XCD, a block's
     // column items together
@@ -1192,22 +1200,29 @@ hipError_t launch_fused_tt(const FusedAttnArgs& a, hipStream_t st) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fused_kernel<HD, TT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
-  const int64_t ntn = (a.Hkv * HD + 255) / 256, items = (int64_t)a.nbpad * ((ntn + TT - 1) / TT);
-  hipLaunchKernelGGL((attn_fused_kernel<HD, TT>), dim3((unsigned)((items + 7) / 8 * 8)),
-                     dim3(512), lds, st, a);
+  const int64_t ntn = (a.Hkv * HD + 255) / 256, nti = (ntn + TT - 1) / TT;
+  // (the layout of the kernel's item mapping: with 8 % nti == 0, 8 / nti
+  // XCDs per column item each take every (8 / nti)-th block)
+  const int64_t grid = nti % 8 != 0 && 8 % nti == 0
+                           ? 8 * ((a.nbpad + 8 / nti - 1) / (8 / nti))
+                           : (a.nbpad * nti + 7) / 8 * 8;
+  hipLaunchKernelGGL((attn_fused_kernel<HD, TT>), dim3((unsigned)grid), dim3(512), lds, st, a);
   return hipGetLastError();
 }
 
-// At hd 128, two column tiles per item wherever their query heads fit the
-// item's LDS (MHA; GQA up to 4 query heads per kv head): the latent rows'
-// addresses, the queries and the rotary tables are set up once for both, one
-// softmax and one pass of latent sums serve both tiles' heads, and the V
-// latent rows are read once for them.  (At hd 64 the two-tile kernel spills.)
+// At hd 128, four (else two) column tiles per item wherever their query heads
+// fit the item's LDS (four: MHA and GQA with 2 query heads per kv head; two:
+// up to 4): the latent rows' addresses, the queries and the rotary tables are
+// set up once for all, one softmax serves every tile's heads, and with four
+// tiles each block's latent rows are fetched by 4 XCDs rather than 8.  On the
+// 7B step: 1087 us per layer with one tile, 954 with two, 936 with four, 957
+// with eight.  (At hd 64 the multi-tile kernel spills.)
 template <int HD>
 hipError_t launch_fused(const FusedAttnArgs& a, hipStream_t st) {
   if constexpr (HD == 128) {
     const int64_t ntn = (a.Hkv * HD + 255) / 256;
     const int grp = a.Hkv > 0 ? a.H / a.Hkv : 1;
+    if (ntn >= 4 && 4 * (256 / HD) * grp <= kFusedQH) return launch_fused_tt<HD, 4>(a, st);
     if (ntn >= 2 && 2 * (256 / HD) * grp <= kFusedQH) return launch_fused_tt<HD, 2>(a, st);
   }
   return launch_fused_tt<HD, 1>(a, st);
