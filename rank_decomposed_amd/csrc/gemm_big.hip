@@ -712,21 +712,23 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------- fused decode attention
 // Decode attention with the reconstruction on chip: one workgroup takes a
-// 256-row block of one sequence's cached rows and the 256 K columns of 256/HD
-// kv heads.  It expands the block's K latents into K (the large-tile k-loop
-// over r_k), rotates and rounds them to bf16 as the reconstruction would
-// store them, and scores them against the sequence's query heads of those kv
-// heads.  Then it forms the block's softmax partials (max m, sum l) and, per
-// query head, the p-weighted sum of the block's V latent rows, which it
-// writes with m and l: the combine over a sequence's blocks follows and
-// applies V_v there (sum_rows p (l V_v) = (sum_rows p l) V_v), so V is
-// never formed and the reconstructed rows never reach HBM.
-// Blocks come from blk_off (blk_off[i] = first block of sequence i).  With
-// a multiple of 8 column tiles each XCD keeps its share of them for every
-// block, so the two up-projection tiles it reads stay in its L2 (both
-// factors together exceed one L2); otherwise the (block, column tile) pairs
-// go to the XCDs in contiguous runs.
-constexpr int kFusedQH = 16;  // query heads per column tile at most
+// 256-row block of one sequence's cached rows and TT column tiles, each the
+// 256 K columns of 256/HD kv heads (an item).  Tile by tile it expands the
+// block's K latents into K (the large-tile k-loop over r_k), rotates and
+// rounds them to bf16 as the reconstruction would store them, and scores them
+// against the sequence's query heads of those kv heads.  Then it forms the
+// block's softmax partials (max m, sum l) and, per query head, the p-weighted
+// sum of the block's V latent rows, which it writes with m and l: the combine
+// over a sequence's blocks follows and applies V_v there
+// (sum_rows p (l V_v) = (sum_rows p l) V_v), so V is never formed and the
+// reconstructed rows never reach HBM.
+// Blocks come from blk_off (blk_off[i] = first block of sequence i).  With a
+// multiple of 8 column items each XCD keeps its share of them for every
+// block; with 8 / (column items) XCDs per item each takes every few blocks:
+// either way the up-projection tiles an XCD reads stay in its L2 (all of
+// them exceed one L2).  Otherwise the (block, column item) pairs go to the
+// XCDs in contiguous runs.
+constexpr int kFusedQH = 16;  // query heads per item at most
 
 // A load instructions per lane for a 256-row tile of BK-deep k-tiles
 template <int BK, int MBW>
