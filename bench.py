@@ -148,6 +148,10 @@ def main():
                     help="for hardware-counter runs: negate 256 Mi bf16 (a reference kernel "
                          "of known traffic: 512 MiB in, 512 MiB out), run one launch class "
                          "(e.g. gateup_T64) eagerly over every layer set twice, and exit")
+    ap.add_argument("--probe-step", action="store_true",
+                    help="for hardware-counter runs: the same reference kernel, then 2 layers "
+                         "of the unfused and of the fused decode step, eagerly, twice each, "
+                         "and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the low-rank path here has no "
@@ -160,6 +164,9 @@ def main():
     dev = torch.device("cuda:0")
     lr.load()
     stream = torch.cuda.current_stream(dev)
+    if args.probe_step:
+        probe_step(torch, lr, dev)
+        return
     base, sets = make_layer_sets(torch, dev, 0.6, args.layer_sets, 1234)
     if args.layout == "packed":
         pack_sets(lr, sets)
@@ -220,12 +227,7 @@ def main():
     if args.probe_class:
         name, T = args.probe_class.split("_T")
         roles = dict(GROUPS)[name]
-        src = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1.0)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)     # one elementwise kernel: reads 512 MiB, writes 512 MiB
-        torch.cuda.synchronize()
+        reference_kernel(torch, dev)
         for _ in range(2):
             for layer in sets:
                 call(int(T), layer, roles)
@@ -525,6 +527,53 @@ def tp_share(torch, lr, dev, stream, reps, n_sets=32, P=8):
             "bound": "hbm" if T <= 64 else "mfma",
             "factor_layout": "packed" if T <= 64 else "rowmajor"}
     return out
+
+
+def reference_kernel(torch, dev):
+    """One elementwise kernel of known traffic for counter runs: negating 256 Mi
+    bf16 reads 512 MiB and writes 512 MiB."""
+    src = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def probe_step(torch, lr, dev):
+    """Counter-run workload of the decode step: the reference kernel, then 2
+    layers of the unfused and of the fused step (the decode-step inputs of the
+    timed leg), eagerly, twice each."""
+    from synth.decode_step import DecodeStepInputs
+    reference_kernel(torch, dev)
+    si = DecodeStepInputs(n_layers=2, device=dev)
+    c = si.cfg
+    prep = lr.lowrank_prepare_decode(si.lengths, si.tables, si.block, si.cap)
+    rope = torch.empty((si.max_seq_rows, c["head_dim"] // 2, 2), dtype=torch.float32, device=dev)
+    lr.lowrank_rope_table(c["head_dim"], si.max_seq_rows, 10000.0, rope)
+    dp = {k: torch.from_numpy(np.ascontiguousarray(prep[k])).to(dev)
+          for k in ("remap", "seq_off", "pos", "slot_mapping")}
+    nv = torch.tensor([prep["n_valid"]], dtype=torch.int32, device=dev)
+    layers = []
+    for li in range(2):
+        Ut, Vt, g1, g2 = si.device_layer(li)
+        w = lr.layer_weights(c, Ut, Vt, g1, g2, rope, si.max_seq_rows)
+        st = lr.decode_state(si.device_pool(li, 0), si.device_pool(li, 1), dp["slot_mapping"],
+                             dp["remap"], dp["seq_off"], dp["pos"], nv, si.max_seq_rows)
+        layers.append((w, st))
+    for fused in (False, True):
+        size = (lr.lowrank_decode_step_fused_workspace_bytes if fused
+                else lr.lowrank_decode_step_workspace_bytes)
+        fn = lr.lowrank_layer_decode_step_fused if fused else lr.lowrank_layer_decode_step
+        ws = torch.zeros(size(*layers[0]), dtype=torch.uint8, device=dev)
+        h = torch.from_numpy(si.h0.astype(np.float32)).to(dev)
+        for _ in range(2):
+            for w, st in layers:
+                fn(w, st, h, ws)
+        torch.cuda.synchronize()
+        log("probe: %s decode step, 2 layers twice" % ("fused" if fused else "unfused"))
+        del ws
+        torch.cuda.empty_cache()
 
 
 def decode_step(torch, lr, dev, stream, n_layers, reps, fused=False):
