@@ -753,15 +753,44 @@ __device__ __forceinline__ void tile_rows(int (&prow)[gBM / (64 / (BK / 8)) / (2
   }
 }
 
+// Stage t of the ring: k-tile t of the A rows (through the row list) and of B.
+template <int BN, int BK, int NS, int MBW>
+__device__ __forceinline__ void ring_stage(int t, __amdgpu_buffer_rsrc_t ra, int64_t lda,
+                                           __amdgpu_buffer_rsrc_t rb, int64_t ldb, int K,
+                                           uint8_t* smem, int wave, int lane,
+                                           const int (&prow)[gBM / (64 / (BK / 8)) / (2 * gBM / (32 * MBW))]) {
+  constexpr int NW = 2 * gBM / (32 * MBW);
+  constexpr int kStage = big_stage_bytes<BN, BK>();
+  uint8_t* st = smem + (t % NS) * kStage;
+  load_tile_rows<gBM, BK, NW>(ra, lda, t * BK, K - t * BK, st, wave, lane, prow);
+  load_tile<BN, BK, NW>(rb, ldb, t * BK, K - t * BK, st + gBM * BK * 2, wave, lane);
+}
+
+// The ring fill of a k-loop (stages 0 .. NS - 2), for a caller that issues
+// it early: the ring must be dead (after the previous k-loop's last barrier)
+// and no other global load issued between it and tile_mainloop(filled).
+template <int BN, int BK, int NS, int MBW>
+__device__ __forceinline__ void tile_ring_fill(__amdgpu_buffer_rsrc_t ra, int64_t lda,
+                                               __amdgpu_buffer_rsrc_t rb, int64_t ldb, int K,
+                                               uint8_t* smem, int wave, int lane,
+                                               const int (&prow)[gBM / (64 / (BK / 8)) / (2 * gBM / (32 * MBW))]) {
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nk) ring_stage<BN, BK, NS, MBW>(t, ra, lda, rb, ldb, K, smem, wave, lane, prow);
+}
+
 // The A rows of the tile are rows prow[i] of the A buffer for this lane's
 // i-th A load instruction (tile_rows; negative: a zero row), so the operand can
-// be read in place through a row list.
+// be read in place through a row list.  filled: tile_ring_fill has issued
+// the ring fill already.
 template <int BN, int BK, int NS, int MBW>
 __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
                                               __amdgpu_buffer_rsrc_t ra, int64_t lda,
                                               __amdgpu_buffer_rsrc_t rb, int64_t ldb, int K,
                                               uint8_t* smem, int wave, int lane,
-                                              const int (&prow)[gBM / (64 / (BK / 8)) / (2 * gBM / (32 * MBW))]) {
+                                              const int (&prow)[gBM / (64 / (BK / 8)) / (2 * gBM / (32 * MBW))],
+                                              bool filled = false) {
   constexpr int NW = 2 * gBM / (32 * MBW), NBW = BN / 64, KS = BK / 16;
   constexpr int kTileA = gBM * BK * 2;
   constexpr int kStage = big_stage_bytes<BN, BK>();
@@ -773,9 +802,7 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
 #pragma unroll
     for (int j = 0; j < MBW; ++j) acc[i][j] = f32x16{};
   auto load_stage = [&](int t) {
-    uint8_t* st = smem + (t % NS) * kStage;
-    load_tile_rows<gBM, BK, NW>(ra, lda, t * BK, K - t * BK, st, wave, lane, prow);
-    load_tile<BN, BK, NW>(rb, ldb, t * BK, K - t * BK, st + kTileA, wave, lane);
+    ring_stage<BN, BK, NS, MBW>(t, ra, lda, rb, ldb, K, smem, wave, lane, prow);
   };
   auto wait_stage = [&](int younger) {
     if (younger >= NS - 1) wait_vm<(NS - 1) * IPW>();
@@ -794,9 +821,11 @@ __device__ __forceinline__ void tile_mainloop(f32x16 (&acc)[BN / 64][MBW],
     }
   };
   u32x4 af[2][MBW], bfr[2][NBW];
+  if (!filled) {
 #pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < nk) load_stage(t);
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < nk) load_stage(t);
+  }
   wait_stage(min(NS - 2, nk - 1));
   open_stage(0);
   load_frags<NBW, MBW, BK>(af[0], bfr[0], smem, smem + kTileA, wm, wn, lane, 0);
@@ -958,14 +987,21 @@ __global__ __launch_bounds__(512) void attn_fused_kernel(FusedAttnArgs p) {
     const int kt0 = tt * KPT;               // the tile's first kv head in the item
     const int nkt = min(KPT, nkv - kt0);    // its kv heads
     // K = latents . V_k^T (the first k-loop's barriers also publish qs and the
-    // tables)
-    tile_mainloop<BN, gBK, gNS, MBW>(
-        acc,
+    // tables); the ring of every tile after the first was filled during the
+    // previous tile's rotary and scores
+    const __amdgpu_buffer_rsrc_t rkl =
         p.remap ? make_rsrc(p.kl, view_bytes(p.pool_rows, p.rk, p.ldkl))
-                : make_rsrc(p.kl + (int64_t)m0 * p.ldkl, view_bytes(nrows, p.rk, p.ldkl)),
-        p.ldkl,
+                : make_rsrc(p.kl + (int64_t)m0 * p.ldkl, view_bytes(nrows, p.rk, p.ldkl));
+    tile_mainloop<BN, gBK, gNS, MBW>(
+        acc, rkl, p.ldkl,
         make_rsrc(p.vk + (int64_t)n0 * p.ldvk, view_bytes(min(dkv - n0, BN), p.rk, p.ldvk)),
-        p.ldvk, p.rk, smem, wave, lane, prow);
+        p.ldvk, p.rk, smem, wave, lane, prow, tt > 0);
+    if (tt + 1 < TT && n0 + BN < dkv)
+      tile_ring_fill<BN, gBK, gNS, MBW>(
+          rkl, p.ldkl,
+          make_rsrc(p.vk + (int64_t)(n0 + BN) * p.ldvk,
+                    view_bytes(min(dkv - n0 - BN, BN), p.rk, p.ldvk)),
+          p.ldvk, p.rk, smem, wave, lane, prow);
     // rotate each head's column pairs (c, c + HD/2) by the row's position (its
     // index in the sequence), then round to bf16.  acc[i][j] reg v: column
     // wn + 32i + 8(v/4) + 4(lane/32) + v%4, row wm + 32j + lane%32.
