@@ -210,11 +210,15 @@ def test_group_share_pattern_stage1_then_stage2(T):
     x = cs[0]["dx"]
     d = dev()
     ts = [torch.full((T, 1024), float("nan"), dtype=torch.float32, device=d) for _ in cs]
-    lr.lowrank_linear_forward_group([dict(x=x, Ut=lr.pack_factor(c["dUt"]), t_io=t)
-                                     for c, t in zip(cs, ts)])
-    ys = lr.lowrank_linear_forward_group([dict(Vt=lr.pack_factor(c["dVt"]), t_io=t)
-                                          for c, t in zip(cs, ts)])
+    s1 = [dict(x=x, Ut=lr.pack_factor(c["dUt"]), t_io=t) for c, t in zip(cs, ts)]
+    s2 = [dict(Vt=lr.pack_factor(c["dVt"]), t_io=t) for c, t in zip(cs, ts)]
+    need = max(lr.lowrank_group_workspace_bytes(T, s1), lr.lowrank_group_workspace_bytes(T, s2))
+    ws = torch.zeros(need, dtype=torch.uint8, device=d)
+    lr.lowrank_linear_forward_group(s1, workspace=ws)
+    ys = lr.lowrank_linear_forward_group(s2, workspace=ws)
     torch.cuda.synchronize()
+    # a launch where no linear waits counts nothing: its control words stay zero
+    assert not control_counters(ws).any()
     for c, t, y in zip(cs, ts, ys):
         tr, yr = oracle.linear(cs[0]["x"], c["U"], c["V"])
         assert maxrel(to_f64(t), tr) <= 1e-5
