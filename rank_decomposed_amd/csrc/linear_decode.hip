@@ -13,13 +13,17 @@
 // memory; row-major steps touch 16 rows x 64 B per load, which costs a third
 // of the HBM rate on long rows).
 //
-// One kernel per launch; the grid holds every stage-1 tile and then every
-// stage-2 tile of every linear of the launch, tile = blockIdx.x.  Workgroups
-// are 8 waves and two share a CU, so that while the stage-1 tiles stream U_r
-// the stage-2 tiles dispatched beside them already stream their whole share
-// of V_r into registers and only then wait for t.  Workgroups are dispatched
-// in index order and stage-1 tiles never wait, so a waiting stage-2 tile can
-// never hold resources that a stage-1 tile it waits for still needs.
+// One kernel per launch, in one of two forms that share the tile code.  The
+// persistent form (decode_pers_kernel, below; every launch it fits) holds
+// one 8-wave workgroup per CU: workgroup w runs stage-1 tile w, then a run of
+// stage-2 units, with the first V_r fragments issued before its wait for t.
+// The tiled form (decode_kernel) lists every stage-1 tile and then every
+// stage-2 tile of every linear of the launch, tile = blockIdx.x, two 8-wave
+// workgroups per CU, so that while the stage-1 tiles stream U_r the stage-2
+// tiles dispatched beside them already stream their first steps of V_r into
+// registers and only then wait for t.  Workgroups are dispatched in index
+// order and stage-1 tiles never wait, so a waiting stage-2 tile can never
+// hold resources that a stage-1 tile it waits for still needs.
 //   stage-1 tile: 16*RB1 rows of U_r^T over one of S1 K ranges.  S1 is chosen
 //     per launch so that the launch has about one stage-1 tile per CU.  The 8
 //     waves split the range into contiguous runs of k-steps and their partial
