@@ -20,10 +20,14 @@ LENGTHS = [0, 1, 15, 255, 40, 300, 511, 700]
 
 
 @pytest.mark.parametrize("H,Hkv,hd", [(4, 4, 64), (4, 2, 64), (4, 4, 128), (8, 2, 64),
-                                      (16, 2, 128), (2, 1, 128), (16, 16, 128), (32, 8, 64)])
+                                      (16, 2, 128), (2, 1, 128), (16, 16, 128), (32, 8, 64),
+                                      (16, 4, 128), (16, 8, 128), (12, 6, 128), (10, 10, 128)])
 def test_fused_layer_against_oracle_and_unfused(H, Hkv, hd):
-    # 16 x 128 and 8 x 64 K/V columns make 8 and 2 column tiles: the first
-    # takes the layout that keeps one column tile per XCD
+    # items of one, two or four 256-column tiles: 16 x 128 columns make 8
+    # tiles in two four-tile items (four XCDs per item); 4 x 128 with 4
+    # query heads per kv head two-tile items of 16 heads; 8 x 128 with 2
+    # query heads per kv head four-tile items of 16 heads; 6 x 128 and
+    # 10 x 128 a last item with fewer tiles
     cfg = small_cfg(H, Hkv, hd)
     seed = 150 + H + Hkv + hd
     st = Step(seed, cfg, ranks_for(cfg), LENGTHS, n_layers=1, fused=True)
