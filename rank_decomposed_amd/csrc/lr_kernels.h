@@ -112,11 +112,13 @@ hipError_t gemm_nt_big_rows(const void* A, int64_t lda, const void* B, int64_t l
                             int64_t ldc, int64_t M, const int32_t* m_valid, int64_t N, int64_t K,
                             const BigRope* rope, hipStream_t st);
 // Decode attention with the reconstruction on chip (one new token per
-// sequence): per 256-row block of a sequence and 256 K/V columns, K and V are
-// expanded from the gathered latents (rotary on K, both rounded to bf16) and
-// the block's softmax partials part[block][h] = {m, l, o[hd]} are written.
-// blk_off[i]: first block of sequence i (blk_off[S] = blocks); nbpad bounds
-// the blocks (cap / 256 + S).  At most 16 query heads per 256 columns.
+// sequence): per 256-row block of a sequence's cached rows and an item of
+// 256-column K tiles, K is expanded from the latents (rotary, rounded to
+// bf16) and scored, and the block's partials part[block][h] = {m, l, the
+// p-weighted sum of its V latent rows (rv)} are written; V_v is applied by
+// the combine.  blk_off[i]: first block of sequence i (blk_off[S] = blocks);
+// nbpad bounds the blocks (cap / 256 + S).  At most 16 query heads per 256
+// columns.
 struct FusedAttnArgs {
   const uint16_t* kl;  // K latents [cap, ldkl], rk columns (or the pool, see remap)
   int64_t ldkl;
@@ -140,7 +142,7 @@ struct FusedAttnArgs {
   const int32_t* pos;
   const int32_t* blk_off;
   int S, cap, H, Hkv, nbpad;
-  float* part;         // [nbpad][H][hd + 2]
+  float* part;         // [nbpad][H][rv + 2]
 };
 hipError_t attn_fused_decode(const FusedAttnArgs& a, int hd, hipStream_t st);
 size_t prefill_workspace_bytes(int64_t T, int64_t r, int64_t d_out);
