@@ -63,15 +63,16 @@ hipError_t launch(const float* A, int64_t lda, const float* B, int64_t ldb, floa
 
 }  // namespace
 
+// t [T, r] past the decode path's control area
 size_t f32_workspace_bytes(int64_t T, int64_t r) {
-  return (size_t)((T * r * 4 + 255) / 256 * 256);
+  return kCtlAreaBytes + (size_t)((T * r * 4 + 255) / 256 * 256);
 }
 
 hipError_t linear_f32(const DecodeLinear& d, hipStream_t st) {
   float* t = d.t_io;
   int64_t ldt = d.ldt;
   if (!t) {
-    t = static_cast<float*>(d.workspace);
+    t = reinterpret_cast<float*>(static_cast<uint8_t*>(d.workspace) + kCtlAreaBytes);
     ldt = d.r;
   }
   if (d.flags != 2) {

@@ -334,14 +334,20 @@ static bool fused_fits(int64_t r) { return fused_lds_bytes(r) <= (size_t)kLdsMax
 constexpr int64_t kBigT = 1024;
 
 // Calls from kBigT rows on, and calls whose rank tile does not fit on chip,
-// park t in the workspace as bf16 [T, round_up(r, 8)]; the fused kernel
-// needs none.  From kBigT rows on, a stage 1 with too few tiles to fill the
-// chip splits its d_in range: the fp32 partials follow t.
+// park t in the workspace as bf16 [T, round_up(r, 8)], past the decode
+// path's control area; the fused kernel needs none.  From kBigT rows on, a
+// stage 1 with too few tiles to fill the chip splits its d_in range: the
+// fp32 partials follow t.
 size_t prefill_workspace_bytes(int64_t T, int64_t r, int64_t d_out) {
   (void)d_out;
   if (T < kBigT && fused_fits(r)) return 0;
   const size_t tb = (size_t)rup(T * rup(r, 8) * 2, 256);
-  return T >= kBigT ? tb + gemm_split_bytes(T, r) : tb;
+  return kCtlAreaBytes + (T >= kBigT ? tb + gemm_split_bytes(T, r) : tb);
+}
+
+// Where t starts in a workspace (the control area's words are never touched).
+static uint16_t* parked_t(void* workspace) {
+  return reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + kCtlAreaBytes);
 }
 
 namespace {
@@ -362,11 +368,11 @@ __global__ void to_bf16_kernel(const float* src, int64_t lds, uint16_t* dst, int
 // call and rounded into it first.
 hipError_t prefill_big(const DecodeLinear& d, hipStream_t st) {
   const int64_t ldtb = rup(d.r, 8);
-  uint16_t* tws = static_cast<uint16_t*>(d.workspace);
+  uint16_t* tws = parked_t(d.workspace);
   hipError_t e = hipSuccess;
   if (d.flags != 2) {
     if (gemm_split_ranges(d.T, d.r, d.d_in) > 1) {
-      float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(d.workspace) +
+      float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(tws) +
                                              rup(d.T * ldtb * 2, 256));
       e = gemm_nt_big_split(d.x, d.ldx, d.Ut, d.ldu, part, d.t_io, d.ldt,
                             d.t_io && d.flags == 1 ? nullptr : tws, ldtb, d.T, d.r, d.d_in, st);
@@ -446,7 +452,7 @@ hipError_t prefill_linear_bf16(const DecodeLinear& d, hipStream_t st) {
   // workspace, then stage 2 from it.
   hipError_t e = hipSuccess;
   const int64_t ldtb = rup(d.r, 8);
-  uint16_t* tws = static_cast<uint16_t*>(d.workspace);
+  uint16_t* tws = parked_t(d.workspace);
   if (d.flags != 2) {
     GemmArgs g{};
     g.a = d.x;

@@ -44,6 +44,11 @@ struct DecodeLinear {
 // linear gave up (lowrank_workspace_check reads and clears it).
 constexpr int kCtlBlocks = 8;
 constexpr int kCtlBlockWords = 4096;
+// Bytes of the control area.  Every other path that parks data in a
+// workspace (the prefill GEMMs' t and partials, the fp32 path's t) starts
+// past it, so one workspace can serve decode calls and any others in turn
+// without a clearing between them.
+constexpr size_t kCtlAreaBytes = (size_t)kCtlBlocks * kCtlBlockWords * 4;
 constexpr int kCtlErrWord = 1216;
 constexpr uint32_t kWaitErrorMagic = 0x4c525754u;
 constexpr uint32_t kDefaultSpinLimit = 1u << 20;  // polls (~1 us each) before a wait gives up

@@ -26,7 +26,7 @@ __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 // The decode path's control words (counters, flags, error words) must start
 // at zero; they return to zero at the end of every call.
-constexpr size_t kCtlBytes = (size_t)lr::kCtlBlocks * lr::kCtlBlockWords * 4;
+constexpr size_t kCtlBytes = lr::kCtlAreaBytes;
 static_assert(kCtlBytes % 16 == 0 && kCtlBytes <= kScratchBytes, "control area");
 
 __global__ void __launch_bounds__(256) clear_words(uint4* p, size_t n) {

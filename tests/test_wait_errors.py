@@ -15,7 +15,7 @@ import torch
 import oracle
 import rank_decomposed_amd as lr
 import synth
-from gpu_util import bits, dev, make_linear, maxrel, padded, to_f64
+from gpu_util import bits, control_counters, dev, make_linear, maxrel, padded, to_f64
 
 pytestmark = pytest.mark.gpu
 BF16_TOL = 2e-2
@@ -101,3 +101,33 @@ def test_workspace_reused_across_inputs(T):
     for i, y in enumerate(outs):
         assert np.array_equal(bits(y), bits(r1 if i % 2 == 0 else r2)), i
     assert maxrel(to_f64(outs[1]), oracle.linear(x2, c["U"], c["V"])[1]) <= BF16_TOL
+
+
+def test_one_workspace_serves_every_path_in_turn():
+    # The decode path keeps its counters in the workspace's control area; the
+    # other paths park t there too (large-tile prefill GEMMs; the unfused
+    # prefill for a rank tile too large for the fused kernel; fp32), past
+    # that area, so decode calls before and after them on one workspace give
+    # what a fresh workspace gives, with no clearing in between.
+    dec = make_linear(9400, 8, 4096, 1228, 4096, "bf16", fast=True)
+    big = make_linear(9410, 1024, 1024, 300, 768, "bf16", fast=True)
+    unf = make_linear(9420, 100, 2048, 1500, 2048, "bf16", fast=True)
+    f32 = make_linear(9430, 4, 512, 96, 256, "f32", fast=True)
+    calls = [(dec, lr.LR_BF16), (big, lr.LR_BF16), (unf, lr.LR_BF16), (f32, lr.LR_F32)]
+    need = max(lr.lowrank_workspace_bytes(0, dt, c["dx"].shape[0], c["dx"].shape[1],
+                                          c["dUt"].shape[0], c["dVt"].shape[0])
+               for c, dt in calls)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    ref = [lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"]) for c, _ in calls]
+    torch.cuda.synchronize()
+    for i in [0, 1, 0, 2, 0, 3, 0]:
+        c = calls[i][0]
+        print(f"shared workspace: call {i} T={c['dx'].shape[0]}", flush=True)
+        y = lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"], workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y), bits(ref[i])), i
+        assert not control_counters(ws).any(), i
+    assert lr.lowrank_workspace_check(ws) == 0
+    for (c, _), y in zip(calls, ref):
+        tol = 1e-5 if y.dtype == torch.float32 else BF16_TOL
+        assert maxrel(to_f64(y), oracle.linear(c["x"], c["U"], c["V"])[1]) <= tol
