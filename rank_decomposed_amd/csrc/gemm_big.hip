@@ -297,6 +297,13 @@ struct BigArgs {
   int act;                 // bf16 C, staged stores: 1 = silu(G) * product, 2 = relu(product)
   const uint16_t* glu;     // G [M, ldglu] bf16 (act 1), 16-byte aligned rows
   int64_t ldglu;
+  // Split tail (bf16 C with 16-byte row stores only; tail_n 0: none): the
+  // first tail_full tiles of the list (a multiple of 256) run whole; each of
+  // the last tail_n runs as tail_split K ranges of tail_kchunk elements whose
+  // fp32 partials go to tail_part, summed in range order by
+  // tail_reduce_kernel.  So a part-filled last round keeps every CU busy.
+  int tail_full, tail_n, tail_split, tail_kchunk;
+  float* tail_part;        // [tail_n][tail_split][256 * BN], accumulator order
 };
 
 template <int BN, int BK>
@@ -331,8 +338,11 @@ constexpr int big_lds_bytes() {
 // over 256 / (32 * MBW) x 2 waves: MBW = 4 gives 4 waves of 128 x BN/2 (one
 // wave per SIMD, 512 registers), MBW = 2 gives 8 waves of 64 x BN/2 (two
 // per SIMD, at most 256 registers each).
-template <int BN, int BK, int NS, bool OUT_F32, int HD, int MBW>
+// TAIL: the launch has a split tail (a separate instance, so that launches
+// without one keep the plain tile mapping and its register count).
+template <int BN, int BK, int NS, bool OUT_F32, int HD, int MBW, bool TAIL = false>
 __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(BigArgs p) {
+  static_assert(!TAIL || (!OUT_F32 && HD == 0), "split tails: bf16 output, no rotary");
   static_assert(HD == 0 || (BN == 256 && !OUT_F32 && (HD == 64 || HD == 128)), "rotary tiles");
   static_assert((BK == 32 || BK == 64) && NS >= 2, "pipeline shape");
   static_assert(MBW == 2 || MBW == 4, "wave tile");
@@ -348,14 +358,33 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
     const int nv = *p.m_valid;
     M = nv < 0 ? 0 : (nv > p.M ? p.M : nv);
   }
-  const int ntn = (p.N + BN - 1) / BN, ntiles = ntn * ((M + gBM - 1) / gBM) * p.ksplit;
-  const int per_xcd = (ntiles + 7) / 8;
-  const int vtile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;  // (tile, K range)
-  if ((int)blockIdx.x / 8 >= per_xcd || vtile >= ntiles) return;
-  const int tile = group_rows(vtile / p.ksplit, ntn, (M + gBM - 1) / gBM);
-  const int kr = vtile % p.ksplit;
+  const int ntn = (p.N + BN - 1) / BN, ntm = (M + gBM - 1) / gBM;
+  int vt, kr, kc = p.kchunk;  // list position of the tile, its K range and range length
+  bool tail_unit = false;     // a K range of a split-tail tile: fp32 partial out
+  if constexpr (!TAIL) {
+    const int ntiles = ntn * ntm * p.ksplit;
+    const int per_xcd = (ntiles + 7) / 8;
+    const int v = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;  // (tile, K range)
+    if ((int)blockIdx.x / 8 >= per_xcd || v >= ntiles) return;
+    vt = v / p.ksplit;
+    kr = v % p.ksplit;
+  } else if ((int)blockIdx.x < p.tail_full) {
+    // the whole tiles in XCD runs as above (tail_full is a multiple of 8)
+    const int per_xcd = p.tail_full / 8;
+    vt = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    kr = 0;
+  } else {
+    // then range kr of every tail tile, range by range (dispatched last)
+    const int j = (int)blockIdx.x - p.tail_full;
+    if (j >= p.tail_n * p.tail_split) return;
+    vt = p.tail_full + j % p.tail_n;
+    kr = j / p.tail_n;
+    kc = p.tail_kchunk;
+    tail_unit = true;
+  }
+  const int tile = group_rows(vt, ntn, ntm);
   const int m0 = (tile / ntn) * gBM, n0 = (tile % ntn) * BN;
-  const int kbeg = kr * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
+  const int kbeg = kr * kc, kend = min(p.K, kbeg + kc);
   const __amdgpu_buffer_rsrc_t ra =
       make_rsrc(p.a + (int64_t)m0 * p.lda, view_bytes(min(M - m0, gBM), p.K, p.lda));
   const __amdgpu_buffer_rsrc_t rb =
@@ -438,6 +467,24 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
   k_tile(nk - 1, std::false_type{});
   lds_barrier();
   // (the barrier above: operand tiles dead, the epilogue may reuse the LDS)
+  if constexpr (TAIL) {
+    if (tail_unit) {
+      // this range's partial in accumulator order, 16 bytes per lane: slot
+      // ((wave, i, j, q), lane) holds acc[i][j][4q .. 4q + 3]
+      f32x4* dst = reinterpret_cast<f32x4*>(
+          p.tail_part + ((int64_t)(vt - p.tail_full) * p.tail_split + kr) * (gBM * BN));
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int j = 0; j < MBW; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dst[((wave * NBW * MBW + i * MBW + j) * 4 + q) * 64 + lane] =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                      acc[i][j][4 * q + 3]};
+      return;
+    }
+  }
 
   // acc[i][j] reg r -> n = wn + 32i + 8(r/4) + 4(lane/32) + r%4, m = wm + 32j + lane%32
   if constexpr (HD > 0) {
@@ -543,6 +590,39 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
         }
       }
     }
+}
+
+// One workgroup per split-tail tile (the tile's thread layout): its K-range
+// partials summed in range order, then the bf16 epilogue of gemm_big_kernel.
+template <int BN, int MBW>
+__global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void tail_reduce_kernel(BigArgs p) {
+  constexpr int NBW = BN / 64;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntn = (p.N + BN - 1) / BN, ntm = (p.M + gBM - 1) / gBM;
+  const int vt = p.tail_full + (int)blockIdx.x;
+  const int tile = group_rows(vt, ntn, ntm);
+  const int m0 = (tile / ntn) * gBM, n0 = (tile % ntn) * BN;
+  const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
+  const f32x4* src =
+      reinterpret_cast<const f32x4*>(p.tail_part + (int64_t)blockIdx.x * p.tail_split * (gBM * BN));
+  f32x16 acc[NBW][MBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i)
+#pragma unroll
+    for (int j = 0; j < MBW; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = ((wave * NBW * MBW + i * MBW + j) * 4 + q) * 64 + lane;
+        f32x4 v = src[e];
+        for (int k = 1; k < p.tail_split; ++k) v += src[(int64_t)k * (gBM * BN / 4) + e];
+        acc[i][j][4 * q] = v.x;
+        acc[i][j][4 * q + 1] = v.y;
+        acc[i][j][4 * q + 2] = v.z;
+        acc[i][j][4 * q + 3] = v.w;
+      }
+  store_staged<BN, MBW>(acc, static_cast<uint16_t*>(p.c), p.ldc, m0 + wm, n0 + wn, p.M, p.N,
+                        smem, wave, lane);
 }
 
 // Persistent variant (bf16 output, 16-byte row stores, no rotary): one
@@ -692,7 +772,7 @@ hipError_t launch_persist(const BigArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BN, bool OUT_F32, int HD = 0>
+template <int BN, bool OUT_F32, int HD = 0, bool TAIL = false>
 hipError_t launch_big(const BigArgs& a, hipStream_t st) {
   constexpr int kBK = kBigBK, kNS = big_ns<BN>();
   constexpr int lds = big_lds_bytes<BN, kBK, kNS, HD>();
@@ -700,13 +780,31 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW>),
+        reinterpret_cast<const void*>(&gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW, TAIL>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + gBM - 1) / gBM) * a.ksplit;
-  hipLaunchKernelGGL((gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW>),
-                     dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(2 * gBM / (32 * gMBW) * 64), lds,
+  const int grid = TAIL ? a.tail_full + a.tail_n * a.tail_split : tiles;
+  hipLaunchKernelGGL((gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW, TAIL>),
+                     dim3((unsigned)((grid + 7) / 8 * 8)), dim3(2 * gBM / (32 * gMBW) * 64), lds,
                      st, a);
+  return hipGetLastError();
+}
+
+// gemm_big_kernel with a split tail (bf16 C, 16-byte row stores), then the
+// tail's reduction.
+template <int BN>
+hipError_t launch_big_tail(const BigArgs& a, hipStream_t st) {
+  constexpr int lds = gBM * BN * 2;  // the bf16 staging of store_staged
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tail_reduce_kernel<BN, gMBW>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  });
+  hipError_t e = launch_big<BN, false, 0, true>(a, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((tail_reduce_kernel<BN, gMBW>), dim3((unsigned)a.tail_n),
+                     dim3(2 * gBM / (32 * gMBW) * 64), lds, st, a);
   return hipGetLastError();
 }
 
@@ -1305,6 +1403,48 @@ double tile_efficiency(int M, int N, int BN) {
   return (double)tiles / (rounds * 256) * ((double)N / (((N + BN - 1) / BN) * BN));
 }
 
+// Split tail of a launch of BN-wide tiles: past at least one whole round of
+// 256 tiles, a last round holding at most 128 tiles splits each of them into
+// up to 4 K ranges (as many as the idle CUs allow), so that round keeps
+// every CU busy for a fraction of a tile's time.  n == 0: no split.
+struct TailPlan {
+  int full = 0, n = 0, split = 1, kchunk = 0;
+};
+TailPlan tail_plan(int64_t M, int64_t N, int64_t K, int BN) {
+  TailPlan t;
+  const int64_t tiles = ((N + BN - 1) / BN) * ((M + gBM - 1) / gBM);
+  const int64_t rem = tiles % 256;
+  if (tiles < 256 || rem == 0 || rem > 128 || tiles > (int64_t(1) << 30)) return t;
+  const int64_t ways = std::min<int64_t>(4, 256 / rem), nkt = (K + kBigBK - 1) / kBigBK;
+  const int64_t kchunk = (nkt + ways - 1) / ways * kBigBK;
+  const int64_t split = (K + kchunk - 1) / kchunk;
+  if (split < 2) return t;
+  t.full = (int)(tiles - rem);
+  t.n = (int)rem;
+  t.split = (int)split;
+  t.kchunk = (int)kchunk;
+  return t;
+}
+size_t tail_bytes(const TailPlan& t, int BN) { return (size_t)t.n * t.split * gBM * BN * 4; }
+
+// Time of one round of 256 whole tiles (one per CU) of K depth, measured on
+// MI355X (bf16, 64-deep k-tiles): 6 + 25 K/1024 us at BN 256, 4 + 15.3 K/1024
+// at BN 128.  A split tail costs its units' round plus the partials' round
+// trip, (0.49 + 0.27 K/4096) us per MB (fitted to 1194- and 597-column stage-1
+// launches of 16384 rows at K = 4096 and 11008).
+double round_us(int BN, int64_t K) {
+  return BN == 256 ? 6.0 + 25.0 * K / 1024 : 4.0 + 15.3 * K / 1024;
+}
+double plain_us(int64_t M, int64_t N, int64_t K, int BN) {
+  const int64_t tiles = ((N + BN - 1) / BN) * ((M + gBM - 1) / gBM);
+  return (double)((tiles + 255) / 256) * round_us(BN, K);
+}
+double tail_us(const TailPlan& t, int BN, int64_t K) {
+  const double mb = tail_bytes(t, BN) / 1e6;
+  return t.full / 256 * round_us(BN, K) + round_us(BN, t.kchunk) +
+         mb * (0.49 + 0.27 * K / 4096.0);
+}
+
 }  // namespace
 
 bool gemm_big_supported(int64_t lda, int64_t ldb) {
@@ -1312,14 +1452,45 @@ bool gemm_big_supported(int64_t lda, int64_t ldb) {
   return lda < (int64_t(1) << 22) && ldb < (int64_t(1) << 22) && lda % 8 == 0 && ldb % 8 == 0;
 }
 
+size_t gemm_tail_bytes(int64_t M, int64_t N) {
+  // K only sets how many ranges a tail tile takes (at most 4): size for 4
+  const int64_t kmax = int64_t(1) << 30;
+  return std::max(tail_bytes(tail_plan(M, N, kmax, 256), 256),
+                  tail_bytes(tail_plan(M, N, kmax, 128), 128));
+}
+
 hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                        int64_t ldc, bool c_f32, uint16_t* C2, int64_t ldc2, int64_t M,
-                       int64_t N, int64_t K, hipStream_t st) {
+                       int64_t N, int64_t K, hipStream_t st, float* part, size_t part_bytes) {
   BigArgs a{static_cast<const uint16_t*>(A), lda, static_cast<const uint16_t*>(B), ldb, C, ldc,
             C2, ldc2, (int)M, (int)N, (int)K, store_width(C, ldc, c_f32 ? 4 : 2),
             nullptr, nullptr, 0, nullptr, 0, 1, (int)K, 0};
   const bool narrow = tile_efficiency((int)M, (int)N, 128) > tile_efficiency((int)M, (int)N, 256) + 0.05;
   if (c_f32) return narrow ? launch_big<128, true>(a, st) : launch_big<256, true>(a, st);
+  if (part && a.vec == 2) {
+    // a split tail where the time estimates give it a clear edge
+    double best = plain_us(M, N, K, narrow ? 128 : 256);
+    int bn = 0;
+    TailPlan use;
+    for (const int cand : {256, 128}) {
+      const TailPlan t = tail_plan(M, N, K, cand);
+      if (t.n == 0 || tail_bytes(t, cand) > part_bytes) continue;
+      const double us = tail_us(t, cand, K);
+      if (us < 0.97 * best) {
+        best = us;
+        bn = cand;
+        use = t;
+      }
+    }
+    if (bn) {
+      a.tail_full = use.full;
+      a.tail_n = use.n;
+      a.tail_split = use.split;
+      a.tail_kchunk = use.kchunk;
+      a.tail_part = part;
+      return bn == 128 ? launch_big_tail<128>(a, st) : launch_big_tail<256>(a, st);
+    }
+  }
   return narrow ? launch_big<128, false>(a, st) : launch_big<256, false>(a, st);
 }
 

@@ -333,16 +333,23 @@ static bool fused_fits(int64_t r) { return fused_lds_bytes(r) <= (size_t)kLdsMax
 // far closer to their peak than the fused kernel's 64-row tiles.
 constexpr int64_t kBigT = 1024;
 
+// fp32 scratch after t on the large-tile path: the partials of a stage 1
+// that splits d_in, or of either stage's split tail (one at a time).
+static size_t big_part_bytes(int64_t T, int64_t r, int64_t d_out) {
+  return std::max({gemm_split_bytes(T, r), gemm_tail_bytes(T, r), gemm_tail_bytes(T, d_out)});
+}
+
 // Calls from kBigT rows on, and calls whose rank tile does not fit on chip,
 // park t in the workspace as bf16 [T, round_up(r, 8)], past the decode
 // path's control area; the fused kernel needs none.  From kBigT rows on, a
-// stage 1 with too few tiles to fill the chip splits its d_in range: the
-// fp32 partials follow t.
+// stage 1 with too few tiles to fill the chip splits its d_in range, and a
+// stage whose last round of tiles is part-filled may split that round's
+// tiles over K: the fp32 partials follow t.
 size_t prefill_workspace_bytes(int64_t T, int64_t r, int64_t d_out) {
   (void)d_out;
   if (T < kBigT && fused_fits(r)) return 0;
   const size_t tb = (size_t)rup(T * rup(r, 8) * 2, 256);
-  return kCtlAreaBytes + (T >= kBigT ? tb + gemm_split_bytes(T, r) : tb);
+  return kCtlAreaBytes + (T >= kBigT ? tb + big_part_bytes(T, r, d_out) : tb);
 }
 
 // Where t starts in a workspace (the control area's words are never touched).
@@ -369,18 +376,19 @@ __global__ void to_bf16_kernel(const float* src, int64_t lds, uint16_t* dst, int
 hipError_t prefill_big(const DecodeLinear& d, hipStream_t st) {
   const int64_t ldtb = rup(d.r, 8);
   uint16_t* tws = parked_t(d.workspace);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(tws) + rup(d.T * ldtb * 2, 256));
+  const size_t part_bytes = big_part_bytes(d.T, d.r, d.d_out);
   hipError_t e = hipSuccess;
   if (d.flags != 2) {
     if (gemm_split_ranges(d.T, d.r, d.d_in) > 1) {
-      float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(tws) +
-                                             rup(d.T * ldtb * 2, 256));
       e = gemm_nt_big_split(d.x, d.ldx, d.Ut, d.ldu, part, d.t_io, d.ldt,
                             d.t_io && d.flags == 1 ? nullptr : tws, ldtb, d.T, d.r, d.d_in, st);
     } else if (d.t_io)
       e = gemm_nt_big(d.x, d.ldx, d.Ut, d.ldu, d.t_io, d.ldt, true, d.flags == 1 ? nullptr : tws,
                       ldtb, d.T, d.r, d.d_in, st);
     else
-      e = gemm_nt_big(d.x, d.ldx, d.Ut, d.ldu, tws, ldtb, false, nullptr, 0, d.T, d.r, d.d_in, st);
+      e = gemm_nt_big(d.x, d.ldx, d.Ut, d.ldu, tws, ldtb, false, nullptr, 0, d.T, d.r, d.d_in, st,
+                      part, part_bytes);
     if (e != hipSuccess || d.flags == 1) return e;
   } else {
     const int64_t n = d.T * d.r;
@@ -394,7 +402,8 @@ hipError_t prefill_big(const DecodeLinear& d, hipStream_t st) {
   if (d.act)
     return gemm_nt_big_act(tws, ldtb, d.Vt, d.ldv, static_cast<uint16_t*>(d.y), d.ldy, d.act,
                            static_cast<const uint16_t*>(d.glu), d.ldglu, d.T, d.d_out, d.r, st);
-  return gemm_nt_big(tws, ldtb, d.Vt, d.ldv, d.y, d.ldy, false, nullptr, 0, d.T, d.d_out, d.r, st);
+  return gemm_nt_big(tws, ldtb, d.Vt, d.ldv, d.y, d.ldy, false, nullptr, 0, d.T, d.d_out, d.r, st,
+                     part, part_bytes);
 }
 
 }  // namespace

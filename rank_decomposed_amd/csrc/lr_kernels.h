@@ -79,9 +79,15 @@ hipError_t decode_group_bf16(const DecodeLinear* ds, int n, hipStream_t st);
 // accumulation; C bf16, or fp32 with an optional bf16 copy C2.  256-row
 // tiles on MFMA 32x32x16 (many-token shapes).
 bool gemm_big_supported(int64_t lda, int64_t ldb);
+// part (optional, part_bytes): fp32 scratch that lets a bf16 launch whose
+// last round of tiles is part-filled split that round's tiles over K (see
+// gemm_tail_bytes); a launch that does not fit it runs unsplit.
 hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                        int64_t ldc, bool c_f32, uint16_t* C2, int64_t ldc2, int64_t M,
-                       int64_t N, int64_t K, hipStream_t st);
+                       int64_t N, int64_t K, hipStream_t st, float* part = nullptr,
+                       size_t part_bytes = 0);
+// Scratch for the split tail of any bf16 gemm_nt_big of this M, N.
+size_t gemm_tail_bytes(int64_t M, int64_t N);
 // C (bf16, 16-byte aligned rows) = act(A . B^T): act 1 = silu(G) * (A . B^T)
 // with G bf16 [M, ldg] (16-byte aligned rows), act 2 = relu(A . B^T); the
 // product is rounded to bf16 before the activation.

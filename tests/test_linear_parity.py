@@ -120,6 +120,43 @@ def test_bf16_prefill_split_k(T, shape):
     assert np.array_equal(bits(y_t), bits(y))
 
 
+@pytest.mark.parametrize("T,shape", [(5000, (8200, 3300, 3400)), (5000, (8200, 1600, 1700))])
+def test_bf16_prefill_split_tail(T, shape):
+    # launches whose last round of 256-row tiles is part-filled split that
+    # round's tiles over K (fp32 partials summed in range order by a second
+    # kernel): 260 tiles of 256 x 256 in stage 1 and 280 in stage 2 of the
+    # first shape, 260 of 256 x 128 in stage 1 of the second, with ragged
+    # rows (5000), ragged columns (3300, 3400, 1600) and a ragged last k-tile
+    # in the last of four 2112-deep ranges (d_in 8200).  Every output element
+    # is written once (y starts as NaN); seeded rows, the first and the last
+    # included, against the oracle; a repeat call and a graph replay give the
+    # same bits.
+    d_in, r, d_out = shape
+    c = make_linear(3600 + r, T, d_in, r, d_out, "bf16", fast=True, ld_extra=8)
+    y = torch.full((T, d_out), float("nan"), dtype=torch.bfloat16, device=dev())
+    ws = torch.zeros(lr.lowrank_workspace_bytes(0, lr.LR_BF16, T, d_in, r, d_out),
+                     dtype=torch.uint8, device=dev())
+    lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"], y=y, workspace=ws)
+    y2 = lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"], workspace=ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y.float()).any()
+    assert np.array_equal(bits(y), bits(y2))
+    rows = np.sort(np.random.default_rng(3600 + r).choice(T, 200, replace=False))
+    rows[0], rows[-1] = 0, T - 1
+    _, yr = oracle.linear(c["x"][rows], c["U"], c["V"])
+    assert maxrel(to_f64(y)[rows], yr) <= BF16_TOL
+    y3 = torch.full_like(y, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lr.lowrank_linear_forward(c["dx"], c["dUt"], c["dVt"], y=y3, workspace=ws)
+    for rep in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y3), bits(y)), rep
+        y3.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("T", [5, 24, 64, 200, 1100])
 @pytest.mark.parametrize("shape", [(640, 96, 320), (650, 100, 330)])
 def test_bf16_stage_flags(T, shape):
