@@ -87,6 +87,72 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
+// The same per row for rows of whole 4-element groups (the vec case above):
+// one wave per row with the row held in registers, NV 16-byte chunks per
+// lane, all of a lane's loads in flight at once and h read once.  Each
+// lane's squares fold in the order of rmsnorm_kernel's threads.
+template <int NV>
+__global__ __launch_bounds__(256) void rmsnorm_wave_kernel(const float* __restrict__ h,
+                                                           int64_t ldh,
+                                                           const uint16_t* __restrict__ g,
+                                                           uint16_t* __restrict__ x, int64_t ldx,
+                                                           int rows, int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int b = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (b >= rows) return;
+  const f32x4* row = reinterpret_cast<const f32x4*>(h + (int64_t)b * ldh);
+  const int nc = d / 4;
+  f32x4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < nc ? row[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    ss = fmaf(v[i].x, v[i].x, fmaf(v[i].y, v[i].y, fmaf(v[i].z, v[i].z, fmaf(v[i].w, v[i].w, ss))));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float scale = 1.0f / sqrtf(ss / (float)d + eps);
+  const u32x2* gw = reinterpret_cast<const u32x2*>(g);
+  u32x2* out = reinterpret_cast<u32x2*>(x + (int64_t)b * ldx);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nc) break;
+    const u32x2 w = gw[c];
+    out[c] = u32x2{pack_bf2(v[i].x * scale * bf2f(w.x & 0xffffu), v[i].y * scale * bf2f(w.x >> 16)),
+                   pack_bf2(v[i].z * scale * bf2f(w.y & 0xffffu), v[i].w * scale * bf2f(w.y >> 16))};
+  }
+}
+
+// RMSNorm of `rows` rows of h [rows, ldh] into x: the wave-per-row kernel
+// where a row fits its registers (d <= 8192, whole 4-element groups, aligned
+// rows), else one workgroup per row.
+hipError_t launch_rmsnorm(const float* h, int64_t ldh, const uint16_t* g, uint16_t* x,
+                          int64_t ldx, int64_t rows, int64_t d, float eps, hipStream_t st) {
+  const bool vec = (d & 3) == 0 && (ldh & 3) == 0 && (ldx & 3) == 0 &&
+                   (reinterpret_cast<uintptr_t>(h) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(x) & 7) == 0 &&
+                   (reinterpret_cast<uintptr_t>(g) & 7) == 0;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const int nv = (int)((d + 255) / 256);  // 16-byte chunks per lane
+  if (vec && nv <= 4)
+    hipLaunchKernelGGL(rmsnorm_wave_kernel<4>, grid, block, 0, st, h, ldh, g, x, ldx, (int)rows, (int)d, eps);
+  else if (vec && nv <= 8)
+    hipLaunchKernelGGL(rmsnorm_wave_kernel<8>, grid, block, 0, st, h, ldh, g, x, ldx, (int)rows, (int)d, eps);
+  else if (vec && nv <= 16)
+    hipLaunchKernelGGL(rmsnorm_wave_kernel<16>, grid, block, 0, st, h, ldh, g, x, ldx, (int)rows, (int)d, eps);
+  else if (vec && nv <= 24)
+    hipLaunchKernelGGL(rmsnorm_wave_kernel<24>, grid, block, 0, st, h, ldh, g, x, ldx, (int)rows, (int)d, eps);
+  else if (vec && nv <= 32)
+    hipLaunchKernelGGL(rmsnorm_wave_kernel<32>, grid, block, 0, st, h, ldh, g, x, ldx, (int)rows, (int)d, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)rows), block, 0, st, h, ldh, g, x, ldx, (int)d, eps);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- append
 // pool[slot[b], 0:r] = bf16(lat[b, 0:r]); out-of-range slots are skipped.
 __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ lat, int64_t ldl,
@@ -832,9 +898,7 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
   };
 
   // attention block
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, st, h, d,
-                     static_cast<const uint16_t*>(w->attn_norm), x, d, (int)d, w->eps);
-  LR_CHECK(hipGetLastError());
+  LR_CHECK(launch_rmsnorm(h, d, static_cast<const uint16_t*>(w->attn_norm), x, d, T, d, w->eps, st));
   {
     // q (full) and the k, v latents (stage 1 only) read the same x
     const DecodeLinear qkv[3] = {linear(0, x, d, d, dq, q, nullptr, nullptr),
@@ -960,9 +1024,7 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
   LR_CHECK(hipGetLastError());
   LR_CHECK(residual_linear(3, o, dq));
   // MLP block
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, st, h, d,
-                     static_cast<const uint16_t*>(w->ffn_norm), x, d, (int)d, w->eps);
-  LR_CHECK(hipGetLastError());
+  LR_CHECK(launch_rmsnorm(h, d, static_cast<const uint16_t*>(w->ffn_norm), x, d, T, d, w->eps, st));
   const dim3 egrid((unsigned)((T * ffn + 255) / 256 < 4096 ? (T * ffn + 255) / 256 : 4096));
   // on the large-tile prefill path the activation runs in the epilogue of
   // the last MLP GEMM (relu of fc1; silu(gate) * up in the up projection)
