@@ -592,37 +592,50 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
     }
 }
 
-// One workgroup per split-tail tile (the tile's thread layout): its K-range
-// partials summed in range order, then the bf16 epilogue of gemm_big_kernel.
+// Sum of the split tail's K-range partials, in range order, into bf16 C.
+// Entry e of a partial (accumulator order, 16 bytes: gemm_big_kernel's
+// wave, (i, j) block, register quad q and lane) is 4 consecutive columns of
+// one row.  Each thread takes 4 entries 256 apart with every range's loads in
+// flight at once; a block of 1024 entries never straddles two tiles.
 template <int BN, int MBW>
-__global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void tail_reduce_kernel(BigArgs p) {
-  constexpr int NBW = BN / 64;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) void tail_reduce_kernel(BigArgs p) {
+  constexpr int NBW = BN / 64, PER_TILE = gBM * BN / 4, CH = 4, MAXR = 4;
+  static_assert(PER_TILE % (256 * CH) == 0, "whole blocks per tile");
   const int ntn = (p.N + BN - 1) / BN, ntm = (p.M + gBM - 1) / gBM;
-  const int vt = p.tail_full + (int)blockIdx.x;
-  const int tile = group_rows(vt, ntn, ntm);
+  const int64_t first = (int64_t)blockIdx.x * (256 * CH);
+  const int tt = (int)(first / PER_TILE);  // tail tile of this block
+  const int tile = group_rows(p.tail_full + tt, ntn, ntm);
   const int m0 = (tile / ntn) * gBM, n0 = (tile % ntn) * BN;
-  const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
-  const f32x4* src =
-      reinterpret_cast<const f32x4*>(p.tail_part + (int64_t)blockIdx.x * p.tail_split * (gBM * BN));
-  f32x16 acc[NBW][MBW];
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.tail_part) + (int64_t)tt * p.tail_split * PER_TILE;
+  f32x4 v[CH][MAXR];
 #pragma unroll
-  for (int i = 0; i < NBW; ++i)
+  for (int c = 0; c < CH; ++c)
 #pragma unroll
-    for (int j = 0; j < MBW; ++j)
+    for (int k = 0; k < MAXR; ++k) {
+      const int e = (int)(first % PER_TILE) + c * 256 + (int)threadIdx.x;
+      v[c][k] = k < p.tail_split ? src[(int64_t)k * PER_TILE + e] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = ((wave * NBW * MBW + i * MBW + j) * 4 + q) * 64 + lane;
-        f32x4 v = src[e];
-        for (int k = 1; k < p.tail_split; ++k) v += src[(int64_t)k * (gBM * BN / 4) + e];
-        acc[i][j][4 * q] = v.x;
-        acc[i][j][4 * q + 1] = v.y;
-        acc[i][j][4 * q + 2] = v.z;
-        acc[i][j][4 * q + 3] = v.w;
-      }
-  store_staged<BN, MBW>(acc, static_cast<uint16_t*>(p.c), p.ldc, m0 + wm, n0 + wn, p.M, p.N,
-                        smem, wave, lane);
+  for (int c = 0; c < CH; ++c) {
+    f32x4 sum = v[c][0];
+#pragma unroll
+    for (int k = 1; k < MAXR; ++k)
+      if (k < p.tail_split) sum += v[c][k];
+    const int e = (int)(first % PER_TILE) + c * 256 + (int)threadIdx.x;
+    const int lane = e & 63, q = (e >> 6) & 3, ij = (e >> 8) % (NBW * MBW);
+    const int wave = (e >> 8) / (NBW * MBW), i = ij / MBW, j = ij % MBW;
+    const int m = m0 + (wave >> 1) * (32 * MBW) + 32 * j + (lane & 31);
+    const int n = n0 + (wave & 1) * (BN / 2) + 32 * i + 8 * q + 4 * (lane >> 5);
+    if (m >= p.M) continue;
+    uint16_t* c16 = static_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + n;
+    const u32x2 o{pack_bf2(sum.x, sum.y), pack_bf2(sum.z, sum.w)};
+    if (n + 3 < p.N) {
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(c16));
+    } else {
+      const uint32_t w[2] = {o.x, o.y};
+      for (int x = 0; x < 4 && n + x < p.N; ++x) c16[x] = (uint16_t)(w[x >> 1] >> (16 * (x & 1)));
+    }
+  }
 }
 
 // Persistent variant (bf16 output, 16-byte row stores, no rotary): one
@@ -795,16 +808,11 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
 // tail's reduction.
 template <int BN>
 hipError_t launch_big_tail(const BigArgs& a, hipStream_t st) {
-  constexpr int lds = gBM * BN * 2;  // the bf16 staging of store_staged
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tail_reduce_kernel<BN, gMBW>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  });
+  if (a.tail_split > 4) return hipErrorInvalidValue;  // tail_reduce_kernel sums up to 4
   hipError_t e = launch_big<BN, false, 0, true>(a, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((tail_reduce_kernel<BN, gMBW>), dim3((unsigned)a.tail_n),
-                     dim3(2 * gBM / (32 * gMBW) * 64), lds, st, a);
+  const unsigned blocks = (unsigned)((int64_t)a.tail_n * (gBM * BN / 4) / 1024);
+  hipLaunchKernelGGL((tail_reduce_kernel<BN, gMBW>), dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1430,8 +1438,8 @@ size_t tail_bytes(const TailPlan& t, int BN) { return (size_t)t.n * t.split * gB
 // Time of one round of 256 whole tiles (one per CU) of K depth, measured on
 // MI355X (bf16, 64-deep k-tiles): 6 + 25 K/1024 us at BN 256, 4 + 15.3 K/1024
 // at BN 128.  A split tail costs its units' round plus the partials' round
-// trip, (0.49 + 0.27 K/4096) us per MB (fitted to 1194- and 597-column stage-1
-// launches of 16384 rows at K = 4096 and 11008).
+// trip, (0.23 + 0.29 K/4096) us per MB (fitted to 1194- and 597-column stage-1
+// launches of 16384 rows at K = 4096 and 11008, and 9216 x 4096 x 4096).
 double round_us(int BN, int64_t K) {
   return BN == 256 ? 6.0 + 25.0 * K / 1024 : 4.0 + 15.3 * K / 1024;
 }
@@ -1442,7 +1450,7 @@ double plain_us(int64_t M, int64_t N, int64_t K, int BN) {
 double tail_us(const TailPlan& t, int BN, int64_t K) {
   const double mb = tail_bytes(t, BN) / 1e6;
   return t.full / 256 * round_us(BN, K) + round_us(BN, t.kchunk) +
-         mb * (0.49 + 0.27 * K / 4096.0);
+         mb * (0.23 + 0.29 * K / 4096.0);
 }
 
 }  // namespace
@@ -1476,7 +1484,7 @@ hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, v
       const TailPlan t = tail_plan(M, N, K, cand);
       if (t.n == 0 || tail_bytes(t, cand) > part_bytes) continue;
       const double us = tail_us(t, cand, K);
-      if (us < 0.97 * best) {
+      if (us < 0.95 * best) {
         best = us;
         bn = cand;
         use = t;
