@@ -669,13 +669,34 @@ __global__ __launch_bounds__(4 * HD) void fused_combine_kernel(
     const float* pb = part + ((int64_t)b * H + h) * pw;
     L = fmaf(expf(pb[0] - M), pb[1], L);
   }
-  for (int n = threadIdx.x; n < rv; n += blockDim.x) {
+  // vec[n] = sum over blocks, in block order, of exp(m_b - M) * s_b[n]: the
+  // weights of up to 64 blocks at a time in LDS, each thread's sums with
+  // four blocks' loads in flight
+  __shared__ float wb[64];
+  const float* ph = part + (int64_t)h * pw + 2;  // s_b[n] at ph[b * H * pw + n]
+  const int64_t bs = (int64_t)H * pw;
+  for (int n0 = 0; n0 < rv; n0 += blockDim.x) {
+    const int n = n0 + (int)threadIdx.x;
     float acc = 0.f;
-    for (int b = b0; b < b1; ++b) {
-      const float* pb = part + ((int64_t)b * H + h) * pw;
-      acc = fmaf(expf(pb[0] - M), pb[2 + n], acc);
+    for (int c0 = b0; c0 < b1; c0 += 64) {
+      const int nb = min(64, b1 - c0);
+      __syncthreads();  // the previous weights are consumed
+      if ((int)threadIdx.x < nb) wb[threadIdx.x] = expf(ph[(c0 + threadIdx.x) * bs - 2] - M);
+      __syncthreads();
+      if (n >= rv) continue;
+      const float* pc = ph + c0 * bs + n;
+      int j = 0;
+      for (; j + 4 <= nb; j += 4) {
+        const float x0 = pc[j * bs], x1 = pc[(j + 1) * bs], x2 = pc[(j + 2) * bs],
+                    x3 = pc[(j + 3) * bs];
+        acc = fmaf(wb[j], x0, acc);
+        acc = fmaf(wb[j + 1], x1, acc);
+        acc = fmaf(wb[j + 2], x2, acc);
+        acc = fmaf(wb[j + 3], x3, acc);
+      }
+      for (; j < nb; ++j) acc = fmaf(wb[j], pc[j * bs], acc);
     }
-    vec[n] = acc;
+    if (n < rv) vec[n] = acc;
   }
   __syncthreads();
   const int c = threadIdx.x >> 2, qtr = threadIdx.x & 3;
