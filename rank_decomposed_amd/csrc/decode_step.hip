@@ -650,7 +650,10 @@ __global__ void row_blocks_kernel(const int32_t* __restrict__ seq_off, int S, in
 // o[i, h] from the block partials of sequence i, each (m_b, l_b, w_b) with w_b
 // the block's p-weighted sum of V latent rows (r_v wide):
 //   o = (sum_b e^(m_b - M) w_b) V_v^T / sum_b e^(m_b - M) l_b
-// over the rows of kv head h / (H / Hkv) of V_v^T.  Thread t takes output
+// over the rows of kv head h / (H / Hkv) of V_v^T.  Up to 64 blocks at a
+// time, thread j takes block j: the maximum M by wave shuffles, the weights
+// e^(m_b - M) and the l_b into LDS, the sum L in block order; then each thread's
+// latent sums with four blocks' loads in flight.  Thread t then takes output
 // column t / 4 and every fourth 8-wide step of r_v (t % 4), summed by two
 // shuffles.  Blocks past nbpad (only from corrupt offsets) are skipped.
 template <int HD>
@@ -659,32 +662,39 @@ __global__ __launch_bounds__(4 * HD) void fused_combine_kernel(
     int nbpad, const uint16_t* __restrict__ vt, int64_t ldv, uint16_t* __restrict__ o,
     int64_t ldo) {
   extern __shared__ float vec[];  // [rv]
+  __shared__ float wb[64], wl[64];
+  __shared__ float msh[2];
   const int h = blockIdx.x, i = blockIdx.y, kvh = h / (H / Hkv);
   const int b0 = max(0, blk_off[i]), b1 = min(nbpad, blk_off[i + 1]);
-  const int64_t pw = rv + 2;
-  float M = -INFINITY;
-  for (int b = b0; b < b1; ++b) M = fmaxf(M, part[((int64_t)b * H + h) * pw]);
-  float L = 0.f;
-  for (int b = b0; b < b1; ++b) {
-    const float* pb = part + ((int64_t)b * H + h) * pw;
-    L = fmaf(expf(pb[0] - M), pb[1], L);
+  const int64_t pw = rv + 2, bs = (int64_t)H * pw;
+  const float* ph = part + (int64_t)h * pw;  // block b: m at ph[b * bs], l at + 1, sums from + 2
+  const int tid = (int)threadIdx.x;
+  // the maximum over the blocks (wave 0, 64 blocks per pass)
+  if (tid < 64) {
+    float M = -INFINITY;
+    for (int c0 = b0; c0 < b1; c0 += 64)
+      if (c0 + tid < b1) M = fmaxf(M, ph[(c0 + tid) * bs]);
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+    if (tid == 0) msh[0] = M;
   }
-  // vec[n] = sum over blocks, in block order, of exp(m_b - M) * s_b[n]: the
-  // weights of up to 64 blocks at a time in LDS, each thread's sums with
-  // four blocks' loads in flight
-  __shared__ float wb[64];
-  const float* ph = part + (int64_t)h * pw + 2;  // s_b[n] at ph[b * H * pw + n]
-  const int64_t bs = (int64_t)H * pw;
-  for (int n0 = 0; n0 < rv; n0 += blockDim.x) {
-    const int n = n0 + (int)threadIdx.x;
-    float acc = 0.f;
-    for (int c0 = b0; c0 < b1; c0 += 64) {
-      const int nb = min(64, b1 - c0);
-      __syncthreads();  // the previous weights are consumed
-      if ((int)threadIdx.x < nb) wb[threadIdx.x] = expf(ph[(c0 + threadIdx.x) * bs - 2] - M);
-      __syncthreads();
-      if (n >= rv) continue;
-      const float* pc = ph + c0 * bs + n;
+  __syncthreads();
+  const float M = msh[0];
+  float L = 0.f;  // thread 0's sum, in block order
+  float acc = 0.f;
+  const int n = tid;  // this thread's latent element (rv <= 4 * HD; larger rv: the loop below)
+  for (int c0 = b0; c0 < b1; c0 += 64) {
+    const int nb = min(64, b1 - c0);
+    __syncthreads();  // the previous weights are consumed
+    if (tid < nb) {
+      wb[tid] = expf(ph[(c0 + tid) * bs] - M);
+      wl[tid] = ph[(c0 + tid) * bs + 1];
+    }
+    __syncthreads();
+    if (tid == 0)
+      for (int j = 0; j < nb; ++j) L = fmaf(wb[j], wl[j], L);
+    if (n < rv) {
+      const float* pc = ph + c0 * bs + 2 + n;
       int j = 0;
       for (; j + 4 <= nb; j += 4) {
         const float x0 = pc[j * bs], x1 = pc[(j + 1) * bs], x2 = pc[(j + 2) * bs],
@@ -696,28 +706,169 @@ __global__ __launch_bounds__(4 * HD) void fused_combine_kernel(
       }
       for (; j < nb; ++j) acc = fmaf(wb[j], pc[j * bs], acc);
     }
-    if (n < rv) vec[n] = acc;
+    // latent elements past the block size (rv > 4 * HD), one block at a time
+    for (int n2 = n + (int)blockDim.x; n2 < rv; n2 += blockDim.x) {
+      float a2 = c0 == b0 ? 0.f : vec[n2];
+      for (int j = 0; j < nb; ++j) a2 = fmaf(wb[j], ph[(c0 + j) * bs + 2 + n2], a2);
+      vec[n2] = a2;
+    }
   }
+  if (n < rv) vec[n] = acc;
+  if (tid == 0) msh[1] = L;
   __syncthreads();
-  const int c = threadIdx.x >> 2, qtr = threadIdx.x & 3;
+  const int c = tid >> 2, qtr = tid & 3;
   const uint16_t* row = vt + (int64_t)(kvh * HD + c) * ldv;
-  float acc = 0.f;
-  for (int n = qtr * 8; n < rv; n += 32) {
-    if (n + 8 <= rv) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(row + n);
+  float ac = 0.f;
+#pragma unroll 4
+  for (int k = qtr * 8; k < rv; k += 32) {
+    if (k + 8 <= rv) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(row + k);
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc = fmaf(vec[n + 2 * e], bf2f(ww[e] & 0xffffu), acc);
-        acc = fmaf(vec[n + 2 * e + 1], bf2f(ww[e] >> 16), acc);
+        ac = fmaf(vec[k + 2 * e], bf2f(ww[e] & 0xffffu), ac);
+        ac = fmaf(vec[k + 2 * e + 1], bf2f(ww[e] >> 16), ac);
       }
     } else {
-      for (int e = n; e < rv; ++e) acc = fmaf(vec[e], bf2f(row[e]), acc);
+      for (int e = k; e < rv; ++e) ac = fmaf(vec[e], bf2f(row[e]), ac);
     }
   }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  if (qtr == 0) o[(int64_t)i * ldo + h * HD + c] = (uint16_t)f2bf(b1 > b0 ? acc / L : 0.f);
+  ac += __shfl_xor(ac, 1);
+  ac += __shfl_xor(ac, 2);
+  if (qtr == 0) o[(int64_t)i * ldo + h * HD + c] = (uint16_t)f2bf(b1 > b0 ? ac / msh[1] : 0.f);
+}
+
+// fused_combine_kernel for NS = 4 * HD / 64 consecutive sequences at once, one
+// wave each (sequence blockIdx.y * NS + wave), so the V_v rows of head h's kv
+// head are read once for all of them: each wave finds its sequence's maximum
+// by shuffles, puts the weights e^(m_b - M) and the l_b of up to 64 blocks at
+// a time in its LDS slots, sums L in block order (lane 0), and accumulates its
+// latent sums (lane: elements lane, lane + 64, ... of r_v, 8 at a time) with
+// four blocks' loads in flight per element; then every thread takes one
+// output column and quarter of r_v for every sequence (four steps of V_v in
+// flight).  Each sequence's sums follow
+// fused_combine_kernel's order, so both give the same bits.  The latent sums
+// take NS * round_up(rv, 4) * 4 bytes of LDS (rows of whole 16-byte chunks, so
+// the V_v step reads each sequence's 8 values as two 16-byte loads).
+template <int HD>
+__global__ __launch_bounds__(4 * HD) void fused_combine_group_kernel(
+    const float* __restrict__ part, int H, int Hkv, int rv, const int32_t* __restrict__ blk_off,
+    int nbpad, int S, const uint16_t* __restrict__ vt, int64_t ldv, uint16_t* __restrict__ o,
+    int64_t ldo) {
+  constexpr int NS = 4 * HD / 64;
+  extern __shared__ float vec[];  // [NS][ldv4]
+  const int ldv4 = (rv + 3) & ~3;
+  __shared__ float wb[NS][64], wl[NS][64], Ls[NS];
+  __shared__ int live[NS];
+  const int h = blockIdx.x, kvh = h / (H / Hkv);
+  const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int i0 = (int)blockIdx.y * NS, i = i0 + wv;
+  const int64_t pw = rv + 2, bs = (int64_t)H * pw;
+  const float* ph = part + (int64_t)h * pw;  // block b: m at ph[b * bs], l at + 1, sums from + 2
+  if (i < S) {
+    float* myv = vec + (int64_t)wv * ldv4;
+    const int b0 = max(0, blk_off[i]), b1 = min(nbpad, blk_off[i + 1]);
+    float M = -INFINITY;
+    for (int c0 = b0; c0 < b1; c0 += 64)
+      if (c0 + lane < b1) M = fmaxf(M, ph[(c0 + lane) * bs]);
+#pragma unroll
+    for (int sft = 32; sft > 0; sft >>= 1) M = fmaxf(M, __shfl_xor(M, sft));
+    float L = 0.f;
+    for (int c0 = b0; c0 < b1; c0 += 64) {
+      const int nb = min(64, b1 - c0);
+      if (lane < nb) {
+        wb[wv][lane] = expf(ph[(c0 + lane) * bs] - M);
+        wl[wv][lane] = ph[(c0 + lane) * bs + 1];
+      }
+      // the reads below take other lanes' writes: LDS runs one wave's accesses in order
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
+      if (lane == 0)
+        for (int j = 0; j < nb; ++j) L = fmaf(wb[wv][j], wl[wv][j], L);
+      const float* pc = ph + c0 * bs + 2;
+      for (int nc = 0; nc < rv; nc += 512) {
+        float acc[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int n = nc + 64 * k + lane;
+          acc[k] = c0 == b0 || n >= rv ? 0.f : myv[n];
+        }
+        int j = 0;
+        for (; j + 4 <= nb; j += 4) {
+          float x[4][8];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int n = nc + 64 * k + lane;
+              x[jj][k] = n < rv ? pc[(j + jj) * bs + n] : 0.f;
+            }
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = fmaf(wb[wv][j + jj], x[jj][k], acc[k]);
+        }
+        for (; j < nb; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int n = nc + 64 * k + lane;
+            acc[k] = fmaf(wb[wv][j], n < rv ? pc[j * bs + n] : 0.f, acc[k]);
+          }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int n = nc + 64 * k + lane;
+          if (n < rv) myv[n] = acc[k];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // this chunk's slots are read before the next overwrites them
+      asm volatile("" ::: "memory");
+    }
+    if (lane == 0) {
+      Ls[wv] = L;
+      live[wv] = b1 > b0;
+    }
+  }
+  __syncthreads();
+  const int c = tid >> 2, qtr = tid & 3;
+  const uint16_t* row = vt + (int64_t)(kvh * HD + c) * ldv;
+  const int ns = min(NS, S - i0);
+  float ac[NS];
+#pragma unroll
+  for (int si = 0; si < NS; ++si) ac[si] = 0.f;
+#pragma unroll 4
+  for (int k = qtr * 8; k < rv; k += 32) {
+    if (k + 8 <= rv) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(row + k);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int si = 0; si < NS; ++si) {
+        if (si >= ns) break;
+        const f32x4* v4 = reinterpret_cast<const f32x4*>(vec + (int64_t)si * ldv4 + k);
+        const f32x4 va = v4[0], vb = v4[1];
+        const float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ac[si] = fmaf(v[2 * e], bf2f(ww[e] & 0xffffu), ac[si]);
+          ac[si] = fmaf(v[2 * e + 1], bf2f(ww[e] >> 16), ac[si]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int si = 0; si < NS; ++si) {
+        if (si >= ns) break;
+        for (int e = k; e < rv; ++e) ac[si] = fmaf(vec[(int64_t)si * ldv4 + e], bf2f(row[e]), ac[si]);
+      }
+    }
+  }
+#pragma unroll
+  for (int si = 0; si < NS; ++si) {
+    if (si >= ns) break;
+    float a = ac[si];
+    a += __shfl_xor(a, 1);
+    a += __shfl_xor(a, 2);
+    if (qtr == 0)
+      o[(int64_t)(i0 + si) * ldo + h * HD + c] = (uint16_t)f2bf(live[si] ? a / Ls[si] : 0.f);
+  }
 }
 
 // ---------------------------------------------------------------- workspace
@@ -988,7 +1139,19 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
     LR_CHECK(attn_fused_decode(fa, (int)w->head_dim, st));
     const size_t vec_lds = (size_t)w->r[2] * 4;
     const uint16_t* vv = static_cast<const uint16_t*>(w->Vt[2]);
-    if (w->head_dim == 128)
+    // several sequences per workgroup where their latent sums fit 64 KB of LDS
+    const int gs = (int)(4 * w->head_dim / 64);
+    const size_t gvec = (size_t)gs * (size_t)rup(w->r[2], 4) * 4;
+    const dim3 ggrid((unsigned)w->n_heads, (unsigned)((S + gs - 1) / gs));
+    if (gvec <= 65536 && w->head_dim == 128)
+      hipLaunchKernelGGL(fused_combine_group_kernel<128>, ggrid, dim3(512), gvec, st, fpart,
+                         (int)w->n_heads, (int)w->n_kv_heads, (int)w->r[2], blk_off,
+                         (int)L.nbpad, S, vv, w->ldv[2], o, dq);
+    else if (gvec <= 65536)
+      hipLaunchKernelGGL(fused_combine_group_kernel<64>, ggrid, dim3(256), gvec, st, fpart,
+                         (int)w->n_heads, (int)w->n_kv_heads, (int)w->r[2], blk_off,
+                         (int)L.nbpad, S, vv, w->ldv[2], o, dq);
+    else if (w->head_dim == 128)
       hipLaunchKernelGGL(fused_combine_kernel<128>, dim3((unsigned)w->n_heads, (unsigned)S),
                          dim3(512), vec_lds, st, fpart, (int)w->n_heads, (int)w->n_kv_heads,
                          (int)w->r[2], blk_off, (int)L.nbpad, vv, w->ldv[2], o, dq);
