@@ -934,6 +934,13 @@ StepLayout step_layout(const lr_layer_weights* w, const StepIn& s, bool fused = 
     for (int k = 0; k < 7; ++k)
       if (!(k == 5 && w->mlp == LR_MLP_RELU))
         lin = std::max(lin, prefill_workspace_bytes(T, w->r[k], dout[k]));
+    // stage 1 of q, k, v (k, v: the latents only) and of gate, up as groups
+    DecodeLinear g[3];
+    for (int k = 0; k < 3; ++k) g[k] = DecodeLinear{T, din[k], w->r[k], dout[k]};
+    g[1].flags = g[2].flags = 1;
+    lin = std::max(lin, prefill_group_workspace_bytes(g, 3));
+    for (int k = 0; k < 2; ++k) g[k] = DecodeLinear{T, din[4 + k], w->r[4 + k], dout[4 + k]};
+    lin = std::max(lin, prefill_group_workspace_bytes(g, 2));
   }
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -1081,6 +1088,8 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
                                  linear(2, x, d, d, L.dkv, nullptr, nullptr, latv)};
     if (dec) {
       LR_CHECK(decode_group_bf16(qkv, 3, st));  // one launch
+    } else if (prefill_group_ok(qkv, 3)) {
+      LR_CHECK(prefill_group_bf16(qkv, 3, st));  // stage 1 as one launch
     } else {
       for (int k = 0; k < 3; ++k) LR_CHECK(prefill_linear_bf16(qkv[k], st));
     }
@@ -1236,8 +1245,13 @@ lr_status layer_step(const lr_layer_weights* w, const StepIn& s, float* h, void*
       LR_CHECK(decode_group_bf16(gu, 2, st));
       hipLaunchKernelGGL(silu_mul_kernel, egrid, dim3(256), 0, st, gate, up, m, (int64_t)T * ffn);
     } else if (prefill_act_ok(upm)) {
-      LR_CHECK(prefill_linear_bf16(gu[0], st));
-      LR_CHECK(prefill_linear_bf16(upm, st));
+      const DecodeLinear gup[2] = {gu[0], upm};
+      if (prefill_group_ok(gup, 2)) {
+        LR_CHECK(prefill_group_bf16(gup, 2, st));  // stage 1 as one launch; gate's y, then up's
+      } else {
+        LR_CHECK(prefill_linear_bf16(gu[0], st));
+        LR_CHECK(prefill_linear_bf16(upm, st));
+      }
     } else {
       LR_CHECK(prefill_linear_bf16(gu[0], st));
       LR_CHECK(prefill_linear_bf16(gu[1], st));

@@ -304,6 +304,20 @@ struct BigArgs {
   // tail_reduce_kernel.  So a part-filled last round keeps every CU busy.
   int tail_full, tail_n, tail_split, tail_kchunk;
   float* tail_part;        // [tail_n][tail_split][256 * BN], accumulator order
+  // Grouped launch (GROUP instances, fp32 C): gnum members side by side in N,
+  // member i over column tiles [gct[i], gct[i + 1]) with its own B rows (gb,
+  // gldb), C (gc, gldc), optional bf16 copy (gc2, gldc2) and width gn; b, ldb,
+  // c, ldc, c2, ldc2 and N above are not used.
+  int gnum;
+  int gct[kMaxGemmGroup + 1];
+  const uint16_t* gb[kMaxGemmGroup];
+  int64_t gldb[kMaxGemmGroup];
+  float* gc[kMaxGemmGroup];
+  int64_t gldc[kMaxGemmGroup];
+  uint16_t* gc2[kMaxGemmGroup];
+  int64_t gldc2[kMaxGemmGroup];
+  int gn[kMaxGemmGroup];
+  int gvec[kMaxGemmGroup];  // each member's store width (as vec)
 };
 
 template <int BN, int BK>
@@ -339,10 +353,13 @@ constexpr int big_lds_bytes() {
 // wave per SIMD, 512 registers), MBW = 2 gives 8 waves of 64 x BN/2 (two
 // per SIMD, at most 256 registers each).
 // TAIL: the launch has a split tail (a separate instance, so that launches
-// without one keep the plain tile mapping and its register count).
-template <int BN, int BK, int NS, bool OUT_F32, int HD, int MBW, bool TAIL = false>
+// without one keep the plain tile mapping and its register count).  GROUP:
+// a grouped launch (the member table of BigArgs).
+template <int BN, int BK, int NS, bool OUT_F32, int HD, int MBW, bool TAIL = false,
+          bool GROUP = false>
 __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(BigArgs p) {
   static_assert(!TAIL || (!OUT_F32 && HD == 0), "split tails: bf16 output, no rotary");
+  static_assert(!GROUP || (OUT_F32 && HD == 0 && !TAIL), "grouped launches: fp32 output");
   static_assert(HD == 0 || (BN == 256 && !OUT_F32 && (HD == 64 || HD == 128)), "rotary tiles");
   static_assert((BK == 32 || BK == 64) && NS >= 2, "pipeline shape");
   static_assert(MBW == 2 || MBW == 4, "wave tile");
@@ -358,7 +375,7 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
     const int nv = *p.m_valid;
     M = nv < 0 ? 0 : (nv > p.M ? p.M : nv);
   }
-  const int ntn = (p.N + BN - 1) / BN, ntm = (M + gBM - 1) / gBM;
+  const int ntn = GROUP ? p.gct[p.gnum] : (p.N + BN - 1) / BN, ntm = (M + gBM - 1) / gBM;
   int vt, kr, kc = p.kchunk;  // list position of the tile, its K range and range length
   bool tail_unit = false;     // a K range of a split-tail tile: fp32 partial out
   if constexpr (!TAIL) {
@@ -383,12 +400,33 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
     tail_unit = true;
   }
   const int tile = group_rows(vt, ntn, ntm);
-  const int m0 = (tile / ntn) * gBM, n0 = (tile % ntn) * BN;
+  const int m0 = (tile / ntn) * gBM;
+  int n0 = (tile % ntn) * BN;  // first column of the tile (within its member's)
+  // the operand and outputs of the tile (its member's in a grouped launch)
+  const uint16_t* pb = p.b;
+  int64_t ldb = p.ldb, ldc = p.ldc, ldc2 = p.ldc2;
+  int N = p.N, vec = p.vec;
+  void* pc = p.c;
+  uint16_t* pc2 = p.c2;
+  if constexpr (GROUP) {
+    const int ct = tile % ntn;
+    int mi = 0;
+    while (mi + 1 < p.gnum && ct >= p.gct[mi + 1]) ++mi;
+    n0 = (ct - p.gct[mi]) * BN;
+    pb = p.gb[mi];
+    ldb = p.gldb[mi];
+    N = p.gn[mi];
+    pc = p.gc[mi];
+    ldc = p.gldc[mi];
+    pc2 = p.gc2[mi];
+    ldc2 = p.gldc2[mi];
+    vec = p.gvec[mi];
+  }
   const int kbeg = kr * kc, kend = min(p.K, kbeg + kc);
   const __amdgpu_buffer_rsrc_t ra =
       make_rsrc(p.a + (int64_t)m0 * p.lda, view_bytes(min(M - m0, gBM), p.K, p.lda));
   const __amdgpu_buffer_rsrc_t rb =
-      make_rsrc(p.b + (int64_t)n0 * p.ldb, view_bytes(min(p.N - n0, BN), p.K, p.ldb));
+      make_rsrc(pb + (int64_t)n0 * ldb, view_bytes(min(N - n0, BN), p.K, ldb));
   const int wm = (wave >> 1) * (32 * MBW), wn = (wave & 1) * (BN / 2);
   const int nk = (kend - kbeg + BK - 1) / BK;
 
@@ -405,7 +443,7 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
     uint8_t* st = smem + (t % NS) * kStage;
     const int k0 = kbeg + t * BK;
     load_tile<gBM, BK, NW>(ra, p.lda, k0, kend - k0, st, wave, lane);
-    load_tile<BN, BK, NW>(rb, p.ldb, k0, kend - k0, st + kTileA, wave, lane);
+    load_tile<BN, BK, NW>(rb, ldb, k0, kend - k0, st + kTileA, wave, lane);
   };
   // k-tile t's loads are done once at most the stages issued after it are
   // pending (`younger` of them; vector-memory loads complete in order)
@@ -542,8 +580,8 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
     }
     lds_barrier();  // tables dead before the epilogue reuses the LDS
   }
-  if (!OUT_F32 && p.vec == 2) {
-    store_staged<BN, MBW>(acc, static_cast<uint16_t*>(p.c), p.ldc, m0 + wm, n0 + wn, M, p.N,
+  if (!OUT_F32 && vec == 2) {
+    store_staged<BN, MBW>(acc, static_cast<uint16_t*>(pc), ldc, m0 + wm, n0 + wn, M, N,
                           smem, wave, lane, HD > 0 ? 0 : p.act, p.glu, p.ldglu);
     return;
   }
@@ -559,33 +597,33 @@ __global__ __launch_bounds__(2 * 256 / (32 * MBW) * 64) void gemm_big_kernel(Big
         const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
         const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
         if (OUT_F32) {
-          float* c = static_cast<float*>(p.c) + kr * p.split_stride + (int64_t)m * p.ldc + n;
-          uint16_t* c2 = p.c2 ? p.c2 + (int64_t)m * p.ldc2 + n : nullptr;
+          float* c = static_cast<float*>(pc) + kr * p.split_stride + (int64_t)m * ldc + n;
+          uint16_t* c2 = pc2 ? pc2 + (int64_t)m * ldc2 + n : nullptr;
           if (p.accum) {
             const float v[4] = {v0, v1, v2, v3};
-            if (p.vec == 2 && n + 3 < p.N) {
+            if (vec == 2 && n + 3 < N) {
               const f32x4 o = *reinterpret_cast<const f32x4*>(c);
               *reinterpret_cast<f32x4*>(c) = f32x4{o.x + v0, o.y + v1, o.z + v2, o.w + v3};
             } else {
-              for (int e = 0; e < 4 && n + e < p.N; ++e) c[e] += v[e];
+              for (int e = 0; e < 4 && n + e < N; ++e) c[e] += v[e];
             }
-          } else if (p.vec == 2 && n + 3 < p.N) {
+          } else if (vec == 2 && n + 3 < N) {
             *reinterpret_cast<f32x4*>(c) = f32x4{v0, v1, v2, v3};
             if (c2) *reinterpret_cast<u32x2*>(c2) = u32x2{pack_bf2(v0, v1), pack_bf2(v2, v3)};
           } else {
             const float v[4] = {v0, v1, v2, v3};
-            for (int e = 0; e < 4 && n + e < p.N; ++e) {
+            for (int e = 0; e < 4 && n + e < N; ++e) {
               c[e] = v[e];
               if (c2) c2[e] = (uint16_t)f2bf(v[e]);
             }
           }
         } else {
-          uint16_t* c = static_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + n;
-          if (p.vec >= 1 && n + 3 < p.N) {
+          uint16_t* c = static_cast<uint16_t*>(pc) + (int64_t)m * ldc + n;
+          if (vec >= 1 && n + 3 < N) {
             *reinterpret_cast<u32x2*>(c) = u32x2{pack_bf2(v0, v1), pack_bf2(v2, v3)};
           } else {
             const float v[4] = {v0, v1, v2, v3};
-            for (int e = 0; e < 4 && n + e < p.N; ++e) c[e] = (uint16_t)f2bf(v[e]);
+            for (int e = 0; e < 4 && n + e < N; ++e) c[e] = (uint16_t)f2bf(v[e]);
           }
         }
       }
@@ -785,7 +823,7 @@ hipError_t launch_persist(const BigArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BN, bool OUT_F32, int HD = 0, bool TAIL = false>
+template <int BN, bool OUT_F32, int HD = 0, bool TAIL = false, bool GROUP = false>
 hipError_t launch_big(const BigArgs& a, hipStream_t st) {
   constexpr int kBK = kBigBK, kNS = big_ns<BN>();
   constexpr int lds = big_lds_bytes<BN, kBK, kNS, HD>();
@@ -793,12 +831,13 @@ hipError_t launch_big(const BigArgs& a, hipStream_t st) {
   static std::once_flag once;
   std::call_once(once, [] {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW, TAIL>),
+        reinterpret_cast<const void*>(&gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW, TAIL, GROUP>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   });
-  const int tiles = ((a.N + BN - 1) / BN) * ((a.M + gBM - 1) / gBM) * a.ksplit;
+  const int ntn = GROUP ? a.gct[a.gnum] : (a.N + BN - 1) / BN;
+  const int tiles = ntn * ((a.M + gBM - 1) / gBM) * a.ksplit;
   const int grid = TAIL ? a.tail_full + a.tail_n * a.tail_split : tiles;
-  hipLaunchKernelGGL((gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW, TAIL>),
+  hipLaunchKernelGGL((gemm_big_kernel<BN, kBK, kNS, OUT_F32, HD, gMBW, TAIL, GROUP>),
                      dim3((unsigned)((grid + 7) / 8 * 8)), dim3(2 * gBM / (32 * gMBW) * 64), lds,
                      st, a);
   return hipGetLastError();
@@ -1500,6 +1539,35 @@ hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, v
     }
   }
   return narrow ? launch_big<128, false>(a, st) : launch_big<256, false>(a, st);
+}
+
+int64_t gemm_group_tiles(const int64_t* N, int n, int64_t M) {
+  int64_t cols = 0;
+  for (int i = 0; i < n; ++i) cols += (N[i] + 127) / 128;
+  return cols * ((M + gBM - 1) / gBM);
+}
+
+hipError_t gemm_nt_big_group(const void* A, int64_t lda, const GemmMember* g, int n, int64_t M,
+                             int64_t K, hipStream_t st) {
+  if (n < 1 || n > kMaxGemmGroup) return hipErrorInvalidValue;
+  BigArgs a{static_cast<const uint16_t*>(A), lda, nullptr, 0, nullptr, 0, nullptr, 0, (int)M, 0,
+            (int)K, 2, nullptr, nullptr, 0, nullptr, 0, 1, (int)K, 0};
+  a.gnum = n;
+  a.gct[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    a.gb[i] = static_cast<const uint16_t*>(g[i].B);
+    a.gldb[i] = g[i].ldb;
+    a.gc[i] = g[i].C;
+    a.gldc[i] = g[i].ldc;
+    a.gc2[i] = g[i].C2;
+    a.gldc2[i] = g[i].ldc2;
+    a.gn[i] = (int)g[i].N;
+    a.gct[i + 1] = a.gct[i] + (int)((g[i].N + 127) / 128);
+    // 16-byte fp32 stores and 8-byte copies where the member's rows allow them
+    const bool c2ok = !g[i].C2 || (reinterpret_cast<uintptr_t>(g[i].C2) % 8 == 0 && g[i].ldc2 % 4 == 0);
+    a.gvec[i] = store_width(g[i].C, g[i].ldc, 4) == 2 && c2ok ? 2 : 0;
+  }
+  return launch_big<128, true, 0, false, true>(a, st);
 }
 
 int gemm_split_ranges(int64_t M, int64_t N, int64_t K) {

@@ -370,6 +370,19 @@ __global__ void to_bf16_kernel(const float* src, int64_t lds, uint16_t* dst, int
   }
 }
 
+// Stage 2 on the large-tile GEMM from the bf16 t at tws: y, y_acc += y, or
+// act(y); part (part_bytes) takes a split tail's partials.
+hipError_t big_stage2(const DecodeLinear& d, const uint16_t* tws, int64_t ldtb, float* part,
+                      size_t part_bytes, hipStream_t st) {
+  if (d.y_acc)
+    return gemm_nt_big_acc(tws, ldtb, d.Vt, d.ldv, d.y_acc, d.ld_acc, d.T, d.d_out, d.r, st);
+  if (d.act)
+    return gemm_nt_big_act(tws, ldtb, d.Vt, d.ldv, static_cast<uint16_t*>(d.y), d.ldy, d.act,
+                           static_cast<const uint16_t*>(d.glu), d.ldglu, d.T, d.d_out, d.r, st);
+  return gemm_nt_big(tws, ldtb, d.Vt, d.ldv, d.y, d.ldy, false, nullptr, 0, d.T, d.d_out, d.r, st,
+                     part, part_bytes);
+}
+
 // Both stages on the large-tile GEMM: t (bf16, [T, ldtb]) in the workspace;
 // an fp32 t_io is written by stage 1 beside it, or read by a stage-2-only
 // call and rounded into it first.
@@ -397,16 +410,79 @@ hipError_t prefill_big(const DecodeLinear& d, hipStream_t st) {
                        d.T, d.r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (d.y_acc)
-    return gemm_nt_big_acc(tws, ldtb, d.Vt, d.ldv, d.y_acc, d.ld_acc, d.T, d.d_out, d.r, st);
-  if (d.act)
-    return gemm_nt_big_act(tws, ldtb, d.Vt, d.ldv, static_cast<uint16_t*>(d.y), d.ldy, d.act,
-                           static_cast<const uint16_t*>(d.glu), d.ldglu, d.T, d.d_out, d.r, st);
-  return gemm_nt_big(tws, ldtb, d.Vt, d.ldv, d.y, d.ldy, false, nullptr, 0, d.T, d.d_out, d.r, st,
-                     part, part_bytes);
+  return big_stage2(d, tws, ldtb, part, part_bytes, st);
+}
+
+// Workspace of a grouped call: the control area, each full member's bf16 t
+// and fp32 t (the latter unused when the member has a t_io), then the
+// split-tail scratch of the largest stage 2.
+struct GroupLayout {
+  size_t tb[kMaxGemmGroup], t32[kMaxGemmGroup], part, part_bytes, total;
+};
+GroupLayout group_layout(const DecodeLinear* ds, int n) {
+  GroupLayout L{};
+  size_t off = kCtlAreaBytes;
+  for (int i = 0; i < n; ++i) {
+    if (ds[i].flags != 0) continue;
+    const int64_t ldtb = rup(ds[i].r, 8);
+    L.tb[i] = off;
+    off += (size_t)rup(ds[i].T * ldtb * 2, 256);
+    L.t32[i] = off;
+    off += (size_t)rup(ds[i].T * ldtb * 4, 256);
+  }
+  L.part = off;
+  for (int i = 0; i < n; ++i)
+    if (ds[i].flags == 0) L.part_bytes = std::max(L.part_bytes, gemm_tail_bytes(ds[i].T, ds[i].d_out));
+  L.total = off + L.part_bytes;
+  return L;
 }
 
 }  // namespace
+
+bool prefill_group_ok(const DecodeLinear* ds, int n) {
+  if (n < 2 || n > kMaxGemmGroup || ds[0].T < kBigT) return false;
+  int64_t N[kMaxGemmGroup];
+  for (int i = 0; i < n; ++i) {
+    const DecodeLinear& d = ds[i];
+    if (d.T != ds[0].T || d.x != ds[0].x || d.ldx != ds[0].ldx || d.d_in != ds[0].d_in) return false;
+    if (d.force_fused || d.packed || (d.flags != 0 && d.flags != 1)) return false;
+    if (!gemm_big_supported(d.ldx, d.ldu)) return false;
+    if (d.flags == 1 && !d.t_io) return false;
+    if (d.flags == 0 && (!prefill_accumulates(d) || (d.act && !prefill_act_ok(d)))) return false;
+    N[i] = d.r;
+  }
+  // only where the members alone would leave CUs idle: the group fills at
+  // most one round of tiles
+  return gemm_group_tiles(N, n, ds[0].T) <= 256;
+}
+
+size_t prefill_group_workspace_bytes(const DecodeLinear* ds, int n) {
+  return group_layout(ds, n).total;
+}
+
+hipError_t prefill_group_bf16(const DecodeLinear* ds, int n, hipStream_t st) {
+  if (!prefill_group_ok(ds, n)) return hipErrorInvalidValue;
+  const GroupLayout L = group_layout(ds, n);
+  uint8_t* ws = static_cast<uint8_t*>(ds[0].workspace);
+  GemmMember g[kMaxGemmGroup];
+  for (int i = 0; i < n; ++i) {
+    const DecodeLinear& d = ds[i];
+    if (d.flags == 1) {
+      g[i] = GemmMember{d.Ut, d.ldu, d.t_io, d.ldt, nullptr, 0, d.r};
+    } else {
+      const int64_t ldtb = rup(d.r, 8);
+      float* t32 = d.t_io ? d.t_io : reinterpret_cast<float*>(ws + L.t32[i]);
+      g[i] = GemmMember{d.Ut, d.ldu, t32, d.t_io ? d.ldt : ldtb,
+                        reinterpret_cast<uint16_t*>(ws + L.tb[i]), ldtb, d.r};
+    }
+  }
+  hipError_t e = gemm_nt_big_group(ds[0].x, ds[0].ldx, g, n, ds[0].T, ds[0].d_in, st);
+  for (int i = 0; i < n && e == hipSuccess; ++i)
+    if (ds[i].flags == 0)
+      e = big_stage2(ds[i], reinterpret_cast<const uint16_t*>(ws + L.tb[i]), rup(ds[i].r, 8),
+                     reinterpret_cast<float*>(ws + L.part), L.part_bytes, st);
+  return e;
+}
 
 bool prefill_accumulates(const DecodeLinear& d) {
   return d.T >= kBigT && gemm_big_supported(d.ldx, d.ldu) && gemm_big_supported(rup(d.r, 8), d.ldv);

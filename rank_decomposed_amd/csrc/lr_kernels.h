@@ -88,6 +88,24 @@ hipError_t gemm_nt_big(const void* A, int64_t lda, const void* B, int64_t ldb, v
                        size_t part_bytes = 0);
 // Scratch for the split tail of any bf16 gemm_nt_big of this M, N.
 size_t gemm_tail_bytes(int64_t M, int64_t N);
+// Up to kMaxGemmGroup products that share A in one launch of 128-column
+// tiles, each member over whole tiles of its own: C_i[M, N_i] (fp32) =
+// A . B_i^T, with an optional bf16 copy C2_i.  For stage 1 of linears that
+// read the same input, where each alone has too few tiles to fill the chip.
+constexpr int kMaxGemmGroup = 3;
+struct GemmMember {
+  const void* B;
+  int64_t ldb;
+  float* C;
+  int64_t ldc;
+  uint16_t* C2;  // or null
+  int64_t ldc2;
+  int64_t N;
+};
+hipError_t gemm_nt_big_group(const void* A, int64_t lda, const GemmMember* g, int n, int64_t M,
+                             int64_t K, hipStream_t st);
+// Tiles of such a launch.
+int64_t gemm_group_tiles(const int64_t* N, int n, int64_t M);
 // C (bf16, 16-byte aligned rows) = act(A . B^T): act 1 = silu(G) * (A . B^T)
 // with G bf16 [M, ldg] (16-byte aligned rows), act 2 = relu(A . B^T); the
 // product is rounded to bf16 before the activation.
@@ -166,6 +184,13 @@ bool prefill_accumulates(const DecodeLinear& d);
 bool prefill_fused_supported(const DecodeLinear& d);
 // Whether prefill_linear_bf16 can apply d.act in the stage-2 epilogue.
 bool prefill_act_ok(const DecodeLinear& d);
+// Linears over the same input x on the large-tile path whose stage 1 runs
+// as one grouped launch (2 or 3 of them, each a full linear or stage 1 with
+// t_io, with too few tiles each to fill the chip); then each full member's
+// stage 2 in order (so a member's act may read an earlier member's y).
+bool prefill_group_ok(const DecodeLinear* ds, int n);
+size_t prefill_group_workspace_bytes(const DecodeLinear* ds, int n);
+hipError_t prefill_group_bf16(const DecodeLinear* ds, int n, hipStream_t st);
 
 // fp32, any T: tiled SIMT path.
 size_t f32_workspace_bytes(int64_t T, int64_t r);

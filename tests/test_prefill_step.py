@@ -56,8 +56,9 @@ def test_prefill_attention_head_shapes(H, Hkv, hd):
 
 
 def test_prefill_step_graph_replays_match_eager():
-    # two layers over 1050 tokens of three sequences (split-K stage 1, residual
-    # add and SwiGLU in the GEMM epilogues, tiled attention) captured once:
+    # two layers over 1050 tokens of three sequences (grouped stage 1 of q, k, v
+    # and gate, up, split-K stage 1 of o and down, residual add and SwiGLU in
+    # the GEMM epilogues, tiled attention) captured once:
     # every replay, with eager runs of the same step in between, equals the
     # eager result bit for bit
     cfg = dict(small_cfg(4, 2, 64, d_ffn=384), mlp="swiglu")
